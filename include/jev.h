@@ -1,0 +1,225 @@
+/*
+ * jev.h — shared-prefix candidate scoring on MI355X (gfx950).
+ *
+ * The operation (from the pages this library follows):
+ *   A vision-language decoder reads one image and text prefix.  The prefix is
+ *   run through the decoder ONCE and its key/value cache kept resident
+ *   ("How to Deploy Visual Jev ...", Step 2; "Ochevid Jev-VL 2B", intro).
+ *   Many independent question suffixes are then run as rows of ONE batched
+ *   forward over that cache, and candidate answers are scored straight from
+ *   the logits at each question's last position, with no generation
+ *   (Step 3; Ochevid "Run": one encoding, one shared prefill, one branch call).
+ *   Multi-token candidates of one question share their common history in a
+ *   prefix tree and are scored by the sum of their tokens' log-probabilities
+ *   ("FastJEV", §3.3 Candidate Prefix Sharing).
+ *
+ * Conventions for every call:
+ *   - Every function returns a jev_status; no C++ exception crosses the ABI.
+ *   - All arguments are validated before anything is enqueued.  On an error
+ *     nothing is launched, outputs are untouched and jev_last_error() says why.
+ *   - "dev" pointers are device memory on the current HIP device; "host"
+ *     pointers are ordinary host memory read during the call only.
+ *   - The caller owns every device buffer (weights, prefix KV store,
+ *     workspace, outputs).  Handles keep pointers only; keep buffers alive
+ *     while a handle that names them is used.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream).  Outputs are valid once the stream has synchronised.
+ *     Hot-path calls allocate no device memory and never block on the GPU.
+ *   - A model or prefix may be used from several host threads or streams at
+ *     once provided each call has its own workspace and output buffers.
+ */
+#ifndef JEV_H
+#define JEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t jev_status;
+#define JEV_OK             0
+#define JEV_E_INVALID     -1   /* bad argument: null pointer, out-of-range id/length/count   */
+#define JEV_E_UNSUPPORTED -2   /* well-formed but outside what the kernels implement          */
+#define JEV_E_WORKSPACE   -3   /* workspace or prefix buffer smaller than required            */
+#define JEV_E_HIP         -4   /* a HIP runtime call or kernel launch failed                  */
+
+/* Storage type of weights, embeddings and prefix inputs. */
+#define JEV_F32  0   /* float32 everywhere; the KV store is float32                          */
+#define JEV_BF16 1   /* bfloat16 weights; KV store float16; residual/norm/softmax in float32 */
+
+/* Decoder shape.  Pre-norm layers: RMSNorm -> q/k/v (rotate-half RoPE) ->
+ * grouped-query attention -> o-proj + residual -> RMSNorm -> SwiGLU MLP +
+ * residual; final RMSNorm; untied LM head.  No biases. */
+typedef struct {
+    int32_t n_layers;     /* >= 0                                                       */
+    int32_t hidden;       /* H; multiple of 64 for JEV_BF16                             */
+    int32_t n_q_heads;    /* Hq                                                         */
+    int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0; q head h reads kv head h / (Hq/Hkv)    */
+    int32_t head_dim;     /* D; 128 for JEV_BF16, 64 or 128 for JEV_F32                 */
+    int32_t mlp;          /* I; multiple of 64 for JEV_BF16                             */
+    int32_t vocab;        /* V                                                          */
+    float   rope_theta;   /* angle of pair t at position p: p * theta^(-2t/D)           */
+    float   rms_eps;      /* RMSNorm(x; g) = g * x / sqrt(mean(x^2) + eps)              */
+    int32_t dtype;        /* JEV_F32 or JEV_BF16                                        */
+} jev_config;
+
+/* One layer's parameters, dev pointers of type `dtype`, row-major [out, in]. */
+typedef struct {
+    const void *attn_norm;  /* [H]                    */
+    const void *wq;         /* [Hq*D, H]              */
+    const void *wk;         /* [Hkv*D, H]             */
+    const void *wv;         /* [Hkv*D, H]             */
+    const void *wo;         /* [H, Hq*D]              */
+    const void *mlp_norm;   /* [H]                    */
+    const void *w_gate;     /* [I, H]                 */
+    const void *w_up;       /* [I, H]                 */
+    const void *w_down;     /* [H, I]                 */
+} jev_layer;
+
+typedef struct {
+    const void      *embed;       /* dev [V, H]                              */
+    const void      *final_norm;  /* dev [H]                                 */
+    const void      *lm_head;     /* dev [V, H]                              */
+    const jev_layer *layers;      /* host array [n_layers]; copied at create */
+} jev_weights;
+
+typedef struct jev_model  jev_model;
+typedef struct jev_prefix jev_prefix;
+
+typedef struct {
+    uint64_t prefills;   /* jev_prefill_prefix calls that launched work            */
+    uint64_t forwards;   /* jev_score_suffixes + jev_score_tree calls that launched */
+    uint64_t rows;       /* decoder rows run by those forwards                      */
+    uint64_t launches;   /* kernels launched by this model, all calls               */
+} jev_stats;
+
+/* ---- model ------------------------------------------------------------------ */
+/* Validates the shape and records the weight pointers.  Makes no HIP call. */
+jev_status jev_model_create(const jev_config *cfg, const jev_weights *w, jev_model **out);
+void       jev_model_destroy(jev_model *m);
+jev_status jev_get_stats(const jev_model *m, jev_stats *out);
+
+/* ---- prefix KV store ---------------------------------------------------------
+ * Layout per layer l (element type float16 for JEV_BF16, float32 for JEV_F32),
+ * with Pc = prefix_len rounded up to a multiple of 64:
+ *     K  [Hkv][Pc][D]   rotated keys, row p = prefix position p
+ *     Vt [Hkv][D][Pc]   values, transposed (position fastest)
+ * and layers stacked: store = { K_0, Vt_0, K_1, Vt_1, ... }.  Columns
+ * [prefix_len, Pc) are padding and never read as values.  The buffer is
+ * written by jev_prefill_prefix and only read afterwards ("FastJEV", §3.2:
+ * a read-only shared anchor with separate per-branch working state). */
+size_t     jev_prefix_bytes(const jev_model *m, int32_t prefix_len);
+/* prefix_len in [0, 32768]; kv_bytes >= jev_prefix_bytes(m, prefix_len). */
+jev_status jev_prefix_create(jev_model *m, int32_t prefix_len, void *kv_buf, size_t kv_bytes,
+                             jev_prefix **out);
+void       jev_prefix_destroy(jev_prefix *p);
+
+/* ---- workspace ----------------------------------------------------------------
+ * Upper bound of the workspace bytes for one call on a prefix of prefix_len:
+ *   prefill:          max_rows = prefix_len, max_seqs = 1,  max_targets = 0
+ *   score_suffixes:   max_rows = sum of suffix lengths (<= B*S_max), max_seqs = B,
+ *                     max_targets = B*C_max
+ *   score_tree:       max_rows = rows of the chosen mode (<= Q*C_max*(S_max+K_max)),
+ *                     max_seqs = Q*C_max, max_targets = Q*C_max*K_max
+ * The workspace is scratch: any content on entry, undefined on exit. */
+size_t     jev_workspace_bytes(const jev_model *m, int32_t prefix_len, int32_t max_rows,
+                               int32_t max_seqs, int32_t max_targets);
+
+/* ---- the hot path -------------------------------------------------------------- */
+
+/* Prefill the prefix once ("How to Deploy Visual Jev ...", Step 2: encode the
+ * shared visual prefix and cache its KV; Ochevid intro: decoder image-prefix
+ * prefill happens once).  Rows 0..n_vis-1 are the given visual embeddings,
+ * rows n_vis..P-1 the embedding rows of text_ids; positions 0..P-1; causal.
+ * Writes every layer's rotated K and V into the prefix store.
+ *   vis_embeds  dev  [n_vis, H] of the model dtype (may be NULL if n_vis == 0)
+ *   text_ids    host [n_text], each in [0, V)
+ *   n_vis + n_text must equal the prefix's prefix_len.
+ * Errors: JEV_E_INVALID (counts, ids, pointers), JEV_E_WORKSPACE, JEV_E_HIP. */
+jev_status jev_prefill_prefix(jev_prefix *p, const void *vis_embeds, int32_t n_vis,
+                              const int32_t *text_ids, int32_t n_text,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Score B question suffixes over the prefix in one batched forward
+ * ("How to Deploy Visual Jev ...", Step 3; Ochevid "Run").  Suffix b is
+ * ids[b, 0:lens[b]] at positions P..P+lens[b]-1; it sees every prefix row and
+ * its own earlier rows, never another suffix's.  At its last valid row the
+ * logits z of the n_cands[b] candidates cand_ids[b, :] are read and
+ *     out_logp[b, c] = z_c - logsumexp_{c' < n_cands[b]} z_{c'}
+ * i.e. the log-softmax over the candidate set (Step 3's softmax over the
+ * candidate logits), which equals the full-vocabulary log-probability
+ * renormalised over the candidates.  Slots c >= n_cands[b] are set to -inf.
+ * Duplicate candidate ids are allowed and score equally.
+ *   ids       host [B, S_max] right-padded; pad slots are never read
+ *   lens      host [B], each in [1, S_max]
+ *   cand_ids  host [B, C_max], each used id in [0, V)
+ *   n_cands   host [B], each in [1, C_max]
+ *   out_logp  dev  [B, C_max] float32
+ * B == 0 launches nothing and returns JEV_OK (Ochevid "Run": an all-skipped
+ * request does no work).  Limits: S_max <= 256, C_max <= 64, sum of lens <= 65536.
+ * Errors: JEV_E_INVALID, JEV_E_UNSUPPORTED, JEV_E_WORKSPACE, JEV_E_HIP. */
+jev_status jev_score_suffixes(const jev_prefix *p,
+                              const int32_t *ids, const int32_t *lens, int32_t B, int32_t S_max,
+                              const int32_t *cand_ids, const int32_t *n_cands, int32_t C_max,
+                              float *out_logp, void *ws, size_t ws_bytes, void *stream);
+
+/* Tree layouts of jev_score_tree. */
+#define JEV_TREE_TRIE      0  /* stem + candidate tokens merged on (parent, token)   */
+#define JEV_TREE_STEM_ONLY 1  /* stem shared, each candidate's tokens its own chain  */
+#define JEV_TREE_FLAT      2  /* every candidate its own sequence stem ‖ tokens      */
+
+/* Score multi-token candidates of Q questions ("FastJEV", §3.3).  Question q
+ * has stem stem_ids[q, 0:stem_lens[q]] and candidates
+ * w = cand_tok[q, c, 0:cand_lens[q, c]].  With l_r the full-vocabulary
+ * log-probabilities at row r,
+ *     out_score[q, c] = sum_k l_{row before w_k}[w_k]
+ * over the history prefix ‖ stem ‖ w_0..w_{k-1} of each token, and
+ *     out_norm[q, c]  = out_score[q, c] - logsumexp over the question's candidates.
+ * All three layouts compute the same values; they differ only in how many
+ * rows run.  In the trie layout, equal tokens are merged only when they
+ * follow the same node, so equal tokens after different histories stay
+ * separate, and a candidate's last token is never fed (no row needs it).
+ *   stem_ids  host [Q, S_max], stem_lens host [Q] in [1, S_max]
+ *   cand_tok  host [Q, C_max, K_max], cand_lens host [Q, C_max] in [1, K_max]
+ *   n_cands   host [Q] in [1, C_max]
+ *   out_score dev [Q, C_max] float32; out_norm dev [Q, C_max] float32 or NULL
+ *   Slots c >= n_cands[q] are set to -inf.
+ * Limits: the rows of one question's group (stem + fed candidate tokens) <= 64,
+ * S_max <= 64, K_max <= 64, C_max <= 64.  Q == 0 launches nothing.
+ * Errors: JEV_E_INVALID, JEV_E_UNSUPPORTED, JEV_E_WORKSPACE, JEV_E_HIP. */
+jev_status jev_score_tree(const jev_prefix *p,
+                          const int32_t *stem_ids, const int32_t *stem_lens, int32_t Q, int32_t S_max,
+                          const int32_t *cand_tok, const int32_t *cand_lens, const int32_t *n_cands,
+                          int32_t C_max, int32_t K_max, int32_t mode,
+                          float *out_score, float *out_norm,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Rows the tree layout `mode` runs for this request (host-only planning; no
+ * HIP call).  Useful to size the workspace exactly.  Returns JEV_OK and sets
+ * *rows, *seqs and *targets, or an error as jev_score_tree would. */
+jev_status jev_tree_plan_size(const int32_t *stem_ids, const int32_t *stem_lens, int32_t Q,
+                              int32_t S_max, const int32_t *cand_tok, const int32_t *cand_lens,
+                              const int32_t *n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                              int32_t *rows, int32_t *seqs, int32_t *targets);
+
+/* Host-only introspection of a tree plan (no HIP call), for tests of the
+ * packing: per row its token, its depth below the prefix, its group and its
+ * 64-bit visibility mask over the group's rows; per target (q, c, k) the row
+ * that predicts it.  Arrays are caller-allocated with the sizes reported by
+ * jev_tree_plan_size.  row_mask bit j set means the row sees row
+ * (group start + j). */
+jev_status jev_tree_plan_rows(const int32_t *stem_ids, const int32_t *stem_lens, int32_t Q,
+                              int32_t S_max, const int32_t *cand_tok, const int32_t *cand_lens,
+                              const int32_t *n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                              int32_t *row_tok, int32_t *row_depth, int32_t *row_group,
+                              uint64_t *row_mask, int32_t *target_row);
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char *jev_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JEV_H */

@@ -1,0 +1,534 @@
+// C-ABI of the shared-prefix candidate scorer (see include/jev.h).
+//
+// One forward = embed -> L x [RMSNorm -> q|k|v GEMM -> RoPE/layout ->
+// attention over prefix + own rows -> merge -> o GEMM (+residual) -> RMSNorm
+// -> gate|up GEMM -> SwiGLU -> down GEMM (+residual)] -> readout, all
+// enqueued on the caller's stream.  The only host->device traffic is one copy
+// of the packed request metadata into the workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/jev.h"
+#include "kernels.h"
+#include "plan.h"
+
+using jevp::Plan;
+using jevp::Status;
+
+struct jev_model {
+  jev_config cfg;
+  jev_weights w;
+  std::vector<jev_layer> layers;
+  std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
+};
+
+struct jev_prefix {
+  jev_model* m;
+  int P;
+  int Pc;
+  void* kv;
+  size_t kv_bytes;
+};
+
+static thread_local std::string g_err;
+
+static jev_status fail(jev_status code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+extern "C" const char* jev_last_error(void) { return g_err.c_str(); }
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline int round64(int x) { return (x + 63) & ~63; }
+
+static bool is_bf16(const jev_model* m) { return m->cfg.dtype == JEV_BF16; }
+static size_t kv_elem(const jev_model* m) { return is_bf16(m) ? 2 : 4; }
+static int nqkv(const jev_config& c) { return (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; }
+
+// ---------------------------------------------------------------------------
+// model / prefix
+// ---------------------------------------------------------------------------
+extern "C" jev_status jev_model_create(const jev_config* cfg, const jev_weights* w, jev_model** out) {
+  if (!cfg || !w || !out) return fail(JEV_E_INVALID, "null argument");
+  const jev_config& c = *cfg;
+  if (c.n_layers < 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.mlp <= 0 ||
+      c.vocab <= 0)
+    return fail(JEV_E_INVALID, "non-positive model dimension");
+  if (!(c.rope_theta > 0.f) || !(c.rms_eps >= 0.f)) return fail(JEV_E_INVALID, "bad rope_theta or rms_eps");
+  if (c.dtype != JEV_F32 && c.dtype != JEV_BF16) return fail(JEV_E_INVALID, "unknown dtype");
+  if (c.n_q_heads % c.n_kv_heads) return fail(JEV_E_UNSUPPORTED, "n_q_heads not a multiple of n_kv_heads");
+  if (c.dtype == JEV_BF16 && (c.hidden % 64 || c.mlp % 64))
+    return fail(JEV_E_UNSUPPORTED, "bf16 models need hidden and mlp multiples of 64");
+  if (c.dtype == JEV_BF16 && c.head_dim != 128) return fail(JEV_E_UNSUPPORTED, "bf16 models need head_dim 128");
+  if (c.dtype == JEV_F32 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(JEV_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!w->embed || !w->final_norm || !w->lm_head || (c.n_layers > 0 && !w->layers))
+    return fail(JEV_E_INVALID, "null weight pointer");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const jev_layer& L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up || !L.w_down)
+      return fail(JEV_E_INVALID, "null pointer in layer " + std::to_string(l));
+  }
+  jev_model* m = new jev_model();
+  m->cfg = c;
+  m->w = *w;
+  m->layers.assign(w->layers, w->layers + c.n_layers);
+  m->w.layers = m->layers.data();
+  *out = m;
+  return JEV_OK;
+}
+
+extern "C" void jev_model_destroy(jev_model* m) { delete m; }
+
+extern "C" jev_status jev_get_stats(const jev_model* m, jev_stats* out) {
+  if (!m || !out) return fail(JEV_E_INVALID, "null argument");
+  out->prefills = m->prefills.load();
+  out->forwards = m->forwards.load();
+  out->rows = m->rows.load();
+  out->launches = m->launches.load();
+  return JEV_OK;
+}
+
+extern "C" size_t jev_prefix_bytes(const jev_model* m, int32_t prefix_len) {
+  if (!m || prefix_len < 0) return 0;
+  const jev_config& c = m->cfg;
+  const size_t Pc = (size_t)round64(prefix_len);
+  return (size_t)c.n_layers * 2 * c.n_kv_heads * Pc * c.head_dim * kv_elem(m);
+}
+
+extern "C" jev_status jev_prefix_create(jev_model* m, int32_t prefix_len, void* kv_buf, size_t kv_bytes,
+                                        jev_prefix** out) {
+  if (!m || !out) return fail(JEV_E_INVALID, "null argument");
+  if (prefix_len < 0) return fail(JEV_E_INVALID, "prefix_len < 0");
+  if (prefix_len > jevp::kMaxPrefix) return fail(JEV_E_UNSUPPORTED, "prefix_len > 32768");
+  const size_t need = jev_prefix_bytes(m, prefix_len);
+  if (need > 0 && !kv_buf) return fail(JEV_E_INVALID, "null kv_buf");
+  if (kv_bytes < need) return fail(JEV_E_WORKSPACE, "kv buffer smaller than jev_prefix_bytes");
+  jev_prefix* p = new jev_prefix();
+  p->m = m;
+  p->P = prefix_len;
+  p->Pc = round64(prefix_len);
+  p->kv = kv_buf;
+  p->kv_bytes = kv_bytes;
+  *out = p;
+  return JEV_OK;
+}
+
+extern "C" void jev_prefix_destroy(jev_prefix* p) { delete p; }
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxAttnSplits = 4;                     // prefix key splits (+1 own-rows split)
+constexpr size_t kGemmPartFloats = 640ull * 128 * 128; // bound of split-K partials (see gemm_bf16_splits)
+
+struct Layout {
+  // metadata (staged from the host in one copy)
+  size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, meta_end;
+  // float buffers
+  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, z, lse_rows, logits;
+  size_t total;
+  int Tc;
+};
+
+Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_mask, bool need_logits) {
+  const jev_config& c = m->cfg;
+  const bool bf = is_bf16(m);
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.tok = take(4ull * T);
+  L.pos = take(4ull * T);
+  L.seq_start = take(4ull * T);
+  L.read_rows = take(4ull * R);
+  L.tgt_ridx = take(4ull * NT);
+  L.tgt_tok = take(4ull * NT);
+  L.out_n = take(4ull * NG);
+  L.mask = take(has_mask ? 8ull * T : 0);
+  L.meta_end = o;
+  const int HqD = c.n_q_heads * c.head_dim;
+  const int wide = std::max(std::max(c.hidden, HqD), c.mlp);
+  const int bigw = std::max(nqkv(c), 2 * c.mlp);
+  L.Tc = round64(std::max(T, 1));
+  const size_t e = kv_elem(m);
+  L.x = take(4ull * T * c.hidden);
+  L.act = take(4ull * T * wide);
+  L.big = take(4ull * T * bigw);
+  L.q = take(e * T * HqD);
+  L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
+  L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
+  L.o_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * HqD : 0);
+  L.lse_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * c.n_q_heads : 0);
+  L.gpart = take(bf ? 4ull * kGemmPartFloats : 0);
+  L.h = take(4ull * R * c.hidden);
+  L.z = take(4ull * NT);
+  L.lse_rows = take(4ull * R);
+  L.logits = take(need_logits ? 4ull * R * c.vocab : 0);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+extern "C" size_t jev_workspace_bytes(const jev_model* m, int32_t prefix_len, int32_t max_rows, int32_t max_seqs,
+                                      int32_t max_targets) {
+  if (!m || prefix_len < 0 || max_rows < 0 || max_seqs < 0 || max_targets < 0) return 0;
+  const int R = std::min(max_rows, max_targets);
+  return make_layout(m, max_rows, R, max_targets, max_seqs, true, max_targets > 0).total;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+namespace {
+enum class Mode { Prefill, Score, Tree };
+
+#define HIP_OK(expr)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess) return fail(JEV_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+struct Forward {
+  const jev_prefix* pf;
+  const jev_model* m;
+  const jev_config& c;
+  const Plan& plan;
+  const Layout& L;
+  void* ws;
+  hipStream_t s;
+  Mode mode;
+  int launches = 0;
+
+  Forward(const jev_prefix* p, const Plan& pl, const Layout& lay, void* w, hipStream_t st, Mode md)
+      : pf(p), m(p->m), c(p->m->cfg), plan(pl), L(lay), ws(w), s(st), mode(md) {}
+
+  // layer l's K / Vt in the prefix store
+  char* store_k(int l) const {
+    const size_t per = (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m);
+    return static_cast<char*>(pf->kv) + (size_t)l * 2 * per;
+  }
+  char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m); }
+
+  jev_status gemm(const float* A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
+                  const void* w2, int n2, float* C, int ldc, int accum) {
+    const int N = n0 + n1 + n2;
+    if (is_bf16(m)) {
+      GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
+      const int splits = jevk_splits(M, N, K);
+      HIP_OK(launch_gemm_bf16(A, lda, M, K, sg, N, C, ldc, accum, splits, at<float>(ws, L.gpart), s, &launches));
+    } else {
+      GemmSegsF sg{{(const float*)w0, (const float*)w1, (const float*)w2}, {n0, n0 + n1, N}};
+      HIP_OK(launch_gemm_f32(A, lda, M, K, sg, N, C, ldc, accum, s));
+      ++launches;
+    }
+    return JEV_OK;
+  }
+
+  static int jevk_splits(int M, int N, int K) {
+    int sp = gemm_bf16_splits(M, N, K);
+    while (sp > 1 && (size_t)sp * M * N > kGemmPartFloats) --sp;
+    return sp;
+  }
+
+  jev_status run(const void* vis, int n_vis) {
+    const int T = plan.T;
+    const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
+    const int HqD = Hq * D, NQKV = nqkv(c);
+    const bool bf = is_bf16(m);
+    const int wide = std::max(std::max(H, HqD), I);
+    float* x = at<float>(ws, L.x);
+    float* act = at<float>(ws, L.act);
+    float* big = at<float>(ws, L.big);
+    const int* tok = at<int>(ws, L.tok);
+    const int* pos = at<int>(ws, L.pos);
+    const int* seq_start = at<int>(ws, L.seq_start);
+    const uint64_t* mask = plan.mask.empty() ? nullptr : at<uint64_t>(ws, L.mask);
+    const double log2_theta = std::log2((double)c.rope_theta);
+    const int P = (mode == Mode::Prefill) ? 0 : pf->P;
+
+    HIP_OK(launch_embed(bf, m->w.embed, tok, T, H, vis, n_vis, x, s));
+    ++launches;
+
+    // attention split plan (bf16 path)
+    int n_split = 0, split_len = 0;
+    if (bf && P > 0) {
+      const long base = (long)((c.n_q_heads / Hkv) * (long)T + 127) / 128 * Hkv;
+      n_split = (int)std::min<long>(kMaxAttnSplits, std::max<long>(1, (512 + base - 1) / base));
+      n_split = std::min(n_split, (P + 255) / 256);
+      n_split = std::max(n_split, 1);
+      split_len = ((P + n_split - 1) / n_split + 63) / 64 * 64;
+      n_split = (P + split_len - 1) / split_len;
+    }
+
+    for (int l = 0; l < c.n_layers; ++l) {
+      const jev_layer& W = m->layers[l];
+      const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
+      HIP_OK(launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, act, wide, s));
+      ++launches;
+      if (jev_status st = gemm(act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0)) return st;
+      // K / V destination: the prefix store (prefill) or the workspace (scoring)
+      void *kdst, *vdst;
+      int kld;
+      if (mode == Mode::Prefill) {
+        kdst = store_k(l);
+        vdst = store_vt(l);
+        kld = pf->Pc;
+      } else {
+        kdst = at<char>(ws, L.ks);
+        vdst = at<char>(ws, L.vts);
+        kld = L.Tc;
+      }
+      HIP_OK(launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q), kdst, kld, 0, s));
+      HIP_OK(launch_v_transpose(bf, big + (size_t)(Hq + Hkv) * D, NQKV, T, Hkv * D, vdst, kld, 0, s));
+      launches += 2;
+      if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
+
+      if (bf) {
+        AttnArgs a{};
+        a.q = at<_Float16>(ws, L.q);
+        a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+        if (P > 0) {
+          a.kp = reinterpret_cast<const _Float16*>(store_k(l));
+          a.vtp = reinterpret_cast<const _Float16*>(store_vt(l));
+        }
+        a.P = P; a.ldp = pf->Pc;
+        a.ks = static_cast<const _Float16*>(kdst);
+        a.vts = static_cast<const _Float16*>(vdst);
+        a.lds = kld;
+        a.seq_start = seq_start; a.mask = mask;
+        a.n_split = n_split; a.split_len = split_len;
+        a.o_part = at<float>(ws, L.o_part);
+        a.lse_part = at<float>(ws, L.lse_part);
+        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+        HIP_OK(launch_attn_f16(a, s));
+        HIP_OK(launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act, s));
+        launches += 2;
+      } else {
+        AttnArgsF a{};
+        a.q = at<float>(ws, L.q);
+        a.T = T; a.Hq = Hq; a.G = Hq / Hkv;
+        if (P > 0) {
+          a.kp = reinterpret_cast<const float*>(store_k(l));
+          a.vtp = reinterpret_cast<const float*>(store_vt(l));
+        }
+        a.P = P; a.ldp = pf->Pc;
+        a.ks = static_cast<const float*>(kdst);
+        a.vts = static_cast<const float*>(vdst);
+        a.lds = kld;
+        a.seq_start = seq_start; a.mask = mask;
+        a.scale = (float)(1.0 / std::sqrt((double)D));
+        a.o = act;
+        HIP_OK(launch_attn_f32(a, D, s));
+        ++launches;
+      }
+      // note: act now holds o [T][HqD] with row stride HqD
+      if (jev_status st = gemm(act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
+      HIP_OK(launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, act, wide, s));
+      ++launches;
+      if (jev_status st = gemm(act, wide, T, H, W.w_gate, I, W.w_up, I, nullptr, 0, big, 2 * I, 0)) return st;
+      HIP_OK(launch_silu_mul(big, T, I, act, s));   // gate|up [T][2I] -> u [T][I]
+      ++launches;
+      if (jev_status st = gemm(act, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
+    }
+    return JEV_OK;
+  }
+
+  jev_status readout(float* out_a, float* out_b) {
+    const int H = c.hidden;
+    const bool bf = is_bf16(m);
+    const int R = (int)plan.read_rows.size();
+    const int NT = (int)plan.tgt_tok.size();
+    float* h = at<float>(ws, L.h);
+    float* z = at<float>(ws, L.z);
+    HIP_OK(launch_rmsnorm(bf, at<float>(ws, L.x), H, at<int>(ws, L.read_rows), R, H, m->w.final_norm, c.rms_eps,
+                          h, H, s));
+    HIP_OK(launch_target_logits(bf, h, H, m->w.lm_head, at<int>(ws, L.tgt_ridx), at<int>(ws, L.tgt_tok), NT, z, s));
+    launches += 2;
+    if (mode == Mode::Score) {
+      const int B = (int)plan.out_n.size();
+      HIP_OK(launch_cand_logsoftmax(z, at<int>(ws, L.out_n), B, NT / std::max(B, 1), out_a, s));
+      ++launches;
+    } else {
+      float* logits = at<float>(ws, L.logits);
+      if (jev_status st = gemm(h, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits, c.vocab, 0))
+        return st;
+      HIP_OK(launch_row_lse(logits, c.vocab, R, at<float>(ws, L.lse_rows), s));
+      ++launches;
+      return JEV_OK;
+    }
+    return JEV_OK;
+  }
+};
+
+// Copy the plan's metadata into the workspace with one host->device copy.
+jev_status stage_meta(const Plan& p, const Layout& L, void* ws, hipStream_t s) {
+  std::vector<char> buf(L.meta_end, 0);
+  auto put = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(buf.data() + off, src, bytes);
+  };
+  put(L.tok, p.tok.data(), 4 * p.tok.size());
+  put(L.pos, p.pos.data(), 4 * p.pos.size());
+  put(L.seq_start, p.seq_start.data(), 4 * p.seq_start.size());
+  put(L.read_rows, p.read_rows.data(), 4 * p.read_rows.size());
+  put(L.tgt_ridx, p.tgt_ridx.data(), 4 * p.tgt_ridx.size());
+  put(L.tgt_tok, p.tgt_tok.data(), 4 * p.tgt_tok.size());
+  put(L.out_n, p.out_n.data(), 4 * p.out_n.size());
+  put(L.mask, p.mask.data(), 8 * p.mask.size());
+  HIP_OK(hipMemcpyAsync(ws, buf.data(), L.meta_end, hipMemcpyHostToDevice, s));
+  return JEV_OK;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// entry points
+// ---------------------------------------------------------------------------
+extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, int32_t n_vis,
+                                         const int32_t* text_ids, int32_t n_text, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  if (!p) return fail(JEV_E_INVALID, "null prefix");
+  const jev_model* m = p->m;
+  if (n_vis < 0 || n_text < 0) return fail(JEV_E_INVALID, "negative counts");
+  if (n_vis + n_text != p->P) return fail(JEV_E_INVALID, "n_vis + n_text must equal prefix_len");
+  if (n_vis > 0 && !vis_embeds) return fail(JEV_E_INVALID, "null vis_embeds");
+  if (n_text > 0 && !text_ids) return fail(JEV_E_INVALID, "null text_ids");
+  for (int i = 0; i < n_text; ++i)
+    if (text_ids[i] < 0 || text_ids[i] >= m->cfg.vocab) return fail(JEV_E_INVALID, "text id out of range");
+  if (p->P == 0 || m->cfg.n_layers == 0) return JEV_OK;
+  Plan plan;
+  plan.T = p->P;
+  plan.n_groups = 1;
+  plan.tok.assign(p->P, 0);
+  for (int i = 0; i < n_text; ++i) plan.tok[n_vis + i] = text_ids[i];
+  plan.pos.resize(p->P);
+  for (int i = 0; i < p->P; ++i) plan.pos[i] = i;
+  plan.seq_start.assign(p->P, 0);
+  const Layout L = make_layout(m, plan.T, 0, 0, 1, false, false);
+  if (!ws) return fail(JEV_E_INVALID, "null workspace");
+  if (ws_bytes < L.total)
+    return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jev_status st = stage_meta(plan, L, ws, s)) return st;
+  Forward f(p, plan, L, ws, s, Mode::Prefill);
+  jev_status st = f.run(vis_embeds, n_vis);
+  const_cast<jev_model*>(m)->launches += f.launches;
+  if (st) return st;
+  const_cast<jev_model*>(m)->prefills++;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
+                                         int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands,
+                                         int32_t C_max, float* out_logp, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(JEV_E_INVALID, "null prefix");
+  jev_model* m = p->m;
+  Plan plan;
+  Status st = jevp::plan_suffixes(p->P, m->cfg.vocab, ids, lens, B, S_max, cand_ids, n_cands, C_max, &plan);
+  if (!st.ok()) return fail(st.code, st.msg);
+  if (B == 0) return JEV_OK;
+  if (!out_logp) return fail(JEV_E_INVALID, "null out_logp");
+  const Layout L = make_layout(m, plan.T, (int)plan.read_rows.size(), (int)plan.tgt_tok.size(),
+                               (int)plan.out_n.size(), false, false);
+  if (!ws) return fail(JEV_E_INVALID, "null workspace");
+  if (ws_bytes < L.total)
+    return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jev_status e = stage_meta(plan, L, ws, s)) return e;
+  Forward f(p, plan, L, ws, s, Mode::Score);
+  jev_status e = f.run(nullptr, 0);
+  if (!e) e = f.readout(out_logp, nullptr);
+  m->launches += f.launches;
+  if (e) return e;
+  m->forwards++;
+  m->rows += (uint64_t)plan.T;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens,
+                                     int32_t Q, int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens,
+                                     const int32_t* n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                                     float* out_score, float* out_norm, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(JEV_E_INVALID, "null prefix");
+  jev_model* m = p->m;
+  Plan plan;
+  Status st = jevp::plan_tree(p->P, m->cfg.vocab, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands,
+                              C_max, K_max, mode, &plan);
+  if (!st.ok()) return fail(st.code, st.msg);
+  if (Q == 0) return JEV_OK;
+  if (!out_score) return fail(JEV_E_INVALID, "null out_score");
+  const int R = (int)plan.read_rows.size();
+  const int NT = (int)plan.tgt_tok.size();
+  const Layout L = make_layout(m, plan.T, R, NT, (int)plan.out_n.size(), true, true);
+  if (!ws) return fail(JEV_E_INVALID, "null workspace");
+  if (ws_bytes < L.total)
+    return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jev_status e = stage_meta(plan, L, ws, s)) return e;
+  Forward f(p, plan, L, ws, s, Mode::Tree);
+  jev_status e = f.run(nullptr, 0);
+  if (!e) e = f.readout(nullptr, nullptr);
+  if (!e) {
+    hipError_t he = launch_tree_finalize(at<float>(ws, L.z), at<float>(ws, L.lse_rows), at<int>(ws, L.tgt_ridx),
+                                         at<int>(ws, L.tgt_tok), at<int>(ws, L.out_n), Q, C_max, K_max, out_score,
+                                         out_norm, s);
+    ++f.launches;
+    if (he != hipSuccess) e = fail(JEV_E_HIP, std::string("tree_finalize: ") + hipGetErrorString(he));
+  }
+  m->launches += f.launches;
+  if (e) return e;
+  m->forwards++;
+  m->rows += (uint64_t)plan.T;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_tree_plan_size(const int32_t* stem_ids, const int32_t* stem_lens, int32_t Q,
+                                         int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens,
+                                         const int32_t* n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                                         int32_t* rows, int32_t* seqs, int32_t* targets) {
+  if (!rows || !seqs || !targets) return fail(JEV_E_INVALID, "null output");
+  Plan plan;
+  Status st = jevp::plan_tree(0, -1, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands, C_max, K_max,
+                              mode, &plan);
+  if (!st.ok()) return fail(st.code, st.msg);
+  *rows = plan.T;
+  *seqs = plan.n_groups;
+  *targets = (int32_t)plan.tgt_tok.size();
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_tree_plan_rows(const int32_t* stem_ids, const int32_t* stem_lens, int32_t Q,
+                                         int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens,
+                                         const int32_t* n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                                         int32_t* row_tok, int32_t* row_depth, int32_t* row_group,
+                                         uint64_t* row_mask, int32_t* target_row) {
+  if (!row_tok || !row_depth || !row_group || !row_mask || !target_row) return fail(JEV_E_INVALID, "null output");
+  Plan plan;
+  Status st = jevp::plan_tree(0, -1, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands, C_max, K_max,
+                              mode, &plan);
+  if (!st.ok()) return fail(st.code, st.msg);
+  for (int r = 0; r < plan.T; ++r) {
+    row_tok[r] = plan.tok[r];
+    row_depth[r] = plan.depth[r];
+    row_group[r] = plan.group[r];
+    row_mask[r] = plan.mask[r];
+  }
+  for (size_t i = 0; i < plan.tgt_tok.size(); ++i)
+    target_row[i] = plan.tgt_tok[i] >= 0 ? plan.read_rows[plan.tgt_ridx[i]] : -1;
+  return JEV_OK;
+}

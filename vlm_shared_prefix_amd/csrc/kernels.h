@@ -1,0 +1,75 @@
+// Host-side declarations of the device kernels' launchers (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Up to three weight row segments forming one GEMM's N axis (e.g. wq | wk | wv).
+// Segment s covers output columns [n_end[s-1], n_end[s]) (n_end[-1] = 0).
+struct GemmSegs {
+  const uint16_t* w[3];
+  int n_end[3];
+};
+struct GemmSegsF {
+  const float* w[3];
+  int n_end[3];
+};
+
+// float16 MFMA attention (head_dim 128).
+struct AttnArgs {
+  const _Float16* q;       // [T][Hq][128]
+  int T, Hq, Hkv, G;
+  const _Float16* kp;      // prefix K  [Hkv][ldp][128]
+  const _Float16* vtp;     // prefix Vt [Hkv][128][ldp]
+  int P, ldp;
+  const _Float16* ks;      // own K  [Hkv][lds][128]
+  const _Float16* vts;     // own Vt [Hkv][128][lds]
+  int lds;
+  const int* seq_start;    // [T] first row of the row's sequence / group
+  const uint64_t* mask;    // [T] visibility over the group (nullptr: causal)
+  int n_split, split_len;  // prefix key splits
+  float* o_part;           // [n_split+1][T][Hq][128]
+  float* lse_part;         // [n_split+1][T][Hq]   (log2 units)
+  float scale_log2;        // log2(e) / sqrt(128)
+};
+
+// float32 attention (head_dim 64 or 128).
+struct AttnArgsF {
+  const float* q;          // [T][Hq][D]
+  int T, Hq, G;
+  const float* kp;
+  const float* vtp;
+  int P, ldp;
+  const float* ks;
+  const float* vts;
+  int lds;
+  const int* seq_start;
+  const uint64_t* mask;
+  float scale;             // 1 / sqrt(D)
+  float* o;                // [T][Hq*D]
+};
+
+hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, int n_vis,
+                        float* x, hipStream_t s);
+hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
+                          float eps, float* y, int ldy, hipStream_t s);
+int gemm_bf16_splits(int M, int N, int K);
+hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
+                            int ldc, int accum, int splits, float* part, hipStream_t s, int* launches);
+hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
+                           int accum, hipStream_t s);
+hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv, int D, const int* pos,
+                          double log2_theta, void* q_out, void* k_out, int ldk, int row0, hipStream_t s);
+hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int HD, void* vt, int ldv, int col0,
+                              hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, float* o,
+                             hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);
+hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, hipStream_t s);
+hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,
+                                int NT, float* z, hipStream_t s);
+hipError_t launch_cand_logsoftmax(const float* z, const int* n_cands, int B, int C, float* out, hipStream_t s);
+hipError_t launch_row_lse(const float* logits, int V, int R, float* lse, hipStream_t s);
+hipError_t launch_tree_finalize(const float* z, const float* lse_rows, const int* ridx, const int* tok,
+                                const int* n_cands, int Q, int C, int K, float* score, float* norm,
+                                hipStream_t s);

@@ -1,0 +1,912 @@
+// Device kernels for shared-prefix candidate scoring on gfx950 (CDNA4).
+//
+// Precision scheme (bf16 models): weights bfloat16; activations and the
+// residual stream float32; GEMM activations enter the matrix cores as two
+// bfloat16 terms (hi + lo, hi = bf16(a), lo = bf16(a - hi)), so a GEMM is
+// W·hi + W·lo with float32 accumulation; q/k/v and the KV store are float16
+// and attention runs on float16 MFMA with float32 softmax; norms, softmax
+// merge and readout are float32.  float32 models run every step in float32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "kernels.h"
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+#define NEG_INF (-__builtin_inff())
+
+namespace jevk {
+
+// ----------------------------------------------------------------------------
+// scalar helpers
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round-to-nearest-even float32 -> bfloat16 bits (finite inputs)
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+template <typename WT> __device__ __forceinline__ float ldw(const WT* p, size_t i);
+template <> __device__ __forceinline__ float ldw<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ldw<u16>(const u16* p, size_t i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// block of 256 threads: sum over the block, result broadcast to all threads
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// ----------------------------------------------------------------------------
+// K1: embedding rows.  Row t < n_vis copies vis[t]; other rows gather E[tok[t]].
+// ----------------------------------------------------------------------------
+template <typename WT>
+__global__ void __launch_bounds__(256) embed_rows(const WT* __restrict__ E, const int* __restrict__ tok, int T,
+                                                  int H, const WT* __restrict__ vis, int n_vis,
+                                                  float* __restrict__ x) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const WT* src = (t < n_vis) ? vis + (size_t)t * H : E + (size_t)tok[t] * H;
+  float* dst = x + (size_t)t * H;
+  for (int i = threadIdx.x; i < H; i += 256) dst[i] = ldw(src, i);
+}
+
+// ----------------------------------------------------------------------------
+// K2: RMSNorm, y[i] = g * x[row_i] / sqrt(mean(x^2) + eps), one block per row.
+// ----------------------------------------------------------------------------
+template <typename WT>
+__global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x, int ldx,
+                                                    const int* __restrict__ rows, int n_rows, int H,
+                                                    const WT* __restrict__ g, float eps,
+                                                    float* __restrict__ y, int ldy) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  if (i >= n_rows) return;
+  const int src = rows ? rows[i] : i;
+  const float* xr = x + (size_t)src * ldx;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += 256) { float v = xr[k]; ss += v * v; }
+  ss = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  float* yr = y + (size_t)i * ldy;
+  for (int k = threadIdx.x; k < H; k += 256) yr[k] = ldw(g, k) * (xr[k] * r);
+}
+
+// ----------------------------------------------------------------------------
+// K3 (bf16 models): Y[M,N] = A[M,K] · W[N,K]^T on MFMA 32x32x16 bf16, with the
+// float32 activation split into bf16 hi + lo on its way into LDS.
+// Block tile 128x128, K step 64, 4 waves in a 2x2 arrangement (64x64 each).
+// W is described by up to three row segments (e.g. wq | wk | wv).
+// Grid: 1-D, rounded up to a multiple of 8; the linear block id is remapped so
+// that blocks dispatched to the same XCD share a W tile (same N tile and K
+// split, different M tiles) and reuse it from that XCD's L2.
+// ----------------------------------------------------------------------------
+#define GBM 128
+#define GBN 128
+#define GBK 64
+#define GLD (GBK + 8)   // LDS row stride in bf16 elements (144 B: conflict-free 16 B reads)
+
+__device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
+  if (n < s.n_end[0]) return s.w[0] + (size_t)n * K;
+  if (n < s.n_end[1]) return s.w[1] + (size_t)(n - s.n_end[0]) * K;
+  return s.w[2] + (size_t)(n - s.n_end[1]) * K;
+}
+
+__global__ void __launch_bounds__(256, 2) gemm_bf16s(const float* __restrict__ A, int lda, int M, int K,
+                                                     GemmSegs seg, int N, int m_tiles, int n_tiles,
+                                                     int splits, int k_chunk, float* __restrict__ C,
+                                                     int ldc, size_t split_stride, int accum) {
+  __shared__ __attribute__((aligned(16))) u16 sAh[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) u16 sAl[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) u16 sW[GBN * GLD];
+
+  const int nb = m_tiles * n_tiles * splits;
+  const int per = gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (v >= nb) return;
+  const int mt = v % m_tiles;
+  const int rest = v / m_tiles;
+  const int ks = rest % splits;
+  const int nt = rest / splits;
+  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int kbeg = ks * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ql = lane & 31, hl = lane >> 5;
+  const bool wave_active = (m0 + wm * 64) < M;
+
+  // global -> register staging
+  float4 ra[8];
+  uint4 rw[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 4, c4 = idx & 15;
+      const int gm = m0 + row;
+      ra[i] = (gm < M) ? *reinterpret_cast<const float4*>(A + (size_t)gm * lda + k0 + c4 * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int nr = idx >> 3, c8 = idx & 7;
+      const int gn = n0 + nr;
+      rw[i] = (gn < N) ? *reinterpret_cast<const uint4*>(seg_row(seg, gn, K) + k0 + c8 * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 4, c4 = idx & 15;
+      const float f[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+      u16 h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = f32_to_bf16(f[j]);
+        l[j] = f32_to_bf16(f[j] - bf16_to_f32(h[j]));
+      }
+      uint2 hv = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      uint2 lv = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+      *reinterpret_cast<uint2*>(&sAh[row * GLD + c4 * 4]) = hv;
+      *reinterpret_cast<uint2*>(&sAl[row * GLD + c4 * 4]) = lv;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int nr = idx >> 3, c8 = idx & 7;
+      *reinterpret_cast<uint4*>(&sW[nr * GLD + c8 * 8]) = rw[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (kbeg < kend) {
+    gload(kbeg);
+    sstore();
+    __syncthreads();
+    for (int k0 = kbeg; k0 < kend; k0 += GBK) {
+      const bool more = (k0 + GBK) < kend;
+      if (more) gload(k0 + GBK);
+      if (wave_active) {
+#pragma unroll
+        for (int kk = 0; kk < GBK / 16; ++kk) {
+          bf16x8 ah[2], al[2], bw[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int r = wm * 64 + i * 32 + ql;
+            ah[i] = *reinterpret_cast<const bf16x8*>(&sAh[r * GLD + kk * 16 + hl * 8]);
+            al[i] = *reinterpret_cast<const bf16x8*>(&sAl[r * GLD + kk * 16 + hl * 8]);
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c = wn * 64 + j * 32 + ql;
+            bw[j] = *reinterpret_cast<const bf16x8*>(&sW[c * GLD + kk * 16 + hl * 8]);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+            }
+        }
+      }
+      __syncthreads();
+      if (more) {
+        sstore();
+        __syncthreads();
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + ql;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (row < M) {
+          float* p = Cb + (size_t)row * ldc + col;
+          *p = add ? (*p + acc[i][j][r]) : acc[i][j][r];
+        }
+      }
+    }
+}
+
+// Deterministic split-K reduction: out = (accum ? out : 0) + sum_s part[s] (fixed order).
+__global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ part, size_t split_stride,
+                                                     int splits, int M, int N, int ldp,
+                                                     float* __restrict__ out, int ldo, int accum) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[k * split_stride + (size_t)m * ldp + n];
+  float* o = out + (size_t)m * ldo + n;
+  *o = accum ? (*o + s) : s;
+}
+
+// ----------------------------------------------------------------------------
+// K3 (float32 models): tiled VALU GEMM, 64x64 tile, 4x4 outputs per thread.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ const float* seg_row_f(const GemmSegsF& s, int n, int K) {
+  if (n < s.n_end[0]) return s.w[0] + (size_t)n * K;
+  if (n < s.n_end[1]) return s.w[1] + (size_t)(n - s.n_end[0]) * K;
+  return s.w[2] + (size_t)(n - s.n_end[1]) * K;
+}
+
+__global__ void __launch_bounds__(256) gemm_f32(const float* __restrict__ A, int lda, int M, int K,
+                                                GemmSegsF seg, int N, float* __restrict__ C, int ldc,
+                                                int accum) {
+  __shared__ float sA[16][64 + 1];
+  __shared__ float sB[16][64 + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;     // 0..1023: row = idx/16, k = idx%16
+      const int r = idx >> 4, kk = idx & 15;
+      const int gm = m0 + r, gk = k0 + kk, gn = n0 + r;
+      sA[kk][r] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : 0.f;
+      sB[kk][r] = (gn < N && gk < K) ? seg_row_f(seg, gn, K)[gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sA[kk][ty * 4 + i]; b[i] = sB[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= N) continue;
+      float* p = C + (size_t)row * ldc + col;
+      *p = accum ? (*p + acc[i][j]) : acc[i][j];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// RoPE + layout: q/k from the fused projection output [T][(Hq+2Hkv)*D] are
+// rotated at their row's position (rotate-half: pair t with t + D/2, angle
+// pos * theta^(-2t/D), angle and sin/cos in float64) and written as
+//   Q  [T][Hq][D]         (query rows, token-major)
+//   K  [Hkv][ldk][D]      at row `row0 + t`
+// V is written transposed by v_transpose below.
+// ----------------------------------------------------------------------------
+template <typename OT> __device__ __forceinline__ OT cvt_out(float v);
+template <> __device__ __forceinline__ f16 cvt_out<f16>(float v) { return (f16)v; }
+template <> __device__ __forceinline__ float cvt_out<float>(float v) { return v; }
+
+template <typename OT>
+__global__ void __launch_bounds__(256) rope_qk(const float* __restrict__ qkv, int T, int Hq, int Hkv, int D,
+                                               const int* __restrict__ pos, double log2_theta,
+                                               OT* __restrict__ q_out, OT* __restrict__ k_out, int ldk,
+                                               int row0) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const int half = D >> 1;
+  const int nh = Hq + Hkv;
+  const double p = (double)pos[t];
+  const float* src = qkv + (size_t)t * (size_t)(Hq + 2 * Hkv) * D;
+  for (int idx = threadIdx.x; idx < nh * half; idx += 256) {
+    const int h = idx / half, i = idx % half;
+    const double inv_freq = exp2(-(2.0 * i / (double)D) * log2_theta);
+    double sd, cd;
+    sincos(p * inv_freq, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    const float a = src[h * D + i], b = src[h * D + i + half];
+    const float ra = a * c - b * s;
+    const float rb = b * c + a * s;
+    if (h < Hq) {
+      OT* d = q_out + ((size_t)t * Hq + h) * D;
+      d[i] = cvt_out<OT>(ra);
+      d[i + half] = cvt_out<OT>(rb);
+    } else {
+      OT* d = k_out + ((size_t)(h - Hq) * ldk + row0 + t) * D;
+      d[i] = cvt_out<OT>(ra);
+      d[i + half] = cvt_out<OT>(rb);
+    }
+  }
+}
+
+// V [T][Hkv*D] (a column slice of the projection output) -> Vt [Hkv][D][ldv] at column col0 + t.
+// 64x64 tile transpose through LDS so both the read and the write are coalesced.
+template <typename OT>
+__global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src, int lds, int T, int HD,
+                                                   OT* __restrict__ vt, int ldv, int col0) {
+  __shared__ float tile[64][65];
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r, c = c0 + tx;
+    tile[r][tx] = (t < T && c < HD) ? src[(size_t)t * lds + c] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int c = c0 + r, t = t0 + tx;     // c = hk*D + d
+    if (c < HD && t < T) vt[(size_t)c * ldv + col0 + t] = cvt_out<OT>(tile[tx][r]);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// K4/K5: attention of query rows over (a) the shared prefix keys and (b) the
+// rows' own keys, float16 MFMA 32x32x16, float32 online softmax (base 2).
+//
+// Per KV head hk the query rows are r = t*G + g (token-major, G = Hq/Hkv), so
+// one block of 128 rows covers ~128/G tokens and all G heads that share hk;
+// every prefix K/V tile loaded into LDS is used by all 128 rows.
+// Scores are formed transposed, S^T = K · Q^T: the MFMA "A" operand is a
+// 32-key slice of K and the "B" operand is the wave's 32 queries, so each
+// lane's accumulators all belong to ONE query row (lane % 32) and the softmax
+// rescale is a per-lane scalar.  O^T = V^T · P^T likewise keeps a lane on its
+// query; P^T is fed straight from the score registers, with the key order
+// inside each 16-key step permuted identically in V^T's reads.
+//
+// blockIdx.z < n_split: prefix keys [z*split_len, min(P, (z+1)*split_len)).
+// blockIdx.z == n_split: own keys — causal within the row's sequence
+// (mask == nullptr) or the row's 64-bit ancestor mask over its group.
+// Each split writes a normalised partial O and its log2-sum-exp; attn_merge
+// combines them.
+// ----------------------------------------------------------------------------
+#define AT_BR 128
+#define AT_BK 64
+#define KLD (128 + 8)    // halfs; 272 B rows
+#define VLD (AT_BK + 4)  // halfs; 136 B rows
+
+__global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) f16 sK[AT_BK * KLD];
+  __shared__ __attribute__((aligned(16))) f16 sV[128 * VLD];
+
+  const int hk = blockIdx.y, split = blockIdx.z;
+  const int G = a.G, T = a.T, Hq = a.Hq;
+  const int R = G * T;
+  const int r0 = blockIdx.x * AT_BR;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int ql = lane & 31, hl = lane >> 5;
+  const int r = r0 + wave * 32 + ql;
+  const bool rvalid = r < R;
+  const int t = rvalid ? r / G : 0;
+  const int hq = hk * G + (rvalid ? r % G : 0);
+
+  f16x8 qreg[8];
+  {
+    const f16* qp = a.q + ((size_t)t * Hq + hq) * 128 + hl * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (rvalid) qreg[c] = *reinterpret_cast<const f16x8*>(qp + c * 16);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[c][e] = (f16)0.f;
+    }
+  }
+
+  const bool own = split >= a.n_split;
+  int kb, ke, ld;
+  const f16 *Kb, *Vb;
+  if (!own) {
+    kb = split * a.split_len;
+    ke = min(a.P, kb + a.split_len);
+    Kb = a.kp + (size_t)hk * a.ldp * 128;
+    Vb = a.vtp + (size_t)hk * 128 * a.ldp;
+    ld = a.ldp;
+  } else {
+    const int t_first = r0 / G;
+    const int t_last = min(R - 1, r0 + AT_BR - 1) / G;
+    kb = a.seq_start[t_first];
+    ke = t_last + 1;
+    Kb = a.ks + (size_t)hk * a.lds * 128;
+    Vb = a.vts + (size_t)hk * 128 * a.lds;
+    ld = a.lds;
+  }
+  const int my_start = (own && rvalid) ? a.seq_start[t] : 0;
+  const uint64_t my_mask = (own && rvalid && a.mask) ? a.mask[t] : 0ull;
+  const bool use_mask = a.mask != nullptr;
+
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
+
+  for (int k0 = kb & ~7; k0 < ke; k0 += AT_BK) {
+    __syncthreads();
+    // K tile: 64 keys x 128 d
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int key = idx >> 4, c = idx & 15;
+      const int gk = k0 + key;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (gk < ke) val = *reinterpret_cast<const uint4*>(Kb + (size_t)gk * 128 + c * 8);
+      *reinterpret_cast<uint4*>(&sK[key * KLD + c * 8]) = val;
+    }
+    // V^T tile: 128 d x 64 keys
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int d = idx >> 3, c = idx & 7;
+      const int gk = k0 + c * 8;
+      const f16* src = Vb + (size_t)d * ld + gk;
+      uint4 val;
+      if (gk + 8 <= ke) {
+        val = *reinterpret_cast<const uint4*>(src);
+      } else {
+        u16 e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = (gk + j < ke) ? reinterpret_cast<const u16*>(src)[j] : (u16)0;
+        val = make_uint4((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
+                         (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16));
+      }
+      uint2* dst = reinterpret_cast<uint2*>(&sV[d * VLD + c * 8]);
+      dst[0] = make_uint2(val.x, val.y);
+      dst[1] = make_uint2(val.z, val.w);
+    }
+    __syncthreads();
+
+    // scores for the two 32-key halves
+    f32x16 s[2];
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[hs][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f16x8 kop = *reinterpret_cast<const f16x8*>(&sK[(hs * 32 + ql) * KLD + c * 16 + hl * 8]);
+        s[hs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qreg[c], s[hs], 0, 0, 0);
+      }
+    }
+    // mask + scale; key of register i = k0 + hs*32 + 8*(i/4) + 4*hl + (i%4)
+    float mx = NEG_INF;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + hs * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        bool ok = rvalid && key >= kb && key < ke;
+        if (own) {
+          ok = ok && key >= my_start && key <= t;
+          if (use_mask) ok = ok && ((my_mask >> ((key - my_start) & 63)) & 1ull);
+        }
+        const float v = ok ? s[hs][i] * a.scale_log2 : NEG_INF;
+        s[hs][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(s[hs][i] - m_use);
+        s[hs][i] = pv;
+        rs += pv;
+      }
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
+
+    // O^T += V^T · P^T, four 16-key steps
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        f16x8 pop;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pop[j] = (f16)s[hs][8 * p + j];
+        const int kofs = hs * 32 + 16 * p + 4 * hl;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const f16* vrow = &sV[(dt * 32 + ql) * VLD + kofs];
+          const f16x4 v0 = *reinterpret_cast<const f16x4*>(vrow);
+          const f16x4 v1 = *reinterpret_cast<const f16x4*>(vrow + 8);
+          f16x8 vop;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { vop[j] = v0[j]; vop[4 + j] = v1[j]; }
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop, acc[dt], 0, 0, 0);
+        }
+      }
+  }
+
+  if (!rvalid) return;
+  const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+  float* op = a.o_part + (((size_t)split * T + t) * Hq + hq) * 128;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d = dt * 32 + 8 * ii + 4 * hl;
+      float4 v = make_float4(acc[dt][4 * ii] * inv, acc[dt][4 * ii + 1] * inv, acc[dt][4 * ii + 2] * inv,
+                             acc[dt][4 * ii + 3] * inv);
+      *reinterpret_cast<float4*>(op + d) = v;
+    }
+  if (hl == 0)
+    a.lse_part[((size_t)split * T + t) * Hq + hq] = (l_run > 0.f) ? m_run + log2f(l_run) : NEG_INF;
+}
+
+// Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M).
+__global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
+                                                  const float* __restrict__ lse_part, int S, int T, int Hq,
+                                                  int D, float* __restrict__ o) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one (t, hq)
+  const int d4 = D >> 2;
+  if (i >= (size_t)T * Hq * d4) return;
+  const size_t th = i / d4;
+  const int c = (int)(i % d4);
+  float M = NEG_INF;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lse_part[(size_t)s * T * Hq + th]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  if (M != NEG_INF) {
+    for (int s = 0; s < S; ++s) {
+      const float l = lse_part[(size_t)s * T * Hq + th];
+      if (l == NEG_INF) continue;
+      const float w = __builtin_amdgcn_exp2f(l - M);
+      const float4 v = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * D)[c];
+      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  reinterpret_cast<float4*>(o + th * D)[c] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+// ----------------------------------------------------------------------------
+// float32 attention (float32 models): one thread per (row t, q head), online
+// softmax over the prefix keys then the row's own visible keys; writes o directly.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64) attn_fwd_f32(AttnArgsF a) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= a.T * a.Hq) return;
+  const int t = i / a.Hq, hq = i % a.Hq;
+  const int hk = hq / a.G;
+  float q[D], acc[D];
+  const float* qp = a.q + ((size_t)t * a.Hq + hq) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) { q[d] = qp[d] * a.scale; acc[d] = 0.f; }
+  float m = NEG_INF, l = 0.f;
+  auto visit = [&](const float* krow, const float* vcol, int ldv) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(q[d], krow[d], s);
+    const float mn = fmaxf(m, s);
+    const float al = expf(m - mn);
+    const float p = expf(s - mn);
+    l = l * al + p;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = acc[d] * al + p * vcol[(size_t)d * ldv];
+    m = mn;
+  };
+  const float* Kp = a.kp + (size_t)hk * a.ldp * D;
+  const float* Vp = a.vtp + (size_t)hk * D * a.ldp;
+  for (int j = 0; j < a.P; ++j) visit(Kp + (size_t)j * D, Vp + j, a.ldp);
+  const float* Ks = a.ks + (size_t)hk * a.lds * D;
+  const float* Vs = a.vts + (size_t)hk * D * a.lds;
+  const int st = a.seq_start[t];
+  const uint64_t mk = a.mask ? a.mask[t] : 0ull;
+  for (int j = st; j <= t; ++j) {
+    if (a.mask && !((mk >> ((j - st) & 63)) & 1ull)) continue;
+    visit(Ks + (size_t)j * D, Vs + j, a.lds);
+  }
+  float* op = a.o + (size_t)t * a.Hq * D + (size_t)hq * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+}
+
+// ----------------------------------------------------------------------------
+// SwiGLU: u[t][i] = silu(gu[t][i]) * gu[t][I + i]
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) silu_mul(const float* __restrict__ gu, int T, int I,
+                                                float* __restrict__ u) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * I) return;
+  const size_t t = i / I, c = i % I;
+  const float g = gu[t * 2 * I + c], up = gu[t * 2 * I + I + c];
+  u[i] = g / (1.0f + expf(-g)) * up;
+}
+
+// ----------------------------------------------------------------------------
+// K7: candidate logits z[p] = h[ridx[p]] · W_lm[tok[p]] (float32 accumulate),
+// one wave per target; tok < 0 marks an unused slot (z = -inf).
+// ----------------------------------------------------------------------------
+template <typename WT>
+__global__ void __launch_bounds__(256) target_logits(const float* __restrict__ h, int H,
+                                                     const WT* __restrict__ W, const int* __restrict__ ridx,
+                                                     const int* __restrict__ tok, int NT,
+                                                     float* __restrict__ z) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= NT) return;
+  const int w = tok[p];
+  if (w < 0) {
+    if (lane == 0) z[p] = NEG_INF;
+    return;
+  }
+  const float* hr = h + (size_t)ridx[p] * H;
+  const WT* wr = W + (size_t)w * H;
+  float s = 0.f;
+  for (int k = lane; k < H; k += 64) s = fmaf(hr[k], ldw(wr, k), s);
+  s = wave_sum(s);
+  if (lane == 0) z[p] = s;
+}
+
+// out[b][c] = z[b*C + c] - logsumexp_{c < n_b} z[b*C + c]; slots c >= n_b are -inf.
+__global__ void cand_logsoftmax(const float* __restrict__ z, const int* __restrict__ n_cands, int B, int C,
+                                float* __restrict__ out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int n = n_cands[b];
+  const float* zb = z + (size_t)b * C;
+  float m = NEG_INF;
+  for (int c = 0; c < n; ++c) m = fmaxf(m, zb[c]);
+  float s = 0.f;
+  for (int c = 0; c < n; ++c) s += expf(zb[c] - m);
+  const float lse = m + logf(s);
+  for (int c = 0; c < C; ++c) out[(size_t)b * C + c] = (c < n) ? zb[c] - lse : NEG_INF;
+}
+
+// Row-wise logsumexp of logits [R][V] (natural log), one block per row.
+__global__ void __launch_bounds__(256) row_lse(const float* __restrict__ logits, int V, int R,
+                                               float* __restrict__ lse) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  if (r >= R) return;
+  const float* z = logits + (size_t)r * V;
+  float m = NEG_INF;
+  for (int k = threadIdx.x; k < V; k += 256) m = fmaxf(m, z[k]);
+  m = wave_max(m);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = 0.f;
+  for (int k = threadIdx.x; k < V; k += 256) s += expf(z[k] - m);
+  s = block_sum256(s, red);
+  if (threadIdx.x == 0) lse[r] = m + logf(s);
+}
+
+// Tree readout: score[q][c] = sum_k (z[t] - lse[ridx[t]]) over targets t = (q*C + c)*K + k
+// with tok >= 0; norm = score - logsumexp over the question's candidates.  One block per question.
+__global__ void tree_finalize(const float* __restrict__ z, const float* __restrict__ lse_rows,
+                              const int* __restrict__ ridx, const int* __restrict__ tok,
+                              const int* __restrict__ n_cands, int Q, int C, int K,
+                              float* __restrict__ score, float* __restrict__ norm) {
+  __shared__ float sc[64];
+  const int q = blockIdx.x;
+  const int c = threadIdx.x;
+  if (q >= Q) return;
+  const int n = n_cands[q];
+  float s = NEG_INF;
+  if (c < n) {
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const int tt = (q * C + c) * K + k;
+      if (tok[tt] < 0) break;
+      acc += (double)z[tt] - (double)lse_rows[ridx[tt]];
+    }
+    s = (float)acc;
+  }
+  if (c < 64) sc[c] = s;
+  __syncthreads();
+  if (c < C) {
+    score[(size_t)q * C + c] = s;
+    if (norm) {
+      float m = NEG_INF;
+      for (int j = 0; j < n; ++j) m = fmaxf(m, sc[j]);
+      float e = 0.f;
+      for (int j = 0; j < n; ++j) e += expf(sc[j] - m);
+      norm[(size_t)q * C + c] = (c < n) ? s - (m + logf(e)) : NEG_INF;
+    }
+  }
+}
+
+}  // namespace jevk
+
+// ============================================================================
+// launch wrappers (host)
+// ============================================================================
+using namespace jevk;
+
+static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, int n_vis,
+                        float* x, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (bf16)
+    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, n_vis, x);
+  else
+    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, n_vis, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
+                          float eps, float* y, int ldy, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (bf16)
+    rmsnorm_rows<u16><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const u16*)g, eps, y, ldy);
+  else
+    rmsnorm_rows<float><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const float*)g, eps, y, ldy);
+  return hipGetLastError();
+}
+
+int gemm_bf16_splits(int M, int N, int K) {
+  const long tiles = (long)cdiv(M, GBM) * cdiv(N, GBN);
+  if (tiles >= 256) return 1;
+  int s = cdiv(384, tiles);
+  const int kmax = K / 512;          // every split keeps >= 512 of K
+  if (s > kmax) s = kmax;
+  if (s > 8) s = 8;
+  return s < 1 ? 1 : s;
+}
+
+hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
+                            int ldc, int accum, int splits, float* part, hipStream_t s, int* launches) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int mt = cdiv(M, GBM), nt = cdiv(N, GBN);
+  int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
+  splits = cdiv(K, k_chunk);
+  const int nb = mt * nt * splits;
+  const int grid = cdiv(nb, 8) * 8;
+  if (splits == 1) {
+    gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+    ++*launches;
+    return hipGetLastError();
+  }
+  const size_t stride = (size_t)M * N;
+  gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, stride, 0);
+  splitk_reduce<<<cdiv((long)M * N, 256), 256, 0, s>>>(part, stride, splits, M, N, N, C, ldc, accum);
+  *launches += 2;
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
+                           int accum, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  dim3 grid(cdiv(N, 64), cdiv(M, 64));
+  gemm_f32<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, C, ldc, accum);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv, int D, const int* pos,
+                          double log2_theta, void* q_out, void* k_out, int ldk, int row0, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (f16out)
+    rope_qk<f16><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (f16*)q_out, (f16*)k_out, ldk, row0);
+  else
+    rope_qk<float><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (float*)q_out, (float*)k_out, ldk, row0);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int HD, void* vt, int ldv, int col0,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid(cdiv(T, 64), cdiv(HD, 64));
+  if (f16out)
+    v_transpose<f16><<<grid, 256, 0, s>>>(src, lds, T, HD, (f16*)vt, ldv, col0);
+  else
+    v_transpose<float><<<grid, 256, 0, s>>>(src, lds, T, HD, (float*)vt, ldv, col0);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  dim3 grid(cdiv((long)a.G * a.T, AT_BR), a.Hkv, a.n_split + 1);
+  attn_fwd_f16<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, float* o,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int n = a.T * a.Hq;
+  if (D == 64)
+    attn_fwd_f32<64><<<cdiv(n, 64), 64, 0, s>>>(a);
+  else
+    attn_fwd_f32<128><<<cdiv(n, 64), 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  silu_mul<<<cdiv((long)T * I, 256), 256, 0, s>>>(gu, T, I, u);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,
+                                int NT, float* z, hipStream_t s) {
+  if (NT <= 0) return hipSuccess;
+  if (bf16)
+    target_logits<u16><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const u16*)W, ridx, tok, NT, z);
+  else
+    target_logits<float><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const float*)W, ridx, tok, NT, z);
+  return hipGetLastError();
+}
+
+hipError_t launch_cand_logsoftmax(const float* z, const int* n_cands, int B, int C, float* out, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  cand_logsoftmax<<<cdiv(B, 64), 64, 0, s>>>(z, n_cands, B, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_lse(const float* logits, int V, int R, float* lse, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  row_lse<<<R, 256, 0, s>>>(logits, V, R, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_finalize(const float* z, const float* lse_rows, const int* ridx, const int* tok,
+                                const int* n_cands, int Q, int C, int K, float* score, float* norm,
+                                hipStream_t s) {
+  if (Q <= 0) return hipSuccess;
+  tree_finalize<<<Q, 64, 0, s>>>(z, lse_rows, ridx, tok, n_cands, Q, C, K, score, norm);
+  return hipGetLastError();
+}

@@ -1,0 +1,133 @@
+"""Device-side convenience around the C-ABI: upload weights, own the prefix KV
+store and the workspace, call the three hot-path entry points.
+
+Marshalling only: tensors are torch device buffers, every computation is a
+call into libjev.so.  Weights and inputs come as NumPy float32 arrays (for
+bfloat16 models they must be bfloat16-representable, as the seeded generator
+produces them).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import jev as J
+
+LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """float32 array -> device tensor holding float32 values or raw bfloat16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return torch.from_numpy(a).to(device)
+    u = a.view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("array is not bfloat16-representable")
+    bits = (u >> np.uint32(16)).astype(np.uint16).view(np.int16)
+    return torch.from_numpy(bits).to(device)
+
+
+class Session:
+    """A model on one device plus a prefix and a reusable workspace."""
+
+    def __init__(self, cfg, glob: Dict[str, np.ndarray], layers, device="cuda:0"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.dtype = J.JEV_BF16 if cfg.dtype == "bf16" else J.JEV_F32
+        dev = self.device
+        self.glob = {k: to_device(v, cfg.dtype, dev) for k, v in glob.items()}
+        self.layers = []
+        for l in range(cfg.n_layers):
+            W = layers(l) if callable(layers) else layers[l]
+            self.layers.append({k: to_device(W[k], cfg.dtype, dev) for k in LAYER_KEYS})
+        self.jcfg = J.make_config(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                                  cfg.mlp, cfg.vocab, cfg.rope_theta, cfg.rms_eps, self.dtype)
+        self.jw, self._keep = J.make_weights(self.glob["embed"], self.glob["final_norm"], self.glob["lm_head"],
+                                             self.layers)
+        self.model = J.jev_model_create(self.jcfg, self.jw)
+        self.prefix = None
+        self.kv = None
+        self.P = 0
+        self.ws = None
+
+    @classmethod
+    def from_source(cls, ws_src, device="cuda:0", free_host=True):
+        """Upload a jev_synth.WeightSource layer by layer."""
+        layers = []
+        dev = torch.device(device)
+
+        def get(l):
+            W = ws_src.layer(l)
+            if free_host:
+                ws_src.drop_layer(l)
+            return W
+        return cls(ws_src.cfg, ws_src.glob, get, device)
+
+    # ------------------------------------------------------------------ buffers
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self.ws is None or self.ws.numel() < nbytes:
+            self.ws = None
+            torch.cuda.synchronize(self.device)
+            self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def close(self):
+        if self.prefix:
+            J.jev_prefix_destroy(self.prefix)
+            self.prefix = None
+        if self.model:
+            J.jev_model_destroy(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ calls
+    def prefill(self, vis: np.ndarray, text_ids: np.ndarray, stream=None):
+        P = int(vis.shape[0]) + int(len(text_ids))
+        if self.prefix:
+            J.jev_prefix_destroy(self.prefix)
+            self.prefix = None
+        nb = J.jev_prefix_bytes(self.model, P)
+        self.kv = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        self.prefix = J.jev_prefix_create(self.model, P, self.kv)
+        self.P = P
+        self.vis = to_device(vis, self.cfg.dtype, self.device) if vis.shape[0] else None
+        ws = self.workspace(J.jev_workspace_bytes(self.model, P, max(P, 1), 1, 0))
+        J.jev_prefill_prefix(self.prefix, self.vis, int(vis.shape[0]), text_ids, ws, stream)
+
+    def suffix_ws_bytes(self, suf) -> int:
+        B, C = suf["cands"].shape
+        T = int(np.sum(suf["lens"]))
+        return J.jev_workspace_bytes(self.model, self.P, T, B, B * C)
+
+    def score_suffixes(self, suf, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        B, C = suf["cands"].shape
+        if out is None:
+            out = torch.empty((B, C), dtype=torch.float32, device=self.device)
+        ws = self.workspace(self.suffix_ws_bytes(suf))
+        J.jev_score_suffixes(self.prefix, suf["ids"], suf["lens"], suf["cands"], suf["n_cands"], out, ws, stream)
+        return out
+
+    def tree_ws_bytes(self, tree, mode) -> int:
+        rows, seqs, targets = J.jev_tree_plan_size(tree["stem_ids"], tree["stem_lens"], tree["cand_tok"],
+                                                   tree["cand_lens"], tree["n_cands"], mode)
+        return J.jev_workspace_bytes(self.model, self.P, rows, max(seqs, tree["stem_lens"].shape[0]), targets)
+
+    def score_tree(self, tree, mode=J.JEV_TREE_TRIE, stream=None):
+        Q, C, _ = tree["cand_tok"].shape
+        score = torch.empty((Q, C), dtype=torch.float32, device=self.device)
+        norm = torch.empty((Q, C), dtype=torch.float32, device=self.device)
+        ws = self.workspace(self.tree_ws_bytes(tree, mode))
+        J.jev_score_tree(self.prefix, tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                         tree["n_cands"], mode, score, norm, ws, stream)
+        return score, norm
+
+    def stats(self) -> dict:
+        return J.jev_get_stats(self.model)
