@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of shared-prefix candidate scoring on one MI355X.
+
+One step = the whole per-image path on one batch: prefill the prefix once
+(jev_prefill_prefix) and score every suffix's candidates in one batched
+forward over it (jev_score_suffixes).  Default workload: the Qwen2.5-VL-7B-
+shaped decoder (28 layers, hidden 3584, 28/4 heads of 128, MLP 18944,
+vocab 152064, bf16 random-init weights), a 1024-position prefix (1000 visual
+embeddings + 24 text ids) and 32 suffixes of 6..16 tokens with 2 candidates
+each; all inputs synthetic and seeded, resident in HBM before timing.
+
+Prints ONE JSON line.  `value` = candidates scored per second over whole
+steps (prefill + score).  Extra fields give the score-only and prefill-only
+times, the per-kernel breakdown from the library's event timing, the
+roofline of the dominant kernel and of the shared-prefix attention, and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c3]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "candidates scored/sec + attention MFMA util, 7B-shaped prefix 1024, 32 suffixes"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload_name(cfg):
+    return (f"{cfg.name}: {cfg.n_layers}-layer decoder, hidden {cfg.hidden}, {cfg.n_q_heads}/{cfg.n_kv_heads} "
+            f"heads x {cfg.head_dim}, MLP {cfg.mlp}, vocab {cfg.vocab}, {cfg.dtype}; prefix {cfg.prefix_len} "
+            f"({cfg.n_vis} visual + {cfg.n_text} text); {cfg.n_suffix} suffixes of {cfg.len_lo}-{cfg.len_hi} "
+            f"tokens, {cfg.n_cands} candidates each")
+
+
+def cpu_baseline(cfg, seed, budget_layers=2):
+    """The oracle as it stands on a bounded sample, scaled to the whole step.
+
+    Sample: the oracle's prefix-once scoring (jev_oracle.score_suffixes) of all
+    suffixes with the model cut to 0 and to `budget_layers` layers (same shapes).
+    The 0-layer run is the embedding + readout cost; the difference gives the
+    per-layer cost; estimate = readout + n_layers * per-layer.
+    """
+    import jev_synth as S
+    from oracle import jev_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    pre, suf = S.prefix_inputs(cfg, seed), S.suffix_inputs(cfg, seed)
+    c0 = S.with_overrides(cfg, n_layers=0)
+    ck = S.with_overrides(cfg, n_layers=budget_layers)
+    ws = S.WeightSource(ck, seed)
+    ws.glob
+    for l in range(budget_layers):
+        ws.layer(l)
+    t = time.perf_counter()
+    O.score_suffixes(ws, c0, pre, suf)
+    t0 = time.perf_counter() - t
+    t = time.perf_counter()
+    O.score_suffixes(ws, ck, pre, suf)
+    tk = time.perf_counter() - t
+    per_layer = max(tk - t0, 0.0) / budget_layers
+    est = t0 + cfg.n_layers * per_layer
+    n_c = int(np.sum(suf["n_cands"]))
+    return {"value": n_c / est, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"jev_oracle.score_suffixes (prefix once, layer-major, float32 numpy) on all "
+                       f"{cfg.n_suffix} suffixes with the model cut to 0 and {budget_layers} of "
+                       f"{cfg.n_layers} layers; measured {t0:.2f} s and {tk:.2f} s, scaled to "
+                       f"{cfg.n_layers} layers = {est:.1f} s per step"),
+            "seconds_per_step": est}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+              f"requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import jev_synth as S
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+
+    cfg = S.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    t = time.time()
+    sess = Session.generated(cfg, args.seed, dev)
+    pre, suf = S.prefix_inputs(cfg, args.seed), S.suffix_inputs(cfg, args.seed)
+    log(f"[bench] weights drawn and uploaded in {time.time() - t:.1f} s")
+    n_cand = int(np.sum(suf["n_cands"]))
+    T = int(np.sum(suf["lens"]))
+
+    # resident inputs and buffers
+    sess.prefill(pre["vis"], pre["text_ids"])
+    out = sess.score_suffixes(suf)
+    ws_bytes = max(sess.suffix_ws_bytes(suf), J.jev_workspace_bytes(sess.model, sess.P, sess.P, 1, 0))
+    sess.workspace(ws_bytes)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def prefill_only():
+        J.jev_prefill_prefix(sess.prefix, sess.vis, int(pre["vis"].shape[0]), pre["text_ids"], sess.ws)
+
+    def score_only():
+        J.jev_score_suffixes(sess.prefix, suf["ids"], suf["lens"], suf["cands"], suf["n_cands"], out, sess.ws)
+
+    def step():
+        prefill_only()
+        score_only()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    t_wall = time.perf_counter()
+    ms_step = timed(step, args.steps)
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall_ms:.3f})")
+    ms_score = timed(score_only, args.steps)
+    ms_prefill = timed(prefill_only, max(1, args.steps // 2))
+    log(f"[bench] score-only {ms_score:.3f} ms, prefill-only {ms_prefill:.3f} ms")
+
+    # per-kernel event timing (separate pass; same steps)
+    J.jev_profile_start(sess.model)
+    for _ in range(args.profile_steps):
+        step()
+    prof_step = J.jev_profile_stop(sess.model)
+    J.jev_profile_start(sess.model)
+    for _ in range(args.profile_steps):
+        score_only()
+    prof_score = J.jev_profile_stop(sess.model)
+    dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
+    d = prof_step[dom]
+    avg_ms = d["ms"] / d["launches"]
+    if d["flops"] > 0:
+        ach = d["flops"] / d["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": d["launches"],
+                "algorithmic_flops_per_launch": d["flops"] / d["launches"]}
+    else:
+        ach = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "launches": d["launches"]}
+    at = prof_score.get("attention")
+    attn = None
+    if at:
+        a_ms = at["ms"] / at["launches"]
+        a_tf = at["flops"] / at["launches"] / (a_ms * 1e-3) / 1e12
+        kv_bytes = 2.0 * cfg.n_kv_heads * cfg.prefix_len * cfg.head_dim * 2
+        attn = {"kernel": "attention (score call, shared prefix + own rows)",
+                "achieved_tflops": round(a_tf, 2), "mfma_util": round(a_tf / PEAK_BF16_TFLOPS, 4),
+                "prefix_kv_gbs": round(kv_bytes / (a_ms * 1e-3) / 1e9, 1),
+                "prefix_kv_hbm_frac": round(kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "avg_launch_us": round(a_ms * 1e3, 2),
+                "algorithmic_flops_per_launch": at["flops"] / at["launches"],
+                "query_rows": cfg.group * T, "padded_rows": cfg.group * cfg.n_suffix * cfg.s_max}
+    kernels = {k: {"launches": v["launches"], "ms_total": round(v["ms"], 4),
+                   "us_avg": round(v["ms"] * 1e3 / v["launches"], 2)} for k, v in prof_step.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline on a bounded sample ...")
+        cpu = cpu_baseline(cfg, args.seed)
+        log(f"[bench] CPU oracle: {cpu['value']:.3f} candidates/s")
+
+    res = {
+        "metric": METRIC,
+        "value": round(n_cand / (ms_step * 1e-3), 2),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and inputs of the workload's shapes)",
+        "config": {"workload": workload_name(cfg), "prefix_len": cfg.prefix_len, "suffixes": cfg.n_suffix,
+                   "suffix_rows": T, "candidates": n_cand, "seed": args.seed,
+                   "step": "jev_prefill_prefix + jev_score_suffixes"},
+        "score_only": {"ms": round(ms_score, 4), "candidates_per_s": round(n_cand / (ms_score * 1e-3), 2)},
+        "prefill_ms": round(ms_prefill, 4),
+        "roofline": roof,
+        "attention": attn,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    sess.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -216,6 +216,25 @@ jev_status jev_tree_plan_rows(const int32_t *stem_ids, const int32_t *stem_lens,
                               int32_t *row_tok, int32_t *row_depth, int32_t *row_group,
                               uint64_t *row_mask, int32_t *target_row);
 
+/* ---- diagnostics ----------------------------------------------------------------
+ * Per-kernel timing with HIP events recorded on the call's stream around every
+ * launch, plus the algorithmic work of each launch (flops counted once, i.e.
+ * without the second pass of the split bf16 activations; bytes = operands
+ * read once and results written once).  While enabled, calls on the model
+ * must come from one host thread; events add a small gap between launches.
+ * jev_profile_stop synchronises on the last recorded event, fills up to
+ * max_out entries (one per kernel kind that ran) and sets *n_out to the
+ * number of kinds. */
+typedef struct {
+    char     name[32];
+    uint64_t launches;
+    double   ms;       /* summed launch durations        */
+    double   flops;    /* summed algorithmic flops       */
+    double   bytes;    /* summed algorithmic bytes       */
+} jev_kernel_stat;
+jev_status jev_profile_start(jev_model *m);
+jev_status jev_profile_stop(jev_model *m, jev_kernel_stat *out, int32_t max_out, int32_t *n_out);
+
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *jev_last_error(void);
 

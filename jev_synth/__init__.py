@@ -240,6 +240,21 @@ def weights_layer(cfg: Config, seed: int, layer: int, pool=None) -> Dict[str, np
     return out
 
 
+def iter_layers(cfg: Config, seed: int, workers: int = 0):
+    """Yield (l, weights_layer(cfg, seed, l)) in order, drawing up to `workers` layers ahead."""
+    workers = workers or _threads()
+    if cfg.n_layers == 0:
+        return
+    with ThreadPoolExecutor(workers) as ex:
+        futs = {}
+        nxt = 0
+        for l in range(cfg.n_layers):
+            while nxt < cfg.n_layers and nxt < l + workers:
+                futs[nxt] = ex.submit(weights_layer, cfg, seed, nxt)
+                nxt += 1
+            yield l, futs.pop(l).result()
+
+
 class WeightSource:
     """Lazy, cached access to a model's weights: .glob and .layer(l)."""
 

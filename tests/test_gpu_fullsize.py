@@ -1,0 +1,116 @@
+"""GPU parity at the full workload sizes against stored oracle outputs.
+
+tests/golden/<config>_s<seed>.json were written by tests/golden/make_golden.py,
+which calls only the CPU oracle; each file carries a fingerprint of the
+inputs, checked here before comparing.  Every output element is compared.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import jev_synth as S
+from tests.gpu_common import TOL, check_suffix_out, say
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name, seed):
+    path = os.path.join(GOLD, f"{name}_s{seed}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle output {path}")
+    with open(path) as f:
+        g = json.load(f)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(GOLD, "make_golden.py"))
+    mg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mg)
+    assert g["fingerprint"] == mg.fingerprint(S.CONFIGS[name], seed), "generated inputs differ from the stored ones"
+    return g
+
+
+_SESS = {}
+
+
+def session(name, seed):
+    """One uploaded model per (config, seed), kept for the module's tests."""
+    from vlm_shared_prefix_amd.session import Session
+    key = (name, seed)
+    if key not in _SESS:
+        for k in list(_SESS):
+            _SESS.pop(k).close()
+        say(f"[fullsize] drawing and uploading {name} seed {seed}")
+        cfg = S.CONFIGS[name]
+        sess = Session.generated(cfg, seed)
+        pre = S.prefix_inputs(cfg, seed)
+        sess.prefill(pre["vis"], pre["text_ids"])
+        _SESS[key] = sess
+    return _SESS[key]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cleanup():
+    yield
+    for k in list(_SESS):
+        _SESS.pop(k).close()
+
+
+@pytest.mark.parametrize("name,seed", [("c2", 0), ("c2", 1), ("c2", 2), ("c3", 0)])
+def test_fullsize_suffixes(name, seed):
+    g = load_golden(name, seed)
+    cfg = S.CONFIGS[name]
+    suf = S.suffix_inputs(cfg, seed)
+    say(f"[fullsize] {name} seed {seed}: B={len(suf['lens'])}, rows={int(suf['lens'].sum())}")
+    got = session(name, seed).score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, np.array(g["out"], np.float32), suf["n_cands"], cfg.dtype, f"{name}/s{seed}")
+
+
+@pytest.mark.parametrize("B", S.C4_BATCHES)
+def test_fullsize_batch_sweep(B):
+    """Config 4: every batch size B gives the answers of the same suffixes in the pool."""
+    g = load_golden("c4", 0)
+    cfg = S.CONFIGS["c4"]
+    suf = S.suffix_inputs(cfg, 0, n=B)
+    say(f"[fullsize] c4 B={B}")
+    got = session("c4", 0).score_suffixes(suf).cpu().numpy()
+    ref = np.array(g["out"], np.float32)[:B]
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"c4/B{B}")
+
+
+def test_fullsize_serial_equals_batched():
+    """Config 4: B single-suffix calls over the same prefix match one batched call."""
+    g = load_golden("c4", 0)
+    cfg = S.CONFIGS["c4"]
+    suf = S.suffix_inputs(cfg, 0, n=8)
+    sess = session("c4", 0)
+    batched = sess.score_suffixes(suf).cpu().numpy()
+    serial = np.stack([sess.score_suffixes({k: v[b:b + 1] for k, v in suf.items()}).cpu().numpy()[0]
+                       for b in range(8)])
+    ref = np.array(g["out"], np.float32)[:8]
+    check_suffix_out(serial, ref, suf["n_cands"], cfg.dtype, "c4/serial")
+    assert np.max(np.abs(serial - batched)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_fullsize_tree(mode):
+    g = load_golden("c5", 0)
+    cfg = S.CONFIGS["c5"]
+    tree = S.tree_inputs(cfg, 0)
+    say(f"[fullsize] c5 tree mode {mode}")
+    score, norm = session("c5", 0).score_tree(tree, mode)
+    for key, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
+        ref = np.array(g[key], np.float32)
+        valid = np.isfinite(ref)
+        err = float(np.max(np.abs(got[valid] - ref[valid])))
+        say(f"  c5 mode {mode} {key}: max |d| = {err:.3e}")
+        assert err <= TOL["bf16"], (key, err)
+        assert np.all(np.isneginf(got[~valid]))
+    # argmax over each question's candidates where the oracle margin is >= 0.05
+    from oracle import jev_oracle as O
+    ref = np.array(g["norm"], np.float32)
+    m = O.margins(ref, tree["n_cands"])
+    sel = m >= 0.05
+    assert np.array_equal(O.argmax_first(ref, tree["n_cands"])[sel],
+                          O.argmax_first(norm.cpu().numpy(), tree["n_cands"])[sel])

@@ -21,11 +21,36 @@
 using jevp::Plan;
 using jevp::Status;
 
+// Per-kernel event timing (diagnostics; one stream at a time while enabled).
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<ProfRec> recs;
+  hipEvent_t take() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  ~Profiler() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
 struct jev_model {
   jev_config cfg;
   jev_weights w;
   std::vector<jev_layer> layers;
   std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
+  Profiler prof;
 };
 
 struct jev_prefix {
@@ -205,19 +230,55 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+enum Kind {
+  K_EMBED, K_RMSNORM, K_GEMM, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE, K_SILU, K_TARGET, K_CANDSM,
+  K_LMHEAD, K_ROWLSE, K_TREEFIN, K_NKINDS
+};
+const char* const kKindName[K_NKINDS] = {"embed_rows", "rmsnorm_rows", "gemm", "splitk_reduce", "rope_qk",
+                                         "v_transpose", "attention", "attn_merge", "silu_mul", "target_logits",
+                                         "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize"};
+
 struct Forward {
   const jev_prefix* pf;
-  const jev_model* m;
+  jev_model* m;
   const jev_config& c;
   const Plan& plan;
   const Layout& L;
   void* ws;
   hipStream_t s;
   Mode mode;
+  Profiler* prof;
   int launches = 0;
+  double own_pairs = 0;   // (row, own visible key) pairs of the attention
 
   Forward(const jev_prefix* p, const Plan& pl, const Layout& lay, void* w, hipStream_t st, Mode md)
-      : pf(p), m(p->m), c(p->m->cfg), plan(pl), L(lay), ws(w), s(st), mode(md) {}
+      : pf(p), m(p->m), c(p->m->cfg), plan(pl), L(lay), ws(w), s(st), mode(md),
+        prof(p->m->prof.on ? &p->m->prof : nullptr) {
+    for (int t = 0; t < plan.T; ++t)
+      own_pairs += plan.mask.empty() ? (double)(t - plan.seq_start[t] + 1)
+                                     : (double)__builtin_popcountll(plan.mask[t]);
+  }
+
+  // Launch one kernel through `fn`, timing it with events when profiling is on.
+  template <class Fn>
+  jev_status run_k(int kind, double flops, double bytes, Fn&& fn) {
+    hipEvent_t a = nullptr;
+    if (prof) {
+      a = prof->take();
+      if (a) (void)hipEventRecord(a, s);
+    }
+    const hipError_t e = fn();
+    ++launches;
+    if (e != hipSuccess) return fail(JEV_E_HIP, std::string(kKindName[kind]) + ": " + hipGetErrorString(e));
+    if (prof && a) {
+      hipEvent_t b = prof->take();
+      if (b) {
+        (void)hipEventRecord(b, s);
+        prof->recs.push_back({kind, a, b, flops, bytes});
+      }
+    }
+    return JEV_OK;
+  }
 
   // layer l's K / Vt in the prefix store
   char* store_k(int l) const {
@@ -226,25 +287,34 @@ struct Forward {
   }
   char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m); }
 
-  jev_status gemm(const float* A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
-                  const void* w2, int n2, float* C, int ldc, int accum) {
-    const int N = n0 + n1 + n2;
-    if (is_bf16(m)) {
-      GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
-      const int splits = jevk_splits(M, N, K);
-      HIP_OK(launch_gemm_bf16(A, lda, M, K, sg, N, C, ldc, accum, splits, at<float>(ws, L.gpart), s, &launches));
-    } else {
-      GemmSegsF sg{{(const float*)w0, (const float*)w1, (const float*)w2}, {n0, n0 + n1, N}};
-      HIP_OK(launch_gemm_f32(A, lda, M, K, sg, N, C, ldc, accum, s));
-      ++launches;
-    }
-    return JEV_OK;
-  }
-
-  static int jevk_splits(int M, int N, int K) {
+  static int splits_for(int M, int N, int K) {
     int sp = gemm_bf16_splits(M, N, K);
     while (sp > 1 && (size_t)sp * M * N > kGemmPartFloats) --sp;
     return sp;
+  }
+
+  jev_status gemm(const float* A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
+                  const void* w2, int n2, float* C, int ldc, int accum, int kind = K_GEMM) {
+    const int N = n0 + n1 + n2;
+    const double flops = 2.0 * M * N * K;
+    const double wbytes = (double)N * K * (is_bf16(m) ? 2 : 4);
+    const double bytes = wbytes + 4.0 * M * K + 4.0 * M * N * (accum ? 2 : 1);
+    if (is_bf16(m)) {
+      GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
+      int eff = 1;
+      float* part = at<float>(ws, L.gpart);
+      const int splits = splits_for(M, N, K);
+      if (jev_status st = run_k(kind, flops, bytes, [&] {
+            return launch_gemm_bf16(A, lda, M, K, sg, N, C, ldc, accum, splits, part, s, &eff);
+          }))
+        return st;
+      if (eff > 1)
+        return run_k(K_SPLITK, 0.0, 4.0 * M * N * (eff + (accum ? 2 : 1)),
+                 [&] { return launch_splitk_reduce(part, eff, M, N, C, ldc, accum, s); });
+      return JEV_OK;
+    }
+    GemmSegsF sg{{(const float*)w0, (const float*)w1, (const float*)w2}, {n0, n0 + n1, N}};
+    return run_k(kind, flops, bytes, [&] { return launch_gemm_f32(A, lda, M, K, sg, N, C, ldc, accum, s); });
   }
 
   jev_status run(const void* vis, int n_vis) {
@@ -252,6 +322,7 @@ struct Forward {
     const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
     const int HqD = Hq * D, NQKV = nqkv(c);
     const bool bf = is_bf16(m);
+    const double e = (double)kv_elem(m);
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
     float* act = at<float>(ws, L.act);
@@ -262,26 +333,32 @@ struct Forward {
     const uint64_t* mask = plan.mask.empty() ? nullptr : at<uint64_t>(ws, L.mask);
     const double log2_theta = std::log2((double)c.rope_theta);
     const int P = (mode == Mode::Prefill) ? 0 : pf->P;
+    const double rowbytes = 4.0 * T * H;
 
-    HIP_OK(launch_embed(bf, m->w.embed, tok, T, H, vis, n_vis, x, s));
-    ++launches;
+    if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * (bf ? 1.5 : 2.0),
+                          [&] { return launch_embed(bf, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
+      return st;
 
-    // attention split plan (bf16 path)
+    // attention split plan (bf16 path): enough prefix splits to give ~512 blocks
     int n_split = 0, split_len = 0;
     if (bf && P > 0) {
-      const long base = (long)((c.n_q_heads / Hkv) * (long)T + 127) / 128 * Hkv;
+      const long base = ((long)(Hq / Hkv) * T + 127) / 128 * Hkv;
       n_split = (int)std::min<long>(kMaxAttnSplits, std::max<long>(1, (512 + base - 1) / base));
       n_split = std::min(n_split, (P + 255) / 256);
       n_split = std::max(n_split, 1);
       split_len = ((P + n_split - 1) / n_split + 63) / 64 * 64;
       n_split = (P + split_len - 1) / split_len;
     }
+    const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
+    const double attn_bytes = e * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + (double)T * HqD) + 4.0 * T * HqD;
 
     for (int l = 0; l < c.n_layers; ++l) {
       const jev_layer& W = m->layers[l];
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
-      HIP_OK(launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, act, wide, s));
-      ++launches;
+      if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
+            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, act, wide, s);
+          }))
+        return st;
       if (jev_status st = gemm(act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0)) return st;
       // K / V destination: the prefix store (prefill) or the workspace (scoring)
       void *kdst, *vdst;
@@ -295,9 +372,14 @@ struct Forward {
         vdst = at<char>(ws, L.vts);
         kld = L.Tc;
       }
-      HIP_OK(launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q), kdst, kld, 0, s));
-      HIP_OK(launch_v_transpose(bf, big + (size_t)(Hq + Hkv) * D, NQKV, T, Hkv * D, vdst, kld, 0, s));
-      launches += 2;
+      if (jev_status st = run_k(K_ROPE, 0.0, (double)T * (Hq + Hkv) * D * (4 + e), [&] {
+            return launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q), kdst, kld, 0, s);
+          }))
+        return st;
+      if (jev_status st = run_k(K_VT, 0.0, (double)T * Hkv * D * (4 + e), [&] {
+            return launch_v_transpose(bf, big + (size_t)(Hq + Hkv) * D, NQKV, T, Hkv * D, vdst, kld, 0, s);
+          }))
+        return st;
       if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
 
       if (bf) {
@@ -317,9 +399,11 @@ struct Forward {
         a.o_part = at<float>(ws, L.o_part);
         a.lse_part = at<float>(ws, L.lse_part);
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-        HIP_OK(launch_attn_f16(a, s));
-        HIP_OK(launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act, s));
-        launches += 2;
+        if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
+        if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 2) * T * HqD, [&] {
+              return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act, s);
+            }))
+          return st;
       } else {
         AttnArgsF a{};
         a.q = at<float>(ws, L.q);
@@ -335,16 +419,17 @@ struct Forward {
         a.seq_start = seq_start; a.mask = mask;
         a.scale = (float)(1.0 / std::sqrt((double)D));
         a.o = act;
-        HIP_OK(launch_attn_f32(a, D, s));
-        ++launches;
+        if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f32(a, D, s); })) return st;
       }
-      // note: act now holds o [T][HqD] with row stride HqD
+      // act now holds o [T][HqD] with row stride HqD
       if (jev_status st = gemm(act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
-      HIP_OK(launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, act, wide, s));
-      ++launches;
+      if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
+            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, act, wide, s);
+          }))
+        return st;
       if (jev_status st = gemm(act, wide, T, H, W.w_gate, I, W.w_up, I, nullptr, 0, big, 2 * I, 0)) return st;
-      HIP_OK(launch_silu_mul(big, T, I, act, s));   // gate|up [T][2I] -> u [T][I]
-      ++launches;
+      if (jev_status st = run_k(K_SILU, 0.0, 12.0 * T * I, [&] { return launch_silu_mul(big, T, I, act, s); }))
+        return st;   // gate|up [T][2I] -> u [T][I]
       if (jev_status st = gemm(act, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
     }
     return JEV_OK;
@@ -355,26 +440,38 @@ struct Forward {
     const bool bf = is_bf16(m);
     const int R = (int)plan.read_rows.size();
     const int NT = (int)plan.tgt_tok.size();
+    const double we = bf ? 2.0 : 4.0;
     float* h = at<float>(ws, L.h);
     float* z = at<float>(ws, L.z);
-    HIP_OK(launch_rmsnorm(bf, at<float>(ws, L.x), H, at<int>(ws, L.read_rows), R, H, m->w.final_norm, c.rms_eps,
-                          h, H, s));
-    HIP_OK(launch_target_logits(bf, h, H, m->w.lm_head, at<int>(ws, L.tgt_ridx), at<int>(ws, L.tgt_tok), NT, z, s));
-    launches += 2;
+    if (jev_status st = run_k(K_RMSNORM, 0.0, 8.0 * R * H, [&] {
+          return launch_rmsnorm(bf, at<float>(ws, L.x), H, at<int>(ws, L.read_rows), R, H, m->w.final_norm,
+                                c.rms_eps, h, H, s);
+        }))
+      return st;
+    if (jev_status st = run_k(K_TARGET, 2.0 * NT * H, NT * H * we, [&] {
+          return launch_target_logits(bf, h, H, m->w.lm_head, at<int>(ws, L.tgt_ridx), at<int>(ws, L.tgt_tok), NT,
+                                      z, s);
+        }))
+      return st;
     if (mode == Mode::Score) {
       const int B = (int)plan.out_n.size();
-      HIP_OK(launch_cand_logsoftmax(z, at<int>(ws, L.out_n), B, NT / std::max(B, 1), out_a, s));
-      ++launches;
-    } else {
-      float* logits = at<float>(ws, L.logits);
-      if (jev_status st = gemm(h, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits, c.vocab, 0))
-        return st;
-      HIP_OK(launch_row_lse(logits, c.vocab, R, at<float>(ws, L.lse_rows), s));
-      ++launches;
-      return JEV_OK;
+      return run_k(K_CANDSM, 0.0, 8.0 * NT,
+               [&] { return launch_cand_logsoftmax(z, at<int>(ws, L.out_n), B, NT / std::max(B, 1), out_a, s); });
     }
-    return JEV_OK;
+    float* logits = at<float>(ws, L.logits);
+    if (jev_status st = gemm(h, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits, c.vocab, 0,
+                             K_LMHEAD))
+      return st;
+    if (jev_status st = run_k(K_ROWLSE, 0.0, 4.0 * R * c.vocab,
+                          [&] { return launch_row_lse(logits, c.vocab, R, at<float>(ws, L.lse_rows), s); }))
+      return st;
+    const int Q = (int)plan.out_n.size();
+    return run_k(K_TREEFIN, 0.0, 8.0 * NT, [&] {
+      return launch_tree_finalize(z, at<float>(ws, L.lse_rows), at<int>(ws, L.tgt_ridx), at<int>(ws, L.tgt_tok),
+                                  at<int>(ws, L.out_n), Q, tree_C, tree_K, out_a, out_b, s);
+    });
   }
+  int tree_C = 0, tree_K = 0;
 };
 
 // Copy the plan's metadata into the workspace with one host->device copy.
@@ -427,9 +524,9 @@ extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, 
   if (jev_status st = stage_meta(plan, L, ws, s)) return st;
   Forward f(p, plan, L, ws, s, Mode::Prefill);
   jev_status st = f.run(vis_embeds, n_vis);
-  const_cast<jev_model*>(m)->launches += f.launches;
+  p->m->launches += f.launches;
   if (st) return st;
-  const_cast<jev_model*>(m)->prefills++;
+  p->m->prefills++;
   return JEV_OK;
 }
 
@@ -481,15 +578,10 @@ extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_id
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (jev_status e = stage_meta(plan, L, ws, s)) return e;
   Forward f(p, plan, L, ws, s, Mode::Tree);
+  f.tree_C = C_max;
+  f.tree_K = K_max;
   jev_status e = f.run(nullptr, 0);
-  if (!e) e = f.readout(nullptr, nullptr);
-  if (!e) {
-    hipError_t he = launch_tree_finalize(at<float>(ws, L.z), at<float>(ws, L.lse_rows), at<int>(ws, L.tgt_ridx),
-                                         at<int>(ws, L.tgt_tok), at<int>(ws, L.out_n), Q, C_max, K_max, out_score,
-                                         out_norm, s);
-    ++f.launches;
-    if (he != hipSuccess) e = fail(JEV_E_HIP, std::string("tree_finalize: ") + hipGetErrorString(he));
-  }
+  if (!e) e = f.readout(out_score, out_norm);
   m->launches += f.launches;
   if (e) return e;
   m->forwards++;
@@ -530,5 +622,47 @@ extern "C" jev_status jev_tree_plan_rows(const int32_t* stem_ids, const int32_t*
   }
   for (size_t i = 0; i < plan.tgt_tok.size(); ++i)
     target_row[i] = plan.tgt_tok[i] >= 0 ? plan.read_rows[plan.tgt_ridx[i]] : -1;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_profile_start(jev_model* m) {
+  if (!m) return fail(JEV_E_INVALID, "null model");
+  m->prof.recs.clear();
+  m->prof.used = 0;
+  m->prof.on = true;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_profile_stop(jev_model* m, jev_kernel_stat* out, int32_t max_out, int32_t* n_out) {
+  if (!m || !n_out || (max_out > 0 && !out)) return fail(JEV_E_INVALID, "null argument");
+  Profiler& P = m->prof;
+  P.on = false;
+  std::vector<jev_kernel_stat> acc(K_NKINDS);
+  for (int k = 0; k < K_NKINDS; ++k) {
+    std::memset(&acc[k], 0, sizeof(jev_kernel_stat));
+    std::strncpy(acc[k].name, kKindName[k], sizeof(acc[k].name) - 1);
+  }
+  if (!P.recs.empty()) {
+    hipError_t e = hipEventSynchronize(P.recs.back().b);
+    if (e != hipSuccess) return fail(JEV_E_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+  }
+  for (const ProfRec& r : P.recs) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) continue;
+    jev_kernel_stat& a = acc[r.kind];
+    a.launches++;
+    a.ms += ms;
+    a.flops += r.flops;
+    a.bytes += r.bytes;
+  }
+  P.recs.clear();
+  P.used = 0;
+  int n = 0;
+  for (int k = 0; k < K_NKINDS; ++k)
+    if (acc[k].launches) {
+      if (n < max_out) out[n] = acc[k];
+      ++n;
+    }
+  *n_out = n;
   return JEV_OK;
 }

@@ -53,8 +53,12 @@ hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, 
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
                           float eps, float* y, int ldy, hipStream_t s);
 int gemm_bf16_splits(int M, int N, int K);
+// Launches the GEMM; with *eff_splits > 1 it wrote split partials [splits][M][N] into `part`
+// and launch_splitk_reduce must follow.
 hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
-                            int ldc, int accum, int splits, float* part, hipStream_t s, int* launches);
+                            int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
+                                hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
                            int accum, hipStream_t s);
 hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv, int D, const int* pos,

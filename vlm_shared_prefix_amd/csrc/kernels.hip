@@ -803,22 +803,26 @@ int gemm_bf16_splits(int M, int N, int K) {
 }
 
 hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
-                            int ldc, int accum, int splits, float* part, hipStream_t s, int* launches) {
+                            int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+  *eff_splits = 1;
   if (M <= 0 || N <= 0) return hipSuccess;
   const int mt = cdiv(M, GBM), nt = cdiv(N, GBN);
-  int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
+  const int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
   splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
   const int nb = mt * nt * splits;
   const int grid = cdiv(nb, 8) * 8;
-  if (splits == 1) {
+  if (splits == 1)
     gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
-    ++*launches;
-    return hipGetLastError();
-  }
-  const size_t stride = (size_t)M * N;
-  gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, stride, 0);
-  splitk_reduce<<<cdiv((long)M * N, 256), 256, 0, s>>>(part, stride, splits, M, N, N, C, ldc, accum);
-  *launches += 2;
+  else
+    gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, (size_t)M * N, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
+                                hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  splitk_reduce<<<cdiv((long)M * N, 256), 256, 0, s>>>(part, (size_t)M * N, splits, M, N, N, C, ldc, accum);
   return hipGetLastError();
 }
 

@@ -49,6 +49,11 @@ class jev_stats(C.Structure):
                 ("launches", C.c_uint64)]
 
 
+class jev_kernel_stat(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_uint64), ("ms", C.c_double),
+                ("flops", C.c_double), ("bytes", C.c_double)]
+
+
 _i32p = C.POINTER(C.c_int32)
 _u64p = C.POINTER(C.c_uint64)
 _vp = C.c_void_p
@@ -70,6 +75,8 @@ _sig = {
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p]),
     "jev_tree_plan_rows": (C.c_int32, [_i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _u64p, _i32p]),
+    "jev_profile_start": (C.c_int32, [_vp]),
+    "jev_profile_stop": (C.c_int32, [_vp, C.POINTER(jev_kernel_stat), C.c_int32, _i32p]),
     "jev_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -150,6 +157,22 @@ def jev_prefix_destroy(prefix: int) -> None:
 
 def jev_workspace_bytes(model: int, prefix_len: int, max_rows: int, max_seqs: int, max_targets: int) -> int:
     return int(_lib.jev_workspace_bytes(model, prefix_len, max_rows, max_seqs, max_targets))
+
+
+def jev_profile_start(model: int) -> None:
+    _check(_lib.jev_profile_start(model), "jev_profile_start")
+
+
+def jev_profile_stop(model: int) -> dict:
+    """Per-kernel totals {name: {launches, ms, flops, bytes}} since jev_profile_start."""
+    arr = (jev_kernel_stat * 32)()
+    n = C.c_int32()
+    _check(_lib.jev_profile_stop(model, arr, 32, C.byref(n)), "jev_profile_stop")
+    out = {}
+    for i in range(min(n.value, 32)):
+        k = arr[i]
+        out[k.name.decode()] = {"launches": int(k.launches), "ms": k.ms, "flops": k.flops, "bytes": k.bytes}
+    return out
 
 
 # ---------------------------------------------------------------------------- hot path

@@ -54,17 +54,19 @@ class Session:
         self.ws = None
 
     @classmethod
-    def from_source(cls, ws_src, device="cuda:0", free_host=True):
-        """Upload a jev_synth.WeightSource layer by layer."""
-        layers = []
-        dev = torch.device(device)
+    def generated(cls, cfg, seed, device="cuda:0"):
+        """Draw the seeded weights (several layers at a time) and upload them layer by layer."""
+        import jev_synth as S
+        glob = S.weights_global(cfg, seed)
+        it = S.iter_layers(cfg, seed)
+        cache = {}
 
         def get(l):
-            W = ws_src.layer(l)
-            if free_host:
-                ws_src.drop_layer(l)
-            return W
-        return cls(ws_src.cfg, ws_src.glob, get, device)
+            while l not in cache:
+                k, W = next(it)
+                cache[k] = W
+            return cache.pop(l)
+        return cls(cfg, glob, get, device)
 
     # ------------------------------------------------------------------ buffers
     def workspace(self, nbytes: int) -> torch.Tensor:
