@@ -159,7 +159,7 @@ struct Layout {
   // metadata (staged from the host in one copy)
   size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, meta_end;
   // float buffers
-  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, z, lse_rows, logits;
+  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, logits;
   size_t total;
   int Tc;
 };
@@ -191,13 +191,14 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.x = take(4ull * T * c.hidden);
   L.act = take(4ull * T * wide);
   L.big = take(4ull * T * bigw);
-  L.q = take(e * T * HqD);
+  L.q = take(e * T * HqD * (bf ? 2 : 1));   // bf16 models: q hi and lo planes
   L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
   L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
   L.o_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * HqD : 0);
   L.lse_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * c.n_q_heads : 0);
   L.gpart = take(bf ? 4ull * kGemmPartFloats : 0);
   L.h = take(4ull * R * c.hidden);
+  L.hsplit = take(bf && need_logits ? 4ull * R * c.hidden : 0);
   L.z = take(4ull * NT);
   L.lse_rows = take(4ull * R);
   L.logits = take(need_logits ? 4ull * R * c.vocab : 0);
@@ -293,7 +294,13 @@ struct Forward {
     return sp;
   }
 
-  jev_status gemm(const float* A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
+  // A operand: float32 rows (float32 models) or bfloat16 hi/lo planes (bf16 models)
+  struct AOp {
+    const float* f;
+    const uint16_t* hi;
+    const uint16_t* lo;
+  };
+  jev_status gemm(AOp A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
                   const void* w2, int n2, float* C, int ldc, int accum, int kind = K_GEMM) {
     const int N = n0 + n1 + n2;
     const double flops = 2.0 * M * N * K;
@@ -305,7 +312,7 @@ struct Forward {
       float* part = at<float>(ws, L.gpart);
       const int splits = splits_for(M, N, K);
       if (jev_status st = run_k(kind, flops, bytes, [&] {
-            return launch_gemm_bf16(A, lda, M, K, sg, N, C, ldc, accum, splits, part, s, &eff);
+            return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, splits, part, s, &eff);
           }))
         return st;
       if (eff > 1)
@@ -314,7 +321,7 @@ struct Forward {
       return JEV_OK;
     }
     GemmSegsF sg{{(const float*)w0, (const float*)w1, (const float*)w2}, {n0, n0 + n1, N}};
-    return run_k(kind, flops, bytes, [&] { return launch_gemm_f32(A, lda, M, K, sg, N, C, ldc, accum, s); });
+    return run_k(kind, flops, bytes, [&] { return launch_gemm_f32(A.f, lda, M, K, sg, N, C, ldc, accum, s); });
   }
 
   jev_status run(const void* vis, int n_vis) {
@@ -326,6 +333,9 @@ struct Forward {
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
     float* act = at<float>(ws, L.act);
+    uint16_t* act_hi = reinterpret_cast<uint16_t*>(act);          // bf16 models: hi plane
+    uint16_t* act_lo = act_hi + (size_t)T * wide;                  // and lo plane, same rows
+    const AOp A_act{act, act_hi, act_lo};
     float* big = at<float>(ws, L.big);
     const int* tok = at<int>(ws, L.tok);
     const int* pos = at<int>(ws, L.pos);
@@ -356,10 +366,11 @@ struct Forward {
       const jev_layer& W = m->layers[l];
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
       if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
-            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, act, wide, s);
+            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, bf ? nullptr : act,
+                                  bf ? act_hi : nullptr, bf ? act_lo : nullptr, wide, s);
           }))
         return st;
-      if (jev_status st = gemm(act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0)) return st;
+      if (jev_status st = gemm(A_act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0)) return st;
       // K / V destination: the prefix store (prefill) or the workspace (scoring)
       void *kdst, *vdst;
       int kld;
@@ -373,7 +384,8 @@ struct Forward {
         kld = L.Tc;
       }
       if (jev_status st = run_k(K_ROPE, 0.0, (double)T * (Hq + Hkv) * D * (4 + e), [&] {
-            return launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q), kdst, kld, 0, s);
+            return launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q),
+                                  bf ? at<char>(ws, L.q) + (size_t)T * HqD * 2 : nullptr, kdst, kld, 0, s);
           }))
         return st;
       if (jev_status st = run_k(K_VT, 0.0, (double)T * Hkv * D * (4 + e), [&] {
@@ -385,6 +397,7 @@ struct Forward {
       if (bf) {
         AttnArgs a{};
         a.q = at<_Float16>(ws, L.q);
+        a.q_lo = a.q + (size_t)T * HqD;
         a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
         if (P > 0) {
           a.kp = reinterpret_cast<const _Float16*>(store_k(l));
@@ -401,7 +414,7 @@ struct Forward {
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
         if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
         if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 2) * T * HqD, [&] {
-              return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act, s);
+              return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act_hi, act_lo, s);
             }))
           return st;
       } else {
@@ -422,15 +435,18 @@ struct Forward {
         if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f32(a, D, s); })) return st;
       }
       // act now holds o [T][HqD] with row stride HqD
-      if (jev_status st = gemm(act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
+      if (jev_status st = gemm(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
       if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
-            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, act, wide, s);
+            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, bf ? nullptr : act,
+                                  bf ? act_hi : nullptr, bf ? act_lo : nullptr, wide, s);
           }))
         return st;
-      if (jev_status st = gemm(act, wide, T, H, W.w_gate, I, W.w_up, I, nullptr, 0, big, 2 * I, 0)) return st;
-      if (jev_status st = run_k(K_SILU, 0.0, 12.0 * T * I, [&] { return launch_silu_mul(big, T, I, act, s); }))
+      if (jev_status st = gemm(A_act, wide, T, H, W.w_gate, I, W.w_up, I, nullptr, 0, big, 2 * I, 0)) return st;
+      if (jev_status st = run_k(K_SILU, 0.0, 12.0 * T * I, [&] {
+            return launch_silu_mul(big, T, I, bf ? nullptr : act, bf ? act_hi : nullptr, bf ? act_lo : nullptr, s);
+          }))
         return st;   // gate|up [T][2I] -> u [T][I]
-      if (jev_status st = gemm(act, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
+      if (jev_status st = gemm(A_act, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
     }
     return JEV_OK;
   }
@@ -443,9 +459,12 @@ struct Forward {
     const double we = bf ? 2.0 : 4.0;
     float* h = at<float>(ws, L.h);
     float* z = at<float>(ws, L.z);
+    const bool split_h = bf && mode == Mode::Tree;
+    uint16_t* h_hi = split_h ? at<uint16_t>(ws, L.hsplit) : nullptr;
+    uint16_t* h_lo = split_h ? h_hi + (size_t)R * H : nullptr;
     if (jev_status st = run_k(K_RMSNORM, 0.0, 8.0 * R * H, [&] {
           return launch_rmsnorm(bf, at<float>(ws, L.x), H, at<int>(ws, L.read_rows), R, H, m->w.final_norm,
-                                c.rms_eps, h, H, s);
+                                c.rms_eps, h, h_hi, h_lo, H, s);
         }))
       return st;
     if (jev_status st = run_k(K_TARGET, 2.0 * NT * H, NT * H * we, [&] {
@@ -459,8 +478,8 @@ struct Forward {
                [&] { return launch_cand_logsoftmax(z, at<int>(ws, L.out_n), B, NT / std::max(B, 1), out_a, s); });
     }
     float* logits = at<float>(ws, L.logits);
-    if (jev_status st = gemm(h, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits, c.vocab, 0,
-                             K_LMHEAD))
+    if (jev_status st = gemm(AOp{h, h_hi, h_lo}, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits,
+                             c.vocab, 0, K_LMHEAD))
       return st;
     if (jev_status st = run_k(K_ROWLSE, 0.0, 4.0 * R * c.vocab,
                           [&] { return launch_row_lse(logits, c.vocab, R, at<float>(ws, L.lse_rows), s); }))

@@ -16,7 +16,8 @@ struct GemmSegsF {
 
 // float16 MFMA attention (head_dim 128).
 struct AttnArgs {
-  const _Float16* q;       // [T][Hq][128]
+  const _Float16* q;       // [T][Hq][128]  q rounded to f16 (hi)
+  const _Float16* q_lo;    // [T][Hq][128]  q - hi, rounded to f16
   int T, Hq, Hkv, G;
   const _Float16* kp;      // prefix K  [Hkv][ldp][128]
   const _Float16* vtp;     // prefix Vt [Hkv][128][ldp]
@@ -50,26 +51,29 @@ struct AttnArgsF {
 
 hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, int n_vis,
                         float* x, hipStream_t s);
+// y (float32) and/or yh/yl (bfloat16 hi/lo planes) may be null.
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
-                          float eps, float* y, int ldy, hipStream_t s);
+                          float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
 int gemm_bf16_splits(int M, int N, int K);
 // Launches the GEMM; with *eff_splits > 1 it wrote split partials [splits][M][N] into `part`
 // and launch_splitk_reduce must follow.
-hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
-                            int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
+// A is given as two bfloat16 planes (hi, lo) with row stride lda; the product is W·hi + W·lo.
+hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
+                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
 hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
                                 hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
                            int accum, hipStream_t s);
+// q_lo (nullable): second f16 term of q (q - f16(q)); only for f16 output.
 hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv, int D, const int* pos,
-                          double log2_theta, void* q_out, void* k_out, int ldk, int row0, hipStream_t s);
+                          double log2_theta, void* q_out, void* q_lo, void* k_out, int ldk, int row0, hipStream_t s);
 hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int HD, void* vt, int ldv, int col0,
                               hipStream_t s);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, float* o,
-                             hipStream_t s);
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
+                             uint16_t* ol, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);
-hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, hipStream_t s);
+hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh, uint16_t* ul, hipStream_t s);
 hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,
                                 int NT, float* z, hipStream_t s);
 hipError_t launch_cand_logsoftmax(const float* z, const int* n_cands, int B, int C, float* out, hipStream_t s);

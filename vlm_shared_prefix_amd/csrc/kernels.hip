@@ -79,7 +79,8 @@ template <typename WT>
 __global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x, int ldx,
                                                     const int* __restrict__ rows, int n_rows, int H,
                                                     const WT* __restrict__ g, float eps,
-                                                    float* __restrict__ y, int ldy) {
+                                                    float* __restrict__ y, u16* __restrict__ yh,
+                                                    u16* __restrict__ yl, int ldy) {
   __shared__ float red[4];
   const int i = blockIdx.x;
   if (i >= n_rows) return;
@@ -89,8 +90,15 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x,
   for (int k = threadIdx.x; k < H; k += 256) { float v = xr[k]; ss += v * v; }
   ss = block_sum256(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  float* yr = y + (size_t)i * ldy;
-  for (int k = threadIdx.x; k < H; k += 256) yr[k] = ldw(g, k) * (xr[k] * r);
+  for (int k = threadIdx.x; k < H; k += 256) {
+    const float v = ldw(g, k) * (xr[k] * r);
+    if (y) y[(size_t)i * ldy + k] = v;
+    if (yh) {
+      const u16 h = f32_to_bf16(v);
+      yh[(size_t)i * ldy + k] = h;
+      yl[(size_t)i * ldy + k] = f32_to_bf16(v - bf16_to_f32(h));
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -113,9 +121,9 @@ __device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
   return s.w[2] + (size_t)(n - s.n_end[1]) * K;
 }
 
-__global__ void __launch_bounds__(256, 2) gemm_bf16s(const float* __restrict__ A, int lda, int M, int K,
-                                                     GemmSegs seg, int N, int m_tiles, int n_tiles,
-                                                     int splits, int k_chunk, float* __restrict__ C,
+__global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+                                                     int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
+                                                     int n_tiles, int splits, int k_chunk, float* __restrict__ C,
                                                      int ldc, size_t split_stride, int accum) {
   __shared__ __attribute__((aligned(16))) u16 sAh[GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sAl[GBM * GLD];
@@ -139,49 +147,39 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const float* __restrict__ A
   const int ql = lane & 31, hl = lane >> 5;
   const bool wave_active = (m0 + wm * 64) < M;
 
-  // global -> register staging
-  float4 ra[8];
-  uint4 rw[4];
+  // global -> register staging; rows past M / N read row 0 and are zeroed at the LDS store
+  uint4 rh[4], rl[4], rw[4];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
-      const int row = idx >> 4, c4 = idx & 15;
-      const int gm = m0 + row;
-      ra[i] = (gm < M) ? *reinterpret_cast<const float4*>(A + (size_t)gm * lda + k0 + c4 * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int row = idx >> 3, c8 = idx & 7;
+      const int gm = (m0 + row < M) ? m0 + row : 0;
+      const size_t off = (size_t)gm * lda + k0 + c8 * 8;
+      rh[i] = *reinterpret_cast<const uint4*>(Ah + off);
+      rl[i] = *reinterpret_cast<const uint4*>(Al + off);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
       const int nr = idx >> 3, c8 = idx & 7;
-      const int gn = n0 + nr;
-      rw[i] = (gn < N) ? *reinterpret_cast<const uint4*>(seg_row(seg, gn, K) + k0 + c8 * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
+      const int gn = (n0 + nr < N) ? n0 + nr : 0;
+      rw[i] = *reinterpret_cast<const uint4*>(seg_row(seg, gn, K) + k0 + c8 * 8);
     }
   };
   auto sstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx >> 4, c4 = idx & 15;
-      const float f[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-      u16 h[4], l[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] = f32_to_bf16(f[j]);
-        l[j] = f32_to_bf16(f[j] - bf16_to_f32(h[j]));
-      }
-      uint2 hv = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-      uint2 lv = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
-      *reinterpret_cast<uint2*>(&sAh[row * GLD + c4 * 4]) = hv;
-      *reinterpret_cast<uint2*>(&sAl[row * GLD + c4 * 4]) = lv;
-    }
-#pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
-      const int nr = idx >> 3, c8 = idx & 7;
-      *reinterpret_cast<uint4*>(&sW[nr * GLD + c8 * 8]) = rw[i];
+      const int row = idx >> 3, c8 = idx & 7;
+      const uint32_t ma = (m0 + row < M) ? 0xFFFFFFFFu : 0u;
+      const uint32_t mw = (n0 + row < N) ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<uint4*>(&sAh[row * GLD + c8 * 8]) =
+          make_uint4(rh[i].x & ma, rh[i].y & ma, rh[i].z & ma, rh[i].w & ma);
+      *reinterpret_cast<uint4*>(&sAl[row * GLD + c8 * 8]) =
+          make_uint4(rl[i].x & ma, rl[i].y & ma, rl[i].z & ma, rl[i].w & ma);
+      *reinterpret_cast<uint4*>(&sW[row * GLD + c8 * 8]) =
+          make_uint4(rw[i].x & mw, rw[i].y & mw, rw[i].z & mw, rw[i].w & mw);
     }
   };
 
@@ -240,14 +238,17 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const float* __restrict__ A
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + ql;
-      if (col >= N) continue;
+      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
+      float old[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (row < M) {
-          float* p = Cb + (size_t)row * ldc + col;
-          *p = add ? (*p + acc[i][j][r]) : acc[i][j][r];
-        }
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
       }
     }
 }
@@ -333,8 +334,8 @@ template <> __device__ __forceinline__ float cvt_out<float>(float v) { return v;
 template <typename OT>
 __global__ void __launch_bounds__(256) rope_qk(const float* __restrict__ qkv, int T, int Hq, int Hkv, int D,
                                                const int* __restrict__ pos, double log2_theta,
-                                               OT* __restrict__ q_out, OT* __restrict__ k_out, int ldk,
-                                               int row0) {
+                                               OT* __restrict__ q_out, OT* __restrict__ q_lo, OT* __restrict__ k_out,
+                                               int ldk, int row0) {
   const int t = blockIdx.x;
   if (t >= T) return;
   const int half = D >> 1;
@@ -351,9 +352,14 @@ __global__ void __launch_bounds__(256) rope_qk(const float* __restrict__ qkv, in
     const float ra = a * c - b * s;
     const float rb = b * c + a * s;
     if (h < Hq) {
-      OT* d = q_out + ((size_t)t * Hq + h) * D;
-      d[i] = cvt_out<OT>(ra);
-      d[i + half] = cvt_out<OT>(rb);
+      const size_t o = ((size_t)t * Hq + h) * D;
+      const OT qa = cvt_out<OT>(ra), qb = cvt_out<OT>(rb);
+      q_out[o + i] = qa;
+      q_out[o + i + half] = qb;
+      if (q_lo) {
+        q_lo[o + i] = cvt_out<OT>(ra - (float)qa);
+        q_lo[o + i + half] = cvt_out<OT>(rb - (float)qb);
+      }
     } else {
       OT* d = k_out + ((size_t)(h - Hq) * ldk + row0 + t) * D;
       d[i] = cvt_out<OT>(ra);
@@ -406,9 +412,21 @@ __global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src
 #define KLD (128 + 8)    // halfs; 272 B rows
 #define VLD (AT_BK + 4)  // halfs; 136 B rows
 
+// zero the 16-bit lanes j >= cnt of an 8 x f16 chunk (cnt in [0, 8])
+__device__ __forceinline__ uint4 keep_first(uint4 v, int cnt) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = (2 * j < cnt) ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (2 * j + 1 < cnt) ? 0xFFFF0000u : 0u;
+    w[j] &= (lo | hi);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16 sK[AT_BK * KLD];
-  __shared__ __attribute__((aligned(16))) f16 sV[128 * VLD];
+  __shared__ __attribute__((aligned(16))) f16 sK[2][AT_BK * KLD];
+  __shared__ __attribute__((aligned(16))) f16 sV[2][128 * VLD];
 
   const int hk = blockIdx.y, split = blockIdx.z;
   const int G = a.G, T = a.T, Hq = a.Hq;
@@ -419,18 +437,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int ql = lane & 31, hl = lane >> 5;
   const int r = r0 + wave * 32 + ql;
   const bool rvalid = r < R;
-  const int t = rvalid ? r / G : 0;
-  const int hq = hk * G + (rvalid ? r % G : 0);
+  const int rc = rvalid ? r : R - 1;          // clamped row: loads stay in bounds
+  const int t = rc / G;
+  const int hq = hk * G + rc % G;
 
-  f16x8 qreg[8];
+  // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
+  // of q, which would shift every score of the row coherently, stays out.
+  f16x8 qreg[8], qlo[8];
   {
-    const f16* qp = a.q + ((size_t)t * Hq + hq) * 128 + hl * 8;
+    const size_t qo = ((size_t)t * Hq + hq) * 128 + hl * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (rvalid) qreg[c] = *reinterpret_cast<const f16x8*>(qp + c * 16);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[c][e] = (f16)0.f;
+      qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 16);
+      qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 16);
     }
   }
 
@@ -452,9 +471,52 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     Vb = a.vts + (size_t)hk * 128 * a.lds;
     ld = a.lds;
   }
-  const int my_start = (own && rvalid) ? a.seq_start[t] : 0;
-  const uint64_t my_mask = (own && rvalid && a.mask) ? a.mask[t] : 0ull;
-  const bool use_mask = a.mask != nullptr;
+  const int my_start = own ? a.seq_start[t] : 0;
+  const bool use_mask = own && a.mask != nullptr;
+  const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
+  // visible keys of this row within the split: [vis_lo, vis_hi)
+  const int vis_lo = own ? max(kb, my_start) : kb;
+  const int vis_hi = own ? min(ke, t + 1) : ke;
+
+  // tile loader: every load is issued unconditionally from an in-bounds address
+  // (rows < ke <= ld; a V chunk at a multiple of 8 below ld ends inside its row)
+  // and out-of-range data is zeroed afterwards, so the loads of a tile are in flight together.
+  uint4 rk[4], rv[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int key = k0 + (idx >> 4), c = idx & 15;
+      const int krow = key < ke ? key : 0;
+      rk[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)krow * 128 + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int d = idx >> 3, gk = k0 + (idx & 7) * 8;
+      const int col = gk < ld ? gk : 0;
+      rv[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)d * ld + col);
+    }
+  };
+  auto sstore = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const uint32_t m = (k0 + (idx >> 4) < ke) ? 0xFFFFFFFFu : 0u;
+      const uint4 v = make_uint4(rk[i].x & m, rk[i].y & m, rk[i].z & m, rk[i].w & m);
+      *reinterpret_cast<uint4*>(&sK[buf][(idx >> 4) * KLD + (idx & 15) * 8]) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int d = idx >> 3, c = idx & 7;
+      const int cnt = min(max(ke - (k0 + c * 8), 0), 8);
+      const uint4 v = keep_first(rv[i], cnt);
+      uint2* dst = reinterpret_cast<uint2*>(&sV[buf][d * VLD + c * 8]);
+      dst[0] = make_uint2(v.x, v.y);
+      dst[1] = make_uint2(v.z, v.w);
+    }
+  };
 
   float m_run = NEG_INF, l_run = 0.f;
   f32x16 acc[4];
@@ -463,42 +525,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
 
-  for (int k0 = kb & ~7; k0 < ke; k0 += AT_BK) {
+  const int kfirst = kb & ~7;
+  const int ntiles = (ke > kfirst) ? (ke - kfirst + AT_BK - 1) / AT_BK : 0;
+  if (ntiles > 0) {
+    gload(kfirst);
+    sstore(kfirst, 0);
     __syncthreads();
-    // K tile: 64 keys x 128 d
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = idx >> 4, c = idx & 15;
-      const int gk = k0 + key;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (gk < ke) val = *reinterpret_cast<const uint4*>(Kb + (size_t)gk * 128 + c * 8);
-      *reinterpret_cast<uint4*>(&sK[key * KLD + c * 8]) = val;
-    }
-    // V^T tile: 128 d x 64 keys
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int d = idx >> 3, c = idx & 7;
-      const int gk = k0 + c * 8;
-      const f16* src = Vb + (size_t)d * ld + gk;
-      uint4 val;
-      if (gk + 8 <= ke) {
-        val = *reinterpret_cast<const uint4*>(src);
-      } else {
-        u16 e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (gk + j < ke) ? reinterpret_cast<const u16*>(src)[j] : (u16)0;
-        val = make_uint4((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
-                         (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16));
-      }
-      uint2* dst = reinterpret_cast<uint2*>(&sV[d * VLD + c * 8]);
-      dst[0] = make_uint2(val.x, val.y);
-      dst[1] = make_uint2(val.z, val.w);
-    }
-    __syncthreads();
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = kfirst + it * AT_BK;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) gload(k0 + AT_BK);      // in flight while this tile is computed
 
-    // scores for the two 32-key halves
+    // scores for the two 32-key halves (unscaled)
     f32x16 s[2];
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
@@ -506,67 +546,91 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       for (int i = 0; i < 16; ++i) s[hs][i] = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const f16x8 kop = *reinterpret_cast<const f16x8*>(&sK[(hs * 32 + ql) * KLD + c * 16 + hl * 8]);
+        const f16x8 kop = *reinterpret_cast<const f16x8*>(&sK[buf][(hs * 32 + ql) * KLD + c * 16 + hl * 8]);
         s[hs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qreg[c], s[hs], 0, 0, 0);
+        s[hs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qlo[c], s[hs], 0, 0, 0);
       }
     }
-    // mask + scale; key of register i = k0 + hs*32 + 8*(i/4) + 4*hl + (i%4)
+    // Only tiles that cross the split's range or hold own-row keys need a mask;
+    // the test is uniform over the block.  Rows past R hold a clamped row's
+    // finite scores and are never stored, so they need no mask.  A row sees
+    // keys in [vis_lo, vis_hi) (and, with a tree mask, only its ancestors).
+    // key of register i = k0 + hs*32 + 8*(i/4) + 4*hl + (i%4)
+    if (own || k0 < kb || k0 + AT_BK > ke) {
+      const int base = k0 + 4 * hl;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = base + hs * 32 + 8 * (i >> 2) + (i & 3);
+          const bool in = (unsigned)(key - vis_lo) < (unsigned)(vis_hi - vis_lo);
+          s[hs][i] = in ? s[hs][i] : NEG_INF;
+        }
+      if (use_mask) {
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rel = base + hs * 32 + 8 * (i >> 2) + (i & 3) - my_start;
+            const bool bit = (my_mask >> (rel & 63)) & 1ull;
+            s[hs][i] = bit ? s[hs][i] : NEG_INF;
+          }
+      }
+    }
     float mx = NEG_INF;
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + hs * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
-        bool ok = rvalid && key >= kb && key < ke;
-        if (own) {
-          ok = ok && key >= my_start && key <= t;
-          if (use_mask) ok = ok && ((my_mask >> ((key - my_start) & 63)) & 1ull);
-        }
-        const float v = ok ? s[hs][i] * a.scale_log2 : NEG_INF;
-        s[hs][i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[hs][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx);                 // running max, unscaled
     const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float sl = a.scale_log2;
+    const float neg_ms = -m_use * sl;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl);
+    // p = 2^(s*scale - m*scale), rounded to f16 for the P·V product; the row sum
+    // is taken over the same rounded values so the weights stay normalised.
     float rs = 0.f;
+    f16x8 pops[2][2];
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(s[hs][i] - m_use);
-        s[hs][i] = pv;
-        rs += pv;
-      }
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f16 ph = (f16)__builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, neg_ms));
+          pops[hs][p][j] = ph;
+          rs += (float)ph;
+        }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    // rescale the accumulators only when some lane's max moved
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
+    }
 
     // O^T += V^T · P^T, four 16-key steps
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        f16x8 pop;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pop[j] = (f16)s[hs][8 * p + j];
+        const f16x8 pop = pops[hs][p];
         const int kofs = hs * 32 + 16 * p + 4 * hl;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const f16* vrow = &sV[(dt * 32 + ql) * VLD + kofs];
-          const f16x4 v0 = *reinterpret_cast<const f16x4*>(vrow);
-          const f16x4 v1 = *reinterpret_cast<const f16x4*>(vrow + 8);
-          f16x8 vop;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) { vop[j] = v0[j]; vop[4 + j] = v1[j]; }
+          const f16* vrow = &sV[buf][(dt * 32 + ql) * VLD + kofs];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
+          const f16x8 vop = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop, acc[dt], 0, 0, 0);
         }
       }
+    if (more) sstore(k0 + AT_BK, buf ^ 1);
+    __syncthreads();
   }
 
   if (!rvalid) return;
@@ -582,13 +646,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       *reinterpret_cast<float4*>(op + d) = v;
     }
   if (hl == 0)
-    a.lse_part[((size_t)split * T + t) * Hq + hq] = (l_run > 0.f) ? m_run + log2f(l_run) : NEG_INF;
+    a.lse_part[((size_t)split * T + t) * Hq + hq] = (l_run > 0.f) ? m_run * a.scale_log2 + log2f(l_run) : NEG_INF;
 }
 
 // Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M).
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
-                                                  int D, float* __restrict__ o) {
+                                                  int D, u16* __restrict__ oh, u16* __restrict__ ol) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one (t, hq)
   const int d4 = D >> 2;
   if (i >= (size_t)T * Hq * d4) return;
@@ -609,7 +673,18 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  reinterpret_cast<float4*>(o + th * D)[c] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  u16 h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = f32_to_bf16(v[j]);
+    l[j] = f32_to_bf16(v[j] - bf16_to_f32(h[j]));
+  }
+  const size_t at4 = th * D + 4 * c;
+  *reinterpret_cast<uint2*>(oh + at4) =
+      make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  *reinterpret_cast<uint2*>(ol + at4) =
+      make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
 }
 
 // ----------------------------------------------------------------------------
@@ -660,12 +735,19 @@ __global__ void __launch_bounds__(64) attn_fwd_f32(AttnArgsF a) {
 // SwiGLU: u[t][i] = silu(gu[t][i]) * gu[t][I + i]
 // ----------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) silu_mul(const float* __restrict__ gu, int T, int I,
-                                                float* __restrict__ u) {
+                                                float* __restrict__ u, u16* __restrict__ uh,
+                                                u16* __restrict__ ul) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)T * I) return;
   const size_t t = i / I, c = i % I;
   const float g = gu[t * 2 * I + c], up = gu[t * 2 * I + I + c];
-  u[i] = g / (1.0f + expf(-g)) * up;
+  const float v = g / (1.0f + expf(-g)) * up;
+  if (u) u[i] = v;
+  if (uh) {
+    const u16 h = f32_to_bf16(v);
+    uh[i] = h;
+    ul[i] = f32_to_bf16(v - bf16_to_f32(h));
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -783,12 +865,12 @@ hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, 
 }
 
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
-                          float eps, float* y, int ldy, hipStream_t s) {
+                          float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   if (bf16)
-    rmsnorm_rows<u16><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const u16*)g, eps, y, ldy);
+    rmsnorm_rows<u16><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const u16*)g, eps, y, yh, yl, ldy);
   else
-    rmsnorm_rows<float><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const float*)g, eps, y, ldy);
+    rmsnorm_rows<float><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const float*)g, eps, y, yh, yl, ldy);
   return hipGetLastError();
 }
 
@@ -802,8 +884,8 @@ int gemm_bf16_splits(int M, int N, int K) {
   return s < 1 ? 1 : s;
 }
 
-hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C,
-                            int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
+                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
   *eff_splits = 1;
   if (M <= 0 || N <= 0) return hipSuccess;
   const int mt = cdiv(M, GBM), nt = cdiv(N, GBN);
@@ -813,9 +895,9 @@ hipError_t launch_gemm_bf16(const float* A, int lda, int M, int K, const GemmSeg
   const int nb = mt * nt * splits;
   const int grid = cdiv(nb, 8) * 8;
   if (splits == 1)
-    gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
   else
-    gemm_bf16s<<<grid, 256, 0, s>>>(A, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, (size_t)M * N, 0);
+    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, (size_t)M * N, 0);
   return hipGetLastError();
 }
 
@@ -835,12 +917,14 @@ hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegs
 }
 
 hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv, int D, const int* pos,
-                          double log2_theta, void* q_out, void* k_out, int ldk, int row0, hipStream_t s) {
+                          double log2_theta, void* q_out, void* q_lo, void* k_out, int ldk, int row0, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (f16out)
-    rope_qk<f16><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (f16*)q_out, (f16*)k_out, ldk, row0);
+    rope_qk<f16><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (f16*)q_out, (f16*)q_lo, (f16*)k_out, ldk,
+                                   row0);
   else
-    rope_qk<float><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (float*)q_out, (float*)k_out, ldk, row0);
+    rope_qk<float><<<T, 256, 0, s>>>(qkv, T, Hq, Hkv, D, pos, log2_theta, (float*)q_out, (float*)q_lo,
+                                     (float*)k_out, ldk, row0);
   return hipGetLastError();
 }
 
@@ -862,10 +946,10 @@ hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, float* o,
-                             hipStream_t s) {
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
+                             uint16_t* ol, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, o);
+  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol);
   return hipGetLastError();
 }
 
@@ -879,9 +963,9 @@ hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, hipStream_t s) {
+hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh, uint16_t* ul, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  silu_mul<<<cdiv((long)T * I, 256), 256, 0, s>>>(gu, T, I, u);
+  silu_mul<<<cdiv((long)T * I, 256), 256, 0, s>>>(gu, T, I, u, uh, ul);
   return hipGetLastError();
 }
 
