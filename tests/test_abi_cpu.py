@@ -1,0 +1,284 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/jev.h declares, validates arguments before any HIP call, and plans
+suffix batches and candidate trees as the pages describe.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import jev_synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jev.h")
+LIB = os.path.join(ROOT, "vlm_shared_prefix_amd", "libjev.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libjev.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jev_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    lib = C.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 15
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    from vlm_shared_prefix_amd import jev as J
+    assert set(J.EXPORTED) == set(names), set(names) ^ set(J.EXPORTED)
+
+
+def _cfg(**kw):
+    from vlm_shared_prefix_amd import jev as J
+    base = dict(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128, mlp=512, vocab=1000,
+                rope_theta=1e4, rms_eps=1e-6, dtype=J.JEV_BF16)
+    base.update(kw)
+    return J.make_config(**base)
+
+
+def _fake_weights(n_layers):
+    """Non-null dummy pointers: creation only records them (no HIP call)."""
+    from vlm_shared_prefix_amd import jev as J
+    arr = (J.jev_layer * max(n_layers, 1))()
+    for i in range(n_layers):
+        arr[i] = J.jev_layer(*([0x1000 + i] * 9))
+    return J.jev_weights(0x100, 0x200, 0x300, arr), arr
+
+
+def test_model_create_validation():
+    from vlm_shared_prefix_amd import jev as J
+    w, keep = _fake_weights(2)
+    m = J.jev_model_create(_cfg(), w)
+    assert m
+    st = J.jev_get_stats(m)
+    assert st == {"prefills": 0, "forwards": 0, "rows": 0, "launches": 0}
+    J.jev_model_destroy(m)
+    cases = [
+        (dict(n_q_heads=5), J.JEV_E_UNSUPPORTED),          # Hq % Hkv
+        (dict(head_dim=64), J.JEV_E_UNSUPPORTED),          # bf16 needs D = 128
+        (dict(hidden=250), J.JEV_E_UNSUPPORTED),           # bf16 needs H % 64 == 0
+        (dict(vocab=0), J.JEV_E_INVALID),
+        (dict(dtype=7), J.JEV_E_INVALID),
+        (dict(rope_theta=-1.0), J.JEV_E_INVALID),
+    ]
+    for kw, code in cases:
+        with pytest.raises(J.JevError) as e:
+            J.jev_model_create(_cfg(**kw), w)
+        assert e.value.code == code, kw
+    # float32 models accept head_dim 64 and any hidden size
+    m = J.jev_model_create(_cfg(dtype=J.JEV_F32, head_dim=64, hidden=250, mlp=688), w)
+    J.jev_model_destroy(m)
+    bad = J.jev_weights(0, 0x200, 0x300, keep)
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_create(_cfg(), bad)
+    assert e.value.code == J.JEV_E_INVALID
+
+
+@pytest.fixture
+def model():
+    from vlm_shared_prefix_amd import jev as J
+    w, keep = _fake_weights(2)
+    m = J.jev_model_create(_cfg(), w)
+    yield m, keep
+    J.jev_model_destroy(m)
+
+
+class _FakeDev:
+    """Stands in for a device tensor: a pointer and a size, never dereferenced on this path."""
+
+    def __init__(self, nbytes, ptr=0x7000):
+        self._n, self._p = nbytes, ptr
+
+    def data_ptr(self):
+        return self._p
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+
+def test_prefix_and_workspace_sizes(model):
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    # store = L * 2 * Hkv * round64(P) * D * 2 bytes (f16)
+    assert J.jev_prefix_bytes(m, 100) == 2 * 2 * 2 * 128 * 128 * 2
+    assert J.jev_prefix_bytes(m, 0) == 0
+    a = J.jev_workspace_bytes(m, 100, 50, 4, 12)
+    b = J.jev_workspace_bytes(m, 100, 100, 8, 24)
+    assert 0 < a < b
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefix_create(m, 100, _FakeDev(10))
+    assert e.value.code == J.JEV_E_WORKSPACE
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefix_create(m, 40000, _FakeDev(1 << 40))
+    assert e.value.code == J.JEV_E_UNSUPPORTED
+
+
+def test_score_validation_before_any_launch(model):
+    """Every bad argument is rejected on the host; B = 0 does no work (Ochevid: all-skipped requests)."""
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    p = J.jev_prefix_create(m, 10, _FakeDev(J.jev_prefix_bytes(m, 10)))
+    ws = _FakeDev(1 << 30)
+    out = _FakeDev(1 << 20)
+    ids = np.zeros((2, 4), np.int32)
+    lens = np.array([4, 2], np.int32)
+    cands = np.array([[1, 2], [3, 4]], np.int32)
+    nc = np.array([2, 2], np.int32)
+    bad = [
+        (dict(lens=np.array([5, 2], np.int32)), J.JEV_E_INVALID),      # L_b > S_max
+        (dict(lens=np.array([0, 2], np.int32)), J.JEV_E_INVALID),      # L_b < 1
+        (dict(ids=np.full((2, 4), 1000, np.int32)), J.JEV_E_INVALID),  # id >= V
+        (dict(cands=np.array([[1, -1], [3, 4]], np.int32)), J.JEV_E_INVALID),
+        (dict(nc=np.array([3, 2], np.int32)), J.JEV_E_INVALID),        # n_cands > C_max
+        (dict(nc=np.array([0, 2], np.int32)), J.JEV_E_INVALID),
+        (dict(ids=np.zeros((2, 300), np.int32), lens=np.array([4, 2], np.int32)), J.JEV_E_UNSUPPORTED),
+    ]
+    for kw, code in bad:
+        a = dict(ids=ids, lens=lens, cands=cands, nc=nc)
+        a.update(kw)
+        with pytest.raises(J.JevError) as e:
+            J.jev_score_suffixes(p, a["ids"], a["lens"], a["cands"], a["nc"], out, ws, stream=0)
+        assert e.value.code == code, kw
+    # too small a workspace
+    with pytest.raises(J.JevError) as e:
+        J.jev_score_suffixes(p, ids, lens, cands, nc, out, _FakeDev(100), stream=0)
+    assert e.value.code == J.JEV_E_WORKSPACE
+    # B = 0: OK and nothing launched
+    J.jev_score_suffixes(p, np.zeros((0, 4), np.int32), np.zeros(0, np.int32), np.zeros((0, 2), np.int32),
+                         np.zeros(0, np.int32), None, None, stream=0)
+    assert J.jev_get_stats(m)["launches"] == 0
+    # prefill: counts must add up to the prefix length; ids in range
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefill_prefix(p, _FakeDev(1), 3, np.zeros(5, np.int32), ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefill_prefix(p, _FakeDev(1), 5, np.full(5, 5000, np.int32), ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID
+    J.jev_prefix_destroy(p)
+
+
+# ---------------------------------------------------------------- tree planning
+def reference_trie(tree, mode):
+    """Independent pure-Python packer: rows (token, depth, group), visibility and predictor rows."""
+    Q, C, K = tree["cand_tok"].shape
+    rows, target = [], {}
+    for q in range(Q):
+        s = int(tree["stem_lens"][q])
+        stem = [int(x) for x in tree["stem_ids"][q, :s]]
+
+        def chain(tokens, depth0, parent, group, anc):
+            out = []
+            for i, tkn in enumerate(tokens):
+                rows.append({"tok": tkn, "depth": depth0 + i, "group": group, "anc": set(anc) | {len(rows)}})
+                anc = rows[-1]["anc"]
+                out.append(len(rows) - 1)
+            return out
+
+        n = int(tree["n_cands"][q])
+        if mode != 2:
+            g = q
+            stem_rows = chain(stem, 0, None, g, set())
+            last = stem_rows[-1]
+            children = {}
+        for c in range(n):
+            Kc = int(tree["cand_lens"][q, c])
+            w = [int(x) for x in tree["cand_tok"][q, c, :Kc]]
+            if mode == 2:
+                g = ("flat", q, c)
+                stem_rows = chain(stem, 0, None, g, set())
+                last = stem_rows[-1]
+                children = {}
+            parent = last
+            for k in range(Kc):
+                target[(q, c, k)] = parent
+                if k == Kc - 1:
+                    break
+                key = (parent, w[k])
+                if mode == 0 and key in children:
+                    parent = children[key]
+                    continue
+                rows.append({"tok": w[k], "depth": s + k, "group": g, "anc": rows[parent]["anc"] | {len(rows)}})
+                if mode == 0:
+                    children[key] = len(rows) - 1
+                parent = len(rows) - 1
+    return rows, target
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("name,seed", [("t1", 1), ("m5", 0), ("c5", 0)])
+def test_tree_plan_matches_reference(name, seed, mode):
+    from vlm_shared_prefix_amd import jev as J
+    tree = S.tree_inputs(S.CONFIGS[name], seed)
+    plan = J.jev_tree_plan_rows(tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                                tree["n_cands"], mode)
+    rows, target = reference_trie(tree, mode)
+    assert len(plan["tok"]) == len(rows)
+    np.testing.assert_array_equal(plan["tok"], [r["tok"] for r in rows])
+    np.testing.assert_array_equal(plan["depth"], [r["depth"] for r in rows])
+    # groups: same partition of rows
+    ref_g = [r["group"] for r in rows]
+    for i in range(len(rows)):
+        for j in range(i + 1, min(len(rows), i + 70)):
+            assert (plan["group"][i] == plan["group"][j]) == (ref_g[i] == ref_g[j])
+    # visibility: bit j of row r <-> row (group start + j) is an ancestor-or-self of r
+    start = {}
+    for i, g in enumerate(plan["group"]):
+        start.setdefault(int(g), i)
+    for r, row in enumerate(rows):
+        s0 = start[int(plan["group"][r])]
+        vis = {s0 + b for b in range(64) if (int(plan["mask"][r]) >> b) & 1}
+        assert vis == row["anc"], r
+    Q, C, K = tree["cand_tok"].shape
+    for q in range(Q):
+        for c in range(C):
+            for k in range(K):
+                want = target.get((q, c, k), -1)
+                assert plan["target_row"][q, c, k] == want
+
+
+def test_trie_merges_only_same_parent_and_token():
+    """Equal tokens after different histories stay separate ("FastJEV" §3.3)."""
+    from vlm_shared_prefix_amd import jev as J
+    stem = np.array([[7, 8]], np.int32)
+    cand = np.array([[[1, 2, 3], [1, 2, 4], [5, 2, 3], [1, 2, 3]]], np.int32)
+    lens = np.array([[3, 3, 3, 3]], np.int32)
+    nc = np.array([4], np.int32)
+    sizes = {m: J.jev_tree_plan_size(stem, np.array([2], np.int32), cand, lens, nc, m)[0] for m in (0, 1, 2)}
+    # trie: stem 2 + {1, 1->2} shared by cands 0,1,3 + {5, 5->2} for cand 2  = 6 rows
+    # stem-only: 2 + 4 * 2 = 10 rows; flat: 4 * (2 + 2) = 16 rows
+    assert sizes == {0: 6, 1: 10, 2: 16}
+    plan = J.jev_tree_plan_rows(stem, np.array([2], np.int32), cand, lens, nc, 0)
+    # identical candidates 0 and 3 share every predictor row
+    np.testing.assert_array_equal(plan["target_row"][0, 0], plan["target_row"][0, 3])
+    # token 2 under parent 1 and under parent 5 are different rows
+    assert plan["target_row"][0, 0, 2] != plan["target_row"][0, 2, 2]
+
+
+def test_tree_validation():
+    from vlm_shared_prefix_amd import jev as J
+    stem = np.zeros((1, 70), np.int32)
+    cand = np.zeros((1, 1, 2), np.int32)
+    with pytest.raises(J.JevError) as e:
+        J.jev_tree_plan_size(stem, np.array([70], np.int32), cand, np.array([[2]], np.int32),
+                             np.array([1], np.int32), 0)
+    assert e.value.code == J.JEV_E_UNSUPPORTED          # S_max > 64
+    stem = np.zeros((1, 60), np.int32)
+    cand = np.zeros((1, 3, 4), np.int32)
+    cand[0, :, 0] = [1, 2, 3]
+    with pytest.raises(J.JevError) as e:                 # group of 60 + 3*3 rows > 64
+        J.jev_tree_plan_size(stem, np.array([60], np.int32), cand, np.full((1, 3), 4, np.int32),
+                             np.array([3], np.int32), 1)
+    assert e.value.code == J.JEV_E_UNSUPPORTED
+    with pytest.raises(J.JevError) as e:
+        J.jev_tree_plan_size(stem, np.array([60], np.int32), cand, np.full((1, 3), 4, np.int32),
+                             np.array([3], np.int32), 5)
+    assert e.value.code == J.JEV_E_INVALID
