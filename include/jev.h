@@ -54,7 +54,7 @@ typedef int32_t jev_status;
  * residual; final RMSNorm; untied LM head.  No biases. */
 typedef struct {
     int32_t n_layers;     /* >= 0                                                       */
-    int32_t hidden;       /* H; multiple of 64 for JEV_BF16                             */
+    int32_t hidden;       /* H; multiple of 64 and <= 8192 for JEV_BF16                 */
     int32_t n_q_heads;    /* Hq                                                         */
     int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0; q head h reads kv head h / (Hq/Hkv)    */
     int32_t head_dim;     /* D; 128 for JEV_BF16, 64 or 128 for JEV_F32                 */

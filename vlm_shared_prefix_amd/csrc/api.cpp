@@ -91,6 +91,7 @@ extern "C" jev_status jev_model_create(const jev_config* cfg, const jev_weights*
   if (c.n_q_heads % c.n_kv_heads) return fail(JEV_E_UNSUPPORTED, "n_q_heads not a multiple of n_kv_heads");
   if (c.dtype == JEV_BF16 && (c.hidden % 64 || c.mlp % 64))
     return fail(JEV_E_UNSUPPORTED, "bf16 models need hidden and mlp multiples of 64");
+  if (c.dtype == JEV_BF16 && c.hidden > 8192) return fail(JEV_E_UNSUPPORTED, "bf16 models need hidden <= 8192");
   if (c.dtype == JEV_BF16 && c.head_dim != 128) return fail(JEV_E_UNSUPPORTED, "bf16 models need head_dim 128");
   if (c.dtype == JEV_F32 && c.head_dim != 64 && c.head_dim != 128)
     return fail(JEV_E_UNSUPPORTED, "head_dim must be 64 or 128");
@@ -159,7 +160,7 @@ struct Layout {
   // metadata (staged from the host in one copy)
   size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, meta_end;
   // float buffers
-  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, logits;
+  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, logits, rope;
   size_t total;
   int Tc;
 };
@@ -202,6 +203,7 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.z = take(4ull * NT);
   L.lse_rows = take(4ull * R);
   L.logits = take(need_logits ? 4ull * R * c.vocab : 0);
+  L.rope = take(bf ? 8ull * T * 64 : 0);
   L.total = o;
   return L;
 }
@@ -324,7 +326,145 @@ struct Forward {
     return run_k(kind, flops, bytes, [&] { return launch_gemm_f32(A.f, lda, M, K, sg, N, C, ldc, accum, s); });
   }
 
+  // bf16 GEMM whose split-K partials (if any) are left for a fused consumer:
+  // on return *splits_out is 1 (C written / accumulated) or > 1 (partials in gpart, stride M*N).
+  jev_status gemm_deferred(AOp A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
+                           const void* w2, int n2, float* C, int ldc, int accum, int* splits_out) {
+    const int N = n0 + n1 + n2;
+    const double flops = 2.0 * M * N * K;
+    const double bytes = 2.0 * N * K + 4.0 * M * K + 4.0 * M * N * (accum ? 2 : 1);
+    GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
+    float* part = at<float>(ws, L.gpart);
+    const int splits = splits_for(M, N, K);
+    return run_k(K_GEMM, flops, bytes, [&] {
+      return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, splits, part, s, splits_out);
+    });
+  }
+
+  // Forward of a bf16 model: every GEMM consumer fused with the split-K reduction.
+  jev_status run_bf16(const void* vis, int n_vis) {
+    const int T = plan.T;
+    const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
+    const int HqD = Hq * D, NQKV = nqkv(c);
+    const int wide = std::max(std::max(H, HqD), I);
+    float* x = at<float>(ws, L.x);
+    uint16_t* a_hi = at<uint16_t>(ws, L.act);                 // normalised activations / attention output
+    uint16_t* a_lo = a_hi + (size_t)T * wide;
+    const AOp A_act{nullptr, a_hi, a_lo};
+    float* big = at<float>(ws, L.big);                        // projection output (fp32) ...
+    uint16_t* u_hi = reinterpret_cast<uint16_t*>(big);        // ... or the SwiGLU planes [T][I]
+    uint16_t* u_lo = u_hi + (size_t)T * I;
+    const AOp A_u{nullptr, u_hi, u_lo};
+    float* part = at<float>(ws, L.gpart);
+    const int* tok = at<int>(ws, L.tok);
+    const int* pos = at<int>(ws, L.pos);
+    const int* seq_start = at<int>(ws, L.seq_start);
+    const uint64_t* mask = plan.mask.empty() ? nullptr : at<uint64_t>(ws, L.mask);
+    const double log2_theta = std::log2((double)c.rope_theta);
+    const int P = (mode == Mode::Prefill) ? 0 : pf->P;
+    const double rowbytes = 4.0 * T * H;
+
+    if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 1.5,
+                              [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
+      return st;
+    if (c.n_layers == 0) return JEV_OK;
+    float2* rope = at<float2>(ws, L.rope);
+    if (jev_status st = run_k(K_ROPE, 0.0, 8.0 * T * 64,
+                              [&] { return launch_rope_table(pos, T, log2_theta, rope, s); }))
+      return st;
+    if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
+          return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[0].attn_norm, c.rms_eps, a_hi, a_lo,
+                                      wide, s);
+        }))
+      return st;
+
+    int n_split = 0, split_len = 0;
+    if (P > 0) {
+      const long base = ((long)(Hq / Hkv) * T + 127) / 128 * Hkv;
+      n_split = (int)std::min<long>(kMaxAttnSplits, std::max<long>(1, (512 + base - 1) / base));
+      n_split = std::min(n_split, (P + 255) / 256);
+      n_split = std::max(n_split, 1);
+      split_len = ((P + n_split - 1) / n_split + 63) / 64 * 64;
+      n_split = (P + split_len - 1) / split_len;
+    }
+    const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
+    const double attn_bytes = 2.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + 2.0 * T * HqD) + 4.0 * T * HqD;
+
+    for (int l = 0; l < c.n_layers; ++l) {
+      const jev_layer& W = m->layers[l];
+      const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
+      int sp = 1;
+      if (jev_status st = gemm_deferred(A_act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0, &sp))
+        return st;
+      void *kdst, *vdst;
+      int kld;
+      if (mode == Mode::Prefill) {
+        kdst = store_k(l);
+        vdst = store_vt(l);
+        kld = pf->Pc;
+      } else {
+        kdst = at<char>(ws, L.ks);
+        vdst = at<char>(ws, L.vts);
+        kld = L.Tc;
+      }
+      _Float16* q_hi = at<_Float16>(ws, L.q);
+      _Float16* q_lo = q_hi + (size_t)T * HqD;
+      if (jev_status st = run_k(K_ROPE, 0.0, (double)T * NQKV * 4 * sp + (double)T * (2 * HqD + 2 * Hkv * D) * 2, [&] {
+            return launch_qkv_post(sp > 1 ? part : big, NQKV, (size_t)T * NQKV, sp, T, Hq, Hkv, rope, q_hi, q_lo,
+                                   kdst, kld, vdst, kld, s);
+          }))
+        return st;
+      if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
+
+      AttnArgs a{};
+      a.q = q_hi;
+      a.q_lo = q_lo;
+      a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+      if (P > 0) {
+        a.kp = reinterpret_cast<const _Float16*>(store_k(l));
+        a.vtp = reinterpret_cast<const _Float16*>(store_vt(l));
+      }
+      a.P = P; a.ldp = pf->Pc;
+      a.ks = static_cast<const _Float16*>(kdst);
+      a.vts = static_cast<const _Float16*>(vdst);
+      a.lds = kld;
+      a.seq_start = seq_start; a.mask = mask;
+      a.n_split = n_split; a.split_len = split_len;
+      a.o_part = at<float>(ws, L.o_part);
+      a.lse_part = at<float>(ws, L.lse_part);
+      a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
+      if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 2) * T * HqD, [&] {
+            return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, a_hi, a_lo, s);
+          }))
+        return st;
+      // o-proj: x += o·W_oᵀ, then m = RMSNorm(x; g2) into the activation planes
+      if (jev_status st = gemm_deferred(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      if (jev_status st = run_k(K_RMSNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
+            return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H, W.mlp_norm, c.rms_eps,
+                                        a_hi, a_lo, wide, s);
+          }))
+        return st;
+      if (jev_status st = run_k(K_GEMM, 2.0 * T * 2 * I * H, 2.0 * 2 * I * H + 4.0 * T * H + 4.0 * T * I, [&] {
+            return launch_gemm_swiglu(a_hi, a_lo, wide, T, H, static_cast<const uint16_t*>(W.w_gate),
+                                      static_cast<const uint16_t*>(W.w_up), I, u_hi, u_lo, I, s);
+          }))
+        return st;
+      // down: x += u·W_dᵀ, then the next layer's input norm
+      if (jev_status st = gemm_deferred(A_u, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      const void* next_g = (l + 1 < c.n_layers) ? m->layers[l + 1].attn_norm : nullptr;
+      if (jev_status st = run_k(K_RMSNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
+            return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
+                                        next_g ? next_g : W.mlp_norm, c.rms_eps, next_g ? a_hi : nullptr,
+                                        next_g ? a_lo : nullptr, wide, s);
+          }))
+        return st;
+    }
+    return JEV_OK;
+  }
+
   jev_status run(const void* vis, int n_vis) {
+    if (is_bf16(m)) return run_bf16(vis, n_vis);
     const int T = plan.T;
     const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
     const int HqD = Hq * D, NQKV = nqkv(c);

@@ -60,6 +60,32 @@ int gemm_bf16_splits(int M, int N, int K);
 // A is given as two bfloat16 planes (hi, lo) with row stride lda; the product is W·hi + W·lo.
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
                             float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
+// Direct-to-LDS, double-buffered variant; bn = 128 or 256 (N tile). Requires K % 64 == 0.
+hipError_t launch_gemm_bf16_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
+                               int* eff_splits);
+// 4-stage direct-to-LDS variant, K step 32; bn = 128 or 256. Requires K % 32 == 0.
+hipError_t launch_gemm_bf16_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
+                               int* eff_splits);
+// 4 waves of 128x128; tile 0 = 256x256 block, 1 = 128x512 block; 3-stage direct-to-LDS ring, K step 32.
+hipError_t launch_gemm_bf16_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int tile, float* part, hipStream_t s,
+                               int* eff_splits);
+// gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu].
+hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
+                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+// x[row] += sum of `splits` partials [M][H] (splits may be 0), then RMSNorm of x into bf16 hi/lo
+// planes (skipped when yh is null).  H % 4 == 0, H <= 8192.
+hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
+                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
+// Sum of `splits` projection partials (row stride lds) -> RoPE (table cs) -> q hi/lo [T][Hq][128] f16,
+// K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1.
+// cs[t][i] = (cos, sin) of pos[t] * theta^(-2i/128), i < 64 (head_dim 128).
+hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s);
+hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
+                           const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
+                           hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
                                 hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,

@@ -121,10 +121,15 @@ __device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
   return s.w[2] + (size_t)(n - s.n_end[1]) * K;
 }
 
+// SWIGLU: seg.w[0] = W_gate, seg.w[1] = W_up, N = I; the tile's 128 W rows are
+// [gate 32 | up 32] for each of the two column waves, so a lane holds gate and up
+// of the same output column and the epilogue writes silu(g)*u as bf16 hi/lo planes.
+template <bool SWIGLU>
 __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah, const u16* __restrict__ Al,
                                                      int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
                                                      int n_tiles, int splits, int k_chunk, float* __restrict__ C,
-                                                     int ldc, size_t split_stride, int accum) {
+                                                     int ldc, size_t split_stride, int accum,
+                                                     u16* __restrict__ oh, u16* __restrict__ ol) {
   __shared__ __attribute__((aligned(16))) u16 sAh[GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sAl[GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sW[GBN * GLD];
@@ -137,7 +142,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   const int rest = v / m_tiles;
   const int ks = rest % splits;
   const int nt = rest / splits;
-  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int m0 = mt * GBM, n0 = nt * (SWIGLU ? GBN / 2 : GBN);
   const int kbeg = ks * k_chunk;
   const int kend = min(K, kbeg + k_chunk);
 
@@ -146,6 +151,16 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   const int wm = wave >> 1, wn = wave & 1;
   const int ql = lane & 31, hl = lane >> 5;
   const bool wave_active = (m0 + wm * 64) < M;
+  // W row of tile row nr: plain = n0 + nr; SwiGLU = gate/up row n0 + (nr>>6)*32 + (nr&31)
+  auto w_row = [&](int nr, bool& ok) -> const u16* {
+    if (SWIGLU) {
+      const int n = n0 + (nr >> 6) * 32 + (nr & 31);
+      ok = n < N;
+      return (((nr >> 5) & 1) ? seg.w[1] : seg.w[0]) + (size_t)(ok ? n : 0) * K;
+    }
+    ok = n0 + nr < N;
+    return seg_row(seg, ok ? n0 + nr : 0, K);
+  };
 
   // global -> register staging; rows past M / N read row 0 and are zeroed at the LDS store
   uint4 rh[4], rl[4], rw[4];
@@ -163,8 +178,8 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
       const int nr = idx >> 3, c8 = idx & 7;
-      const int gn = (n0 + nr < N) ? n0 + nr : 0;
-      rw[i] = *reinterpret_cast<const uint4*>(seg_row(seg, gn, K) + k0 + c8 * 8);
+      bool ok;
+      rw[i] = *reinterpret_cast<const uint4*>(w_row(nr, ok) + k0 + c8 * 8);
     }
   };
   auto sstore = [&]() {
@@ -172,8 +187,10 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
       const int row = idx >> 3, c8 = idx & 7;
+      bool okw;
+      (void)w_row(row, okw);
       const uint32_t ma = (m0 + row < M) ? 0xFFFFFFFFu : 0u;
-      const uint32_t mw = (n0 + row < N) ? 0xFFFFFFFFu : 0u;
+      const uint32_t mw = okw ? 0xFFFFFFFFu : 0u;
       *reinterpret_cast<uint4*>(&sAh[row * GLD + c8 * 8]) =
           make_uint4(rh[i].x & ma, rh[i].y & ma, rh[i].z & ma, rh[i].w & ma);
       *reinterpret_cast<uint4*>(&sAl[row * GLD + c8 * 8]) =
@@ -231,6 +248,23 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   }
 
   if (!wave_active) return;
+  if (SWIGLU) {
+    const int col = n0 + wn * 32 + ql;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (row < M && col < N) {
+          const float g = acc[i][0][r], u = acc[i][1][r];
+          const float val = g / (1.0f + expf(-g)) * u;
+          const u16 h = f32_to_bf16(val);
+          oh[(size_t)row * ldc + col] = h;
+          ol[(size_t)row * ldc + col] = f32_to_bf16(val - bf16_to_f32(h));
+        }
+      }
+    return;
+  }
   float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
   const bool add = (splits == 1) && accum;
 #pragma unroll
@@ -239,6 +273,456 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + ql;
       const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// K3 v3: same product, direct global->LDS loads (global_load_lds_dwordx4) into
+// a double-buffered, XOR-swizzled LDS layout; one barrier per K step.
+// Tile 128 x BN (BN = 128 or 256), 4 waves in 2x2 (64 x BN/2 each), K step 64.
+// LDS row = 64 bf16 = 8 chunks of 16 B; chunk c of row r sits in slot
+// c ^ (r & 7), so the 32 rows an MFMA operand read touches hit distinct banks.
+// One wave-wide load instruction fills 1 KB = 8 rows x 8 slots; lane l loads
+// row 8j + l/8, chunk (l%8) ^ (row & 7).  Rows past M (or N) load a clamped
+// valid row: they only feed output rows (columns) that are never stored.
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void g2lds16(const void* gptr, void* lptr) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lptr, 16, 0, 0);
+}
+
+template <int BN>
+__global__ void __launch_bounds__(256, 1) gemm_bf16s_v3(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
+                                                        int n_tiles, int splits, int k_chunk,
+                                                        float* __restrict__ C, int ldc, size_t split_stride,
+                                                        int accum) {
+  constexpr int A_BYTES = GBM * 128;            // one plane of a stage
+  constexpr int W_BYTES = BN * 128;
+  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
+  constexpr int WT = BN / 64;                   // 32-col MFMA tiles per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int nb = m_tiles * n_tiles * splits;
+  const int per = gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (v >= nb) return;
+  const int mt = v % m_tiles;
+  const int rest = v / m_tiles;
+  const int ks = rest % splits;
+  const int nt = rest / splits;
+  const int m0 = mt * GBM, n0 = nt * BN;
+  const int kbeg = ks * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ql = lane & 31, hl = lane >> 5;
+
+  // this lane's source rows for its load instructions (fixed over K)
+  const int lr = lane >> 3, ls = lane & 7;
+  constexpr int A_INSTR = GBM / 8;              // 16 per plane
+  constexpr int W_INSTR = BN / 8;               // 16 or 32
+  constexpr int PER_WAVE_A = A_INSTR / 4;       // 4
+  constexpr int PER_WAVE_W = W_INSTR / 4;       // 4 or 8
+  const u16* a_src[PER_WAVE_A];
+  const u16* al_src[PER_WAVE_A];
+  int a_dst[PER_WAVE_A];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE_A; ++i) {
+    const int j = wave + 4 * i;                 // instruction index 0..15
+    const int row = 8 * j + lr;
+    const int gm = (m0 + row < M) ? m0 + row : 0;
+    const int chunk = ls ^ (row & 7);
+    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
+    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
+    a_dst[i] = j * 1024;
+  }
+  const u16* w_src[PER_WAVE_W];
+  int w_dst[PER_WAVE_W];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE_W; ++i) {
+    const int j = wave + 4 * i;
+    const int row = 8 * j + lr;
+    const int gn = (n0 + row < N) ? n0 + row : 0;
+    const int chunk = ls ^ (row & 7);
+    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
+    w_dst[i] = j * 1024;
+  }
+  auto issue = [&](int k0, int stage) {
+    unsigned char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE_A; ++i) {
+      g2lds16(a_src[i] + k0, base + a_dst[i]);
+      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PER_WAVE_W; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
+  };
+
+  f32x16 acc[2][WT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (kend - kbeg) / GBK;
+  if (nk > 0) {
+    issue(kbeg, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (int it = 0; it < nk; ++it) {
+    const int stage = it & 1;
+    if (it + 1 < nk) issue(kbeg + (it + 1) * GBK, stage ^ 1);
+    const unsigned char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < GBK / 16; ++kk) {
+      const int c = kk * 2 + hl;                 // 16-B chunk of this lane's 8 k values
+      bf16x8 ah[2], al[2], bw[WT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + ql;
+        const int off = r * 128 + ((c ^ (r & 7)) << 4);
+        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
+        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
+      }
+#pragma unroll
+      for (int j = 0; j < WT; ++j) {
+        const int r = wn * (BN / 2) + j * 32 + ql;
+        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 128 + ((c ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (m0 + wm * 64 >= M) return;
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+      const int col = n0 + wn * (BN / 2) + j * 32 + ql;
+      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// K3 v4: 4-stage direct-to-LDS ring, K step 32, prefetch distance 3.
+// LDS row = 32 bf16 = 4 chunks of 16 B (64 B); chunk c of row r sits in slot
+// c ^ ((r >> 2) & 3): the 16 rows a 16-lane operand read touches then fall in
+// 16 distinct 4-bank groups.  One wave-wide load fills 1 KB = 16 rows; lane l
+// loads row 16j + l/4, chunk (l%4) ^ ((row >> 2) & 3).
+// ----------------------------------------------------------------------------
+template <int BN>
+__global__ void __launch_bounds__(256, 1) gemm_bf16s_v4(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
+                                                        int n_tiles, int splits, int k_chunk,
+                                                        float* __restrict__ C, int ldc, size_t split_stride,
+                                                        int accum) {
+  constexpr int BK4 = 32;
+  constexpr int NSTAGE = 4;
+  constexpr int A_BYTES = GBM * 64;
+  constexpr int W_BYTES = BN * 64;
+  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
+  constexpr int WT = BN / 64;
+  constexpr int A_INSTR = GBM / 16;             // 8 per plane
+  constexpr int W_INSTR = BN / 16;              // 8 or 16
+  constexpr int PA = A_INSTR / 4;               // 2 per wave per plane
+  constexpr int PW = W_INSTR / 4;               // 2 or 4 per wave
+  constexpr int PER_STAGE = 2 * PA + PW;        // loads per wave per stage
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int nb = m_tiles * n_tiles * splits;
+  const int per = gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (v >= nb) return;
+  const int mt = v % m_tiles;
+  const int rest = v / m_tiles;
+  const int ks = rest % splits;
+  const int nt = rest / splits;
+  const int m0 = mt * GBM, n0 = nt * BN;
+  const int kbeg = ks * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ql = lane & 31, hl = lane >> 5;
+
+  const int lr = lane >> 2, ls = lane & 3;
+  const u16* a_src[PA];
+  const u16* al_src[PA];
+  int a_dst[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {
+    const int j = wave + 4 * i;
+    const int row = 16 * j + lr;
+    const int gm = (m0 + row < M) ? m0 + row : 0;
+    const int chunk = ls ^ ((row >> 2) & 3);
+    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
+    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
+    a_dst[i] = j * 1024;
+  }
+  const u16* w_src[PW];
+  int w_dst[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int j = wave + 4 * i;
+    const int row = 16 * j + lr;
+    const int gn = (n0 + row < N) ? n0 + row : 0;
+    const int chunk = ls ^ ((row >> 2) & 3);
+    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
+    w_dst[i] = j * 1024;
+  }
+  auto issue = [&](int k0, int stage) {
+    unsigned char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      g2lds16(a_src[i] + k0, base + a_dst[i]);
+      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PW; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
+  };
+
+  f32x16 acc[2][WT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (kend - kbeg) / BK4;
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < nk) issue(kbeg + st * BK4, st);
+
+  for (int it = 0; it < nk; ++it) {
+    // this wave's loads of stage `it` are in once at most the loads of the
+    // (up to two) later stages are still outstanding
+    const int later = min(nk - 1 - it, NSTAGE - 2);
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER_STAGE) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER_STAGE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave's stage-`it` data is in LDS; stage it-1 is free
+    if (it + NSTAGE - 1 < nk) issue(kbeg + (it + NSTAGE - 1) * BK4, (it + NSTAGE - 1) % NSTAGE);
+    const unsigned char* base = smem + (it % NSTAGE) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < BK4 / 16; ++kk) {
+      const int c = kk * 2 + hl;
+      bf16x8 ah[2], al[2], bw[WT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + ql;
+        const int off = r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
+        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
+      }
+#pragma unroll
+      for (int j = 0; j < WT; ++j) {
+        const int r = wn * (BN / 2) + j * 32 + ql;
+        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  if (m0 + wm * 64 >= M) return;
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+      const int col = n0 + wn * (BN / 2) + j * 32 + ql;
+      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// K3 v5: BMxBN block with 4 waves of 128x128 each (4x4 MFMA 32x32 tiles per
+// wave, 256 accumulators), K step 32, 3-stage direct-to-LDS ring.
+// Wave layout WM x WN = (BM/128) x (BN/128) with WM*WN = 4.
+// ----------------------------------------------------------------------------
+template <int BM, int BN>
+__global__ void __launch_bounds__(256, 1) gemm_bf16s_v5(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
+                                                        int n_tiles, int splits, int k_chunk,
+                                                        float* __restrict__ C, int ldc, size_t split_stride,
+                                                        int accum) {
+  constexpr int BK5 = 32;
+  constexpr int NSTAGE = 3;
+  constexpr int WN_ = BN / 128;
+  constexpr int A_BYTES = BM * 64;
+  constexpr int W_BYTES = BN * 64;
+  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
+  constexpr int PA = BM / 16 / 4;               // load instructions per wave per A plane
+  constexpr int PW = BN / 16 / 4;
+  constexpr int PER_STAGE = 2 * PA + PW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int nb = m_tiles * n_tiles * splits;
+  const int per = gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (v >= nb) return;
+  const int mt = v % m_tiles;
+  const int rest = v / m_tiles;
+  const int ks = rest % splits;
+  const int nt = rest / splits;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int kbeg = ks * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / WN_, wn = wave % WN_;
+  const int ql = lane & 31, hl = lane >> 5;
+
+  const int lr = lane >> 2, ls = lane & 3;
+  const u16* a_src[PA];
+  const u16* al_src[PA];
+  int a_dst[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {
+    const int j = wave + 4 * i;
+    const int row = 16 * j + lr;
+    const int gm = (m0 + row < M) ? m0 + row : 0;
+    const int chunk = ls ^ ((row >> 2) & 3);
+    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
+    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
+    a_dst[i] = j * 1024;
+  }
+  const u16* w_src[PW];
+  int w_dst[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int j = wave + 4 * i;
+    const int row = 16 * j + lr;
+    const int gn = (n0 + row < N) ? n0 + row : 0;
+    const int chunk = ls ^ ((row >> 2) & 3);
+    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
+    w_dst[i] = j * 1024;
+  }
+  auto issue = [&](int k0, int stage) {
+    unsigned char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      g2lds16(a_src[i] + k0, base + a_dst[i]);
+      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PW; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (kend - kbeg) / BK5;
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < nk) issue(kbeg + st * BK5, st);
+
+  for (int it = 0; it < nk; ++it) {
+    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER_STAGE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + NSTAGE - 1 < nk) issue(kbeg + (it + NSTAGE - 1) * BK5, (it + NSTAGE - 1) % NSTAGE);
+    const unsigned char* base = smem + (it % NSTAGE) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < BK5 / 16; ++kk) {
+      const int c = kk * 2 + hl;
+      bf16x8 ah[4], al[4], bw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + ql;
+        const int off = r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
+        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + ql;
+        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  if (m0 + wm * 128 >= M) return;
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + ql;
+      const int rbase = m0 + wm * 128 + i * 32 + 4 * hl;
       float old[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -649,6 +1133,141 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     a.lse_part[((size_t)split * T + t) * Hq + hq] = (l_run > 0.f) ? m_run * a.scale_log2 + log2f(l_run) : NEG_INF;
 }
 
+// ----------------------------------------------------------------------------
+// Fused split-K reduce + residual + RMSNorm (bf16 models), one block per row:
+//   x[row] += sum_s part[s][row]      (fixed order; nothing to add if splits == 0)
+//   y = g * x / sqrt(mean(x^2) + eps) written as bf16 hi/lo planes (skipped if yh == nullptr)
+// H % 4 == 0 and H <= 8192.
+// ----------------------------------------------------------------------------
+template <typename WT>
+__global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
+                                                     float* __restrict__ x, int H, const WT* __restrict__ g,
+                                                     float eps, u16* __restrict__ yh, u16* __restrict__ yl,
+                                                     int ldy) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int H4 = H >> 2;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)row * H);
+  float4 v[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = threadIdx.x + 256 * j;
+    if (k < H4) {
+      float4 a = xr[k];
+      for (int sp = 0; sp < splits; ++sp) {
+        const float4 b = reinterpret_cast<const float4*>(part + sp * split_stride + (size_t)row * H)[k];
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      if (splits > 0) xr[k] = a;
+      v[j] = a;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+  }
+  if (yh == nullptr) return;
+  ss = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = threadIdx.x + 256 * j;
+    if (k < H4) {
+      const float in[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      u16 h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y = ldw(g, 4 * k + e) * (in[e] * r);
+        h[e] = f32_to_bf16(y);
+        l[e] = f32_to_bf16(y - bf16_to_f32(h[e]));
+      }
+      const size_t o = (size_t)row * ldy + 4 * k;
+      *reinterpret_cast<uint2*>(yh + o) =
+          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      *reinterpret_cast<uint2*>(yl + o) =
+          make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// RoPE table for the rows of one forward: cs[t][i] = (cos, sin)(pos[t] * theta^(-2i/128)),
+// angle and sin/cos in float64; shared by every layer of the forward.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rope_table(const int* __restrict__ pos, int T, double log2_theta,
+                                                  float2* __restrict__ cs) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * 64) return;
+  const int t = idx >> 6, i = idx & 63;
+  double sd, cd;
+  sincos((double)pos[t] * exp2(-(2.0 * i / 128.0) * log2_theta), &sd, &cd);
+  cs[idx] = make_float2((float)cd, (float)sd);
+}
+
+// ----------------------------------------------------------------------------
+// Fused split-K reduce + RoPE + KV layout for the q|k|v projection (head_dim 128).
+// src: projection output [T][(Hq+2Hkv)*128] (splits == 1) or its split partials.
+// Grid (ceil(T/16), Hq + 2 Hkv): y < Hq + Hkv rotates head y over 16 rows (q as
+// f16 hi + lo, k as f16 into K[hk][ldk][128]); the last Hkv values of y
+// transpose one kv head's V over 16 rows into Vt[hk][128][ldv] via LDS.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, int lds, size_t split_stride,
+                                                int splits, int T, int Hq, int Hkv,
+                                                const float2* __restrict__ cs,
+                                                f16* __restrict__ q_hi, f16* __restrict__ q_lo,
+                                                f16* __restrict__ kdst, int ldk, f16* __restrict__ vtdst,
+                                                int ldv) {
+  __shared__ float vt[16][129];
+  const int t0 = blockIdx.x * 16;
+  const int nqk = Hq + Hkv;
+  const int h = blockIdx.y;
+  auto ld = [&](int t, int c) {
+    float a = src[(size_t)t * lds + c];
+    for (int sp = 1; sp < splits; ++sp) a += src[sp * split_stride + (size_t)t * lds + c];
+    return a;
+  };
+  if (h < nqk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int rr = idx >> 6, i = idx & 63;
+      const int t = t0 + rr;
+      if (t >= T) continue;
+      const float a = ld(t, h * 128 + i), b = ld(t, h * 128 + i + 64);
+      const float2 e = cs[t * 64 + i];
+      const float ra = a * e.x - b * e.y, rb = b * e.x + a * e.y;
+      if (h < Hq) {
+        const size_t o = ((size_t)t * Hq + h) * 128;
+        const f16 qa = (f16)ra, qb = (f16)rb;
+        q_hi[o + i] = qa;
+        q_hi[o + i + 64] = qb;
+        q_lo[o + i] = (f16)(ra - (float)qa);
+        q_lo[o + i + 64] = (f16)(rb - (float)qb);
+      } else {
+        f16* kd = kdst + ((size_t)(h - Hq) * ldk + t) * 128;
+        kd[i] = (f16)ra;
+        kd[i + 64] = (f16)rb;
+      }
+    }
+  } else {
+    const int hk = h - nqk;
+    const int c0 = nqk * 128 + hk * 128;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int rr = idx >> 7, d = idx & 127;
+      const int t = t0 + rr;
+      vt[rr][d] = (t < T) ? ld(t, c0 + d) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int d = idx >> 4, rr = idx & 15;
+      const int t = t0 + rr;
+      if (t < T) vtdst[((size_t)hk * 128 + d) * ldv + t] = (f16)vt[rr][d];
+    }
+  }
+}
+
 // Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M).
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
@@ -874,11 +1493,14 @@ hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, i
   return hipGetLastError();
 }
 
+// Split-K count: as many K splits as fill one round of 512 resident blocks
+// (2 per CU) without exceeding it, at most 8, each split keeping >= 256 of K.
+// Chosen by measurement on the 2B/7B projection shapes: a partial second
+// round of blocks costs more than the extra split partials save.
 int gemm_bf16_splits(int M, int N, int K) {
   const long tiles = (long)cdiv(M, GBM) * cdiv(N, GBN);
-  if (tiles >= 256) return 1;
-  int s = cdiv(384, tiles);
-  const int kmax = K / 512;          // every split keeps >= 512 of K
+  int s = (int)(512 / tiles);
+  const int kmax = K / 256;
   if (s > kmax) s = kmax;
   if (s > 8) s = 8;
   return s < 1 ? 1 : s;
@@ -895,9 +1517,151 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
   const int nb = mt * nt * splits;
   const int grid = cdiv(nb, 8) * 8;
   if (splits == 1)
-    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+    gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum,
+                                           nullptr, nullptr);
   else
-    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N, (size_t)M * N, 0);
+    gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
+                                           (size_t)M * N, 0, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int BN>
+static hipError_t launch_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
+                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+  const int mt = cdiv(M, GBM), nt = cdiv(N, BN);
+  const int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
+  splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
+  const int nb = mt * nt * splits;
+  const int grid = cdiv(nb, 8) * 8;
+  const size_t lds = 2 * (2 * GBM * 128 + BN * 128);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v3<BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (splits == 1)
+    gemm_bf16s_v3<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+  else
+    gemm_bf16s_v3<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
+                                             (size_t)M * N, 0);
+  return hipGetLastError();
+}
+
+template <int BN>
+static hipError_t launch_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
+                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+  const int mt = cdiv(M, GBM), nt = cdiv(N, BN);
+  const int k_chunk = cdiv(cdiv(K, splits), 32) * 32;
+  splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
+  const int nb = mt * nt * splits;
+  const int grid = cdiv(nb, 8) * 8;
+  const size_t lds = 4 * (2 * GBM * 64 + BN * 64);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v4<BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (splits == 1)
+    gemm_bf16s_v4<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+  else
+    gemm_bf16s_v4<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
+                                             (size_t)M * N, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
+                               int* eff_splits) {
+  *eff_splits = 1;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (bn == 256) return launch_v4<256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+  return launch_v4<128>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+}
+
+template <int BM, int BN>
+static hipError_t launch_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
+                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+  const int mt = cdiv(M, BM), nt = cdiv(N, BN);
+  const int k_chunk = cdiv(cdiv(K, splits), 32) * 32;
+  splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
+  const int nb = mt * nt * splits;
+  const int grid = cdiv(nb, 8) * 8;
+  const size_t lds = 3 * (2 * BM * 64 + BN * 64);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v5<BM, BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (splits == 1)
+    gemm_bf16s_v5<BM, BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
+  else
+    gemm_bf16s_v5<BM, BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
+                                                 (size_t)M * N, 0);
+  return hipGetLastError();
+}
+
+// tile: 0 = 256x256, 1 = 128x512
+hipError_t launch_gemm_bf16_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int tile, float* part, hipStream_t s,
+                               int* eff_splits) {
+  *eff_splits = 1;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (tile == 1) return launch_v5<128, 512>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+  return launch_v5<256, 256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+}
+
+hipError_t launch_gemm_bf16_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
+                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
+                               int* eff_splits) {
+  *eff_splits = 1;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (bn == 256) return launch_v3<256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+  return launch_v3<128>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
+}
+
+hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
+                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s) {
+  if (M <= 0 || I <= 0) return hipSuccess;
+  const int mt = cdiv(M, GBM), nt = cdiv(I, GBN / 2);
+  const int nb = mt * nt;
+  const int grid = cdiv(nb, 8) * 8;
+  GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
+  gemm_bf16s<true><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
+                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (bf16)
+    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy);
+  else
+    residual_norm<float><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  rope_table<<<cdiv((long)T * 64, 256), 256, 0, s>>>(pos, T, log2_theta, cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
+                           const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
+                           hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid(cdiv(T, 16), Hq + 2 * Hkv);
+  qkv_post<<<grid, 256, 0, s>>>(src, lds, split_stride, splits, T, Hq, Hkv, cs, (f16*)q_hi, (f16*)q_lo, (f16*)kdst,
+                                ldk, (f16*)vtdst, ldv);
   return hipGetLastError();
 }
 
