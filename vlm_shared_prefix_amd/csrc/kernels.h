@@ -60,18 +60,6 @@ int gemm_bf16_splits(int M, int N, int K);
 // A is given as two bfloat16 planes (hi, lo) with row stride lda; the product is W·hi + W·lo.
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
                             float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
-// Direct-to-LDS, double-buffered variant; bn = 128 or 256 (N tile). Requires K % 64 == 0.
-hipError_t launch_gemm_bf16_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
-                               int* eff_splits);
-// 4-stage direct-to-LDS variant, K step 32; bn = 128 or 256. Requires K % 32 == 0.
-hipError_t launch_gemm_bf16_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
-                               int* eff_splits);
-// 4 waves of 128x128; tile 0 = 256x256 block, 1 = 128x512 block; 3-stage direct-to-LDS ring, K step 32.
-hipError_t launch_gemm_bf16_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int tile, float* part, hipStream_t s,
-                               int* eff_splits);
 // gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu].
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
                               const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);

@@ -287,456 +287,6 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
     }
 }
 
-// ----------------------------------------------------------------------------
-// K3 v3: same product, direct global->LDS loads (global_load_lds_dwordx4) into
-// a double-buffered, XOR-swizzled LDS layout; one barrier per K step.
-// Tile 128 x BN (BN = 128 or 256), 4 waves in 2x2 (64 x BN/2 each), K step 64.
-// LDS row = 64 bf16 = 8 chunks of 16 B; chunk c of row r sits in slot
-// c ^ (r & 7), so the 32 rows an MFMA operand read touches hit distinct banks.
-// One wave-wide load instruction fills 1 KB = 8 rows x 8 slots; lane l loads
-// row 8j + l/8, chunk (l%8) ^ (row & 7).  Rows past M (or N) load a clamped
-// valid row: they only feed output rows (columns) that are never stored.
-// ----------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void g2lds16(const void* gptr, void* lptr) {
-  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lptr, 16, 0, 0);
-}
-
-template <int BN>
-__global__ void __launch_bounds__(256, 1) gemm_bf16s_v3(const u16* __restrict__ Ah, const u16* __restrict__ Al,
-                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
-                                                        int n_tiles, int splits, int k_chunk,
-                                                        float* __restrict__ C, int ldc, size_t split_stride,
-                                                        int accum) {
-  constexpr int A_BYTES = GBM * 128;            // one plane of a stage
-  constexpr int W_BYTES = BN * 128;
-  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
-  constexpr int WT = BN / 64;                   // 32-col MFMA tiles per wave
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-  const int nb = m_tiles * n_tiles * splits;
-  const int per = gridDim.x >> 3;
-  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (v >= nb) return;
-  const int mt = v % m_tiles;
-  const int rest = v / m_tiles;
-  const int ks = rest % splits;
-  const int nt = rest / splits;
-  const int m0 = mt * GBM, n0 = nt * BN;
-  const int kbeg = ks * k_chunk;
-  const int kend = min(K, kbeg + k_chunk);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ql = lane & 31, hl = lane >> 5;
-
-  // this lane's source rows for its load instructions (fixed over K)
-  const int lr = lane >> 3, ls = lane & 7;
-  constexpr int A_INSTR = GBM / 8;              // 16 per plane
-  constexpr int W_INSTR = BN / 8;               // 16 or 32
-  constexpr int PER_WAVE_A = A_INSTR / 4;       // 4
-  constexpr int PER_WAVE_W = W_INSTR / 4;       // 4 or 8
-  const u16* a_src[PER_WAVE_A];
-  const u16* al_src[PER_WAVE_A];
-  int a_dst[PER_WAVE_A];
-#pragma unroll
-  for (int i = 0; i < PER_WAVE_A; ++i) {
-    const int j = wave + 4 * i;                 // instruction index 0..15
-    const int row = 8 * j + lr;
-    const int gm = (m0 + row < M) ? m0 + row : 0;
-    const int chunk = ls ^ (row & 7);
-    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
-    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
-    a_dst[i] = j * 1024;
-  }
-  const u16* w_src[PER_WAVE_W];
-  int w_dst[PER_WAVE_W];
-#pragma unroll
-  for (int i = 0; i < PER_WAVE_W; ++i) {
-    const int j = wave + 4 * i;
-    const int row = 8 * j + lr;
-    const int gn = (n0 + row < N) ? n0 + row : 0;
-    const int chunk = ls ^ (row & 7);
-    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
-    w_dst[i] = j * 1024;
-  }
-  auto issue = [&](int k0, int stage) {
-    unsigned char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < PER_WAVE_A; ++i) {
-      g2lds16(a_src[i] + k0, base + a_dst[i]);
-      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PER_WAVE_W; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
-  };
-
-  f32x16 acc[2][WT];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < WT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = (kend - kbeg) / GBK;
-  if (nk > 0) {
-    issue(kbeg, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  for (int it = 0; it < nk; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < nk) issue(kbeg + (it + 1) * GBK, stage ^ 1);
-    const unsigned char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      const int c = kk * 2 + hl;                 // 16-B chunk of this lane's 8 k values
-      bf16x8 ah[2], al[2], bw[WT];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + ql;
-        const int off = r * 128 + ((c ^ (r & 7)) << 4);
-        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
-        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
-      }
-#pragma unroll
-      for (int j = 0; j < WT; ++j) {
-        const int r = wn * (BN / 2) + j * 32 + ql;
-        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 128 + ((c ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  if (m0 + wm * 64 >= M) return;
-  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
-  const bool add = (splits == 1) && accum;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const int col = n0 + wn * (BN / 2) + j * 32 + ql;
-      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
-      float old[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
-      }
-    }
-}
-
-// ----------------------------------------------------------------------------
-// K3 v4: 4-stage direct-to-LDS ring, K step 32, prefetch distance 3.
-// LDS row = 32 bf16 = 4 chunks of 16 B (64 B); chunk c of row r sits in slot
-// c ^ ((r >> 2) & 3): the 16 rows a 16-lane operand read touches then fall in
-// 16 distinct 4-bank groups.  One wave-wide load fills 1 KB = 16 rows; lane l
-// loads row 16j + l/4, chunk (l%4) ^ ((row >> 2) & 3).
-// ----------------------------------------------------------------------------
-template <int BN>
-__global__ void __launch_bounds__(256, 1) gemm_bf16s_v4(const u16* __restrict__ Ah, const u16* __restrict__ Al,
-                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
-                                                        int n_tiles, int splits, int k_chunk,
-                                                        float* __restrict__ C, int ldc, size_t split_stride,
-                                                        int accum) {
-  constexpr int BK4 = 32;
-  constexpr int NSTAGE = 4;
-  constexpr int A_BYTES = GBM * 64;
-  constexpr int W_BYTES = BN * 64;
-  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
-  constexpr int WT = BN / 64;
-  constexpr int A_INSTR = GBM / 16;             // 8 per plane
-  constexpr int W_INSTR = BN / 16;              // 8 or 16
-  constexpr int PA = A_INSTR / 4;               // 2 per wave per plane
-  constexpr int PW = W_INSTR / 4;               // 2 or 4 per wave
-  constexpr int PER_STAGE = 2 * PA + PW;        // loads per wave per stage
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-  const int nb = m_tiles * n_tiles * splits;
-  const int per = gridDim.x >> 3;
-  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (v >= nb) return;
-  const int mt = v % m_tiles;
-  const int rest = v / m_tiles;
-  const int ks = rest % splits;
-  const int nt = rest / splits;
-  const int m0 = mt * GBM, n0 = nt * BN;
-  const int kbeg = ks * k_chunk;
-  const int kend = min(K, kbeg + k_chunk);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ql = lane & 31, hl = lane >> 5;
-
-  const int lr = lane >> 2, ls = lane & 3;
-  const u16* a_src[PA];
-  const u16* al_src[PA];
-  int a_dst[PA];
-#pragma unroll
-  for (int i = 0; i < PA; ++i) {
-    const int j = wave + 4 * i;
-    const int row = 16 * j + lr;
-    const int gm = (m0 + row < M) ? m0 + row : 0;
-    const int chunk = ls ^ ((row >> 2) & 3);
-    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
-    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
-    a_dst[i] = j * 1024;
-  }
-  const u16* w_src[PW];
-  int w_dst[PW];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int j = wave + 4 * i;
-    const int row = 16 * j + lr;
-    const int gn = (n0 + row < N) ? n0 + row : 0;
-    const int chunk = ls ^ ((row >> 2) & 3);
-    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
-    w_dst[i] = j * 1024;
-  }
-  auto issue = [&](int k0, int stage) {
-    unsigned char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < PA; ++i) {
-      g2lds16(a_src[i] + k0, base + a_dst[i]);
-      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PW; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
-  };
-
-  f32x16 acc[2][WT];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < WT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = (kend - kbeg) / BK4;
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
-    if (st < nk) issue(kbeg + st * BK4, st);
-
-  for (int it = 0; it < nk; ++it) {
-    // this wave's loads of stage `it` are in once at most the loads of the
-    // (up to two) later stages are still outstanding
-    const int later = min(nk - 1 - it, NSTAGE - 2);
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER_STAGE) : "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER_STAGE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();   // every wave's stage-`it` data is in LDS; stage it-1 is free
-    if (it + NSTAGE - 1 < nk) issue(kbeg + (it + NSTAGE - 1) * BK4, (it + NSTAGE - 1) % NSTAGE);
-    const unsigned char* base = smem + (it % NSTAGE) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < BK4 / 16; ++kk) {
-      const int c = kk * 2 + hl;
-      bf16x8 ah[2], al[2], bw[WT];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + ql;
-        const int off = r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
-        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
-      }
-#pragma unroll
-      for (int j = 0; j < WT; ++j) {
-        const int r = wn * (BN / 2) + j * 32 + ql;
-        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
-        }
-    }
-  }
-
-  if (m0 + wm * 64 >= M) return;
-  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
-  const bool add = (splits == 1) && accum;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const int col = n0 + wn * (BN / 2) + j * 32 + ql;
-      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
-      float old[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
-      }
-    }
-}
-
-// ----------------------------------------------------------------------------
-// K3 v5: BMxBN block with 4 waves of 128x128 each (4x4 MFMA 32x32 tiles per
-// wave, 256 accumulators), K step 32, 3-stage direct-to-LDS ring.
-// Wave layout WM x WN = (BM/128) x (BN/128) with WM*WN = 4.
-// ----------------------------------------------------------------------------
-template <int BM, int BN>
-__global__ void __launch_bounds__(256, 1) gemm_bf16s_v5(const u16* __restrict__ Ah, const u16* __restrict__ Al,
-                                                        int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
-                                                        int n_tiles, int splits, int k_chunk,
-                                                        float* __restrict__ C, int ldc, size_t split_stride,
-                                                        int accum) {
-  constexpr int BK5 = 32;
-  constexpr int NSTAGE = 3;
-  constexpr int WN_ = BN / 128;
-  constexpr int A_BYTES = BM * 64;
-  constexpr int W_BYTES = BN * 64;
-  constexpr int STAGE = 2 * A_BYTES + W_BYTES;
-  constexpr int PA = BM / 16 / 4;               // load instructions per wave per A plane
-  constexpr int PW = BN / 16 / 4;
-  constexpr int PER_STAGE = 2 * PA + PW;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-  const int nb = m_tiles * n_tiles * splits;
-  const int per = gridDim.x >> 3;
-  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (v >= nb) return;
-  const int mt = v % m_tiles;
-  const int rest = v / m_tiles;
-  const int ks = rest % splits;
-  const int nt = rest / splits;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int kbeg = ks * k_chunk;
-  const int kend = min(K, kbeg + k_chunk);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave / WN_, wn = wave % WN_;
-  const int ql = lane & 31, hl = lane >> 5;
-
-  const int lr = lane >> 2, ls = lane & 3;
-  const u16* a_src[PA];
-  const u16* al_src[PA];
-  int a_dst[PA];
-#pragma unroll
-  for (int i = 0; i < PA; ++i) {
-    const int j = wave + 4 * i;
-    const int row = 16 * j + lr;
-    const int gm = (m0 + row < M) ? m0 + row : 0;
-    const int chunk = ls ^ ((row >> 2) & 3);
-    a_src[i] = Ah + (size_t)gm * lda + chunk * 8;
-    al_src[i] = Al + (size_t)gm * lda + chunk * 8;
-    a_dst[i] = j * 1024;
-  }
-  const u16* w_src[PW];
-  int w_dst[PW];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int j = wave + 4 * i;
-    const int row = 16 * j + lr;
-    const int gn = (n0 + row < N) ? n0 + row : 0;
-    const int chunk = ls ^ ((row >> 2) & 3);
-    w_src[i] = seg_row(seg, gn, K) + chunk * 8;
-    w_dst[i] = j * 1024;
-  }
-  auto issue = [&](int k0, int stage) {
-    unsigned char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < PA; ++i) {
-      g2lds16(a_src[i] + k0, base + a_dst[i]);
-      g2lds16(al_src[i] + k0, base + A_BYTES + a_dst[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PW; ++i) g2lds16(w_src[i] + k0, base + 2 * A_BYTES + w_dst[i]);
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = (kend - kbeg) / BK5;
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
-    if (st < nk) issue(kbeg + st * BK5, st);
-
-  for (int it = 0; it < nk; ++it) {
-    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER_STAGE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (it + NSTAGE - 1 < nk) issue(kbeg + (it + NSTAGE - 1) * BK5, (it + NSTAGE - 1) % NSTAGE);
-    const unsigned char* base = smem + (it % NSTAGE) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < BK5 / 16; ++kk) {
-      const int c = kk * 2 + hl;
-      bf16x8 ah[4], al[4], bw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + ql;
-        const int off = r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-        ah[i] = *reinterpret_cast<const bf16x8*>(base + off);
-        al[i] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + off);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + ql;
-        bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * A_BYTES + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  if (m0 + wm * 128 >= M) return;
-  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
-  const bool add = (splits == 1) && accum;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + ql;
-      const int rbase = m0 + wm * 128 + i * 32 + 4 * hl;
-      float old[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r >> 2) + (r & 3);
-        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
-      }
-    }
-}
-
 // Deterministic split-K reduction: out = (accum ? out : 0) + sum_s part[s] (fixed order).
 __global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ part, size_t split_stride,
                                                      int splits, int M, int N, int ldp,
@@ -894,7 +444,7 @@ __global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src
 #define AT_BR 128
 #define AT_BK 64
 #define KLD (128 + 8)    // halfs; 272 B rows
-#define VLD (AT_BK + 4)  // halfs; 136 B rows
+#define VLD (AT_BK + 8)  // halfs; 144 B rows: conflict-free 16 B operand reads
 
 // zero the 16-bit lanes j >= cnt of an 8 x f16 chunk (cnt in [0, 8])
 __device__ __forceinline__ uint4 keep_first(uint4 v, int cnt) {
@@ -982,23 +532,30 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       rv[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)d * ld + col);
     }
   };
+  // LDS V^T tile: within each 16-key group, keys are stored in the order
+  // 0-3, 8-11, 4-7, 12-15, so the 8 keys one lane feeds to a P·V step
+  // ({4h..4h+3} and {8+4h..8+4h+3}) are contiguous (one 16 B read).
   auto sstore = [&](int k0, int buf) {
+    const bool full = k0 + AT_BK <= ke;     // uniform over the block
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
-      const uint32_t m = (k0 + (idx >> 4) < ke) ? 0xFFFFFFFFu : 0u;
-      const uint4 v = make_uint4(rk[i].x & m, rk[i].y & m, rk[i].z & m, rk[i].w & m);
+      uint4 v = rk[i];
+      if (!full) {
+        const uint32_t m = (k0 + (idx >> 4) < ke) ? 0xFFFFFFFFu : 0u;
+        v = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+      }
       *reinterpret_cast<uint4*>(&sK[buf][(idx >> 4) * KLD + (idx & 15) * 8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
       const int d = idx >> 3, c = idx & 7;
-      const int cnt = min(max(ke - (k0 + c * 8), 0), 8);
-      const uint4 v = keep_first(rv[i], cnt);
-      uint2* dst = reinterpret_cast<uint2*>(&sV[buf][d * VLD + c * 8]);
-      dst[0] = make_uint2(v.x, v.y);
-      dst[1] = make_uint2(v.z, v.w);
+      uint4 v = rv[i];
+      if (!full) v = keep_first(v, min(max(ke - (k0 + c * 8), 0), 8));
+      f16* row = &sV[buf][d * VLD + (c >> 1) * 16 + (c & 1) * 4];
+      *reinterpret_cast<uint2*>(row) = make_uint2(v.x, v.y);       // keys 8c .. 8c+3
+      *reinterpret_cast<uint2*>(row + 8) = make_uint2(v.z, v.w);   // keys 8c+4 .. 8c+7
     }
   };
 
@@ -1022,18 +579,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     const bool more = it + 1 < ntiles;
     if (more) gload(k0 + AT_BK);      // in flight while this tile is computed
 
-    // scores for the two 32-key halves (unscaled)
+    // scores for the two 32-key halves (unscaled); the two halves' accumulation
+    // chains are interleaved so consecutive MFMAs are independent
     f32x16 s[2];
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hs][i] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const f16x8 kop = *reinterpret_cast<const f16x8*>(&sK[buf][(hs * 32 + ql) * KLD + c * 16 + hl * 8]);
-        s[hs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qreg[c], s[hs], 0, 0, 0);
-        s[hs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qlo[c], s[hs], 0, 0, 0);
-      }
+    for (int c = 0; c < 8; ++c) {
+      const f16x8 k0op = *reinterpret_cast<const f16x8*>(&sK[buf][ql * KLD + c * 16 + hl * 8]);
+      const f16x8 k1op = *reinterpret_cast<const f16x8*>(&sK[buf][(32 + ql) * KLD + c * 16 + hl * 8]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qreg[c], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qreg[c], s[1], 0, 0, 0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qlo[c], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qlo[c], s[1], 0, 0, 0);
     }
     // Only tiles that cross the split's range or hold own-row keys need a mask;
     // the test is uniform over the block.  Rows past R hold a clamped row's
@@ -1072,8 +632,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     const float sl = a.scale_log2;
     const float neg_ms = -m_use * sl;
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl);
-    // p = 2^(s*scale - m*scale), rounded to f16 for the P·V product; the row sum
-    // is taken over the same rounded values so the weights stay normalised.
+    // p = 2^(s*scale - m*scale); the row sum is taken in f32 and p is rounded
+    // to nearest f16 for the P·V product (unbiased, so the two stay consistent).
     float rs = 0.f;
     f16x8 pops[2][2];
 #pragma unroll
@@ -1082,9 +642,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const f16 ph = (f16)__builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, neg_ms));
-          pops[hs][p][j] = ph;
-          rs += (float)ph;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, neg_ms));
+          rs += pv;
+          pops[hs][p][j] = (f16)pv;
         }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
@@ -1103,13 +663,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const f16x8 pop = pops[hs][p];
-        const int kofs = hs * 32 + 16 * p + 4 * hl;
+        const int kofs = hs * 32 + 16 * p + 8 * hl;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const f16* vrow = &sV[buf][(dt * 32 + ql) * VLD + kofs];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
-          const f16x8 vop = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          const f16x8 vop = *reinterpret_cast<const f16x8*>(&sV[buf][(dt * 32 + ql) * VLD + kofs]);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop, acc[dt], 0, 0, 0);
         }
       }
@@ -1523,109 +1080,6 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
     gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
                                            (size_t)M * N, 0, nullptr, nullptr);
   return hipGetLastError();
-}
-
-template <int BN>
-static hipError_t launch_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
-                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
-  const int mt = cdiv(M, GBM), nt = cdiv(N, BN);
-  const int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
-  splits = cdiv(K, k_chunk);
-  *eff_splits = splits;
-  const int nb = mt * nt * splits;
-  const int grid = cdiv(nb, 8) * 8;
-  const size_t lds = 2 * (2 * GBM * 128 + BN * 128);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v3<BN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  if (splits == 1)
-    gemm_bf16s_v3<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
-  else
-    gemm_bf16s_v3<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
-                                             (size_t)M * N, 0);
-  return hipGetLastError();
-}
-
-template <int BN>
-static hipError_t launch_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
-                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
-  const int mt = cdiv(M, GBM), nt = cdiv(N, BN);
-  const int k_chunk = cdiv(cdiv(K, splits), 32) * 32;
-  splits = cdiv(K, k_chunk);
-  *eff_splits = splits;
-  const int nb = mt * nt * splits;
-  const int grid = cdiv(nb, 8) * 8;
-  const size_t lds = 4 * (2 * GBM * 64 + BN * 64);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v4<BN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  if (splits == 1)
-    gemm_bf16s_v4<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
-  else
-    gemm_bf16s_v4<BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
-                                             (size_t)M * N, 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_bf16_v4(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
-                               int* eff_splits) {
-  *eff_splits = 1;
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (bn == 256) return launch_v4<256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
-  return launch_v4<128>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
-}
-
-template <int BM, int BN>
-static hipError_t launch_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
-                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
-  const int mt = cdiv(M, BM), nt = cdiv(N, BN);
-  const int k_chunk = cdiv(cdiv(K, splits), 32) * 32;
-  splits = cdiv(K, k_chunk);
-  *eff_splits = splits;
-  const int nb = mt * nt * splits;
-  const int grid = cdiv(nb, 8) * 8;
-  const size_t lds = 3 * (2 * BM * 64 + BN * 64);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16s_v5<BM, BN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  if (splits == 1)
-    gemm_bf16s_v5<BM, BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum);
-  else
-    gemm_bf16s_v5<BM, BN><<<grid, 256, lds, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
-                                                 (size_t)M * N, 0);
-  return hipGetLastError();
-}
-
-// tile: 0 = 256x256, 1 = 128x512
-hipError_t launch_gemm_bf16_v5(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int tile, float* part, hipStream_t s,
-                               int* eff_splits) {
-  *eff_splits = 1;
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (tile == 1) return launch_v5<128, 512>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
-  return launch_v5<256, 256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
-}
-
-hipError_t launch_gemm_bf16_v3(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg,
-                               int N, float* C, int ldc, int accum, int splits, int bn, float* part, hipStream_t s,
-                               int* eff_splits) {
-  *eff_splits = 1;
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (bn == 256) return launch_v3<256>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
-  return launch_v3<128>(Ah, Al, lda, M, K, seg, N, C, ldc, accum, splits, part, s, eff_splits);
 }
 
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
