@@ -153,7 +153,6 @@ extern "C" void jev_prefix_destroy(jev_prefix* p) { delete p; }
 // workspace layout
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kMaxAttnSplits = 4;                     // prefix key splits (+1 own-rows split)
 constexpr size_t kGemmPartFloats = 640ull * 128 * 128; // bound of split-K partials (see gemm_bf16_splits)
 
 struct Layout {
@@ -165,7 +164,19 @@ struct Layout {
   int Tc;
 };
 
-Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_mask, bool need_logits) {
+// Rows of attention partials a call of T rows may need: max over T' <= T of splits(T') * T'
+// when splits(T') > 1 (the split count falls as rows grow).
+size_t attn_part_rows(const jev_config& c, int T, int P) {
+  const int G = c.n_q_heads / c.n_kv_heads;
+  size_t best = 0;
+  for (int t = 1; t <= T; ++t) {
+    const int ns = attn_splits(t, G, c.n_kv_heads, P, 1);
+    if (ns > 1) best = std::max(best, (size_t)ns * t);
+  }
+  return best;
+}
+
+Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_mask, bool need_logits, int P) {
   const jev_config& c = m->cfg;
   const bool bf = is_bf16(m);
   Layout L{};
@@ -195,8 +206,9 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.q = take(e * T * HqD * (bf ? 2 : 1));   // bf16 models: q hi and lo planes
   L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
   L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
-  L.o_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * HqD : 0);
-  L.lse_part = take(bf ? 4ull * (kMaxAttnSplits + 1) * T * c.n_q_heads : 0);
+  const size_t prow = bf ? attn_part_rows(c, T, P) : 0;
+  L.o_part = take(4ull * prow * HqD);
+  L.lse_part = take(4ull * prow * c.n_q_heads);
   L.gpart = take(bf ? 4ull * kGemmPartFloats : 0);
   L.h = take(4ull * R * c.hidden);
   L.hsplit = take(bf && need_logits ? 4ull * R * c.hidden : 0);
@@ -213,7 +225,7 @@ extern "C" size_t jev_workspace_bytes(const jev_model* m, int32_t prefix_len, in
                                       int32_t max_targets) {
   if (!m || prefix_len < 0 || max_rows < 0 || max_seqs < 0 || max_targets < 0) return 0;
   const int R = std::min(max_rows, max_targets);
-  return make_layout(m, max_rows, R, max_targets, max_seqs, true, max_targets > 0).total;
+  return make_layout(m, max_rows, R, max_targets, max_seqs, true, max_targets > 0, prefix_len).total;
 }
 
 // ---------------------------------------------------------------------------
@@ -378,15 +390,8 @@ struct Forward {
         }))
       return st;
 
-    int n_split = 0, split_len = 0;
-    if (P > 0) {
-      const long base = ((long)(Hq / Hkv) * T + 127) / 128 * Hkv;
-      n_split = (int)std::min<long>(kMaxAttnSplits, std::max<long>(1, (512 + base - 1) / base));
-      n_split = std::min(n_split, (P + 255) / 256);
-      n_split = std::max(n_split, 1);
-      split_len = ((P + n_split - 1) / n_split + 63) / 64 * 64;
-      n_split = (P + split_len - 1) / split_len;
-    }
+    // attention splits: about one block per compute unit (partials merged when > 1)
+    const int n_split = attn_splits(T, Hq / Hkv, Hkv, P, 1);
     const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
     const double attn_bytes = 2.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + 2.0 * T * HqD) + 4.0 * T * HqD;
 
@@ -429,15 +434,18 @@ struct Forward {
       a.vts = static_cast<const _Float16*>(vdst);
       a.lds = kld;
       a.seq_start = seq_start; a.mask = mask;
-      a.n_split = n_split; a.split_len = split_len;
+      a.n_split = n_split;
       a.o_part = at<float>(ws, L.o_part);
       a.lse_part = at<float>(ws, L.lse_part);
+      a.oh = a_hi; a.ol = a_lo;
       a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
       if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
-      if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 2) * T * HqD, [&] {
-            return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, a_hi, a_lo, s);
-          }))
-        return st;
+      if (n_split > 1) {
+        if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 1) * T * HqD, [&] {
+              return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, s);
+            }))
+          return st;
+      }
       // o-proj: x += o·W_oᵀ, then m = RMSNorm(x; g2) into the activation planes
       if (jev_status st = gemm_deferred(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       if (jev_status st = run_k(K_RMSNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
@@ -463,19 +471,17 @@ struct Forward {
     return JEV_OK;
   }
 
-  jev_status run(const void* vis, int n_vis) {
-    if (is_bf16(m)) return run_bf16(vis, n_vis);
+  jev_status run(const void* vis, int n_vis) { return is_bf16(m) ? run_bf16(vis, n_vis) : run_f32(vis, n_vis); }
+
+  // float32 models: every step in float32 (VALU GEMMs, one-thread-per-row attention).
+  jev_status run_f32(const void* vis, int n_vis) {
     const int T = plan.T;
     const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
     const int HqD = Hq * D, NQKV = nqkv(c);
-    const bool bf = is_bf16(m);
-    const double e = (double)kv_elem(m);
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
     float* act = at<float>(ws, L.act);
-    uint16_t* act_hi = reinterpret_cast<uint16_t*>(act);          // bf16 models: hi plane
-    uint16_t* act_lo = act_hi + (size_t)T * wide;                  // and lo plane, same rows
-    const AOp A_act{act, act_hi, act_lo};
+    const AOp A_act{act, nullptr, nullptr};
     float* big = at<float>(ws, L.big);
     const int* tok = at<int>(ws, L.tok);
     const int* pos = at<int>(ws, L.pos);
@@ -485,29 +491,18 @@ struct Forward {
     const int P = (mode == Mode::Prefill) ? 0 : pf->P;
     const double rowbytes = 4.0 * T * H;
 
-    if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * (bf ? 1.5 : 2.0),
-                          [&] { return launch_embed(bf, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
+    if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 2.0,
+                              [&] { return launch_embed(false, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
       return st;
-
-    // attention split plan (bf16 path): enough prefix splits to give ~512 blocks
-    int n_split = 0, split_len = 0;
-    if (bf && P > 0) {
-      const long base = ((long)(Hq / Hkv) * T + 127) / 128 * Hkv;
-      n_split = (int)std::min<long>(kMaxAttnSplits, std::max<long>(1, (512 + base - 1) / base));
-      n_split = std::min(n_split, (P + 255) / 256);
-      n_split = std::max(n_split, 1);
-      split_len = ((P + n_split - 1) / n_split + 63) / 64 * 64;
-      n_split = (P + split_len - 1) / split_len;
-    }
     const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
-    const double attn_bytes = e * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + (double)T * HqD) + 4.0 * T * HqD;
+    const double attn_bytes = 4.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + (double)T * HqD) + 4.0 * T * HqD;
 
     for (int l = 0; l < c.n_layers; ++l) {
       const jev_layer& W = m->layers[l];
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
       if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
-            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, bf ? nullptr : act,
-                                  bf ? act_hi : nullptr, bf ? act_lo : nullptr, wide, s);
+            return launch_rmsnorm(false, x, H, nullptr, T, H, W.attn_norm, c.rms_eps, act, nullptr, nullptr, wide,
+                                  s);
           }))
         return st;
       if (jev_status st = gemm(A_act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0)) return st;
@@ -523,68 +518,41 @@ struct Forward {
         vdst = at<char>(ws, L.vts);
         kld = L.Tc;
       }
-      if (jev_status st = run_k(K_ROPE, 0.0, (double)T * (Hq + Hkv) * D * (4 + e), [&] {
-            return launch_rope_qk(bf, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q),
-                                  bf ? at<char>(ws, L.q) + (size_t)T * HqD * 2 : nullptr, kdst, kld, 0, s);
+      if (jev_status st = run_k(K_ROPE, 0.0, (double)T * (Hq + Hkv) * D * 8, [&] {
+            return launch_rope_qk(false, big, T, Hq, Hkv, D, pos, log2_theta, at<char>(ws, L.q), nullptr, kdst, kld,
+                                  0, s);
           }))
         return st;
-      if (jev_status st = run_k(K_VT, 0.0, (double)T * Hkv * D * (4 + e), [&] {
-            return launch_v_transpose(bf, big + (size_t)(Hq + Hkv) * D, NQKV, T, Hkv * D, vdst, kld, 0, s);
+      if (jev_status st = run_k(K_VT, 0.0, (double)T * Hkv * D * 8, [&] {
+            return launch_v_transpose(false, big + (size_t)(Hq + Hkv) * D, NQKV, T, Hkv * D, vdst, kld, 0, s);
           }))
         return st;
       if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
 
-      if (bf) {
-        AttnArgs a{};
-        a.q = at<_Float16>(ws, L.q);
-        a.q_lo = a.q + (size_t)T * HqD;
-        a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
-        if (P > 0) {
-          a.kp = reinterpret_cast<const _Float16*>(store_k(l));
-          a.vtp = reinterpret_cast<const _Float16*>(store_vt(l));
-        }
-        a.P = P; a.ldp = pf->Pc;
-        a.ks = static_cast<const _Float16*>(kdst);
-        a.vts = static_cast<const _Float16*>(vdst);
-        a.lds = kld;
-        a.seq_start = seq_start; a.mask = mask;
-        a.n_split = n_split; a.split_len = split_len;
-        a.o_part = at<float>(ws, L.o_part);
-        a.lse_part = at<float>(ws, L.lse_part);
-        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-        if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
-        if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 2) * T * HqD, [&] {
-              return launch_attn_merge(a.o_part, a.lse_part, n_split + 1, T, Hq, D, act_hi, act_lo, s);
-            }))
-          return st;
-      } else {
-        AttnArgsF a{};
-        a.q = at<float>(ws, L.q);
-        a.T = T; a.Hq = Hq; a.G = Hq / Hkv;
-        if (P > 0) {
-          a.kp = reinterpret_cast<const float*>(store_k(l));
-          a.vtp = reinterpret_cast<const float*>(store_vt(l));
-        }
-        a.P = P; a.ldp = pf->Pc;
-        a.ks = static_cast<const float*>(kdst);
-        a.vts = static_cast<const float*>(vdst);
-        a.lds = kld;
-        a.seq_start = seq_start; a.mask = mask;
-        a.scale = (float)(1.0 / std::sqrt((double)D));
-        a.o = act;
-        if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f32(a, D, s); })) return st;
+      AttnArgsF a{};
+      a.q = at<float>(ws, L.q);
+      a.T = T; a.Hq = Hq; a.G = Hq / Hkv;
+      if (P > 0) {
+        a.kp = reinterpret_cast<const float*>(store_k(l));
+        a.vtp = reinterpret_cast<const float*>(store_vt(l));
       }
+      a.P = P; a.ldp = pf->Pc;
+      a.ks = static_cast<const float*>(kdst);
+      a.vts = static_cast<const float*>(vdst);
+      a.lds = kld;
+      a.seq_start = seq_start; a.mask = mask;
+      a.scale = (float)(1.0 / std::sqrt((double)D));
+      a.o = act;
+      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f32(a, D, s); })) return st;
       // act now holds o [T][HqD] with row stride HqD
       if (jev_status st = gemm(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
       if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
-            return launch_rmsnorm(bf, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, bf ? nullptr : act,
-                                  bf ? act_hi : nullptr, bf ? act_lo : nullptr, wide, s);
+            return launch_rmsnorm(false, x, H, nullptr, T, H, W.mlp_norm, c.rms_eps, act, nullptr, nullptr, wide, s);
           }))
         return st;
       if (jev_status st = gemm(A_act, wide, T, H, W.w_gate, I, W.w_up, I, nullptr, 0, big, 2 * I, 0)) return st;
-      if (jev_status st = run_k(K_SILU, 0.0, 12.0 * T * I, [&] {
-            return launch_silu_mul(big, T, I, bf ? nullptr : act, bf ? act_hi : nullptr, bf ? act_lo : nullptr, s);
-          }))
+      if (jev_status st = run_k(K_SILU, 0.0, 12.0 * T * I,
+                                [&] { return launch_silu_mul(big, T, I, act, nullptr, nullptr, s); }))
         return st;   // gate|up [T][2I] -> u [T][I]
       if (jev_status st = gemm(A_act, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1)) return st;
     }
@@ -675,7 +643,7 @@ extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, 
   plan.pos.resize(p->P);
   for (int i = 0; i < p->P; ++i) plan.pos[i] = i;
   plan.seq_start.assign(p->P, 0);
-  const Layout L = make_layout(m, plan.T, 0, 0, 1, false, false);
+  const Layout L = make_layout(m, plan.T, 0, 0, 1, false, false, 0);
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
@@ -700,7 +668,7 @@ extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids
   if (B == 0) return JEV_OK;
   if (!out_logp) return fail(JEV_E_INVALID, "null out_logp");
   const Layout L = make_layout(m, plan.T, (int)plan.read_rows.size(), (int)plan.tgt_tok.size(),
-                               (int)plan.out_n.size(), false, false);
+                               (int)plan.out_n.size(), false, false, p->P);
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
@@ -730,7 +698,7 @@ extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_id
   if (!out_score) return fail(JEV_E_INVALID, "null out_score");
   const int R = (int)plan.read_rows.size();
   const int NT = (int)plan.tgt_tok.size();
-  const Layout L = make_layout(m, plan.T, R, NT, (int)plan.out_n.size(), true, true);
+  const Layout L = make_layout(m, plan.T, R, NT, (int)plan.out_n.size(), true, true, p->P);
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");

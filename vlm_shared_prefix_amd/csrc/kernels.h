@@ -15,21 +15,24 @@ struct GemmSegsF {
 };
 
 // float16 MFMA attention (head_dim 128).
+// float16 attention (head_dim 128) of T query rows: prefix keys then the rows' own keys.
 struct AttnArgs {
   const _Float16* q;       // [T][Hq][128]  q rounded to f16 (hi)
   const _Float16* q_lo;    // [T][Hq][128]  q - hi, rounded to f16
   int T, Hq, Hkv, G;
   const _Float16* kp;      // prefix K  [Hkv][ldp][128]
-  const _Float16* vtp;     // prefix Vt [Hkv][128][ldp]
+  const _Float16* vtp;     // prefix Vt [Hkv][128][ldp], columns [P, round8(P)) zero
   int P, ldp;
   const _Float16* ks;      // own K  [Hkv][lds][128]
-  const _Float16* vts;     // own Vt [Hkv][128][lds]
+  const _Float16* vts;     // own Vt [Hkv][128][lds], columns [T, round8(T)) zero
   int lds;
   const int* seq_start;    // [T] first row of the row's sequence / group
   const uint64_t* mask;    // [T] visibility over the group (nullptr: causal)
-  int n_split, split_len;  // prefix key splits
-  float* o_part;           // [n_split+1][T][Hq][128]
-  float* lse_part;         // [n_split+1][T][Hq]   (log2 units)
+  int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
+  float* o_part;           // [n_split][T][Hq][128]  (n_split > 1)
+  float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1)
+  uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1)
+  uint16_t* ol;
   float scale_log2;        // log2(e) / sqrt(128)
 };
 
@@ -68,7 +71,8 @@ hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, i
 hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
                                 int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
 // Sum of `splits` projection partials (row stride lds) -> RoPE (table cs) -> q hi/lo [T][Hq][128] f16,
-// K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1.
+// K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1 and zeros in
+// columns T..round8(T)-1 (ldv >= round8(T)).
 // cs[t][i] = (cos, sin) of pos[t] * theta^(-2i/128), i < 64 (head_dim 128).
 hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s);
 hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
@@ -83,6 +87,10 @@ hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv,
                           double log2_theta, void* q_out, void* q_lo, void* k_out, int ldk, int row0, hipStream_t s);
 hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int HD, void* vt, int ldv, int col0,
                               hipStream_t s);
+constexpr int kAttnMaxSplits = 8;
+// Splits for the bf16 attention of T rows (G q heads per KV head) over P prefix keys plus
+// own_tiles tiles of own keys: about one block per compute unit, at least two tiles each.
+int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, hipStream_t s);

@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 typedef _Float16 f16;
@@ -427,47 +429,61 @@ __global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src
 //
 // Per KV head hk the query rows are r = t*G + g (token-major, G = Hq/Hkv), so
 // one block of 128 rows covers ~128/G tokens and all G heads that share hk;
-// every prefix K/V tile loaded into LDS is used by all 128 rows.
+// every K/V tile staged in LDS is used by all 128 rows.
 // Scores are formed transposed, S^T = K · Q^T: the MFMA "A" operand is a
 // 32-key slice of K and the "B" operand is the wave's 32 queries, so each
-// lane's accumulators all belong to ONE query row (lane % 32) and the softmax
+// lane's accumulators belong to ONE query row (lane % 32) and the softmax
 // rescale is a per-lane scalar.  O^T = V^T · P^T likewise keeps a lane on its
-// query; P^T is fed straight from the score registers, with the key order
-// inside each 16-key step permuted identically in V^T's reads.
+// query; P^T is fed straight from the score registers.  The K rows of each
+// 32-key slice are read in the order that swaps key-index bits 2 and 3, which
+// makes score register i of half hs hold key 32*hs + 16*(i/8) + 8*(lane/32) + i%8:
+// the 8 keys one lane feeds to a P·V step are then consecutive in V^T.
 //
-// blockIdx.z < n_split: prefix keys [z*split_len, min(P, (z+1)*split_len)).
-// blockIdx.z == n_split: own keys — causal within the row's sequence
-// (mask == nullptr) or the row's 64-bit ancestor mask over its group.
-// Each split writes a normalised partial O and its log2-sum-exp; attn_merge
-// combines them.
+// Key tiles of 64: a row tile sees the prefix tiles [0, ceil(P/64)) followed by
+// the tiles of its own keys (from the first row's sequence start, causal within
+// the row's sequence, or the row's 64-bit ancestor mask over its group).
+// blockIdx.z = split takes the contiguous share [z*n/S, (z+1)*n/S) of those n
+// tiles.  Tiles arrive by direct global->LDS loads (16 B per lane) into a
+// double buffer, the next tile's loads in flight while the current one is
+// computed.  LDS rows are XOR-swizzled by 16 B chunk so the operand reads are
+// bank-conflict free.  With S == 1 the block writes o as bf16 hi/lo planes;
+// otherwise it writes a normalised partial o and its log2-sum-exp for
+// attn_merge.
 // ----------------------------------------------------------------------------
 #define AT_BR 128
 #define AT_BK 64
-#define KLD (128 + 8)    // halfs; 272 B rows
-#define VLD (AT_BK + 8)  // halfs; 144 B rows: conflict-free 16 B operand reads
 
-// zero the 16-bit lanes j >= cnt of an 8 x f16 chunk (cnt in [0, 8])
-__device__ __forceinline__ uint4 keep_first(uint4 v, int cnt) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = (2 * j < cnt) ? 0x0000FFFFu : 0u;
-    const uint32_t hi = (2 * j + 1 < cnt) ? 0xFFFF0000u : 0u;
-    w[j] &= (lo | hi);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// Key-index bit swap 2 <-> 3 inside a 32-key slice (the A-operand row order of S^T).
+__device__ __forceinline__ int attn_key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Reductions across the two 32-lane halves of the wave (lanes l and l^32 hold the same query).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16 sK[2][AT_BK * KLD];
-  __shared__ __attribute__((aligned(16))) f16 sV[2][128 * VLD];
+struct AttnTile {
+  const f16* K;   // [ld][128]
+  const f16* V;   // V^T [128][ld]
+  int ld, k0, ke; // tile keys [k0, k0+64); keys >= ke are not visible (and not read)
+  bool own;
+};
 
-  const int hk = blockIdx.y, split = blockIdx.z;
+__global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) f16 sK0[AT_BK * 128];
+  __shared__ __attribute__((aligned(16))) f16 sK1[AT_BK * 128];
+  __shared__ __attribute__((aligned(16))) f16 sV0[128 * AT_BK];
+  __shared__ __attribute__((aligned(16))) f16 sV1[128 * AT_BK];
+
+  const int x = blockIdx.x, hk = blockIdx.y, z = blockIdx.z, ns = a.n_split;
   const int G = a.G, T = a.T, Hq = a.Hq;
   const int R = G * T;
-  const int r0 = blockIdx.x * AT_BR;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int r0 = x * AT_BR;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hl = lane >> 5;
   const int r = r0 + wave * 32 + ql;
   const bool rvalid = r < R;
@@ -487,153 +503,120 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     }
   }
 
-  const bool own = split >= a.n_split;
-  int kb, ke, ld;
-  const f16 *Kb, *Vb;
-  if (!own) {
-    kb = split * a.split_len;
-    ke = min(a.P, kb + a.split_len);
-    Kb = a.kp + (size_t)hk * a.ldp * 128;
-    Vb = a.vtp + (size_t)hk * 128 * a.ldp;
-    ld = a.ldp;
-  } else {
-    const int t_first = r0 / G;
-    const int t_last = min(R - 1, r0 + AT_BR - 1) / G;
-    kb = a.seq_start[t_first];
-    ke = t_last + 1;
-    Kb = a.ks + (size_t)hk * a.lds * 128;
-    Vb = a.vts + (size_t)hk * 128 * a.lds;
-    ld = a.lds;
-  }
-  const int my_start = own ? a.seq_start[t] : 0;
-  const bool use_mask = own && a.mask != nullptr;
+  // this block's share of the tile sequence
+  const int ntp = (a.P + AT_BK - 1) / AT_BK;
+  const int t_first = r0 / G, t_last = min(R - 1, r0 + AT_BR - 1) / G;
+  const int own_end = t_last + 1;
+  const int own0 = a.seq_start[t_first] & ~7;   // 16 B aligned start of the block's own keys
+  const int nt_all = ntp + (own_end - own0 + AT_BK - 1) / AT_BK;
+  const int vb = (int)(((long)z * nt_all) / ns), ve = (int)(((long)(z + 1) * nt_all) / ns);
+  const int nt = ve - vb;
+  const int max_start = a.seq_start[t_last];
+  const int my_start = a.seq_start[t];
+  const bool use_mask = a.mask != nullptr;
   const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
-  // visible keys of this row within the split: [vis_lo, vis_hi)
-  const int vis_lo = own ? max(kb, my_start) : kb;
-  const int vis_hi = own ? min(ke, t + 1) : ke;
 
-  // tile loader: every load is issued unconditionally from an in-bounds address
-  // (rows < ke <= ld; a V chunk at a multiple of 8 below ld ends inside its row)
-  // and out-of-range data is zeroed afterwards, so the loads of a tile are in flight together.
-  uint4 rk[4], rv[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = k0 + (idx >> 4), c = idx & 15;
-      const int krow = key < ke ? key : 0;
-      rk[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)krow * 128 + c * 8);
+  auto tile = [&](int v) {
+    AttnTile s;
+    if (v < ntp) {
+      s.K = a.kp + (size_t)hk * a.ldp * 128; s.V = a.vtp + (size_t)hk * 128 * a.ldp; s.ld = a.ldp;
+      s.k0 = v * AT_BK; s.ke = a.P; s.own = false;
+    } else {
+      s.K = a.ks + (size_t)hk * a.lds * 128; s.V = a.vts + (size_t)hk * 128 * a.lds; s.ld = a.lds;
+      s.k0 = own0 + (v - ntp) * AT_BK; s.ke = own_end; s.own = true;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int d = idx >> 3, gk = k0 + (idx & 7) * 8;
-      const int col = gk < ld ? gk : 0;
-      rv[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)d * ld + col);
-    }
+    return s;
   };
-  // LDS V^T tile: within each 16-key group, keys are stored in the order
-  // 0-3, 8-11, 4-7, 12-15, so the 8 keys one lane feeds to a P·V step
-  // ({4h..4h+3} and {8+4h..8+4h+3}) are contiguous (one 16 B read).
-  auto sstore = [&](int k0, int buf) {
-    const bool full = k0 + AT_BK <= ke;     // uniform over the block
+  // K tile: 64 rows of 256 B, chunk c (16 B) of key row k at chunk position c ^ (k & 15).
+  // V^T tile: 128 dim rows of 128 B, key chunk c of dim d at position c ^ ((d >> 1) & 7).
+  // Rows / chunks at or past ke load row / column 0 instead (finite, never weighted);
+  // a V chunk straddling ke holds later rows of this call or zeroed padding.
+  auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      uint4 v = rk[i];
-      if (!full) {
-        const uint32_t m = (k0 + (idx >> 4) < ke) ? 0xFFFFFFFFu : 0u;
-        v = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-      }
-      *reinterpret_cast<uint4*>(&sK[buf][(idx >> 4) * KLD + (idx & 15) * 8]) = v;
+      const int slot = i * 256 + tid;
+      const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
+      const int key = s.k0 + row;
+      __builtin_amdgcn_global_load_lds(s.K + (size_t)(key < s.ke ? key : 0) * 128 + c * 8,
+                                       dk + (i * 256 + wave * 64) * 8, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int d = idx >> 3, c = idx & 7;
-      uint4 v = rv[i];
-      if (!full) v = keep_first(v, min(max(ke - (k0 + c * 8), 0), 8));
-      f16* row = &sV[buf][d * VLD + (c >> 1) * 16 + (c & 1) * 4];
-      *reinterpret_cast<uint2*>(row) = make_uint2(v.x, v.y);       // keys 8c .. 8c+3
-      *reinterpret_cast<uint2*>(row + 8) = make_uint2(v.z, v.w);   // keys 8c+4 .. 8c+7
+      const int slot = i * 256 + tid;
+      const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
+      const int key = s.k0 + c * 8;
+      __builtin_amdgcn_global_load_lds(s.V + (size_t)d * s.ld + (key < s.ke ? key : 0),
+                                       dv + (i * 256 + wave * 64) * 8, 16, 0, 0);
     }
   };
 
-  float m_run = NEG_INF, l_run = 0.f;
+  const int prow = attn_key_perm(ql);
+  const float sl = a.scale_log2;
+  float m_ref = NEG_INF, l_run = 0.f;   // m_ref: reference max of the row, in scaled log2 units
   f32x16 acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
 
-  const int kfirst = kb & ~7;
-  const int ntiles = (ke > kfirst) ? (ke - kfirst + AT_BK - 1) / AT_BK : 0;
-  if (ntiles > 0) {
-    gload(kfirst);
-    sstore(kfirst, 0);
-    __syncthreads();
-  }
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = kfirst + it * AT_BK;
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(k0 + AT_BK);      // in flight while this tile is computed
-
-    // scores for the two 32-key halves (unscaled); the two halves' accumulation
-    // chains are interleaved so consecutive MFMAs are independent
+  auto step = [&](int i, const f16* sk, const f16* sv, f16* nk, f16* nv) {
+    if (i + 1 < nt) load_tile(tile(vb + i + 1), nk, nv);   // in flight during this tile
     f32x16 s[2];
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[hs][i] = 0.f;
+      for (int e = 0; e < 16; ++e) s[hs][e] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const f16x8 k0op = *reinterpret_cast<const f16x8*>(&sK[buf][ql * KLD + c * 16 + hl * 8]);
-      const f16x8 k1op = *reinterpret_cast<const f16x8*>(&sK[buf][(32 + ql) * KLD + c * 16 + hl * 8]);
+      const int ch = (2 * c + hl) ^ (prow & 15);
+      const f16x8 k0op = *reinterpret_cast<const f16x8*>(sk + prow * 128 + ch * 8);
+      const f16x8 k1op = *reinterpret_cast<const f16x8*>(sk + (32 + prow) * 128 + ch * 8);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qreg[c], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qreg[c], s[1], 0, 0, 0);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qlo[c], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qlo[c], s[1], 0, 0, 0);
     }
-    // Only tiles that cross the split's range or hold own-row keys need a mask;
-    // the test is uniform over the block.  Rows past R hold a clamped row's
-    // finite scores and are never stored, so they need no mask.  A row sees
-    // keys in [vis_lo, vis_hi) (and, with a tree mask, only its ancestors).
-    // key of register i = k0 + hs*32 + 8*(i/4) + 4*hl + (i%4)
-    if (own || k0 < kb || k0 + AT_BK > ke) {
-      const int base = k0 + 4 * hl;
+    // Masks only where some row of the block does not see the whole tile (uniform test):
+    // a partial last prefix tile, and own-key tiles not fully visible to every row.
+    const AttnTile ts = tile(vb + i);
+    const bool need = ts.own ? (use_mask || ts.k0 < max_start || ts.k0 + AT_BK > t_first + 1)
+                             : (ts.k0 + AT_BK > ts.ke);
+    if (need) {
+      const int lo = ts.own ? my_start : 0;
+      const int hi = ts.own ? t + 1 : ts.ke;
+      const uint64_t mm = (ts.own && use_mask) ? my_mask : ~0ull;
+      const int base = ts.k0 + 8 * hl;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = base + hs * 32 + 8 * (i >> 2) + (i & 3);
-          const bool in = (unsigned)(key - vis_lo) < (unsigned)(vis_hi - vis_lo);
-          s[hs][i] = in ? s[hs][i] : NEG_INF;
+        for (int e = 0; e < 16; ++e) {
+          const int key = base + hs * 32 + 16 * (e >> 3) + (e & 7);
+          const bool in = ((unsigned)(key - lo) < (unsigned)(hi - lo)) && ((mm >> ((key - lo) & 63)) & 1ull);
+          s[hs][e] = in ? s[hs][e] : NEG_INF;
         }
-      if (use_mask) {
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rel = base + hs * 32 + 8 * (i >> 2) + (i & 3) - my_start;
-            const bool bit = (my_mask >> (rel & 63)) & 1ull;
-            s[hs][i] = bit ? s[hs][i] : NEG_INF;
-          }
-      }
     }
     float mx = NEG_INF;
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[hs][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);                 // running max, unscaled
-    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float sl = a.scale_log2;
-    const float neg_ms = -m_use * sl;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl);
-    // p = 2^(s*scale - m*scale); the row sum is taken in f32 and p is rounded
-    // to nearest f16 for the P·V product (unbiased, so the two stay consistent).
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hs][e]);
+    mx = halves_max(mx) * sl;
+    // The reference max moves only when a tile max exceeds it by more than 8: the
+    // weights p = 2^(s*scale - m_ref) stay below 2^8 (exact to f16's relative
+    // precision), and the accumulators are rescaled on few tiles.
+    const bool grow = mx > m_ref + 8.f;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = (m_ref == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == NEG_INF) ? 0.f : m_ref;
+    // the row sum is taken in f32 and p is rounded to nearest f16 for the P·V product
     float rs = 0.f;
     f16x8 pops[2][2];
 #pragma unroll
@@ -642,52 +625,73 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, neg_ms));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, -m_use));
           rs += pv;
           pops[hs][p][j] = (f16)pv;
         }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    // rescale the accumulators only when some lane's max moved
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
-    }
-
+    l_run += halves_sum(rs);
     // O^T += V^T · P^T, four 16-key steps
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const f16x8 pop = pops[hs][p];
-        const int kofs = hs * 32 + 16 * p + 8 * hl;
+        const int c = 4 * hs + 2 * p + hl;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const f16x8 vop = *reinterpret_cast<const f16x8*>(&sV[buf][(dt * 32 + ql) * VLD + kofs]);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop, acc[dt], 0, 0, 0);
+          const int d = dt * 32 + ql;
+          const f16x8 vop = *reinterpret_cast<const f16x8*>(sv + d * AT_BK + ((c ^ ((d >> 1) & 7)) * 8));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pops[hs][p], acc[dt], 0, 0, 0);
         }
       }
-    if (more) sstore(k0 + AT_BK, buf ^ 1);
-    __syncthreads();
+    // The next tile's loads have landed and every wave is done with this tile's buffers.
+    // (The wait is a builtin so the compiler knows the loads are complete; the barrier is
+    // asm with a memory clobber so no LDS access moves across it.)
+    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
+  if (nt > 0) {
+    load_tile(tile(vb), sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0x70);
+    asm volatile("s_barrier" ::: "memory");
+  }
+  for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
+    step(i, sK0, sV0, sK1, sV1);
+    if (i + 1 < nt) step(i + 1, sK1, sV1, sK0, sV0);
   }
 
   if (!rvalid) return;
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-  float* op = a.o_part + (((size_t)split * T + t) * Hq + hq) * 128;
+  if (ns == 1) {
+    const size_t ob = ((size_t)t * Hq + hq) * 128;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = dt * 32 + 8 * ii + 4 * hl;
+        u16 h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[dt][4 * ii + j] * inv;
+          h[j] = f32_to_bf16(v);
+          l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
+        }
+        *reinterpret_cast<uint2*>(a.oh + ob + d) =
+            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(a.ol + ob + d) =
+            make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+      }
+    return;
+  }
+  float* op = a.o_part + (((size_t)z * T + t) * Hq + hq) * 128;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int d = dt * 32 + 8 * ii + 4 * hl;
-      float4 v = make_float4(acc[dt][4 * ii] * inv, acc[dt][4 * ii + 1] * inv, acc[dt][4 * ii + 2] * inv,
-                             acc[dt][4 * ii + 3] * inv);
-      *reinterpret_cast<float4*>(op + d) = v;
+      *reinterpret_cast<float4*>(op + d) = make_float4(acc[dt][4 * ii] * inv, acc[dt][4 * ii + 1] * inv,
+                                                       acc[dt][4 * ii + 2] * inv, acc[dt][4 * ii + 3] * inv);
     }
-  if (hl == 0)
-    a.lse_part[((size_t)split * T + t) * Hq + hq] = (l_run > 0.f) ? m_run * a.scale_log2 + log2f(l_run) : NEG_INF;
+  if (hl == 0) a.lse_part[((size_t)z * T + t) * Hq + hq] = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
 }
 
 // ----------------------------------------------------------------------------
@@ -820,7 +824,8 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       const int idx = threadIdx.x + 256 * j;
       const int d = idx >> 4, rr = idx & 15;
       const int t = t0 + rr;
-      if (t < T) vtdst[((size_t)hk * 128 + d) * ldv + t] = (f16)vt[rr][d];
+      // columns up to the next multiple of 8 are written (zeros past T): attention reads V^T in 8-key chunks
+      if (t < ((T + 7) & ~7)) vtdst[((size_t)hk * 128 + d) * ldv + t] = (f16)vt[rr][d];
     }
   }
 }
@@ -1157,9 +1162,18 @@ hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int
   return hipGetLastError();
 }
 
+int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
+  const long base = (long)cdiv((long)G * T, AT_BR) * Hkv;
+  const int tiles = cdiv(P, AT_BK) + own_tiles;
+  long ns = (256 + base / 2) / base;                   // about one block per compute unit
+  ns = std::min<long>(ns, std::max(1, tiles / 2));     // at least two tiles per split
+  return (int)std::max<long>(1, std::min<long>(ns, kAttnMaxSplits));
+}
+
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  dim3 grid(cdiv((long)a.G * a.T, AT_BR), a.Hkv, a.n_split + 1);
+  if (a.n_split < 1 || a.n_split > kAttnMaxSplits) return hipErrorInvalidValue;
+  dim3 grid(cdiv((long)a.G * a.T, AT_BR), a.Hkv, a.n_split);
   attn_fwd_f16<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
