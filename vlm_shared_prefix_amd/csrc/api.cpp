@@ -153,7 +153,7 @@ extern "C" void jev_prefix_destroy(jev_prefix* p) { delete p; }
 // workspace layout
 // ---------------------------------------------------------------------------
 namespace {
-constexpr size_t kGemmPartFloats = 640ull * 128 * 128; // bound of split-K partials (see gemm_bf16_splits)
+constexpr size_t kGemmPartFloats = 16ull << 20;        // bound of split-K partials (gemm_bf16_plan)
 
 struct Layout {
   // metadata (staged from the host in one copy)
@@ -302,11 +302,6 @@ struct Forward {
   }
   char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m); }
 
-  static int splits_for(int M, int N, int K) {
-    int sp = gemm_bf16_splits(M, N, K);
-    while (sp > 1 && (size_t)sp * M * N > kGemmPartFloats) --sp;
-    return sp;
-  }
 
   // A operand: float32 rows (float32 models) or bfloat16 hi/lo planes (bf16 models)
   struct AOp {
@@ -324,9 +319,8 @@ struct Forward {
       GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
       int eff = 1;
       float* part = at<float>(ws, L.gpart);
-      const int splits = splits_for(M, N, K);
       if (jev_status st = run_k(kind, flops, bytes, [&] {
-            return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, splits, part, s, &eff);
+            return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s, &eff);
           }))
         return st;
       if (eff > 1)
@@ -347,9 +341,8 @@ struct Forward {
     const double bytes = 2.0 * N * K + 4.0 * M * K + 4.0 * M * N * (accum ? 2 : 1);
     GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
     float* part = at<float>(ws, L.gpart);
-    const int splits = splits_for(M, N, K);
     return run_k(K_GEMM, flops, bytes, [&] {
-      return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, splits, part, s, splits_out);
+      return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s, splits_out);
     });
   }
 

@@ -57,12 +57,17 @@ hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, 
 // y (float32) and/or yh/yl (bfloat16 hi/lo planes) may be null.
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
                           float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
-int gemm_bf16_splits(int M, int N, int K);
-// Launches the GEMM; with *eff_splits > 1 it wrote split partials [splits][M][N] into `part`
-// and launch_splitk_reduce must follow.
+struct GemmPlan {
+  bool wide;    // 128 x 256 kernel (else 128 x 128)
+  int splits;   // K splits (partials [splits][M][N] when > 1)
+};
+GemmPlan gemm_bf16_plan(int M, int N, int K, size_t part_cap);
 // A is given as two bfloat16 planes (hi, lo) with row stride lda; the product is W·hi + W·lo.
+// K % 32 == 0.  With *eff_splits > 1 it wrote split partials [splits][M][N] (at most part_cap
+// floats) into `part` and a split-K reduction must follow.
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
-                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits);
+                            float* C, int ldc, int accum, size_t part_cap, float* part, hipStream_t s,
+                            int* eff_splits);
 // gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu].
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
                               const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);

@@ -105,8 +105,9 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x,
 
 // ----------------------------------------------------------------------------
 // K3 (bf16 models): Y[M,N] = A[M,K] · W[N,K]^T on MFMA 32x32x16 bf16, with the
-// float32 activation split into bf16 hi + lo on its way into LDS.
-// Block tile 128x128, K step 64, 4 waves in a 2x2 arrangement (64x64 each).
+// float32 activation given as two bf16 planes (hi + lo): Y = W·hi + W·lo.
+// Block tile 128x128, K step 64, 4 waves in a 2x2 arrangement (64x64 each),
+// register-staged global loads.
 // W is described by up to three row segments (e.g. wq | wk | wv).
 // Grid: 1-D, rounded up to a multiple of 8; the linear block id is remapped so
 // that blocks dispatched to the same XCD share a W tile (same N tile and K
@@ -123,15 +124,10 @@ __device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
   return s.w[2] + (size_t)(n - s.n_end[1]) * K;
 }
 
-// SWIGLU: seg.w[0] = W_gate, seg.w[1] = W_up, N = I; the tile's 128 W rows are
-// [gate 32 | up 32] for each of the two column waves, so a lane holds gate and up
-// of the same output column and the epilogue writes silu(g)*u as bf16 hi/lo planes.
-template <bool SWIGLU>
 __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah, const u16* __restrict__ Al,
                                                      int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
                                                      int n_tiles, int splits, int k_chunk, float* __restrict__ C,
-                                                     int ldc, size_t split_stride, int accum,
-                                                     u16* __restrict__ oh, u16* __restrict__ ol) {
+                                                     int ldc, size_t split_stride, int accum) {
   __shared__ __attribute__((aligned(16))) u16 sAh[GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sAl[GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sW[GBN * GLD];
@@ -144,7 +140,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   const int rest = v / m_tiles;
   const int ks = rest % splits;
   const int nt = rest / splits;
-  const int m0 = mt * GBM, n0 = nt * (SWIGLU ? GBN / 2 : GBN);
+  const int m0 = mt * GBM, n0 = nt * GBN;
   const int kbeg = ks * k_chunk;
   const int kend = min(K, kbeg + k_chunk);
 
@@ -153,13 +149,8 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   const int wm = wave >> 1, wn = wave & 1;
   const int ql = lane & 31, hl = lane >> 5;
   const bool wave_active = (m0 + wm * 64) < M;
-  // W row of tile row nr: plain = n0 + nr; SwiGLU = gate/up row n0 + (nr>>6)*32 + (nr&31)
+  // W row of tile row nr
   auto w_row = [&](int nr, bool& ok) -> const u16* {
-    if (SWIGLU) {
-      const int n = n0 + (nr >> 6) * 32 + (nr & 31);
-      ok = n < N;
-      return (((nr >> 5) & 1) ? seg.w[1] : seg.w[0]) + (size_t)(ok ? n : 0) * K;
-    }
     ok = n0 + nr < N;
     return seg_row(seg, ok ? n0 + nr : 0, K);
   };
@@ -250,23 +241,6 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
   }
 
   if (!wave_active) return;
-  if (SWIGLU) {
-    const int col = n0 + wn * 32 + ql;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (row < M && col < N) {
-          const float g = acc[i][0][r], u = acc[i][1][r];
-          const float val = g / (1.0f + expf(-g)) * u;
-          const u16 h = f32_to_bf16(val);
-          oh[(size_t)row * ldc + col] = h;
-          ol[(size_t)row * ldc + col] = f32_to_bf16(val - bf16_to_f32(h));
-        }
-      }
-    return;
-  }
   float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
   const bool add = (splits == 1) && accum;
 #pragma unroll
@@ -274,6 +248,186 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + ql;
+      const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        old[r] = (add && row < M && col < N) ? Cb[(size_t)row * ldc + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r >> 2) + (r & 3);
+        if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// K3 wide (bf16 models): the same product on a 128 x 256 block tile, 4 waves of
+// 64 x 128 (8 MFMA tiles each, half the LDS bytes per MFMA of the 64 x 64 wave
+// tile), K stages of 32 staged by direct global->LDS loads into a double buffer
+// (the next stage in flight while the current one is multiplied).  LDS rows are
+// 64 B with the 16 B chunk c of row r at position c ^ ((r / 4) % 4), which makes
+// the operand reads bank-conflict free.  All hi-plane MFMAs of a k-step are
+// issued before the lo-plane ones, so no two consecutive MFMAs share an
+// accumulator.  Same block remap and split-K layout as the 128 x 128 kernel.
+// SWIGLU: the 256 W rows are [gate 32 | up 32] x 2 per column wave.
+// ----------------------------------------------------------------------------
+#define G2M 128
+#define G2N 256
+#define G2K 32
+template <bool SWIGLU>
+__global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah, const u16* __restrict__ Al, int lda,
+                                                int M, int K, GemmSegs seg, int N, int m_tiles, int n_tiles,
+                                                int splits, int k_chunk, float* __restrict__ C, int ldc,
+                                                size_t split_stride, int accum, u16* __restrict__ oh,
+                                                u16* __restrict__ ol) {
+  __shared__ __attribute__((aligned(16))) u16 sAh0[G2M * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sAl0[G2M * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sW0[G2N * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sAh1[G2M * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sAl1[G2M * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sW1[G2N * G2K];
+
+  const int nb = m_tiles * n_tiles * splits;
+  const int per = gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (v >= nb) return;
+  const int mt = v % m_tiles;
+  const int rest = v / m_tiles;
+  const int ks = rest % splits;
+  const int ntile = rest / splits;
+  const int m0 = mt * G2M, n0 = ntile * (SWIGLU ? G2N / 2 : G2N);
+  const int kbeg = ks * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+  const int nst = (kend - kbeg) / G2K;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ql = lane & 31, hl = lane >> 5;
+
+  // W tile row nr -> weight row (rows past N read row 0; their outputs are not stored).
+  // K is a multiple of 32 and k_chunk a multiple of G2K.
+  auto w_row = [&](int nr) -> const u16* {
+    if (SWIGLU) {
+      const int gi = nr >> 5;
+      const int n = n0 + (gi >> 2) * 64 + ((gi & 3) >> 1) * 32 + (nr & 31);
+      return ((gi & 1) ? seg.w[1] : seg.w[0]) + (size_t)(n < N ? n : 0) * K;
+    }
+    const int n = n0 + nr;
+    if (n >= N) return seg.w[0];
+    if (n < seg.n_end[0]) return seg.w[0] + (size_t)n * K;
+    if (n < seg.n_end[1]) return seg.w[1] + (size_t)(n - seg.n_end[0]) * K;
+    return seg.w[2] + (size_t)(n - seg.n_end[1]) * K;
+  };
+  // per-thread source rows of its 8 loads (slot = i*256 + tid; row = slot/4; 16 B chunk c = (slot%4) ^ ((row/4)%4))
+  const u16* srcA[2];
+  const u16* srcL[2];
+  const u16* srcW[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = i * 256 + tid, row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+    const size_t off = (size_t)(m0 + row < M ? m0 + row : 0) * lda + c * 8;
+    srcA[i] = Ah + off;
+    srcL[i] = Al + off;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = i * 256 + tid, row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+    srcW[i] = w_row(row) + c * 8;
+  }
+  auto load_stage = [&](int k0, u16* dA, u16* dL, u16* dW) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds(srcA[i] + k0, dA + (i * 256 + wave * 64) * 8, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(srcL[i] + k0, dL + (i * 256 + wave * 64) * 8, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(srcW[i] + k0, dW + (i * 256 + wave * 64) * 8, 16, 0, 0);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const u16* sA, const u16* sL, const u16* sW) {
+#pragma unroll
+    for (int kk = 0; kk < G2K / 16; ++kk) {
+      const int c = kk * 2 + hl;
+      bf16x8 ah[2], al[2], bw[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + ql;
+        const int o = r * G2K + ((c ^ ((r >> 2) & 3)) * 8);
+        ah[i] = *reinterpret_cast<const bf16x8*>(sA + o);
+        al[i] = *reinterpret_cast<const bf16x8*>(sL + o);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + ql;
+        bw[j] = *reinterpret_cast<const bf16x8*>(sW + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  auto step = [&](int s, const u16* cA, const u16* cL, const u16* cW, u16* nA, u16* nL, u16* nW) {
+    if (s + 1 < nst) load_stage(kbeg + (s + 1) * G2K, nA, nL, nW);
+    compute(cA, cL, cW);
+    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
+  if (nst > 0) {
+    load_stage(kbeg, sAh0, sAl0, sW0);
+    __builtin_amdgcn_s_waitcnt(0x70);
+    asm volatile("s_barrier" ::: "memory");
+  }
+  for (int s = 0; s < nst; s += 2) {
+    step(s, sAh0, sAl0, sW0, sAh1, sAl1, sW1);
+    if (s + 1 < nst) step(s + 1, sAh1, sAl1, sW1, sAh0, sAl0, sW0);
+  }
+
+  if (m0 + wm * 64 >= M) return;
+  if (SWIGLU) {
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int col = n0 + wn * 64 + jp * 32 + ql;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (row < M && col < N) {
+            const float g = acc[i][2 * jp][r], u = acc[i][2 * jp + 1][r];
+            const float val = g / (1.0f + expf(-g)) * u;
+            const u16 h = f32_to_bf16(val);
+            oh[(size_t)row * ldc + col] = h;
+            ol[(size_t)row * ldc + col] = f32_to_bf16(val - bf16_to_f32(h));
+          }
+        }
+    }
+    return;
+  }
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + ql;
       const int rbase = m0 + wm * 64 + i * 32 + 4 * hl;
       float old[16];
 #pragma unroll
@@ -1055,46 +1209,63 @@ hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, i
   return hipGetLastError();
 }
 
-// Split-K count: as many K splits as fill one round of 512 resident blocks
-// (2 per CU) without exceeding it, at most 8, each split keeping >= 256 of K.
-// Chosen by measurement on the 2B/7B projection shapes: a partial second
-// round of blocks costs more than the extra split partials save.
-int gemm_bf16_splits(int M, int N, int K) {
-  const long tiles = (long)cdiv(M, GBM) * cdiv(N, GBN);
-  int s = (int)(512 / tiles);
-  const int kmax = K / 256;
-  if (s > kmax) s = kmax;
-  if (s > 8) s = 8;
-  return s < 1 ? 1 : s;
+// Kernel and split-K choice.  The 128 x 256 kernel is used when its tiles with at
+// most 4 K splits give about 1.5 blocks per CU (384 blocks) and each split keeps
+// >= 512 of K; otherwise the 128 x 128 kernel with as many splits as fill one
+// round of 512 resident blocks (2 per CU), at most 8, each >= 256 of K.  Split
+// partials never exceed part_cap floats.  Chosen by measurement on the 2B/7B
+// projection shapes.
+GemmPlan gemm_bf16_plan(int M, int N, int K, size_t part_cap) {
+  GemmPlan p{};
+  const long t2 = (long)cdiv(M, G2M) * cdiv(N, G2N);
+  int s2 = (int)((384 + t2 - 1) / t2);
+  if (s2 <= 4 && K / s2 >= 512) {
+    p.wide = true;
+    p.splits = s2;
+  } else {
+    const long t1 = (long)cdiv(M, GBM) * cdiv(N, GBN);
+    int s1 = (int)(512 / t1);
+    s1 = std::min(s1, K / 256);
+    p.wide = false;
+    p.splits = std::max(1, std::min(s1, 8));
+  }
+  while (p.splits > 1 && (size_t)p.splits * M * N > part_cap) --p.splits;
+  return p;
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
-                            float* C, int ldc, int accum, int splits, float* part, hipStream_t s, int* eff_splits) {
+                            float* C, int ldc, int accum, size_t part_cap, float* part, hipStream_t s,
+                            int* eff_splits) {
   *eff_splits = 1;
   if (M <= 0 || N <= 0) return hipSuccess;
-  const int mt = cdiv(M, GBM), nt = cdiv(N, GBN);
-  const int k_chunk = cdiv(cdiv(K, splits), GBK) * GBK;
-  splits = cdiv(K, k_chunk);
+  if (K % G2K) return hipErrorInvalidValue;
+  const GemmPlan pl = gemm_bf16_plan(M, N, K, part_cap);
+  const int bk = pl.wide ? G2K : GBK;
+  const int mt = cdiv(M, GBM), nt = cdiv(N, pl.wide ? G2N : GBN);
+  const int k_chunk = cdiv(cdiv(K, pl.splits), bk) * bk;
+  const int splits = cdiv(K, k_chunk);
   *eff_splits = splits;
-  const int nb = mt * nt * splits;
-  const int grid = cdiv(nb, 8) * 8;
-  if (splits == 1)
-    gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, 1, k_chunk, C, ldc, 0, accum,
-                                           nullptr, nullptr);
+  const int grid = cdiv(mt * nt * splits, 8) * 8;
+  float* out = splits == 1 ? C : part;
+  const int ldo = splits == 1 ? ldc : N;
+  const int acc = splits == 1 ? accum : 0;
+  if (pl.wide)
+    gemm_bf16w<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+                                           (size_t)M * N, acc, nullptr, nullptr);
   else
-    gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, part, N,
-                                           (size_t)M * N, 0, nullptr, nullptr);
+    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo, (size_t)M * N,
+                                    acc);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
                               const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s) {
   if (M <= 0 || I <= 0) return hipSuccess;
-  const int mt = cdiv(M, GBM), nt = cdiv(I, GBN / 2);
-  const int nb = mt * nt;
-  const int grid = cdiv(nb, 8) * 8;
+  if (K % G2K) return hipErrorInvalidValue;
+  const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
+  const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
-  gemm_bf16s<true><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
+  gemm_bf16w<true><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
   return hipGetLastError();
 }
 
