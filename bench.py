@@ -44,6 +44,57 @@ def workload_name(cfg):
             f"tokens, {cfg.n_cands} candidates each")
 
 
+def roofline(kind, d):
+    """Roofline entry of one kernel kind from the library's event timing.
+
+    achieved = algorithmic flops per launch (each product counted once) / average
+    launch time.  The bf16 GEMMs run every product twice (hi and lo planes of the
+    float32 activations), so the MFMA pipes execute 2x the algorithmic flops:
+    reported as executed_tflops / executed_frac.
+    """
+    from vlm_shared_prefix_amd import profiling
+    n = d["launches"]
+    avg_s = d["ms"] / n * 1e-3
+    traffic = None
+    stored = profiling.stored_traffic(os.path.join(ROOT, "profiles", f"{kind}_traffic.md"))
+    if stored and stored[1] == profiling.source_digest():
+        traffic = stored[0]
+    if d["flops"] > 0:
+        ach = d["flops"] / n / avg_s / 1e12
+        r = {"kernel": kind, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+             "avg_launch_us": round(avg_s * 1e6, 2), "launches": n,
+             "algorithmic_flops_per_launch": d["flops"] / n}
+        if kind in ("gemm", "gemm_swiglu", "lm_head_gemm"):
+            r["executed_tflops"] = round(2 * ach, 2)
+            r["executed_frac"] = round(2 * ach / PEAK_BF16_TFLOPS, 4)
+        return r
+    ach = d["bytes"] / n / avg_s / 1e9
+    return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "avg_launch_us": round(avg_s * 1e6, 2),
+            "launches": n}
+
+
+def attention_entry(prof, prefix_kv_bytes, what):
+    """MFMA utilisation of the attention launches of one call kind (+ its split merge)."""
+    at = prof.get("attn_fwd")
+    if not at:
+        return None
+    a_s = at["ms"] / at["launches"] * 1e-3
+    a_tf = at["flops"] / at["launches"] / a_s / 1e12
+    e = {"what": what, "achieved_tflops": round(a_tf, 2), "mfma_util": round(a_tf / PEAK_BF16_TFLOPS, 4),
+         "avg_launch_us": round(a_s * 1e6, 2), "launches": at["launches"],
+         "algorithmic_flops_per_launch": at["flops"] / at["launches"]}
+    if prefix_kv_bytes:
+        e["prefix_kv_gbs"] = round(prefix_kv_bytes / a_s / 1e9, 1)
+        e["prefix_kv_hbm_frac"] = round(prefix_kv_bytes / a_s / 1e9 / PEAK_HBM_GBS, 4)
+    mg = prof.get("attn_merge")
+    if mg:
+        e["merge_avg_us"] = round(mg["ms"] / mg["launches"] * 1e3, 2)
+        e["with_merge_mfma_util"] = round(at["flops"] / (at["ms"] + mg["ms"]) * 1e3 / 1e12 / PEAK_BF16_TFLOPS, 4)
+    return e
+
+
 def cpu_baseline(cfg, seed, budget_layers=2):
     """The oracle as it stands on a bounded sample, scaled to the whole step.
 
@@ -92,6 +143,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
@@ -152,7 +205,7 @@ def main():
     ms_prefill = timed(prefill_only, max(1, args.steps // 2))
     log(f"[bench] score-only {ms_score:.3f} ms, prefill-only {ms_prefill:.3f} ms")
 
-    # per-kernel event timing (separate pass; same steps)
+    # per-kernel event timing (separate passes over the same calls)
     J.jev_profile_start(sess.model)
     for _ in range(args.profile_steps):
         step()
@@ -161,35 +214,30 @@ def main():
     for _ in range(args.profile_steps):
         score_only()
     prof_score = J.jev_profile_stop(sess.model)
-    dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
-    d = prof_step[dom]
-    avg_ms = d["ms"] / d["launches"]
-    if d["flops"] > 0:
-        ach = d["flops"] / d["launches"] / (avg_ms * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": d["launches"],
-                "algorithmic_flops_per_launch": d["flops"] / d["launches"]}
-    else:
-        ach = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "avg_launch_us": round(avg_ms * 1e3, 2),
-                "launches": d["launches"]}
-    at = prof_score.get("attention")
-    attn = None
-    if at:
-        a_ms = at["ms"] / at["launches"]
-        a_tf = at["flops"] / at["launches"] / (a_ms * 1e-3) / 1e12
-        kv_bytes = 2.0 * cfg.n_kv_heads * cfg.prefix_len * cfg.head_dim * 2
-        attn = {"kernel": "attention (score call, shared prefix + own rows)",
-                "achieved_tflops": round(a_tf, 2), "mfma_util": round(a_tf / PEAK_BF16_TFLOPS, 4),
-                "prefix_kv_gbs": round(kv_bytes / (a_ms * 1e-3) / 1e9, 1),
-                "prefix_kv_hbm_frac": round(kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "avg_launch_us": round(a_ms * 1e3, 2),
-                "algorithmic_flops_per_launch": at["flops"] / at["launches"],
-                "query_rows": cfg.group * T, "padded_rows": cfg.group * cfg.n_suffix * cfg.s_max}
+    J.jev_profile_start(sess.model)
+    for _ in range(args.profile_steps):
+        prefill_only()
+    prof_prefill = J.jev_profile_stop(sess.model)
+    roof = None
+    if prof_step:
+        dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
+        roof = roofline(dom, prof_step[dom])
+    attn = {"score_call": attention_entry(prof_score, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
+                                          f"shared prefix ({cfg.prefix_len} keys) + own rows of the "
+                                          f"{cfg.n_suffix} suffixes"),
+            "prefill": attention_entry(prof_prefill, 0,
+                                       f"causal self-attention of the {cfg.prefix_len} prefix rows"),
+            "query_rows": cfg.group * T, "padded_rows": cfg.group * cfg.n_suffix * cfg.s_max}
     kernels = {k: {"launches": v["launches"], "ms_total": round(v["ms"], 4),
                    "us_avg": round(v["ms"] * 1e3 / v["launches"], 2)} for k, v in prof_step.items()}
+    if args.calib_copy:   # plain copy of a known size for the FETCH_SIZE / WRITE_SIZE scale factors
+        from vlm_shared_prefix_amd import profiling
+        src = torch.empty(profiling.CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

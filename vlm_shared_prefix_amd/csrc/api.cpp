@@ -245,13 +245,15 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Profiled launch kinds, named after the kernels they launch.
 enum Kind {
-  K_EMBED, K_RMSNORM, K_GEMM, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE, K_SILU, K_TARGET, K_CANDSM,
-  K_LMHEAD, K_ROWLSE, K_TREEFIN, K_NKINDS
+  K_EMBED, K_RMSNORM, K_RESNORM, K_ROPETAB, K_QKVPOST, K_GEMM, K_SWIGLU, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE,
+  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_NKINDS
 };
-const char* const kKindName[K_NKINDS] = {"embed_rows", "rmsnorm_rows", "gemm", "splitk_reduce", "rope_qk",
-                                         "v_transpose", "attention", "attn_merge", "silu_mul", "target_logits",
-                                         "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize"};
+const char* const kKindName[K_NKINDS] = {
+    "embed_rows", "rmsnorm_rows", "residual_norm", "rope_table", "qkv_post", "gemm", "gemm_swiglu",
+    "splitk_reduce", "rope_qk", "v_transpose", "attn_fwd", "attn_merge", "silu_mul", "target_logits",
+    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize"};
 
 struct Forward {
   const jev_prefix* pf;
@@ -374,10 +376,10 @@ struct Forward {
       return st;
     if (c.n_layers == 0) return JEV_OK;
     float2* rope = at<float2>(ws, L.rope);
-    if (jev_status st = run_k(K_ROPE, 0.0, 8.0 * T * 64,
+    if (jev_status st = run_k(K_ROPETAB, 0.0, 8.0 * T * 64,
                               [&] { return launch_rope_table(pos, T, log2_theta, rope, s); }))
       return st;
-    if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {
+    if (jev_status st = run_k(K_RESNORM, 0.0, 2 * rowbytes, [&] {
           return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[0].attn_norm, c.rms_eps, a_hi, a_lo,
                                       wide, s);
         }))
@@ -407,7 +409,7 @@ struct Forward {
       }
       _Float16* q_hi = at<_Float16>(ws, L.q);
       _Float16* q_lo = q_hi + (size_t)T * HqD;
-      if (jev_status st = run_k(K_ROPE, 0.0, (double)T * NQKV * 4 * sp + (double)T * (2 * HqD + 2 * Hkv * D) * 2, [&] {
+      if (jev_status st = run_k(K_QKVPOST, 0.0, (double)T * NQKV * 4 * sp + (double)T * (2 * HqD + 2 * Hkv * D) * 2, [&] {
             return launch_qkv_post(sp > 1 ? part : big, NQKV, (size_t)T * NQKV, sp, T, Hq, Hkv, rope, q_hi, q_lo,
                                    kdst, kld, vdst, kld, s);
           }))
@@ -441,12 +443,12 @@ struct Forward {
       }
       // o-proj: x += o·W_oᵀ, then m = RMSNorm(x; g2) into the activation planes
       if (jev_status st = gemm_deferred(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
-      if (jev_status st = run_k(K_RMSNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
+      if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H, W.mlp_norm, c.rms_eps,
                                         a_hi, a_lo, wide, s);
           }))
         return st;
-      if (jev_status st = run_k(K_GEMM, 2.0 * T * 2 * I * H, 2.0 * 2 * I * H + 4.0 * T * H + 4.0 * T * I, [&] {
+      if (jev_status st = run_k(K_SWIGLU, 2.0 * T * 2 * I * H, 2.0 * 2 * I * H + 4.0 * T * H + 4.0 * T * I, [&] {
             return launch_gemm_swiglu(a_hi, a_lo, wide, T, H, static_cast<const uint16_t*>(W.w_gate),
                                       static_cast<const uint16_t*>(W.w_up), I, u_hi, u_lo, I, s);
           }))
@@ -454,7 +456,7 @@ struct Forward {
       // down: x += u·W_dᵀ, then the next layer's input norm
       if (jev_status st = gemm_deferred(A_u, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       const void* next_g = (l + 1 < c.n_layers) ? m->layers[l + 1].attn_norm : nullptr;
-      if (jev_status st = run_k(K_RMSNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
+      if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
                                         next_g ? next_g : W.mlp_norm, c.rms_eps, next_g ? a_hi : nullptr,
                                         next_g ? a_lo : nullptr, wide, s);

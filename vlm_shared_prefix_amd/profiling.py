@@ -1,0 +1,170 @@
+"""HBM traffic of a kernel from rocprofv3 counter runs, calibrated by a plain copy.
+
+Two counter runs of the same command (one with ``--pmc FETCH_SIZE``, one with
+``--pmc WRITE_SIZE``, both ``--output-format csv``) give KiB per dispatch for
+every kernel.  The command also runs a device-to-device copy of a known size
+(``bench.py --calib-copy`` copies ``CALIB_BYTES``); the counter value of that
+copy kernel divided by its true bytes is the scale factor applied to the
+target kernel's reading:
+
+    traffic = FETCH_KiB * 1024 / fetch_scale + WRITE_KiB * 1024 / write_scale
+
+averaged over the target kernel's dispatches.  ``source_digest()`` fingerprints
+the kernel sources, so a stored figure can be dropped once they change.
+
+    python -m vlm_shared_prefix_amd.profiling <fetch_dir> <write_dir> <kernel-substring> [out.md]
+    python -m vlm_shared_prefix_amd.profiling --stats <kernel_trace_dir> [out.md]
+"""
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CALIB_BYTES = 512 << 20          # bytes moved by the calibration copy (read once, written once)
+COPY_KERNEL = "copyBuffer"       # the runtime's device-to-device copy kernel
+
+
+def source_digest() -> str:
+    """sha256 over the HIP/C++ sources of libjev.so (kernels, ABI, planner)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(HERE, "csrc"))):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(HERE, "csrc", name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(run_dir: str, counter: str):
+    """[(dispatch id, kernel name, value)] of one counter, in dispatch order."""
+    paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    out = []
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def per_dispatch(run_dir: str, counter: str, substring: str):
+    vals = [v for _, name, v in _counter_rows(run_dir, counter) if substring in name]
+    if not vals:
+        raise ValueError(f"no dispatch of a kernel containing {substring!r} with {counter}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def calibration_dispatch(run_dir: str, counter: str):
+    """Mean counter value of the calibration copies: the copy-kernel dispatches that follow
+    the fill of the calibration source (the last elementwise kernel of the run)."""
+    rows = _counter_rows(run_dir, counter)
+    fills = [d for d, name, _ in rows if "elementwise" in name]
+    if not fills:
+        raise ValueError("no calibration fill found (run bench.py with --calib-copy)")
+    vals = [v for d, name, v in rows if d > fills[-1] and COPY_KERNEL in name]
+    if not vals:
+        raise ValueError("no calibration copy dispatch after the fill")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(fetch_dir: str, write_dir: str, kernel: str) -> dict:
+    f_copy, _ = calibration_dispatch(fetch_dir, "FETCH_SIZE")
+    w_copy, _ = calibration_dispatch(write_dir, "WRITE_SIZE")
+    f_k, n_f = per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    w_k, n_w = per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    fetch_scale = f_copy * 1024.0 / CALIB_BYTES
+    write_scale = w_copy * 1024.0 / CALIB_BYTES
+    traffic = f_k * 1024.0 / fetch_scale + w_k * 1024.0 / write_scale
+    return {"kernel": kernel, "dispatches": [n_f, n_w], "fetch_kib": f_k, "write_kib": w_k,
+            "copy_fetch_kib": f_copy, "copy_write_kib": w_copy, "fetch_scale": fetch_scale,
+            "write_scale": write_scale, "traffic_bytes_per_launch": traffic, "source_digest": source_digest()}
+
+
+def to_markdown(s: dict, command: str = "") -> str:
+    lines = [f"# HBM traffic of `{s['kernel']}` (rocprofv3 FETCH_SIZE / WRITE_SIZE)", ""]
+    if command:
+        lines += ["Commands (one counter per run):", "", "```", command, "```", ""]
+    lines += [
+        f"- dispatches averaged: {s['dispatches'][0]} (FETCH_SIZE run), {s['dispatches'][1]} (WRITE_SIZE run)",
+        f"- kernel FETCH_SIZE: {s['fetch_kib']:.1f} KiB/dispatch, WRITE_SIZE: {s['write_kib']:.1f} KiB/dispatch",
+        f"- calibration copy of {CALIB_BYTES >> 20} MiB: FETCH_SIZE {s['copy_fetch_kib']:.1f} KiB, "
+        f"WRITE_SIZE {s['copy_write_kib']:.1f} KiB -> scale fetch {s['fetch_scale']:.3f}, "
+        f"write {s['write_scale']:.3f}",
+        f"- traffic_bytes_per_launch: {s['traffic_bytes_per_launch']:.6e}",
+        f"- source_digest: {s['source_digest']}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def stored_traffic(md_path: str):
+    """(bytes per launch, digest) from a summary written by to_markdown, or None."""
+    if not os.path.exists(md_path):
+        return None
+    t = d = None
+    with open(md_path) as f:
+        for line in f:
+            if line.startswith("- traffic_bytes_per_launch:"):
+                t = float(line.split(":", 1)[1])
+            elif line.startswith("- source_digest:"):
+                d = line.split(":", 1)[1].strip()
+    return None if t is None or d is None else (t, d)
+
+
+def _short(name: str) -> str:
+    n = name.split("(")[0].replace("void ", "").replace("jevk::", "")
+    return n[:48]
+
+
+def kernel_stats_markdown(run_dir: str, title: str, command: str = "") -> str:
+    """Per-kernel totals (rocprofv3 --stats) and per-launch-shape medians (kernel trace)."""
+    stats = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise FileNotFoundError(f"no kernel_stats.csv / kernel_trace.csv under {run_dir}")
+    lines = [f"# {title}", ""]
+    if command:
+        lines += ["Command (from the repository root):", "", "```", command, "```", ""]
+    lines += ["Per kernel (durations in microseconds):", "",
+              "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    with open(stats[0]) as f:
+        for r in csv.DictReader(f):
+            lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    groups = {}
+    with open(trace[0]) as f:
+        for r in csv.DictReader(f):
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                   int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    tot = sum(sum(v) for v in groups.values())
+    lines += ["", "Per launch shape (blocks x, y, z), top 16 by total time:", "",
+              "| kernel | blocks | launches | median us | total ms | % |", "|---|---|---|---|---|---|"]
+    for (n, gx, gy, gz), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:16]:
+        v.sort()
+        lines.append(f"| {n} | {gx}x{gy}x{gz} | {len(v)} | {v[len(v) // 2]:.1f} | {sum(v) / 1e3:.2f} | "
+                     f"{100 * sum(v) / tot:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "--stats":
+        md = kernel_stats_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 kernel statistics"),
+                                   os.environ.get("JEV_STATS_COMMAND", ""))
+        if len(sys.argv) > 3:
+            with open(sys.argv[3], "w") as f:
+                f.write(md)
+        print(md)
+        sys.exit(0)
+    if len(sys.argv) < 4:
+        print(__doc__)
+        sys.exit(2)
+    s = summarize(sys.argv[1], sys.argv[2], sys.argv[3])
+    md = to_markdown(s, os.environ.get("JEV_PMC_COMMAND", ""))
+    if len(sys.argv) > 4:
+        with open(sys.argv[4], "w") as f:
+            f.write(md)
+    print(md)
