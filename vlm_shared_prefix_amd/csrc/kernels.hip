@@ -357,32 +357,50 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // One K stage (two 16-wide k-steps).  Schedule: the 8 operand reads of the first
+  // k-step, then its 16 MFMAs with the second k-step's 8 reads issued one per two
+  // MFMAs, then the second k-step's 16 MFMAs (measured best of the orders tried).
   auto compute = [&](const u16* sA, const u16* sL, const u16* sW) {
+    bf16x8 ah[2][2], al[2][2], bw[2][4];
 #pragma unroll
     for (int kk = 0; kk < G2K / 16; ++kk) {
       const int c = kk * 2 + hl;
-      bf16x8 ah[2], al[2], bw[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + i * 32 + ql;
-        const int o = r * G2K + ((c ^ ((r >> 2) & 3)) * 8);
-        ah[i] = *reinterpret_cast<const bf16x8*>(sA + o);
-        al[i] = *reinterpret_cast<const bf16x8*>(sL + o);
+        ah[kk][i] = *reinterpret_cast<const bf16x8*>(sA + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wn * 128 + j * 32 + ql;
-        bw[j] = *reinterpret_cast<const bf16x8*>(sW + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
+        bw[kk][j] = *reinterpret_cast<const bf16x8*>(sW + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + ql;
+        al[kk][i] = *reinterpret_cast<const bf16x8*>(sL + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
+      }
     }
+#pragma unroll
+    for (int kk = 0; kk < G2K / 16; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads of k-step 0
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMAs of k-step 0
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read of k-step 1
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs of k-step 1
   };
   auto step = [&](int s, const u16* cA, const u16* cL, const u16* cW, u16* nA, u16* nL, u16* nW) {
     if (s + 1 < nst) load_stage(kbeg + (s + 1) * G2K, nA, nL, nW);
@@ -645,6 +663,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int t = rc / G;
   const int hq = hk * G + rc % G;
 
+  // The loads the tile range depends on go first; q's loads are in flight meanwhile.
+  const int t_first = r0 / G, t_last = min(R - 1, r0 + AT_BR - 1) / G;
+  const int s_first = a.seq_start[t_first];
+  const int max_start = a.seq_start[t_last];
+  const int my_start = a.seq_start[t];
+  const bool use_mask = a.mask != nullptr;
+  const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
+
   // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
   // of q, which would shift every score of the row coherently, stays out.
   f16x8 qreg[8], qlo[8];
@@ -659,16 +685,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 
   // this block's share of the tile sequence
   const int ntp = (a.P + AT_BK - 1) / AT_BK;
-  const int t_first = r0 / G, t_last = min(R - 1, r0 + AT_BR - 1) / G;
   const int own_end = t_last + 1;
-  const int own0 = a.seq_start[t_first] & ~7;   // 16 B aligned start of the block's own keys
+  const int own0 = s_first & ~7;   // 16 B aligned start of the block's own keys
   const int nt_all = ntp + (own_end - own0 + AT_BK - 1) / AT_BK;
   const int vb = (int)(((long)z * nt_all) / ns), ve = (int)(((long)(z + 1) * nt_all) / ns);
   const int nt = ve - vb;
-  const int max_start = a.seq_start[t_last];
-  const int my_start = a.seq_start[t];
-  const bool use_mask = a.mask != nullptr;
-  const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
 
   auto tile = [&](int v) {
     AttnTile s;
