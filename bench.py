@@ -95,6 +95,56 @@ def attention_entry(prof, prefix_kv_bytes, what):
     return e
 
 
+def tree_section(seed, dev, profile_steps, name="c5"):
+    """Secondary measurement: the long-prefix tree workload (prefix 8192, 16 questions with
+    4 multi-token candidates each, trie sharing) on the same 7B shape; not the headline value."""
+    import torch
+    import jev_synth as S
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    cfg = S.CONFIGS[name]
+    t = time.time()
+    sess = Session.generated(cfg, seed, dev)
+    pre, tree = S.prefix_inputs(cfg, seed), S.tree_inputs(cfg, seed)
+    log(f"[bench] {name}: weights drawn and uploaded in {time.time() - t:.1f} s")
+    sess.prefill(pre["vis"], pre["text_ids"])
+    sess.score_tree(tree, J.JEV_TREE_TRIE)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    ms_tree = timed(lambda: sess.score_tree(tree, J.JEV_TREE_TRIE), 3)
+    ms_prefill = timed(lambda: sess.prefill(pre["vis"], pre["text_ids"]), 1)
+    J.jev_profile_start(sess.model)
+    for _ in range(max(1, profile_steps)):
+        sess.score_tree(tree, J.JEV_TREE_TRIE)
+    prof = J.jev_profile_stop(sess.model)
+    rows = J.jev_tree_plan_size(tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                                tree["n_cands"], J.JEV_TREE_TRIE)[0]
+    n_c = int(np.sum(tree["n_cands"]))
+    desc = (f"{name}: {cfg.n_layers}-layer decoder, hidden {cfg.hidden}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads x "
+            f"{cfg.head_dim}, MLP {cfg.mlp}, vocab {cfg.vocab}, {cfg.dtype}; prefix {cfg.prefix_len}; "
+            f"{cfg.n_questions} questions, {cfg.stem_len}-token stems, {cfg.tree_cands} candidates of "
+            f"{cfg.cand_len_lo}-{cfg.cand_len_hi} tokens; trie sharing, full-vocabulary log-probs")
+    out = {"workload": desc, "tree_rows": int(rows),
+           "tree_call_ms": round(ms_tree, 3), "candidates_per_s": round(n_c / (ms_tree * 1e-3), 1),
+           "prefill_ms": round(ms_prefill, 3),
+           "attention": attention_entry(prof, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
+                                        f"shared prefix ({cfg.prefix_len} keys) + tree rows ({rows})")}
+    log(f"[bench] {name}: tree call {ms_tree:.2f} ms, prefill {ms_prefill:.1f} ms")
+    sess.close()
+    return out
+
+
 def cpu_baseline(cfg, seed, budget_layers=2):
     """The oracle as it stands on a bounded sample, scaled to the whole step.
 
@@ -143,6 +193,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tree", action="store_true",
+                    help="skip the secondary long-prefix tree measurement (config c5)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -239,6 +291,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    tree = None
+    if not args.no_tree:
+        sess.close()
+        del sess
+        torch.cuda.empty_cache()
+        tree = tree_section(args.seed, dev, args.profile_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline on a bounded sample ...")
@@ -266,10 +325,10 @@ def main():
         "roofline": roof,
         "attention": attn,
         "kernels": kernels,
+        "long_prefix_tree": tree,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
-    sess.close()
 
 
 if __name__ == "__main__":

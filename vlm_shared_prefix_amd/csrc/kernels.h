@@ -94,7 +94,8 @@ hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int
                               hipStream_t s);
 constexpr int kAttnMaxSplits = 8;
 // Splits for the bf16 attention of T rows (G q heads per KV head) over P prefix keys plus
-// own_tiles tiles of own keys: about one block per compute unit, at least two tiles each.
+// own_tiles tiles of own keys: about one block per compute unit (two from 64 key tiles on),
+// at least two tiles each.
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,

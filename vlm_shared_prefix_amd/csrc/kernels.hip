@@ -1357,7 +1357,11 @@ hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
   const long base = (long)cdiv((long)G * T, AT_BR) * Hkv;
   const int tiles = cdiv(P, AT_BK) + own_tiles;
-  long ns = (256 + base / 2) / base;                   // about one block per compute unit
+  // About one block per compute unit; two (a full 8 waves per CU) once every split
+  // keeps enough tiles to amortise the larger merge (measured: P = 1024 favours one,
+  // P = 8192 two).
+  const long target = tiles >= 64 ? 512 : 256;
+  long ns = (target + base / 2) / base;
   ns = std::min<long>(ns, std::max(1, tiles / 2));     // at least two tiles per split
   return (int)std::max<long>(1, std::min<long>(ns, kAttnMaxSplits));
 }
