@@ -145,6 +145,76 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     return out
 
 
+def _timer(dev):
+    import torch
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+    return timed
+
+
+def configs_report(seed, dev, reps=5):
+    """Per-config call times: c1, c2 (scoring), c4 (each B, one batched call vs B single-suffix
+    calls on the same prefix), c5 (trie, stem-only, flat).  ms per call, candidates per second."""
+    import torch
+    import jev_synth as S
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    timed = _timer(dev)
+    rep = {}
+    for name in ("c1", "c2", "c4", "c5"):
+        cfg = S.CONFIGS[name]
+        sess = Session.generated(cfg, seed, dev)
+        pre = S.prefix_inputs(cfg, seed)
+        sess.prefill(pre["vis"], pre["text_ids"])
+        ms_pre = timed(lambda: sess.prefill(pre["vis"], pre["text_ids"]), 1)
+        r = {"prefix_len": cfg.prefix_len, "prefill_ms": round(ms_pre, 3)}
+        if name == "c5":
+            tree = S.tree_inputs(cfg, seed)
+            n_c = int(np.sum(tree["n_cands"]))
+            for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"),
+                                (J.JEV_TREE_FLAT, "flat")):
+                sess.score_tree(tree, mode)
+                ms = timed(lambda: sess.score_tree(tree, mode), reps)
+                r[mname] = {"ms": round(ms, 3), "candidates_per_s": round(n_c / (ms * 1e-3), 1)}
+        else:
+            batches = S.C4_BATCHES if name == "c4" else (None,)
+            for B in batches:
+                suf = S.suffix_inputs(cfg, seed, n=B) if B else S.suffix_inputs(cfg, seed)
+                nb = len(suf["lens"])
+                n_c = int(np.sum(suf["n_cands"]))
+                out = sess.score_suffixes(suf)
+                sess.workspace(sess.suffix_ws_bytes(suf))
+                ms = timed(lambda: sess.score_suffixes(suf, out), reps)
+                e = {"B": nb, "rows": int(np.sum(suf["lens"])), "ms": round(ms, 3),
+                     "candidates_per_s": round(n_c / (ms * 1e-3), 1)}
+                if name == "c4":
+                    singles = [{k: v[b:b + 1] for k, v in suf.items()} for b in range(nb)]
+                    o1 = torch.empty((1, out.shape[1]), dtype=torch.float32, device=dev)
+
+                    def serial():
+                        for sb in singles:
+                            sess.score_suffixes(sb, o1)
+                    serial()
+                    ms_s = timed(serial, 1)
+                    e.update({"serial_ms": round(ms_s, 3), "speedup": round(ms_s / ms, 2)})
+                r[f"B{nb}" if name == "c4" else "score"] = e
+        rep[name] = r
+        log(f"[bench] {name}: {r}")
+        sess.close()
+        del sess
+        torch.cuda.empty_cache()
+    return rep
+
+
 def cpu_baseline(cfg, seed, budget_layers=2):
     """The oracle as it stands on a bounded sample, scaled to the whole step.
 
@@ -195,6 +265,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true",
                     help="skip the secondary long-prefix tree measurement (config c5)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time configs c1, c2, c4 (every B, batched and serial) and c5 (every mode)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -257,6 +329,24 @@ def main():
     ms_prefill = timed(prefill_only, max(1, args.steps // 2))
     log(f"[bench] score-only {ms_score:.3f} ms, prefill-only {ms_prefill:.3f} ms")
 
+    # the same suffixes scored one call per suffix over the same prefix (the serial baseline
+    # the method replaces), and with a fresh prefill per question (image-per-question)
+    singles = [{k: v[b:b + 1] for k, v in suf.items()} for b in range(len(suf["lens"]))]
+    outs = [torch.empty((1, out.shape[1]), dtype=torch.float32, device=dev) for _ in singles]
+
+    def serial_calls():
+        for sb, ob in zip(singles, outs):
+            J.jev_score_suffixes(sess.prefix, sb["ids"], sb["lens"], sb["cands"], sb["n_cands"], ob, sess.ws)
+
+    serial_calls()
+    ms_serial = timed(serial_calls, 2)
+    serial = {"suffixes": len(singles), "batched_score_ms": round(ms_score, 4),
+              "serial_score_ms": round(ms_serial, 4), "speedup_vs_serial_calls": round(ms_serial / ms_score, 2),
+              "per_question_prefill_ms": round(len(singles) * (ms_prefill + ms_serial / len(singles)), 3),
+              "speedup_vs_per_question_prefill": round(len(singles) * (ms_prefill + ms_serial / len(singles)) /
+                                                       ms_step, 2)}
+    log(f"[bench] serial: {len(singles)} single-suffix calls {ms_serial:.2f} ms vs batched {ms_score:.2f} ms")
+
     # per-kernel event timing (separate passes over the same calls)
     J.jev_profile_start(sess.model)
     for _ in range(args.profile_steps):
@@ -291,6 +381,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    configs = None
+    if args.all_configs:
+        sess.close()
+        torch.cuda.empty_cache()
+        configs = configs_report(args.seed, dev)
+
     tree = None
     if not args.no_tree:
         sess.close()
@@ -324,8 +420,10 @@ def main():
         "prefill_ms": round(ms_prefill, 4),
         "roofline": roof,
         "attention": attn,
+        "serial_vs_batched": serial,
         "kernels": kernels,
         "long_prefix_tree": tree,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
