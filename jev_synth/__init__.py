@@ -118,6 +118,11 @@ CONFIGS: Dict[str, Config] = {
     "m7": Config("m7", n_layers=2, hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
                  n_vis=290, n_text=10, n_suffix=9, len_lo=1, len_hi=16, s_max=16, n_cands=2),
+    # 7B head structure with long suffixes: a row tile's own keys span several 64-key tiles,
+    # a ragged prefix (300), and key-tile splits that cut through the own-key tiles
+    "m7l": Config("m7l", n_layers=2, hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
+                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
+                  n_vis=290, n_text=10, n_suffix=5, len_lo=60, len_hi=200, s_max=200, n_cands=2),
     # tree workload on the 7B head structure, forced candidate overlap
     "m5": Config("m5", n_layers=2, hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",

@@ -14,7 +14,8 @@ from tests.gpu_common import TOL, check_suffix_out, gpu_session, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,seed", [("c1", 0), ("c1", 1), ("c1", 2), ("m2", 0), ("m7", 0), ("m2", 3)])
+@pytest.mark.parametrize("name,seed", [("c1", 0), ("c1", 1), ("c1", 2), ("m2", 0), ("m7", 0), ("m2", 3),
+                                       ("m7l", 0)])
 def test_score_suffixes_vs_oracle(name, seed):
     cfg = S.CONFIGS[name]
     say(f"[parity] score_suffixes {name} seed {seed}")
