@@ -203,7 +203,8 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.x = take(4ull * T * c.hidden);
   L.act = take(4ull * T * wide);
   L.big = take(4ull * T * bigw);
-  L.q = take(e * T * HqD * (bf ? 2 : 1));   // bf16 models: q hi and lo planes
+  L.q = take(bf ? 2 * 2 * attn_q_plane_elems(T, c.n_q_heads, c.n_kv_heads)   // bf16 models: q hi and lo planes
+                : e * T * HqD);
   L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
   L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
   const size_t prow = bf ? attn_part_rows(c, T, P) : 0;
@@ -408,7 +409,7 @@ struct Forward {
         kld = L.Tc;
       }
       _Float16* q_hi = at<_Float16>(ws, L.q);
-      _Float16* q_lo = q_hi + (size_t)T * HqD;
+      _Float16* q_lo = q_hi + attn_q_plane_elems(T, Hq, Hkv);
       if (jev_status st = run_k(K_QKVPOST, 0.0, (double)T * NQKV * 4 * sp + (double)T * (2 * HqD + 2 * Hkv * D) * 2, [&] {
             return launch_qkv_post(sp > 1 ? part : big, NQKV, (size_t)T * NQKV, sp, T, Hq, Hkv, rope, q_hi, q_lo,
                                    kdst, kld, vdst, kld, s);

@@ -14,11 +14,25 @@ struct GemmSegsF {
   int n_end[3];
 };
 
-// float16 MFMA attention (head_dim 128).
 // float16 attention (head_dim 128) of T query rows: prefix keys then the rows' own keys.
+//
+// q is stored in the order the attention kernel feeds it to the matrix cores: per KV
+// head hk, query row r = t*G + g (head hq = hk*G + g) of R = G*T rows, padded to a
+// multiple of 32 rows (attn_q_rows); in each group of 32 rows, element d of row
+// 32w + l sits at ((d/16)*2 + (d/8)%2)*32*8 + l*8 + d%8 after the group's base, so
+// each 16-dim slice of a group is one contiguous 1 KB run.
+#if defined(__HIPCC__)
+#define JEV_HD __host__ __device__
+#else
+#define JEV_HD
+#endif
+inline JEV_HD int attn_q_rows(int T, int G) { return (G * T + 31) / 32 * 32; }
+inline size_t attn_q_plane_elems(int T, int Hq, int Hkv) {
+  return (size_t)Hkv * attn_q_rows(T, Hq / Hkv) * 128;
+}
 struct AttnArgs {
-  const _Float16* q;       // [T][Hq][128]  q rounded to f16 (hi)
-  const _Float16* q_lo;    // [T][Hq][128]  q - hi, rounded to f16
+  const _Float16* q;       // q rounded to f16 (hi), layout above
+  const _Float16* q_lo;    // q - hi, rounded to f16, same layout
   int T, Hq, Hkv, G;
   const _Float16* kp;      // prefix K  [Hkv][ldp][128]
   const _Float16* vtp;     // prefix Vt [Hkv][128][ldp], columns [P, round8(P)) zero

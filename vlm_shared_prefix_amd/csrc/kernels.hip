@@ -638,6 +638,16 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16 B per lane from base + byte_off into LDS at dst + lane * 16.  The buffer form of the
+// direct load is counted by vmcnt alone, so the waits the compiler places for LDS reads
+// stay exact (the global form is also tracked as an LDS access, forcing full drains).
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(const void* base, int byte_off, void* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, byte_off, 0, 0, 0);
+}
+
 struct AttnTile {
   const f16* K;   // [ld][128]
   const f16* V;   // V^T [128][ld]
@@ -651,7 +661,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) f16 sV0[128 * AT_BK];
   __shared__ __attribute__((aligned(16))) f16 sV1[128 * AT_BK];
 
-  const int x = blockIdx.x, hk = blockIdx.y, z = blockIdx.z, ns = a.n_split;
+  // row tiles in reverse order: with long causal sequences the later tiles see the most keys
+  // and are dispatched first
+  const int x = gridDim.x - 1 - blockIdx.x, hk = blockIdx.y, z = blockIdx.z, ns = a.n_split;
   const int G = a.G, T = a.T, Hq = a.Hq;
   const int R = G * T;
   const int r0 = x * AT_BR;
@@ -675,11 +687,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   // of q, which would shift every score of the row coherently, stays out.
   f16x8 qreg[8], qlo[8];
   {
-    const size_t qo = ((size_t)t * Hq + hq) * 128 + hl * 8;
+    // operand-ordered q: slice c of the wave's 32 rows is one contiguous 1 KB run
+    const size_t qo = ((size_t)hk * attn_q_rows(T, G) + (rc & ~31)) * 128 + (size_t)(hl * 32 + (rc & 31)) * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 16);
-      qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 16);
+      qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 512);
+      qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 512);
     }
   }
 
@@ -712,16 +725,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       const int slot = i * 256 + tid;
       const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
       const int key = s.k0 + row;
-      __builtin_amdgcn_global_load_lds(s.K + (size_t)(key < s.ke ? key : 0) * 128 + c * 8,
-                                       dk + (i * 256 + wave * 64) * 8, 16, 0, 0);
+      dma16(s.K, ((key < s.ke ? key : 0) * 128 + c * 8) * 2, dk + (i * 256 + wave * 64) * 8);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = i * 256 + tid;
       const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
       const int key = s.k0 + c * 8;
-      __builtin_amdgcn_global_load_lds(s.V + (size_t)d * s.ld + (key < s.ke ? key : 0),
-                                       dv + (i * 256 + wave * 64) * 8, 16, 0, 0);
+      dma16(s.V, (d * s.ld + (key < s.ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
     }
   };
 
@@ -971,12 +982,15 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       const float2 e = cs[t * 64 + i];
       const float ra = a * e.x - b * e.y, rb = b * e.x + a * e.y;
       if (h < Hq) {
-        const size_t o = ((size_t)t * Hq + h) * 128;
+        // operand-ordered layout (see AttnArgs): row r = t*G + g of KV head h / G
+        const int G = Hq / Hkv, r = t * G + h % G;
+        const size_t base = ((size_t)(h / G) * attn_q_rows(T, G) + (r & ~31)) * 128 + (size_t)(r & 31) * 8;
+        auto at = [&](int d) { return base + (size_t)(((d >> 4) * 2 + ((d >> 3) & 1)) * 256) + (d & 7); };
         const f16 qa = (f16)ra, qb = (f16)rb;
-        q_hi[o + i] = qa;
-        q_hi[o + i + 64] = qb;
-        q_lo[o + i] = (f16)(ra - (float)qa);
-        q_lo[o + i + 64] = (f16)(rb - (float)qb);
+        q_hi[at(i)] = qa;
+        q_hi[at(i + 64)] = qb;
+        q_lo[at(i)] = (f16)(ra - (float)qa);
+        q_lo[at(i + 64)] = (f16)(rb - (float)qb);
       } else {
         f16* kd = kdst + ((size_t)(h - Hq) * ldk + t) * 128;
         kd[i] = (f16)ra;
@@ -1014,18 +1028,31 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
   if (i >= (size_t)T * Hq * d4) return;
   const size_t th = i / d4;
   const int c = (int)(i % d4);
+  // every split's lse and partial are loaded up front (S <= kAttnMaxSplits), so the
+  // loads are in flight together instead of one round trip per split
+  float lse[kAttnMaxSplits];
+  float4 part[kAttnMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplits; ++s) {
+    if (s < S) {
+      lse[s] = lse_part[(size_t)s * T * Hq + th];
+      part[s] = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * D)[c];
+    }
+  }
   float M = NEG_INF;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse_part[(size_t)s * T * Hq + th]);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplits; ++s)
+    if (s < S) M = fmaxf(M, lse[s]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (M != NEG_INF) {
-    for (int s = 0; s < S; ++s) {
-      const float l = lse_part[(size_t)s * T * Hq + th];
-      if (l == NEG_INF) continue;
-      const float w = __builtin_amdgcn_exp2f(l - M);
-      const float4 v = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * D)[c];
-      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-      wsum += w;
+#pragma unroll
+    for (int s = 0; s < kAttnMaxSplits; ++s) {
+      if (s < S && lse[s] != NEG_INF) {
+        const float w = __builtin_amdgcn_exp2f(lse[s] - M);
+        acc.x += w * part[s].x; acc.y += w * part[s].y; acc.z += w * part[s].z; acc.w += w * part[s].w;
+        wsum += w;
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
