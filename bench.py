@@ -31,6 +31,12 @@ sys.path.insert(0, ROOT)
 METRIC = "candidates scored/sec + attention MFMA util, 7B-shaped prefix 1024, 32 suffixes"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+PRECISION = None               # GEMM precision mode (set in main)
+PRECISION_NOTE = {
+    "f16_down": "f16_down: down projection as one float16 pass on a float16 weight mirror; q|k|v, o and "
+                "gate|up as two bfloat16 passes (hi + lo of the float32 activation); float32 accumulation",
+    "split": "split: every decoder GEMM as two bfloat16 passes (hi + lo of the float32 activation)",
+}
 
 
 def log(msg):
@@ -48,9 +54,10 @@ def roofline(kind, d):
     """Roofline entry of one kernel kind from the library's event timing.
 
     achieved = algorithmic flops per launch (each product counted once) / average
-    launch time.  The bf16 GEMMs run every product twice (hi and lo planes of the
-    float32 activations), so the MFMA pipes execute 2x the algorithmic flops:
-    reported as executed_tflops / executed_frac.
+    launch time.  The two-term bf16 GEMMs (gemm, gemm_swiglu, lm_head_gemm) run every
+    product twice (hi and lo planes of the float32 activations), so the MFMA pipes
+    execute 2x the algorithmic flops: reported as executed_tflops / executed_frac.
+    The float16 GEMMs (gemm_f16, gemm_swiglu_f16) execute each product once.
     """
     from vlm_shared_prefix_amd import profiling
     n = d["launches"]
@@ -65,9 +72,10 @@ def roofline(kind, d):
              "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
              "avg_launch_us": round(avg_s * 1e6, 2), "launches": n,
              "algorithmic_flops_per_launch": d["flops"] / n}
-        if kind in ("gemm", "gemm_swiglu", "lm_head_gemm"):
-            r["executed_tflops"] = round(2 * ach, 2)
-            r["executed_frac"] = round(2 * ach / PEAK_BF16_TFLOPS, 4)
+        passes = 2 if kind in ("gemm", "gemm_swiglu", "lm_head_gemm") else 1
+        if kind.startswith("gemm") or kind == "lm_head_gemm":
+            r["executed_tflops"] = round(passes * ach, 2)
+            r["executed_frac"] = round(passes * ach / PEAK_BF16_TFLOPS, 4)
         return r
     ach = d["bytes"] / n / avg_s / 1e9
     return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -104,7 +112,7 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     from vlm_shared_prefix_amd.session import Session
     cfg = S.CONFIGS[name]
     t = time.time()
-    sess = Session.generated(cfg, seed, dev)
+    sess = Session.generated(cfg, seed, dev, precision=PRECISION)
     pre, tree = S.prefix_inputs(cfg, seed), S.tree_inputs(cfg, seed)
     log(f"[bench] {name}: weights drawn and uploaded in {time.time() - t:.1f} s")
     sess.prefill(pre["vis"], pre["text_ids"])
@@ -172,7 +180,7 @@ def configs_report(seed, dev, reps=5):
     rep = {}
     for name in ("c1", "c2", "c4", "c5"):
         cfg = S.CONFIGS[name]
-        sess = Session.generated(cfg, seed, dev)
+        sess = Session.generated(cfg, seed, dev, precision=PRECISION)
         pre = S.prefix_inputs(cfg, seed)
         sess.prefill(pre["vis"], pre["text_ids"])
         ms_pre = timed(lambda: sess.prefill(pre["vis"], pre["text_ids"]), 1)
@@ -267,6 +275,8 @@ def main():
                     help="skip the secondary long-prefix tree measurement (config c5)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time configs c1, c2, c4 (every B, batched and serial) and c5 (every mode)")
+    ap.add_argument("--precision", default=None,
+                    help="GEMM precision mode of the bf16 models (see Session; default: the library default)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -278,12 +288,15 @@ def main():
     import torch
     import jev_synth as S
     from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd import session as SE
     from vlm_shared_prefix_amd.session import Session
 
+    global PRECISION
+    PRECISION = args.precision or SE.DEFAULT_PRECISION
     cfg = S.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     t = time.time()
-    sess = Session.generated(cfg, args.seed, dev)
+    sess = Session.generated(cfg, args.seed, dev, precision=PRECISION)
     pre, suf = S.prefix_inputs(cfg, args.seed), S.suffix_inputs(cfg, args.seed)
     log(f"[bench] weights drawn and uploaded in {time.time() - t:.1f} s")
     n_cand = int(np.sum(suf["n_cands"]))
@@ -411,10 +424,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+f16",
         "data": "synthetic (seeded random-init weights and inputs of the workload's shapes)",
         "config": {"workload": workload_name(cfg), "prefix_len": cfg.prefix_len, "suffixes": cfg.n_suffix,
                    "suffix_rows": T, "candidates": n_cand, "seed": args.seed,
+                   "gemm_precision": PRECISION_NOTE.get(PRECISION, PRECISION),
                    "step": "jev_prefill_prefix + jev_score_suffixes"},
         "score_only": {"ms": round(ms_score, 4), "candidates_per_s": round(n_cand / (ms_score * 1e-3), 2)},
         "prefill_ms": round(ms_prefill, 4),

@@ -101,6 +101,36 @@ jev_status jev_model_create(const jev_config *cfg, const jev_weights *w, jev_mod
 void       jev_model_destroy(jev_model *m);
 jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 
+/* ---- float16 weight mirror (JEV_BF16 models) ----------------------------------
+ * The pages fix no arithmetic precision below the model's own; the decoder's
+ * matrix products may run in any precision that keeps the scores within the
+ * tolerance of the plain float32 forward.  By default a bf16 model's GEMMs take
+ * each float32 activation as two bfloat16 terms (hi + lo, two matrix-core
+ * passes).  For a mirrored group of matrices they take it as ONE float16 term
+ * against a float16 copy of the weights (one pass, half the matrix-core work):
+ * bfloat16 weights are exact in float16 except below 2^-17 in magnitude
+ * (rounded to float16's subnormal grid) and above 65504 (rejected).
+ * Activations entering a mirrored GEMM must then stay below 65504 in magnitude.
+ *
+ * groups: any OR of JEV_F16_GATE_UP (w_gate, w_up), JEV_F16_QKV (wq, wk, wv),
+ *   JEV_F16_DOWN (w_down) and JEV_F16_O (wo).
+ * jev_model_f16_bytes: size of the mirror buffer for those groups (0 for JEV_F32
+ *   models or unknown bits).
+ * jev_model_attach_f16: buf dev [bytes >= jev_model_f16_bytes(m, groups)],
+ *   caller-owned and kept alive while the model is used.  Converts the groups'
+ *   matrices of every layer into it on `stream`, then synchronises the stream to
+ *   read the range check: JEV_E_UNSUPPORTED if a weight exceeds the float16
+ *   range (the model stays on the two-term path), JEV_E_WORKSPACE if bytes is
+ *   too small.  buf == NULL or groups == 0 detaches the mirror.  Not a hot-path
+ *   call (it blocks); do not call it while another call on this model is in
+ *   flight.  The LM head and embeddings are never mirrored. */
+#define JEV_F16_GATE_UP 1
+#define JEV_F16_QKV     2
+#define JEV_F16_DOWN    4
+#define JEV_F16_O       8
+size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
+jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
+
 /* ---- prefix KV store ---------------------------------------------------------
  * Layout per layer l (element type float16 for JEV_BF16, float32 for JEV_F32),
  * with Pc = prefix_len rounded up to a multiple of 64:

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libjev.so not b
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(jev_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(jev_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_function():

@@ -34,16 +34,16 @@ def load_golden(name, seed):
 _SESS = {}
 
 
-def session(name, seed):
-    """One uploaded model per (config, seed), kept for the module's tests."""
+def session(name, seed, precision="f16_down"):
+    """One uploaded model per (config, seed, precision), kept while consecutive tests use it."""
     from vlm_shared_prefix_amd.session import Session
-    key = (name, seed)
+    key = (name, seed, precision)
     if key not in _SESS:
         for k in list(_SESS):
             _SESS.pop(k).close()
-        say(f"[fullsize] drawing and uploading {name} seed {seed}")
+        say(f"[fullsize] drawing and uploading {name} seed {seed} ({precision})")
         cfg = S.CONFIGS[name]
-        sess = Session.generated(cfg, seed)
+        sess = Session.generated(cfg, seed, precision=precision)
         pre = S.prefix_inputs(cfg, seed)
         sess.prefill(pre["vis"], pre["text_ids"])
         _SESS[key] = sess
@@ -57,14 +57,16 @@ def _cleanup():
         _SESS.pop(k).close()
 
 
-@pytest.mark.parametrize("name,seed", [("c2", 0), ("c2", 1), ("c2", 2), ("c3", 0)])
-def test_fullsize_suffixes(name, seed):
+@pytest.mark.parametrize("name,seed,precision", [("c2", 0, "f16_down"), ("c2", 1, "f16_down"), ("c2", 2, "f16_down"),
+                                                 ("c2", 0, "split"), ("c2", 0, "f16"), ("c3", 0, "f16_down"),
+                                                 ("c3", 0, "split")])
+def test_fullsize_suffixes(name, seed, precision):
     g = load_golden(name, seed)
     cfg = S.CONFIGS[name]
     suf = S.suffix_inputs(cfg, seed)
-    say(f"[fullsize] {name} seed {seed}: B={len(suf['lens'])}, rows={int(suf['lens'].sum())}")
-    got = session(name, seed).score_suffixes(suf).cpu().numpy()
-    check_suffix_out(got, np.array(g["out"], np.float32), suf["n_cands"], cfg.dtype, f"{name}/s{seed}")
+    say(f"[fullsize] {name} seed {seed} ({precision}): B={len(suf['lens'])}, rows={int(suf['lens'].sum())}")
+    got = session(name, seed, precision).score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, np.array(g["out"], np.float32), suf["n_cands"], cfg.dtype, f"{name}/s{seed}/{precision}")
 
 
 @pytest.mark.parametrize("B", S.C4_BATCHES)
@@ -93,13 +95,14 @@ def test_fullsize_serial_equals_batched():
     assert np.max(np.abs(serial - batched)) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
-def test_fullsize_tree(mode):
+@pytest.mark.parametrize("mode,precision", [(0, "f16_down"), (1, "f16_down"), (2, "f16_down"), (0, "split"),
+                                            (2, "split")])
+def test_fullsize_tree(mode, precision):
     g = load_golden("c5", 0)
     cfg = S.CONFIGS["c5"]
     tree = S.tree_inputs(cfg, 0)
-    say(f"[fullsize] c5 tree mode {mode}")
-    score, norm = session("c5", 0).score_tree(tree, mode)
+    say(f"[fullsize] c5 tree mode {mode} ({precision})")
+    score, norm = session("c5", 0, precision).score_tree(tree, mode)
     for key, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
         ref = np.array(g[key], np.float32)
         valid = np.isfinite(ref)

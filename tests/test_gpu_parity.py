@@ -14,12 +14,14 @@ from tests.gpu_common import TOL, check_suffix_out, gpu_session, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,seed", [("c1", 0), ("c1", 1), ("c1", 2), ("m2", 0), ("m7", 0), ("m2", 3),
-                                       ("m7l", 0)])
-def test_score_suffixes_vs_oracle(name, seed):
+@pytest.mark.parametrize("name,seed,precision", [("c1", 0, "f32"), ("c1", 1, "f32"), ("c1", 2, "f32"),
+                                                 ("m2", 0, "f16_down"), ("m7", 0, "f16_down"), ("m2", 3, "f16_down"),
+                                                 ("m7l", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
+                                                 ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16")])
+def test_score_suffixes_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
-    say(f"[parity] score_suffixes {name} seed {seed}")
-    sess, src = gpu_session(cfg, seed)
+    say(f"[parity] score_suffixes {name} seed {seed} ({precision})")
+    sess, src = gpu_session(cfg, seed, precision="split" if precision == "f32" else precision)
     pre, suf = S.prefix_inputs(cfg, seed), S.suffix_inputs(cfg, seed)
     ref = O.score_suffixes(src, cfg, pre, suf)
     sess.prefill(pre["vis"], pre["text_ids"])
@@ -28,11 +30,12 @@ def test_score_suffixes_vs_oracle(name, seed):
     sess.close()
 
 
-@pytest.mark.parametrize("name,seed", [("t1", 1), ("m5", 0)])
-def test_score_tree_vs_oracle(name, seed):
+@pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "f16_down"), ("m5", 0, "split"),
+                                                 ("m5", 0, "f16")])
+def test_score_tree_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
-    say(f"[parity] score_tree {name} seed {seed}")
-    sess, src = gpu_session(cfg, seed)
+    say(f"[parity] score_tree {name} seed {seed} ({precision})")
+    sess, src = gpu_session(cfg, seed, precision="split" if precision == "f32" else precision)
     pre, tree = S.prefix_inputs(cfg, seed), S.tree_inputs(cfg, seed)
     ref = O.score_tree(src, cfg, pre, tree)
     sess.prefill(pre["vis"], pre["text_ids"])

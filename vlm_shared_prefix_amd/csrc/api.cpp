@@ -49,6 +49,13 @@ struct jev_model {
   jev_config cfg;
   jev_weights w;
   std::vector<jev_layer> layers;
+  // float16 mirror of some decoder matrices (caller-owned buffer): the GEMMs of the mirrored
+  // groups run as single float16 passes on float16 activations
+  std::vector<jev_layer> layers16;
+  bool f16_gu = false;     // w_gate, w_up mirrored
+  bool f16_down = false;   // w_down mirrored
+  bool f16_qkv = false;    // wq, wk, wv mirrored
+  bool f16_o = false;      // wo mirrored
   std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
   Profiler prof;
 };
@@ -112,6 +119,79 @@ extern "C" jev_status jev_model_create(const jev_config* cfg, const jev_weights*
 }
 
 extern "C" void jev_model_destroy(jev_model* m) { delete m; }
+
+namespace {
+// element counts of the seven decoder matrices of one layer, in mirror order
+void layer_matrix_elems(const jev_config& c, size_t n[7]) {
+  const size_t H = c.hidden, HqD = (size_t)c.n_q_heads * c.head_dim, HkD = (size_t)c.n_kv_heads * c.head_dim,
+               I = c.mlp;
+  n[0] = HqD * H; n[1] = HkD * H; n[2] = HkD * H; n[3] = H * HqD; n[4] = I * H; n[5] = I * H; n[6] = H * I;
+}
+size_t mirror_align(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+constexpr int32_t kAllGroups = JEV_F16_GATE_UP | JEV_F16_QKV | JEV_F16_DOWN | JEV_F16_O;
+// group of matrix i of a layer (wq, wk, wv, wo, w_gate, w_up, w_down)
+static bool mirrored(int i, int32_t groups) {
+  static const int32_t group_of[7] = {JEV_F16_QKV, JEV_F16_QKV, JEV_F16_QKV, JEV_F16_O,
+                                      JEV_F16_GATE_UP, JEV_F16_GATE_UP, JEV_F16_DOWN};
+  return (groups & group_of[i]) != 0;
+}
+
+extern "C" size_t jev_model_f16_bytes(const jev_model* m, int32_t groups) {
+  if (!m || m->cfg.dtype != JEV_BF16 || (groups & ~kAllGroups)) return 0;
+  size_t n[7], total = 0;
+  layer_matrix_elems(m->cfg, n);
+  for (int l = 0; l < m->cfg.n_layers; ++l)
+    for (int i = 0; i < 7; ++i)
+      if (mirrored(i, groups)) total += mirror_align(2 * n[i]);
+  return total + 256;   // + the range flag
+}
+
+extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* buf, size_t bytes, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!m) return fail(JEV_E_INVALID, "null model");
+  if (groups & ~kAllGroups) return fail(JEV_E_INVALID, "unknown matrix group bits");
+  if (!buf || groups == 0) {   // detach: back to the two-term bf16 path
+    m->f16_gu = m->f16_down = m->f16_qkv = m->f16_o = false;
+    m->layers16.clear();
+    return JEV_OK;
+  }
+  if (m->cfg.dtype != JEV_BF16) return fail(JEV_E_UNSUPPORTED, "a float16 mirror applies to bf16 models only");
+  const size_t need = jev_model_f16_bytes(m, groups);
+  if (bytes < need) return fail(JEV_E_WORKSPACE, "mirror buffer smaller than jev_model_f16_bytes");
+  size_t n[7];
+  layer_matrix_elems(m->cfg, n);
+  char* at = static_cast<char*>(buf);
+  int* bad = reinterpret_cast<int*>(at + need - 256);
+  std::vector<jev_layer> l16(m->layers);
+  if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return fail(JEV_E_HIP, "hipMemsetAsync failed");
+  for (int l = 0; l < m->cfg.n_layers; ++l) {
+    const jev_layer& W = m->layers[l];
+    const void* src[7] = {W.wq, W.wk, W.wv, W.wo, W.w_gate, W.w_up, W.w_down};
+    const void** dst[7] = {&l16[l].wq, &l16[l].wk, &l16[l].wv, &l16[l].wo, &l16[l].w_gate, &l16[l].w_up,
+                           &l16[l].w_down};
+    for (int i = 0; i < 7; ++i) {
+      if (!mirrored(i, groups)) continue;
+      if (launch_bf16_to_f16(static_cast<const uint16_t*>(src[i]), n[i], reinterpret_cast<uint16_t*>(at), bad, s) !=
+          hipSuccess)
+        return fail(JEV_E_HIP, "conversion launch failed");
+      *dst[i] = at;
+      at += mirror_align(2 * n[i]);
+    }
+  }
+  int h_bad = 0;
+  if (hipMemcpyAsync(&h_bad, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(JEV_E_HIP, "mirror conversion failed");
+  if (h_bad) return fail(JEV_E_UNSUPPORTED, "a weight exceeds the float16 range");
+  m->layers16 = std::move(l16);
+  m->f16_gu = (groups & JEV_F16_GATE_UP) != 0;
+  m->f16_down = (groups & JEV_F16_DOWN) != 0;
+  m->f16_qkv = (groups & JEV_F16_QKV) != 0;
+  m->f16_o = (groups & JEV_F16_O) != 0;
+  return JEV_OK;
+}
 
 extern "C" jev_status jev_get_stats(const jev_model* m, jev_stats* out) {
   if (!m || !out) return fail(JEV_E_INVALID, "null argument");
@@ -249,12 +329,12 @@ T* at(void* ws, size_t off) {
 // Profiled launch kinds, named after the kernels they launch.
 enum Kind {
   K_EMBED, K_RMSNORM, K_RESNORM, K_ROPETAB, K_QKVPOST, K_GEMM, K_SWIGLU, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE,
-  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_NKINDS
+  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_GEMM16, K_SWIGLU16, K_NKINDS
 };
 const char* const kKindName[K_NKINDS] = {
     "embed_rows", "rmsnorm_rows", "residual_norm", "rope_table", "qkv_post", "gemm", "gemm_swiglu",
     "splitk_reduce", "rope_qk", "v_transpose", "attn_fwd", "attn_merge", "silu_mul", "target_logits",
-    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize"};
+    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize", "gemm_f16", "gemm_swiglu_f16"};
 
 struct Forward {
   const jev_prefix* pf;
@@ -306,11 +386,13 @@ struct Forward {
   char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m); }
 
 
-  // A operand: float32 rows (float32 models) or bfloat16 hi/lo planes (bf16 models)
+  // A operand: float32 rows (float32 models), bfloat16 hi/lo planes, or one float16 plane
+  // in hi (bf16 models with a float16 mirror: f16 set)
   struct AOp {
     const float* f;
     const uint16_t* hi;
     const uint16_t* lo;
+    bool f16 = false;
   };
   jev_status gemm(AOp A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
                   const void* w2, int n2, float* C, int ldc, int accum, int kind = K_GEMM) {
@@ -341,11 +423,13 @@ struct Forward {
                            const void* w2, int n2, float* C, int ldc, int accum, int* splits_out) {
     const int N = n0 + n1 + n2;
     const double flops = 2.0 * M * N * K;
-    const double bytes = 2.0 * N * K + 4.0 * M * K + 4.0 * M * N * (accum ? 2 : 1);
+    const double bytes = 2.0 * N * K + (A.f16 ? 2.0 : 4.0) * M * K + 4.0 * M * N * (accum ? 2 : 1);
     GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
     float* part = at<float>(ws, L.gpart);
-    return run_k(K_GEMM, flops, bytes, [&] {
-      return launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s, splits_out);
+    return run_k(A.f16 ? K_GEMM16 : K_GEMM, flops, bytes, [&] {
+      return A.f16 ? launch_gemm_f16(A.hi, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s, splits_out)
+                   : launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s,
+                                      splits_out);
     });
   }
 
@@ -356,13 +440,18 @@ struct Forward {
     const int HqD = Hq * D, NQKV = nqkv(c);
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
+    // GEMMs of a mirrored group take one float16 plane (in the hi slot), and the kernels that
+    // produce their inputs write that plane: the input norm and attention output for the
+    // q|k|v and o projections, the post-attention norm for gate|up, the SwiGLU output for down
+    const bool fq = m->f16_qkv, fo = m->f16_o, fg = m->f16_gu, fd = m->f16_down;
     uint16_t* a_hi = at<uint16_t>(ws, L.act);                 // normalised activations / attention output
     uint16_t* a_lo = a_hi + (size_t)T * wide;
-    const AOp A_act{nullptr, a_hi, a_lo};
+    const AOp A_qkv{nullptr, a_hi, a_lo, fq};
+    const AOp A_o{nullptr, a_hi, a_lo, fo};
     float* big = at<float>(ws, L.big);                        // projection output (fp32) ...
     uint16_t* u_hi = reinterpret_cast<uint16_t*>(big);        // ... or the SwiGLU planes [T][I]
     uint16_t* u_lo = u_hi + (size_t)T * I;
-    const AOp A_u{nullptr, u_hi, u_lo};
+    const AOp A_u{nullptr, u_hi, u_lo, fd};
     float* part = at<float>(ws, L.gpart);
     const int* tok = at<int>(ws, L.tok);
     const int* pos = at<int>(ws, L.pos);
@@ -382,7 +471,7 @@ struct Forward {
       return st;
     if (jev_status st = run_k(K_RESNORM, 0.0, 2 * rowbytes, [&] {
           return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[0].attn_norm, c.rms_eps, a_hi, a_lo,
-                                      wide, s);
+                                      wide, fq, s);
         }))
       return st;
 
@@ -393,9 +482,13 @@ struct Forward {
 
     for (int l = 0; l < c.n_layers; ++l) {
       const jev_layer& W = m->layers[l];
+      const jev_layer& WQ = fq ? m->layers16[l] : W;   // the matrices the GEMMs read
+      const jev_layer& WO = fo ? m->layers16[l] : W;
+      const jev_layer& WG = fg ? m->layers16[l] : W;
+      const jev_layer& WD = fd ? m->layers16[l] : W;
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
       int sp = 1;
-      if (jev_status st = gemm_deferred(A_act, wide, T, H, W.wq, HqD, W.wk, Hkv * D, W.wv, Hkv * D, big, NQKV, 0, &sp))
+      if (jev_status st = gemm_deferred(A_qkv, wide, T, H, WQ.wq, HqD, WQ.wk, Hkv * D, WQ.wv, Hkv * D, big, NQKV, 0, &sp))
         return st;
       void *kdst, *vdst;
       int kld;
@@ -434,33 +527,40 @@ struct Forward {
       a.o_part = at<float>(ws, L.o_part);
       a.lse_part = at<float>(ws, L.lse_part);
       a.oh = a_hi; a.ol = a_lo;
+      a.o_f16 = fo ? 1 : 0;
       a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
       if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
       if (n_split > 1) {
         if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 1) * T * HqD, [&] {
-              return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, s);
+              return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, fo, s);
             }))
           return st;
       }
       // o-proj: x += o·W_oᵀ, then m = RMSNorm(x; g2) into the activation planes
-      if (jev_status st = gemm_deferred(A_act, HqD, T, HqD, W.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      if (jev_status st = gemm_deferred(A_o, HqD, T, HqD, WO.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H, W.mlp_norm, c.rms_eps,
-                                        a_hi, a_lo, wide, s);
+                                        a_hi, a_lo, wide, fg, s);
           }))
         return st;
-      if (jev_status st = run_k(K_SWIGLU, 2.0 * T * 2 * I * H, 2.0 * 2 * I * H + 4.0 * T * H + 4.0 * T * I, [&] {
-            return launch_gemm_swiglu(a_hi, a_lo, wide, T, H, static_cast<const uint16_t*>(W.w_gate),
-                                      static_cast<const uint16_t*>(W.w_up), I, u_hi, u_lo, I, s);
+      // activation bytes per element: two bf16 planes, or one float16 plane
+      const double in_b = fg ? 2.0 : 4.0, out_b = fd ? 2.0 : 4.0;
+      if (jev_status st = run_k(fg ? K_SWIGLU16 : K_SWIGLU, 2.0 * T * 2 * I * H,
+                                2.0 * 2 * I * H + in_b * T * H + out_b * T * I, [&] {
+            uint16_t* ul = fd ? nullptr : u_lo;   // u as one float16 plane for a float16 down GEMM
+            return fg ? launch_gemm_swiglu_f16(a_hi, wide, T, H, static_cast<const uint16_t*>(WG.w_gate),
+                                               static_cast<const uint16_t*>(WG.w_up), I, u_hi, ul, I, s)
+                      : launch_gemm_swiglu(a_hi, a_lo, wide, T, H, static_cast<const uint16_t*>(W.w_gate),
+                                           static_cast<const uint16_t*>(W.w_up), I, u_hi, ul, I, s);
           }))
         return st;
       // down: x += u·W_dᵀ, then the next layer's input norm
-      if (jev_status st = gemm_deferred(A_u, I, T, I, W.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      if (jev_status st = gemm_deferred(A_u, I, T, I, WD.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       const void* next_g = (l + 1 < c.n_layers) ? m->layers[l + 1].attn_norm : nullptr;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
                                         next_g ? next_g : W.mlp_norm, c.rms_eps, next_g ? a_hi : nullptr,
-                                        next_g ? a_lo : nullptr, wide, s);
+                                        next_g ? a_lo : nullptr, wide, fq, s);
           }))
         return st;
     }

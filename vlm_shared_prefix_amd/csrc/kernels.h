@@ -45,8 +45,9 @@ struct AttnArgs {
   int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
   float* o_part;           // [n_split][T][Hq][128]  (n_split > 1)
   float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1)
-  uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1)
+  uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1) ...
   uint16_t* ol;
+  int o_f16;               // ... or (non-zero) one float16 plane of o in oh
   float scale_log2;        // log2(e) / sqrt(128)
 };
 
@@ -82,13 +83,27 @@ GemmPlan gemm_bf16_plan(int M, int N, int K, size_t part_cap);
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
                             float* C, int ldc, int accum, size_t part_cap, float* part, hipStream_t s,
                             int* eff_splits);
-// gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu].
+// gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu],
+// or as one float16 plane into uh when ul is null.
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
                               const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+// Single-pass float16 GEMM: A is one float16 plane, seg holds float16 weights; otherwise as
+// launch_gemm_bf16 (split partials when *eff_splits > 1).
+GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap);
+hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C, int ldc,
+                           int accum, size_t part_cap, float* part, hipStream_t s, int* eff_splits);
+// gate|up GEMM with the SwiGLU epilogue on a float16 activation plane and float16 weights; u as in
+// launch_gemm_swiglu (hi/lo planes, or one float16 plane when ul is null).
+hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, const uint16_t* w_gate,
+                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+// float16 copy of n bfloat16 values (n % 8 == 0); sets *bad = 1 if a finite value exceeds the
+// float16 range (*bad is not cleared).
+hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int* bad, hipStream_t s);
 // x[row] += sum of `splits` partials [M][H] (splits may be 0), then RMSNorm of x into bf16 hi/lo
-// planes (skipped when yh is null).  H % 4 == 0, H <= 8192.
+// planes, or one float16 plane into yh when f16out (skipped when yh is null).  H % 4 == 0, H <= 8192.
 hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
-                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
+                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, bool f16out,
+                                hipStream_t s);
 // Sum of `splits` projection partials (row stride lds) -> RoPE (table cs) -> q hi/lo [T][Hq][128] f16,
 // K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1 and zeros in
 // columns T..round8(T)-1 (ldv >= round8(T)).
@@ -113,7 +128,7 @@ constexpr int kAttnMaxSplits = 8;
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
-                             uint16_t* ol, hipStream_t s);
+                             uint16_t* ol, bool f16out, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);
 hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh, uint16_t* ul, hipStream_t s);
 hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,

@@ -273,11 +273,14 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
 // issued before the lo-plane ones, so no two consecutive MFMAs share an
 // accumulator.  Same block remap and split-K layout as the 128 x 128 kernel.
 // SWIGLU: the 256 W rows are [gate 32 | up 32] x 2 per column wave.
+// F16: the activation is one float16 plane (Ah; Al unused), W is the float16
+// mirror of the weights, one f16 MFMA pass.  SWIGLU writes u as bf16 hi/lo planes
+// (oh, ol), or as one float16 plane into oh when ol is null.
 // ----------------------------------------------------------------------------
 #define G2M 128
 #define G2N 256
 #define G2K 32
-template <bool SWIGLU>
+template <bool SWIGLU, bool F16>
 __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah, const u16* __restrict__ Al, int lda,
                                                 int M, int K, GemmSegs seg, int N, int m_tiles, int n_tiles,
                                                 int splits, int k_chunk, float* __restrict__ C, int ldc,
@@ -342,7 +345,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_global_load_lds(srcA[i] + k0, dA + (i * 256 + wave * 64) * 8, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(srcL[i] + k0, dL + (i * 256 + wave * 64) * 8, 16, 0, 0);
+      if (!F16) __builtin_amdgcn_global_load_lds(srcL[i] + k0, dL + (i * 256 + wave * 64) * 8, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -375,10 +378,12 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
         const int r = wn * 128 + j * 32 + ql;
         bw[kk][j] = *reinterpret_cast<const bf16x8*>(sW + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
       }
+      if (!F16) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + ql;
-        al[kk][i] = *reinterpret_cast<const bf16x8*>(sL + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
+        for (int i = 0; i < 2; ++i) {
+          const int r = wm * 64 + i * 32 + ql;
+          al[kk][i] = *reinterpret_cast<const bf16x8*>(sL + r * G2K + ((c ^ ((r >> 2) & 3)) * 8));
+        }
       }
     }
 #pragma unroll
@@ -387,20 +392,33 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16((f16x8)ah[kk][i], (f16x8)bw[kk][j], acc[i][j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+      if (!F16) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[kk][i], bw[kk][j], acc[i][j], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads of k-step 0
+    if (F16) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads of k-step 0
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMAs of k-step 0
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read of k-step 1
+      for (int q = 0; q < 6; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA of k-step 0
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read of k-step 1
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);  // the rest
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads of k-step 0
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMAs of k-step 0
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read of k-step 1
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs of k-step 1
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs of k-step 1
   };
   auto step = [&](int s, const u16* cA, const u16* cL, const u16* cW, u16* nA, u16* nL, u16* nW) {
     if (s + 1 < nst) load_stage(kbeg + (s + 1) * G2K, nA, nL, nW);
@@ -431,9 +449,13 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
           if (row < M && col < N) {
             const float g = acc[i][2 * jp][r], u = acc[i][2 * jp + 1][r];
             const float val = g / (1.0f + expf(-g)) * u;
-            const u16 h = f32_to_bf16(val);
-            oh[(size_t)row * ldc + col] = h;
-            ol[(size_t)row * ldc + col] = f32_to_bf16(val - bf16_to_f32(h));
+            if (ol == nullptr) {   // one float16 plane
+              reinterpret_cast<f16*>(oh)[(size_t)row * ldc + col] = (f16)val;
+            } else {
+              const u16 h = f32_to_bf16(val);
+              oh[(size_t)row * ldc + col] = h;
+              ol[(size_t)row * ldc + col] = f32_to_bf16(val - bf16_to_f32(h));
+            }
           }
         }
     }
@@ -849,6 +871,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
   if (ns == 1) {
     const size_t ob = ((size_t)t * Hq + hq) * 128;
+    if (a.o_f16) {   // one float16 plane
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int d = dt * 32 + 8 * ii + 4 * hl;
+          f16x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = (f16)(acc[dt][4 * ii + j] * inv);
+          *reinterpret_cast<f16x4*>(a.oh + ob + d) = v4;
+        }
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -883,14 +918,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 // ----------------------------------------------------------------------------
 // Fused split-K reduce + residual + RMSNorm (bf16 models), one block per row:
 //   x[row] += sum_s part[s][row]      (fixed order; nothing to add if splits == 0)
-//   y = g * x / sqrt(mean(x^2) + eps) written as bf16 hi/lo planes (skipped if yh == nullptr)
+//   y = g * x / sqrt(mean(x^2) + eps) written as bf16 hi/lo planes, or as one float16
+//   plane into yh when f16out (skipped if yh == nullptr)
 // H % 4 == 0 and H <= 8192.
 // ----------------------------------------------------------------------------
 template <typename WT>
 __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
                                                      float* __restrict__ x, int H, const WT* __restrict__ g,
                                                      float eps, u16* __restrict__ yh, u16* __restrict__ yl,
-                                                     int ldy) {
+                                                     int ldy, int f16out) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int H4 = H >> 2;
@@ -919,6 +955,14 @@ __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ p
     const int k = threadIdx.x + 256 * j;
     if (k < H4) {
       const float in[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      const size_t o = (size_t)row * ldy + 4 * k;
+      if (f16out) {   // one float16 plane
+        f16x4 y4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y4[e] = (f16)(ldw(g, 4 * k + e) * (in[e] * r));
+        *reinterpret_cast<f16x4*>(yh + o) = y4;
+        continue;
+      }
       u16 h[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -926,7 +970,6 @@ __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ p
         h[e] = f32_to_bf16(y);
         l[e] = f32_to_bf16(y - bf16_to_f32(h[e]));
       }
-      const size_t o = (size_t)row * ldy + 4 * k;
       *reinterpret_cast<uint2*>(yh + o) =
           make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
       *reinterpret_cast<uint2*>(yl + o) =
@@ -1019,10 +1062,11 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
   }
 }
 
-// Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M).
+// Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), written as
+// bf16 hi/lo planes or (f16out) one float16 plane.
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
-                                                  int D, u16* __restrict__ oh, u16* __restrict__ ol) {
+                                                  int D, u16* __restrict__ oh, u16* __restrict__ ol, int f16out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one (t, hq)
   const int d4 = D >> 2;
   if (i >= (size_t)T * Hq * d4) return;
@@ -1057,13 +1101,20 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  const size_t at4 = th * D + 4 * c;
+  if (f16out) {   // one float16 plane
+    f16x4 v4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v4[j] = (f16)v[j];
+    *reinterpret_cast<f16x4*>(oh + at4) = v4;
+    return;
+  }
   u16 h[4], l[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     h[j] = f32_to_bf16(v[j]);
     l[j] = f32_to_bf16(v[j] - bf16_to_f32(h[j]));
   }
-  const size_t at4 = th * D + 4 * c;
   *reinterpret_cast<uint2*>(oh + at4) =
       make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
   *reinterpret_cast<uint2*>(ol + at4) =
@@ -1298,7 +1349,7 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
   const int ldo = splits == 1 ? ldc : N;
   const int acc = splits == 1 ? accum : 0;
   if (pl.wide)
-    gemm_bf16w<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+    gemm_bf16w<false, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
                                            (size_t)M * N, acc, nullptr, nullptr);
   else
     gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo, (size_t)M * N,
@@ -1313,17 +1364,95 @@ hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, i
   const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
   const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
-  gemm_bf16w<true><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
+  gemm_bf16w<true, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
+  return hipGetLastError();
+}
+
+// Single-pass float16 GEMMs: the activation as one float16 plane, W the float16 mirror.
+// Always the 128 x 256 kernel; K splits bring the grid to about 448 blocks (1.75 per CU),
+// at most 16, each >= 256 of K (measured on the 7B / 2B projection shapes, split-K
+// consumer included).
+GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap) {
+  GemmPlan p{};
+  p.wide = true;
+  const long t = (long)cdiv(M, G2M) * cdiv(N, G2N);
+  long sp = (448 + t / 2) / t;
+  sp = std::min<long>(sp, std::min(16, std::max(1, K / 256)));
+  p.splits = (int)std::max<long>(1, sp);
+  while (p.splits > 1 && (size_t)p.splits * M * N > part_cap) --p.splits;
+  return p;
+}
+
+hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmSegs& seg, int N, float* C, int ldc,
+                           int accum, size_t part_cap, float* part, hipStream_t s, int* eff_splits) {
+  *eff_splits = 1;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % G2K) return hipErrorInvalidValue;
+  const GemmPlan pl = gemm_f16_plan(M, N, K, part_cap);
+  const int mt = cdiv(M, G2M), nt = cdiv(N, G2N);
+  const int k_chunk = cdiv(cdiv(K, pl.splits), G2K) * G2K;
+  const int splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
+  const int grid = cdiv(mt * nt * splits, 8) * 8;
+  float* out = splits == 1 ? C : part;
+  const int ldo = splits == 1 ? ldc : N;
+  const int acc = splits == 1 ? accum : 0;
+  gemm_bf16w<false, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+                                               (size_t)M * N, acc, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, const uint16_t* w_gate,
+                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s) {
+  if (M <= 0 || I <= 0) return hipSuccess;
+  if (K % G2K) return hipErrorInvalidValue;
+  const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
+  const int grid = cdiv(mt * nt, 8) * 8;
+  GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
+  gemm_bf16w<true, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh,
+                                              ul);
+  return hipGetLastError();
+}
+
+// bfloat16 -> float16 copy of a weight matrix (n % 8 == 0); *bad = 1 if a finite value
+// falls outside the float16 range.
+__global__ void __launch_bounds__(256) bf16_to_f16(const u16* __restrict__ src, size_t n8, u16* __restrict__ dst,
+                                                   int* __restrict__ bad) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+    bool out_of_range = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_to_f32((u16)(w[j] & 0xFFFF)), b = bf16_to_f32((u16)(w[j] >> 16));
+      out_of_range |= (fabsf(a) > 65504.f && isfinite(a)) || (fabsf(b) > 65504.f && isfinite(b));
+      const f16 ha = (f16)a, hb = (f16)b;
+      o[j] = (uint32_t)__builtin_bit_cast(u16, ha) | ((uint32_t)__builtin_bit_cast(u16, hb) << 16);
+    }
+    reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    if (out_of_range) *bad = 1;
+  }
+}
+
+hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int* bad, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const size_t n8 = n / 8;
+  const int grid = (int)std::min<size_t>(4096, (n8 + 255) / 256);
+  bf16_to_f16<<<grid, 256, 0, s>>>(src, n8, dst, bad);
   return hipGetLastError();
 }
 
 hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
-                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s) {
+                                int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, bool f16out,
+                                hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (bf16)
-    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy);
+    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy, f16out);
   else
-    residual_norm<float><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl, ldy);
+    residual_norm<float><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl, ldy,
+                                           f16out);
   return hipGetLastError();
 }
 
@@ -1402,9 +1531,9 @@ hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
-                             uint16_t* ol, hipStream_t s) {
+                             uint16_t* ol, bool f16out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol);
+  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
   return hipGetLastError();
 }
 

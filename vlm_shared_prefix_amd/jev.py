@@ -58,10 +58,17 @@ _i32p = C.POINTER(C.c_int32)
 _u64p = C.POINTER(C.c_uint64)
 _vp = C.c_void_p
 
+JEV_F16_GATE_UP = 1   # w_gate, w_up
+JEV_F16_QKV = 2       # wq, wk, wv
+JEV_F16_DOWN = 4      # w_down
+JEV_F16_O = 8         # wo
+
 _sig = {
     "jev_model_create": (C.c_int32, [C.POINTER(jev_config), C.POINTER(jev_weights), C.POINTER(_vp)]),
     "jev_model_destroy": (None, [_vp]),
     "jev_get_stats": (C.c_int32, [_vp, C.POINTER(jev_stats)]),
+    "jev_model_f16_bytes": (C.c_size_t, [_vp, C.c_int32]),
+    "jev_model_attach_f16": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, _vp]),
     "jev_prefix_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_prefix_create": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, C.POINTER(_vp)]),
     "jev_prefix_destroy": (None, [_vp]),
@@ -138,6 +145,18 @@ def jev_get_stats(model: int) -> dict:
     st = jev_stats()
     _check(_lib.jev_get_stats(model, C.byref(st)), "jev_get_stats")
     return {k: int(getattr(st, k)) for k, _ in jev_stats._fields_}
+
+
+def jev_model_f16_bytes(model: int, groups: int) -> int:
+    return int(_lib.jev_model_f16_bytes(model, groups))
+
+
+def jev_model_attach_f16(model: int, groups: int, buf, stream=None) -> None:
+    """Convert the decoder matrices of `groups` (an OR of JEV_F16_GATE_UP, JEV_F16_QKV, JEV_F16_DOWN, JEV_F16_O) into `buf` (a device
+    tensor of >= jev_model_f16_bytes bytes; None detaches) and run those GEMMs as single float16
+    passes."""
+    nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    _check(_lib.jev_model_attach_f16(model, groups, _dptr(buf), nbytes, _stream(stream)), "jev_model_attach_f16")
 
 
 def jev_prefix_bytes(model: int, prefix_len: int) -> int:

@@ -30,10 +30,23 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(bits).to(device)
 
 
+# mirrored matrix groups per precision mode
+PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOWN,
+              "f16_o": J.JEV_F16_O, "f16_out": J.JEV_F16_DOWN | J.JEV_F16_O,
+              "f16_mlp": J.JEV_F16_GATE_UP | J.JEV_F16_DOWN,
+              "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
+DEFAULT_PRECISION = "f16_down"
+
+
 class Session:
     """A model on one device plus a prefix and a reusable workspace."""
 
-    def __init__(self, cfg, glob: Dict[str, np.ndarray], layers, device="cuda:0"):
+    def __init__(self, cfg, glob: Dict[str, np.ndarray], layers, device="cuda:0", precision: str = DEFAULT_PRECISION):
+        """precision (bf16 models): "split" runs every GEMM on two bfloat16 terms of the activation;
+        "f16_gu", "f16_down", "f16_down" run the gate|up, the down, or both MLP GEMMs as single
+        float16 passes on a float16 mirror of their weights; "f16" does so for every decoder GEMM."""
+        if precision not in PRECISIONS:
+            raise ValueError(f"precision must be one of {PRECISIONS}, not {precision!r}")
         self.cfg = cfg
         self.device = torch.device(device)
         self.dtype = J.JEV_BF16 if cfg.dtype == "bf16" else J.JEV_F32
@@ -48,13 +61,19 @@ class Session:
         self.jw, self._keep = J.make_weights(self.glob["embed"], self.glob["final_norm"], self.glob["lm_head"],
                                              self.layers)
         self.model = J.jev_model_create(self.jcfg, self.jw)
+        self.mirror = None
+        self.precision = precision if self.dtype == J.JEV_BF16 else "f32"
+        groups = PRECISIONS[precision] if self.dtype == J.JEV_BF16 else 0
+        if groups:
+            self.mirror = torch.empty(J.jev_model_f16_bytes(self.model, groups), dtype=torch.uint8, device=dev)
+            J.jev_model_attach_f16(self.model, groups, self.mirror)
         self.prefix = None
         self.kv = None
         self.P = 0
         self.ws = None
 
     @classmethod
-    def generated(cls, cfg, seed, device="cuda:0"):
+    def generated(cls, cfg, seed, device="cuda:0", precision: str = DEFAULT_PRECISION):
         """Draw the seeded weights (several layers at a time) and upload them layer by layer."""
         import jev_synth as S
         glob = S.weights_global(cfg, seed)
@@ -66,7 +85,7 @@ class Session:
                 k, W = next(it)
                 cache[k] = W
             return cache.pop(l)
-        return cls(cfg, glob, get, device)
+        return cls(cfg, glob, get, device, precision)
 
     # ------------------------------------------------------------------ buffers
     def workspace(self, nbytes: int) -> torch.Tensor:
@@ -83,6 +102,7 @@ class Session:
         if self.model:
             J.jev_model_destroy(self.model)
             self.model = None
+        self.mirror = None
 
     def __del__(self):
         try:
