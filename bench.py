@@ -277,6 +277,8 @@ def main():
                     help="also time configs c1, c2, c4 (every B, batched and serial) and c5 (every mode)")
     ap.add_argument("--precision", default=None,
                     help="GEMM precision mode of the bf16 models (see Session; default: the library default)")
+    ap.add_argument("--no-serial", action="store_true",
+                    help="skip the serial-vs-batched section (one call per suffix)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -351,14 +353,16 @@ def main():
         for sb, ob in zip(singles, outs):
             J.jev_score_suffixes(sess.prefix, sb["ids"], sb["lens"], sb["cands"], sb["n_cands"], ob, sess.ws)
 
-    serial_calls()
-    ms_serial = timed(serial_calls, 2)
-    serial = {"suffixes": len(singles), "batched_score_ms": round(ms_score, 4),
-              "serial_score_ms": round(ms_serial, 4), "speedup_vs_serial_calls": round(ms_serial / ms_score, 2),
-              "per_question_prefill_ms": round(len(singles) * (ms_prefill + ms_serial / len(singles)), 3),
-              "speedup_vs_per_question_prefill": round(len(singles) * (ms_prefill + ms_serial / len(singles)) /
-                                                       ms_step, 2)}
-    log(f"[bench] serial: {len(singles)} single-suffix calls {ms_serial:.2f} ms vs batched {ms_score:.2f} ms")
+    serial = None
+    if not args.no_serial:
+        serial_calls()
+        ms_serial = timed(serial_calls, 2)
+        serial = {"suffixes": len(singles), "batched_score_ms": round(ms_score, 4),
+                  "serial_score_ms": round(ms_serial, 4), "speedup_vs_serial_calls": round(ms_serial / ms_score, 2),
+                  "per_question_prefill_ms": round(len(singles) * (ms_prefill + ms_serial / len(singles)), 3),
+                  "speedup_vs_per_question_prefill": round(len(singles) * (ms_prefill + ms_serial / len(singles)) /
+                                                           ms_step, 2)}
+        log(f"[bench] serial: {len(singles)} single-suffix calls {ms_serial:.2f} ms vs batched {ms_score:.2f} ms")
 
     # per-kernel event timing (separate passes over the same calls)
     J.jev_profile_start(sess.model)
