@@ -938,9 +938,16 @@ __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ p
     const int k = threadIdx.x + 256 * j;
     if (k < H4) {
       float4 a = xr[k];
-      for (int sp = 0; sp < splits; ++sp) {
-        const float4 b = reinterpret_cast<const float4*>(part + sp * split_stride + (size_t)row * H)[k];
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      // partials summed in split order; loaded eight at a time so their loads overlap
+      for (int s0 = 0; s0 < splits; s0 += 8) {
+        float4 b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < splits)
+            b[u] = reinterpret_cast<const float4*>(part + (s0 + u) * split_stride + (size_t)row * H)[k];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < splits) { a.x += b[u].x; a.y += b[u].y; a.z += b[u].z; a.w += b[u].w; }
       }
       if (splits > 0) xr[k] = a;
       v[j] = a;
@@ -1009,9 +1016,17 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
   const int t0 = blockIdx.x * 16;
   const int nqk = Hq + Hkv;
   const int h = blockIdx.y;
-  auto ld = [&](int t, int c) {
+  auto ld = [&](int t, int c) {   // split partials summed in order, loaded eight at a time
     float a = src[(size_t)t * lds + c];
-    for (int sp = 1; sp < splits; ++sp) a += src[sp * split_stride + (size_t)t * lds + c];
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+      float b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) b[u] = src[(s0 + u) * split_stride + (size_t)t * lds + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) a += b[u];
+    }
     return a;
   };
   if (h < nqk) {
