@@ -95,6 +95,25 @@ def test_fullsize_serial_equals_batched():
     assert np.max(np.abs(serial - batched)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("q,mode", [(1, 0), (3, 0), (3, 2)])
+def test_fullsize_tree_few_questions(q, mode):
+    """Config 5 with only the first q questions: few query rows against the 8192-key prefix, so the
+    attention splits each row tile's key tiles many ways (the merge of up to 32 partials) and the
+    answers must equal those of the same questions in the full 16-question call."""
+    g = load_golden("c5", 0)
+    cfg = S.CONFIGS["c5"]
+    tree = {k: np.ascontiguousarray(v[:q]) for k, v in S.tree_inputs(cfg, 0).items()}
+    say(f"[fullsize] c5 first {q} questions, tree mode {mode}")
+    score, norm = session("c5", 0).score_tree(tree, mode)
+    for key, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
+        ref = np.array(g[key], np.float32)[:q]
+        valid = np.isfinite(ref)
+        err = float(np.max(np.abs(got[valid] - ref[valid])))
+        say(f"  c5[:{q}] mode {mode} {key}: max |d| = {err:.3e}")
+        assert err <= TOL["bf16"], (key, err)
+        assert np.all(np.isneginf(got[~valid]))
+
+
 @pytest.mark.parametrize("mode,precision", [(0, "f16_down"), (1, "f16_down"), (2, "f16_down"), (0, "split"),
                                             (2, "split")])
 def test_fullsize_tree(mode, precision):

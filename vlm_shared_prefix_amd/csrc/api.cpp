@@ -246,11 +246,16 @@ struct Layout {
 
 // Rows of attention partials a call of T rows may need: max over T' <= T of splits(T') * T'
 // when splits(T') > 1 (the split count falls as rows grow).
+constexpr int AT_KEYS = 64;   // attention key tile
+
 size_t attn_part_rows(const jev_config& c, int T, int P) {
   const int G = c.n_q_heads / c.n_kv_heads;
   size_t best = 0;
   for (int t = 1; t <= T; ++t) {
-    const int ns = attn_splits(t, G, c.n_kv_heads, P, 1);
+    // the split count grows with the tiles; a row tile's own keys span at most t + 7 rows,
+    // and prefills (no prefix keys) count as well
+    const int own = (t + 7 + AT_KEYS - 1) / AT_KEYS;
+    const int ns = std::max(attn_splits(t, G, c.n_kv_heads, P, own), attn_splits(t, G, c.n_kv_heads, 0, own));
     if (ns > 1) best = std::max(best, (size_t)ns * t);
   }
   return best;
@@ -476,7 +481,8 @@ struct Forward {
       return st;
 
     // attention splits: about one block per compute unit (partials merged when > 1)
-    const int n_split = attn_splits(T, Hq / Hkv, Hkv, P, 1);
+    const int own_tiles = attn_own_tiles(plan.seq_start.data(), T, Hq / Hkv);
+    const int n_split = attn_splits(T, Hq / Hkv, Hkv, P, own_tiles);
     const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
     const double attn_bytes = 2.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + 2.0 * T * HqD) + 4.0 * T * HqD;
 
@@ -524,6 +530,7 @@ struct Forward {
       a.lds = kld;
       a.seq_start = seq_start; a.mask = mask;
       a.n_split = n_split;
+      a.own_tiles = own_tiles;
       a.o_part = at<float>(ws, L.o_part);
       a.lse_part = at<float>(ws, L.lse_part);
       a.oh = a_hi; a.ol = a_lo;

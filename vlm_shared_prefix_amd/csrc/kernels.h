@@ -43,6 +43,8 @@ struct AttnArgs {
   const int* seq_start;    // [T] first row of the row's sequence / group
   const uint64_t* mask;    // [T] visibility over the group (nullptr: causal)
   int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
+  int own_tiles;           // bound on any row tile's own-key tiles (attn_own_tiles); the splits
+                           // divide ceil(P/64) + own_tiles tiles
   float* o_part;           // [n_split][T][Hq][128]  (n_split > 1)
   float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1)
   uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1) ...
@@ -121,11 +123,14 @@ hipError_t launch_rope_qk(bool f16out, const float* qkv, int T, int Hq, int Hkv,
                           double log2_theta, void* q_out, void* q_lo, void* k_out, int ldk, int row0, hipStream_t s);
 hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int HD, void* vt, int ldv, int col0,
                               hipStream_t s);
-constexpr int kAttnMaxSplits = 8;
+constexpr int kAttnMaxSplits = 32;
 // Splits for the bf16 attention of T rows (G q heads per KV head) over P prefix keys plus
 // own_tiles tiles of own keys: about one block per compute unit (two from 64 key tiles on),
 // at least two tiles each.
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
+// Own-key tiles (64 keys) of the 128-row tile that needs the most, from the host copy of
+// the rows' sequence starts.
+int attn_own_tiles(const int* seq_start, int T, int G);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, bool f16out, hipStream_t s);

@@ -697,7 +697,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int t = rc / G;
   const int hq = hk * G + rc % G;
 
-  // The loads the tile range depends on go first; q's loads are in flight meanwhile.
+  // The splits divide ntp + own_tiles key tiles (own_tiles: the host's bound on any row
+  // tile's own-key tiles), so a block whose range starts on a prefix tile issues that
+  // tile's loads before the sequence starts it depends on for the rest have arrived.
+  const int ntp = (a.P + AT_BK - 1) / AT_BK;
+  const int nt_u = ntp + a.own_tiles;
+  const int vb = (int)(((long)z * nt_u) / ns), ve_u = (int)(((long)(z + 1) * nt_u) / ns);
+  const bool early = vb < ntp && vb < ve_u;
+  if (early) {
+    const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
+    const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
+    const int k0 = vb * AT_BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = i * 256 + tid;
+      const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
+      const int key = k0 + row;
+      dma16(Kp, ((key < a.P ? key : 0) * 128 + c * 8) * 2, sK0 + (i * 256 + wave * 64) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = i * 256 + tid;
+      const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
+      const int key = k0 + c * 8;
+      dma16(Vp, (d * a.ldp + (key < a.P ? key : 0)) * 2, sV0 + (i * 256 + wave * 64) * 8);
+    }
+  }
+
   const int t_first = r0 / G, t_last = min(R - 1, r0 + AT_BR - 1) / G;
   const int s_first = a.seq_start[t_first];
   const int max_start = a.seq_start[t_last];
@@ -718,13 +744,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     }
   }
 
-  // this block's share of the tile sequence
-  const int ntp = (a.P + AT_BK - 1) / AT_BK;
+  // this block's share of the tile sequence: [vb, ve) of the row tile's real tiles (the last
+  // split also takes any tiles past the bound, should the host's bound be short)
   const int own_end = t_last + 1;
   const int own0 = s_first & ~7;   // 16 B aligned start of the block's own keys
   const int nt_all = ntp + (own_end - own0 + AT_BK - 1) / AT_BK;
-  const int vb = (int)(((long)z * nt_all) / ns), ve = (int)(((long)(z + 1) * nt_all) / ns);
-  const int nt = ve - vb;
+  const int ve = (z == ns - 1) ? nt_all : min(ve_u, nt_all);
+  const int nt = max(0, ve - vb);
 
   auto tile = [&](int v) {
     AttnTile s;
@@ -857,11 +883,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
-  if (nt > 0) {
-    load_tile(tile(vb), sK0, sV0);
-    __builtin_amdgcn_s_waitcnt(0x70);
-    asm volatile("s_barrier" ::: "memory");
-  }
+  if (nt > 0 && !early) load_tile(tile(vb), sK0, sV0);
+  // the first tile has landed (or, with no tile to process, the early loads are done
+  // before the block's LDS is released)
+  __builtin_amdgcn_s_waitcnt(0x70);
+  if (nt > 0) asm volatile("s_barrier" ::: "memory");
   for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
     step(i, sK0, sV0, sK1, sV1);
     if (i + 1 < nt) step(i + 1, sK1, sV1, sK0, sV0);
@@ -1079,6 +1105,7 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
 
 // Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), written as
 // bf16 hi/lo planes or (f16out) one float16 plane.
+template <int MAXS>
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
                                                   int D, u16* __restrict__ oh, u16* __restrict__ ol, int f16out) {
@@ -1087,12 +1114,12 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
   if (i >= (size_t)T * Hq * d4) return;
   const size_t th = i / d4;
   const int c = (int)(i % d4);
-  // every split's lse and partial are loaded up front (S <= kAttnMaxSplits), so the
-  // loads are in flight together instead of one round trip per split
-  float lse[kAttnMaxSplits];
-  float4 part[kAttnMaxSplits];
+  // every split's lse and partial are loaded up front (S <= MAXS), so the loads are in
+  // flight together instead of one round trip per split
+  float lse[MAXS];
+  float4 part[MAXS];
 #pragma unroll
-  for (int s = 0; s < kAttnMaxSplits; ++s) {
+  for (int s = 0; s < MAXS; ++s) {
     if (s < S) {
       lse[s] = lse_part[(size_t)s * T * Hq + th];
       part[s] = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * D)[c];
@@ -1100,13 +1127,13 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
   }
   float M = NEG_INF;
 #pragma unroll
-  for (int s = 0; s < kAttnMaxSplits; ++s)
+  for (int s = 0; s < MAXS; ++s)
     if (s < S) M = fmaxf(M, lse[s]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (M != NEG_INF) {
 #pragma unroll
-    for (int s = 0; s < kAttnMaxSplits; ++s) {
+    for (int s = 0; s < MAXS; ++s) {
       if (s < S && lse[s] != NEG_INF) {
         const float w = __builtin_amdgcn_exp2f(lse[s] - M);
         acc.x += w * part[s].x; acc.y += w * part[s].y; acc.z += w * part[s].z; acc.w += w * part[s].w;
@@ -1525,6 +1552,16 @@ hipError_t launch_v_transpose(bool f16out, const float* src, int lds, int T, int
   return hipGetLastError();
 }
 
+int attn_own_tiles(const int* seq_start, int T, int G) {
+  const int R = G * T;
+  int mx = 0;
+  for (int r0 = 0; r0 < R; r0 += AT_BR) {
+    const int t_first = r0 / G, t_last = std::min(R - 1, r0 + AT_BR - 1) / G;
+    mx = std::max(mx, cdiv(t_last + 1 - (seq_start[t_first] & ~7), AT_BK));
+  }
+  return mx;
+}
+
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
   const long base = (long)cdiv((long)G * T, AT_BR) * Hkv;
   const int tiles = cdiv(P, AT_BK) + own_tiles;
@@ -1548,7 +1585,11 @@ hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, bool f16out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  attn_merge<<<cdiv((long)T * Hq * (D / 4), 256), 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
+  const int grid = cdiv((long)T * Hq * (D / 4), 256);
+  if (S <= 8)
+    attn_merge<8><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
+  else
+    attn_merge<kAttnMaxSplits><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
   return hipGetLastError();
 }
 
