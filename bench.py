@@ -148,7 +148,31 @@ def tree_section(seed, dev, profile_steps, name="c5"):
            "prefill_ms": round(ms_prefill, 3),
            "attention": attention_entry(prof, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                         f"shared prefix ({cfg.prefix_len} keys) + tree rows ({rows})")}
-    log(f"[bench] {name}: tree call {ms_tree:.2f} ms, prefill {ms_prefill:.1f} ms")
+    # the memory-bound end: the same prefix with only the first q question stems (few query
+    # rows per KV head), where the attention is bound by streaming the prefix KV
+    kv_bytes = cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 2 * 2 * cfg.n_layers
+    stream_rows = []
+    for q in (1, 3):
+        tq = {k: np.ascontiguousarray(v[:q]) for k, v in tree.items()}
+        sess.score_tree(tq, J.JEV_TREE_TRIE)
+        J.jev_profile_start(sess.model)
+        for _ in range(max(1, profile_steps)):
+            sess.score_tree(tq, J.JEV_TREE_TRIE)
+        pq = J.jev_profile_stop(sess.model)
+        a = pq["attn_fwd"]
+        a_s = a["ms"] / a["launches"] * 1e-3
+        e = {"questions": q, "rows": int(J.jev_tree_plan_size(tq["stem_ids"], tq["stem_lens"], tq["cand_tok"],
+                                                             tq["cand_lens"], tq["n_cands"], J.JEV_TREE_TRIE)[0]),
+             "attn_avg_launch_us": round(a_s * 1e6, 2),
+             "prefix_kv_gbs": round(kv_bytes / cfg.n_layers / a_s / 1e9, 1),
+             "prefix_kv_hbm_frac": round(kv_bytes / cfg.n_layers / a_s / 1e9 / PEAK_HBM_GBS, 4)}
+        if pq.get("attn_merge"):
+            e["merge_avg_us"] = round(pq["attn_merge"]["ms"] / pq["attn_merge"]["launches"] * 1e3, 2)
+        stream_rows.append(e)
+    out["prefix_kv_stream"] = {"what": f"prefix KV ({kv_bytes // cfg.n_layers / 1e6:.1f} MB per layer) read by the "
+                                       f"attention of the first 1 / 3 questions (trie)", "runs": stream_rows}
+    log(f"[bench] {name}: tree call {ms_tree:.2f} ms, prefill {ms_prefill:.1f} ms; prefix-KV stream "
+        + ", ".join(f"Q={e['questions']} {e['prefix_kv_gbs']} GB/s" for e in stream_rows))
     sess.close()
     return out
 
