@@ -41,8 +41,12 @@ def _rotate(head_vec, pos, theta):
     return out
 
 
-def _hidden_states(cfg, W, rows):
-    """Run every layer over `rows` (list of float64 vectors); returns the final rows."""
+def _hidden_states(cfg, W, rows, skip=None, first_candidate=0):
+    """Run every layer over `rows` (list of float64 vectors); returns the final rows.
+
+    Where skip[l] is set, rows from first_candidate on leave block l with the value
+    they entered it with ("FastJEV", §2.3: candidate evaluation bypasses the
+    selected complete blocks; the context rows keep every block)."""
     Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     per_kv = Hq // Hkv
     eps, theta = cfg.rms_eps, cfg.rope_theta
@@ -84,7 +88,8 @@ def _hidden_states(cfg, W, rows):
             gate = Lw["w_gate"].dot(m)
             up = Lw["w_up"].dot(m)
             act = np.array([gate[t] / (1.0 + math.exp(-gate[t])) * up[t] for t in range(len(gate))])
-            new_x.append(h1 + Lw["w_down"].dot(act))
+            bypass = skip is not None and skip[l] and i >= first_candidate
+            new_x.append(x[i] if bypass else h1 + Lw["w_down"].dot(act))
         x = new_x
     return x
 
@@ -104,7 +109,7 @@ def _prefix_rows(W, prefix):
     return rows
 
 
-def score_suffixes(cfg, W, prefix, suf):
+def score_suffixes(cfg, W, prefix, suf, skip=None):
     """float64 out[b, c] = log-softmax over the candidates of the last-row logits."""
     E = W.glob["embed"]
     pre = _prefix_rows(W, prefix)
@@ -113,7 +118,7 @@ def score_suffixes(cfg, W, prefix, suf):
     for b in range(B):
         L = int(suf["lens"][b])
         rows = pre + [np.asarray(E[t], dtype=np.float64) for t in suf["ids"][b, :L]]
-        lp = _full_log_probs(cfg, W, _hidden_states(cfg, W, rows)[-1])
+        lp = _full_log_probs(cfg, W, _hidden_states(cfg, W, rows, skip, len(pre))[-1])
         n = int(suf["n_cands"][b])
         sel = [lp[int(c)] for c in suf["cands"][b, :n]]
         mx = max(sel)
@@ -123,7 +128,7 @@ def score_suffixes(cfg, W, prefix, suf):
     return out
 
 
-def score_tree(cfg, W, prefix, tree):
+def score_tree(cfg, W, prefix, tree, skip=None):
     """float64 flat tree scores: sum of the candidate tokens' full-vocab log-probs."""
     E = W.glob["embed"]
     pre = _prefix_rows(W, prefix)
@@ -138,7 +143,7 @@ def score_tree(cfg, W, prefix, tree):
             K = int(tree["cand_lens"][q, c])
             w = [int(t) for t in tree["cand_tok"][q, c, :K]]
             fed = stem + w[:K - 1]
-            hs = _hidden_states(cfg, W, pre + [np.asarray(E[t], dtype=np.float64) for t in fed])
+            hs = _hidden_states(cfg, W, pre + [np.asarray(E[t], dtype=np.float64) for t in fed], skip, len(pre))
             tot = 0.0
             for k in range(K):
                 lp = _full_log_probs(cfg, W, hs[len(pre) + s - 1 + k])

@@ -174,20 +174,31 @@ def prefix_rows(ws, cfg, prefix: Dict[str, np.ndarray]) -> np.ndarray:
     return np.concatenate(rows, axis=0) if rows else np.zeros((0, cfg.hidden), F32)
 
 
-def forward_sequence(ws, cfg, x0: np.ndarray) -> np.ndarray:
-    """All layers over one sequence at positions 0..N-1 (plain causal LM)."""
+def forward_sequence(ws, cfg, x0: np.ndarray, skip=None, bypass_from: int = 0) -> np.ndarray:
+    """All layers over one sequence at positions 0..N-1 (plain causal LM).
+
+    Block skipping ("FastJEV", §2.3 and §3.4): where skip[l] is set, rows from
+    bypass_from on (the candidate rows) pass block l unchanged, while the rows
+    before them (the shared context) run it.  Only rows that also skip block l
+    could read the bypassed rows' keys there, so computing the block for every
+    row and then restoring the bypassed rows is exact.
+    """
     x = x0.astype(F32)
     pos = np.arange(x.shape[0])
     for l in range(cfg.n_layers):
-        x, _, _ = layer_forward(ws.layer(l), cfg, x, pos)
+        x_new, _, _ = layer_forward(ws.layer(l), cfg, x, pos)
+        if skip is not None and skip[l]:
+            x_new[bypass_from:] = x[bypass_from:]
+        x = x_new
     return x
 
 
 # ----------------------------------------------------------------------------
 # scoring: the definition (serial) and the prefix-once variant
 # ----------------------------------------------------------------------------
-def score_suffixes_serial(ws, cfg, prefix, suf) -> np.ndarray:
-    """out[b, c]: one independent full forward over prefix ‖ suffix_b per question."""
+def score_suffixes_serial(ws, cfg, prefix, suf, skip=None) -> np.ndarray:
+    """out[b, c]: one independent full forward over prefix ‖ suffix_b per question
+    (suffix rows bypass the blocks marked in skip)."""
     P = prefix_rows(ws, cfg, prefix)
     E = ws.glob["embed"]
     B, C = suf["cands"].shape
@@ -195,16 +206,18 @@ def score_suffixes_serial(ws, cfg, prefix, suf) -> np.ndarray:
     for b in range(B):
         L = int(suf["lens"][b])
         x = np.concatenate([P, E[suf["ids"][b, :L]]], axis=0)
-        h = forward_sequence(ws, cfg, x)
+        h = forward_sequence(ws, cfg, x, skip, P.shape[0])
         lp = log_probs(ws, cfg, h[-1:])[0]
         out[b] = candidate_readout(lp, suf["cands"][b], int(suf["n_cands"][b]), C)
     return out
 
 
-def _run_groups(ws, cfg, prefix, groups: List[np.ndarray], free_layers: bool = False):
+def _run_groups(ws, cfg, prefix, groups: List[np.ndarray], free_layers: bool = False, skip=None):
     """Layer-major forward of the prefix once plus independent row groups over it.
 
     groups[i] = token ids of one independent continuation (positions P..).
+    Where skip[l] is set the groups pass block l unchanged; the prefix runs every
+    block ("FastJEV", §3.4: the shared context keeps all layers).
     Returns the final hidden rows of every group.
     """
     E = ws.glob["embed"]
@@ -217,20 +230,21 @@ def _run_groups(ws, cfg, prefix, groups: List[np.ndarray], free_layers: bool = F
         kp = vp = None
         if Pn:
             xp, kp, vp = layer_forward(W, cfg, xp, pos_p)
-        for i, g in enumerate(groups):
-            pos = Pn + np.arange(len(g))
-            xs[i], _, _ = layer_forward(W, cfg, xs[i], pos, kp, vp)
+        if skip is None or not skip[l]:
+            for i, g in enumerate(groups):
+                pos = Pn + np.arange(len(g))
+                xs[i], _, _ = layer_forward(W, cfg, xs[i], pos, kp, vp)
         if free_layers:
             ws.drop_layer(l)
     return xs
 
 
 def score_suffixes(ws, cfg, prefix, suf, free_layers: bool = False,
-                   return_full: bool = False):
+                   return_full: bool = False, skip=None):
     """Same definition as score_suffixes_serial with the prefix rows computed once."""
     B, C = suf["cands"].shape
     groups = [suf["ids"][b, :int(suf["lens"][b])] for b in range(B)]
-    xs = _run_groups(ws, cfg, prefix, groups, free_layers)
+    xs = _run_groups(ws, cfg, prefix, groups, free_layers, skip)
     out = np.full((B, C), -np.inf, dtype=F32)
     lps = []
     for b in range(B):
@@ -268,22 +282,23 @@ def _tree_finish(tree, lp_rows) -> Dict[str, np.ndarray]:
     return {"score": score, "norm": norm}
 
 
-def score_tree_serial(ws, cfg, prefix, tree) -> Dict[str, np.ndarray]:
-    """Flat definition: every candidate its own full forward over prefix ‖ stem ‖ w[:-1]."""
+def score_tree_serial(ws, cfg, prefix, tree, skip=None) -> Dict[str, np.ndarray]:
+    """Flat definition: every candidate its own full forward over prefix ‖ stem ‖ w[:-1]
+    (stem and candidate rows bypass the blocks marked in skip)."""
     P = prefix_rows(ws, cfg, prefix)
     E = ws.glob["embed"]
     rows = {}
     for key, (fed, w, s) in _tree_sequences(tree).items():
-        h = forward_sequence(ws, cfg, np.concatenate([P, E[fed]], axis=0))
+        h = forward_sequence(ws, cfg, np.concatenate([P, E[fed]], axis=0), skip, P.shape[0])
         rows[key] = (w, log_probs(ws, cfg, h[h.shape[0] - len(w):]))
     return _tree_finish(tree, rows)
 
 
-def score_tree(ws, cfg, prefix, tree, free_layers: bool = False) -> Dict[str, np.ndarray]:
+def score_tree(ws, cfg, prefix, tree, free_layers: bool = False, skip=None) -> Dict[str, np.ndarray]:
     """Flat definition with the prefix rows computed once (see module docstring)."""
     seqs = _tree_sequences(tree)
     keys = list(seqs.keys())
-    xs = _run_groups(ws, cfg, prefix, [seqs[k][0] for k in keys], free_layers)
+    xs = _run_groups(ws, cfg, prefix, [seqs[k][0] for k in keys], free_layers, skip)
     rows = {}
     for key, x in zip(keys, xs):
         fed, w, s = seqs[key]

@@ -176,6 +176,48 @@ def test_identity_blocks_ignore_context():
     np.testing.assert_allclose(a, zero, atol=1e-6)
 
 
+def test_block_skipping_matches_brute_force():
+    """Candidate rows bypassing selected blocks ("FastJEV", §2.3, §3.4), prefix at full depth:
+    the prefix-once oracle, its serial definition and the fp64 brute force agree, for suffixes
+    and trees, and the skip changes the result."""
+    cfg = _small("c1", n_layers=3, n_vis=10, n_text=3, s_max=5, fixed_lens=(5, 1, 3), n_suffix=3,
+                 n_cands=4, hidden=64, mlp=96, vocab=200, n_q_heads=4, n_kv_heads=1, head_dim=16)
+    ws = S.WeightSource(cfg, 5)
+    pre, suf = S.prefix_inputs(cfg, 5), S.suffix_inputs(cfg, 5)
+    skip = np.array([0, 1, 0], dtype=np.uint8)
+    ref = brute.score_suffixes(cfg, ws, pre, suf, skip)
+    assert np.max(np.abs(O.score_suffixes(ws, cfg, pre, suf, skip=skip) - ref)) < 1e-5
+    assert np.max(np.abs(O.score_suffixes_serial(ws, cfg, pre, suf, skip) - ref)) < 1e-5
+    assert np.max(np.abs(O.score_suffixes(ws, cfg, pre, suf) - ref)) > 1e-3
+    tcfg = S.CONFIGS["t1"]
+    tws = S.WeightSource(tcfg, 1)
+    tpre, tree = S.prefix_inputs(tcfg, 1), S.tree_inputs(tcfg, 1)
+    tskip = np.array([1], dtype=np.uint8)
+    tref = brute.score_tree(tcfg, tws, tpre, tree, tskip)
+    got = O.score_tree(tws, tcfg, tpre, tree, skip=tskip)
+    got_serial = O.score_tree_serial(tws, tcfg, tpre, tree, tskip)
+    for k in ("score", "norm"):
+        assert np.max(np.abs(got[k] - tref[k])) < 1e-5
+        assert np.max(np.abs(got_serial[k] - tref[k])) < 1e-5
+
+
+def test_skipping_every_block_is_textbook_readout():
+    """All blocks bypassed: the candidate row is its own embedding, so the answer is
+    log-softmax over the candidates of RMSNorm(E[last]) W_lm^T, whatever the prefix."""
+    cfg = S.CONFIGS["c1"]
+    ws = S.WeightSource(cfg, 0)
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    got = O.score_suffixes(ws, cfg, pre, suf, skip=np.ones(cfg.n_layers, np.uint8))
+    g = ws.glob
+    for b in range(len(suf["lens"])):
+        e = g["embed"][suf["ids"][b, suf["lens"][b] - 1]].astype(np.float64)
+        h = g["final_norm"] * e / np.sqrt(np.mean(e * e) + cfg.rms_eps)
+        z = g["lm_head"][suf["cands"][b]].astype(np.float64) @ h
+        np.testing.assert_allclose(got[b], sps.log_softmax(z), atol=2e-6)
+    none = O.score_suffixes(ws, cfg, pre, suf, skip=np.zeros(cfg.n_layers, np.uint8))
+    np.testing.assert_array_equal(none, O.score_suffixes(ws, cfg, pre, suf))
+
+
 # ---------------------------------------------------------------- method invariants
 @pytest.fixture(scope="module")
 def m2_small():
