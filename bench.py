@@ -388,6 +388,25 @@ def main():
                                                            ms_step, 2)}
         log(f"[bench] serial: {len(singles)} single-suffix calls {ms_serial:.2f} ms vs batched {ms_score:.2f} ms")
 
+    # decision-guided block skipping ("FastJEV", §3.4): the candidate rows bypass a block mask
+    # (here a fixed synthetic one: 12 of 28 blocks, the later ones but not the final block, near
+    # the pages' 43.75-45.83% budgets; ranking blocks needs trained weights and calibration
+    # inputs), the prefix keeps every block.  Not part of `value`.
+    skip = None
+    if cfg.n_layers >= 4:
+        n_skip = (cfg.n_layers * 3 + 3) // 7           # 12 of 28
+        mask = np.zeros(cfg.n_layers, np.uint8)
+        mask[cfg.n_layers - 1 - n_skip:cfg.n_layers - 1] = 1
+        sess.set_skip(mask)
+        score_only()
+        ms_skip = timed(score_only, args.steps)
+        sess.set_skip(None)
+        skip = {"skipped_blocks": [int(i) for i in np.nonzero(mask)[0]], "score_ms": round(ms_skip, 4),
+                "candidates_per_s": round(n_cand / (ms_skip * 1e-3), 2),
+                "speedup_vs_full_depth_score": round(ms_score / ms_skip, 3)}
+        log(f"[bench] block skipping ({int(mask.sum())} of {cfg.n_layers}): score call {ms_skip:.3f} ms "
+            f"vs {ms_score:.3f} ms")
+
     # per-kernel event timing (separate passes over the same calls)
     J.jev_profile_start(sess.model)
     for _ in range(args.profile_steps):
@@ -463,6 +482,7 @@ def main():
         "roofline": roof,
         "attention": attn,
         "serial_vs_batched": serial,
+        "block_skipping": skip,
         "kernels": kernels,
         "long_prefix_tree": tree,
         "configs": configs,

@@ -131,6 +131,18 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
 
+/* ---- decision-guided block skipping ("FastJEV", §2.3 and §3.4) -----------------
+ * The candidate rows of jev_score_suffixes and jev_score_tree bypass the decoder
+ * blocks whose skip[l] is non-zero (x leaves block l as it entered it), while the
+ * shared context keeps every block: jev_prefill_prefix ignores the mask.  The
+ * same blocks apply to shared histories and their continuations (every row of a
+ * scoring call).  Ranking the blocks (the pages calibrate on unlabeled inputs)
+ * is the caller's business; this is the mechanism only.
+ * skip: host [n], n == n_layers; NULL or n == 0 clears the mask.  The mask is
+ * copied; it applies to calls enqueued after this returns (do not change it
+ * while another call on this model is being enqueued). */
+jev_status jev_model_set_skip(jev_model *m, const uint8_t *skip, int32_t n);
+
 /* ---- prefix KV store ---------------------------------------------------------
  * Layout per layer l (element type float16 for JEV_BF16, float32 for JEV_F32),
  * with Pc = prefix_len rounded up to a multiple of 64:

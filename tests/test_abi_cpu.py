@@ -122,6 +122,28 @@ def test_prefix_and_workspace_sizes(model):
     assert e.value.code == J.JEV_E_UNSUPPORTED
 
 
+def test_mirror_and_skip_arguments(model):
+    """Float16 mirror sizes per matrix group and the block-skip mask's checks (no HIP call)."""
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    # _cfg: 2 layers, H 256, Hq 4 / Hkv 2 x 128, I 512 -> per layer q 512x256, k/v 256x256, o 256x512,
+    # gate/up 512x256, down 256x512 (bytes = 2 x elements, each 256-byte aligned) + a 256-byte flag
+    per = {J.JEV_F16_QKV: 2 * (512 * 256 + 2 * 256 * 256), J.JEV_F16_O: 2 * 256 * 512,
+           J.JEV_F16_GATE_UP: 2 * 2 * 512 * 256, J.JEV_F16_DOWN: 2 * 256 * 512}
+    for g, b in per.items():
+        assert J.jev_model_f16_bytes(m, g) == 2 * b + 256
+    assert J.jev_model_f16_bytes(m, 99) == 0
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_attach_f16(m, J.JEV_F16_DOWN, _FakeDev(100), stream=0)
+    assert e.value.code == J.JEV_E_WORKSPACE
+    J.jev_model_attach_f16(m, J.JEV_F16_DOWN, None, stream=0)   # detach: no HIP call
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_set_skip(m, [1, 0, 1])                  # 3 flags for 2 layers
+    assert e.value.code == J.JEV_E_INVALID
+    J.jev_model_set_skip(m, [0, 1])
+    J.jev_model_set_skip(m, None)
+
+
 def test_score_validation_before_any_launch(model):
     """Every bad argument is rejected on the host; B = 0 does no work (Ochevid: all-skipped requests)."""
     from vlm_shared_prefix_amd import jev as J

@@ -50,3 +50,44 @@ def test_score_tree_vs_oracle(name, seed, precision):
             assert err <= TOL[cfg.dtype], (mode, k, err)
             assert np.all(np.isneginf(got[~valid]))
     sess.close()
+
+
+@pytest.mark.parametrize("name,seed,skip", [("c1", 0, (1,)), ("m2", 0, (0, 1)), ("m7", 0, (1, 0)),
+                                            ("m7l", 0, (1, 0))])
+def test_block_skipping_vs_oracle(name, seed, skip):
+    """Candidate rows bypass the masked blocks, the prefix keeps them ("FastJEV", §2.3, §3.4)."""
+    cfg = S.CONFIGS[name]
+    say(f"[parity] score_suffixes {name} seed {seed} skipping blocks {skip}")
+    sess, src = gpu_session(cfg, seed)
+    pre, suf = S.prefix_inputs(cfg, seed), S.suffix_inputs(cfg, seed)
+    mask = np.array(skip, dtype=np.uint8)
+    ref = O.score_suffixes(src, cfg, pre, suf, skip=mask)
+    sess.set_skip(mask)
+    sess.prefill(pre["vis"], pre["text_ids"])          # the prefill keeps every block
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"{name}/s{seed}/skip{skip}")
+    sess.set_skip(None)
+    full = O.score_suffixes(src, cfg, pre, suf)
+    back = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(back, full, suf["n_cands"], cfg.dtype, f"{name}/s{seed}/no skip")
+    sess.close()
+
+
+@pytest.mark.parametrize("name,seed,skip", [("t1", 1, (1,)), ("m5", 0, (0, 1))])
+def test_tree_block_skipping_vs_oracle(name, seed, skip):
+    cfg = S.CONFIGS[name]
+    say(f"[parity] score_tree {name} seed {seed} skipping blocks {skip}")
+    sess, src = gpu_session(cfg, seed)
+    pre, tree = S.prefix_inputs(cfg, seed), S.tree_inputs(cfg, seed)
+    mask = np.array(skip, dtype=np.uint8)
+    ref = O.score_tree(src, cfg, pre, tree, skip=mask)
+    sess.set_skip(mask)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    for mode in (0, 2):
+        score, norm = sess.score_tree(tree, mode)
+        for k, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
+            valid = np.isfinite(ref[k])
+            err = float(np.max(np.abs(got[valid] - ref[k][valid])))
+            say(f"  mode {mode} {k}: max |d| = {err:.3e}")
+            assert err <= TOL[cfg.dtype], (mode, k, err)
+    sess.close()

@@ -56,6 +56,8 @@ struct jev_model {
   bool f16_down = false;   // w_down mirrored
   bool f16_qkv = false;    // wq, wk, wv mirrored
   bool f16_o = false;      // wo mirrored
+  // blocks the candidate rows bypass in scoring calls (empty: none); prefills run every block
+  std::vector<uint8_t> skip;
   std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
   Profiler prof;
 };
@@ -202,6 +204,20 @@ extern "C" jev_status jev_get_stats(const jev_model* m, jev_stats* out) {
   return JEV_OK;
 }
 
+extern "C" jev_status jev_model_set_skip(jev_model* m, const uint8_t* skip, int32_t n) {
+  if (!m) return fail(JEV_E_INVALID, "null model");
+  if (!skip || n == 0) {
+    m->skip.clear();
+    return JEV_OK;
+  }
+  if (n != m->cfg.n_layers) return fail(JEV_E_INVALID, "skip mask length differs from n_layers");
+  std::vector<uint8_t> v(skip, skip + n);
+  bool any = false;
+  for (uint8_t b : v) any |= b != 0;
+  if (any) m->skip = std::move(v); else m->skip.clear();
+  return JEV_OK;
+}
+
 extern "C" size_t jev_prefix_bytes(const jev_model* m, int32_t prefix_len) {
   if (!m || prefix_len < 0) return 0;
   const jev_config& c = m->cfg;
@@ -319,6 +335,16 @@ extern "C" size_t jev_workspace_bytes(const jev_model* m, int32_t prefix_len, in
 // ---------------------------------------------------------------------------
 namespace {
 enum class Mode { Prefill, Score, Tree };
+
+// Layers a forward runs: all of them for a prefill; in scoring calls the candidate rows bypass
+// the blocks of the model's skip mask ("FastJEV", §2.3 and §3.4: the shared context keeps every
+// block, candidate evaluation skips the selected complete blocks).
+std::vector<int> run_layers(const jev_model* m, Mode mode) {
+  std::vector<int> out;
+  for (int l = 0; l < m->cfg.n_layers; ++l)
+    if (mode == Mode::Prefill || m->skip.empty() || !m->skip[l]) out.push_back(l);
+  return out;
+}
 
 #define HIP_OK(expr)                                                                  \
   do {                                                                                \
@@ -469,14 +495,15 @@ struct Forward {
     if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 1.5,
                               [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
       return st;
-    if (c.n_layers == 0) return JEV_OK;
+    const std::vector<int> layers = run_layers(m, mode);
+    if (layers.empty()) return JEV_OK;
     float2* rope = at<float2>(ws, L.rope);
     if (jev_status st = run_k(K_ROPETAB, 0.0, 8.0 * T * 64,
                               [&] { return launch_rope_table(pos, T, log2_theta, rope, s); }))
       return st;
     if (jev_status st = run_k(K_RESNORM, 0.0, 2 * rowbytes, [&] {
-          return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[0].attn_norm, c.rms_eps, a_hi, a_lo,
-                                      wide, fq, s);
+          return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[layers[0]].attn_norm, c.rms_eps, a_hi,
+                                      a_lo, wide, fq, s);
         }))
       return st;
 
@@ -486,7 +513,8 @@ struct Forward {
     const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
     const double attn_bytes = 2.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + 2.0 * T * HqD) + 4.0 * T * HqD;
 
-    for (int l = 0; l < c.n_layers; ++l) {
+    for (size_t li = 0; li < layers.size(); ++li) {
+      const int l = layers[li];
       const jev_layer& W = m->layers[l];
       const jev_layer& WQ = fq ? m->layers16[l] : W;   // the matrices the GEMMs read
       const jev_layer& WO = fo ? m->layers16[l] : W;
@@ -563,7 +591,7 @@ struct Forward {
         return st;
       // down: x += u·W_dᵀ, then the next layer's input norm
       if (jev_status st = gemm_deferred(A_u, I, T, I, WD.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
-      const void* next_g = (l + 1 < c.n_layers) ? m->layers[l + 1].attn_norm : nullptr;
+      const void* next_g = (li + 1 < layers.size()) ? m->layers[layers[li + 1]].attn_norm : nullptr;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
                                         next_g ? next_g : W.mlp_norm, c.rms_eps, next_g ? a_hi : nullptr,
@@ -600,7 +628,7 @@ struct Forward {
     const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
     const double attn_bytes = 4.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + (double)T * HqD) + 4.0 * T * HqD;
 
-    for (int l = 0; l < c.n_layers; ++l) {
+    for (int l : run_layers(m, mode)) {
       const jev_layer& W = m->layers[l];
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
       if (jev_status st = run_k(K_RMSNORM, 0.0, 2 * rowbytes, [&] {

@@ -69,6 +69,7 @@ _sig = {
     "jev_get_stats": (C.c_int32, [_vp, C.POINTER(jev_stats)]),
     "jev_model_f16_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_model_attach_f16": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, _vp]),
+    "jev_model_set_skip": (C.c_int32, [_vp, C.POINTER(C.c_uint8), C.c_int32]),
     "jev_prefix_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_prefix_create": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, C.POINTER(_vp)]),
     "jev_prefix_destroy": (None, [_vp]),
@@ -157,6 +158,16 @@ def jev_model_attach_f16(model: int, groups: int, buf, stream=None) -> None:
     passes."""
     nbytes = 0 if buf is None else buf.numel() * buf.element_size()
     _check(_lib.jev_model_attach_f16(model, groups, _dptr(buf), nbytes, _stream(stream)), "jev_model_attach_f16")
+
+
+def jev_model_set_skip(model: int, skip) -> None:
+    """Blocks the candidate rows of scoring calls bypass (host array of n_layers flags; None clears)."""
+    if skip is None:
+        _check(_lib.jev_model_set_skip(model, None, 0), "jev_model_set_skip")
+        return
+    arr = np.ascontiguousarray(np.asarray(skip, dtype=np.uint8))
+    _check(_lib.jev_model_set_skip(model, arr.ctypes.data_as(C.POINTER(C.c_uint8)), int(arr.size)),
+           "jev_model_set_skip")
 
 
 def jev_prefix_bytes(model: int, prefix_len: int) -> int:

@@ -151,5 +151,9 @@ class Session:
                          tree["n_cands"], mode, score, norm, ws, stream)
         return score, norm
 
+    def set_skip(self, skip) -> None:
+        """Blocks the candidate rows of scoring calls bypass (None clears); prefills keep every block."""
+        J.jev_model_set_skip(self.model, skip)
+
     def stats(self) -> dict:
         return J.jev_get_stats(self.model)
