@@ -148,6 +148,22 @@ def tree_section(seed, dev, profile_steps, name="c5"):
            "prefill_ms": round(ms_prefill, 3),
            "attention": attention_entry(prof, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                         f"shared prefix ({cfg.prefix_len} keys) + tree rows ({rows})")}
+    # trie vs stem-only vs flat schedules ("FastJEV" §4.7, Table 5): the same questions with
+    # independent candidates and with overlapping ones (candidate k+1 repeating a leading run
+    # of candidate k half the time), rows fed and call time per mode
+    schedules = {}
+    for label, tcfg in (("independent", cfg), ("overlapping", S.with_overrides(cfg, overlap=True))):
+        tt = S.tree_inputs(tcfg, seed)
+        runs = {}
+        for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat")):
+            sess.score_tree(tt, mode)
+            ms = timed(lambda: sess.score_tree(tt, mode), 3)
+            r = J.jev_tree_plan_size(tt["stem_ids"], tt["stem_lens"], tt["cand_tok"], tt["cand_lens"],
+                                     tt["n_cands"], mode)[0]
+            runs[mname] = {"rows": int(r), "call_ms": round(ms, 3)}
+        schedules[label] = runs
+    out["schedules"] = schedules
+
     # the memory-bound end: the same prefix with only the first q question stems (few query
     # rows per KV head), where the attention is bound by streaming the prefix KV
     kv_bytes = cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 2 * 2 * cfg.n_layers
