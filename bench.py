@@ -103,6 +103,22 @@ def attention_entry(prof, prefix_kv_bytes, what):
     return e
 
 
+def timed_on(stream, fn, k, warm=0):
+    """ms per call of fn() enqueued k times on `stream`, between events recorded on that stream."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / k
+
+
 def tree_section(seed, dev, profile_steps, name="c5"):
     """Secondary measurement: the long-prefix tree workload (prefix 8192, 16 questions with
     4 multi-token candidates each, trie sharing) on the same 7B shape; not the headline value."""
@@ -131,6 +147,14 @@ def tree_section(seed, dev, profile_steps, name="c5"):
         return a.elapsed_time(b) / k
 
     ms_tree = timed(lambda: sess.score_tree(tree, J.JEV_TREE_TRIE), 3)
+    gstream = torch.cuda.Stream()
+    cap = sess.capture_score_tree(tree, J.JEV_TREE_TRIE, gstream)
+    ms_tree_graph = timed_on(gstream, cap.replay, 3, warm=1)
+    e_score, _ = sess.score_tree(tree, J.JEV_TREE_TRIE)
+    torch.cuda.synchronize()
+    tree_graph = {"tree_call_ms": round(ms_tree_graph, 3),
+                  "bitwise_equal_to_eager": bool(torch.equal(cap.outs[0], e_score))}
+    del cap
     ms_prefill = timed(lambda: sess.prefill(pre["vis"], pre["text_ids"]), 1)
     J.jev_profile_start(sess.model)
     for _ in range(max(1, profile_steps)):
@@ -145,7 +169,7 @@ def tree_section(seed, dev, profile_steps, name="c5"):
             f"{cfg.cand_len_lo}-{cfg.cand_len_hi} tokens; trie sharing, full-vocabulary log-probs")
     out = {"workload": desc, "tree_rows": int(rows),
            "tree_call_ms": round(ms_tree, 3), "candidates_per_s": round(n_c / (ms_tree * 1e-3), 1),
-           "prefill_ms": round(ms_prefill, 3),
+           "graph_replay": tree_graph, "prefill_ms": round(ms_prefill, 3),
            "attention": attention_entry(prof, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                         f"shared prefix ({cfg.prefix_len} keys) + tree rows ({rows})")}
     # trie vs stem-only vs flat schedules ("FastJEV" §4.7, Table 5): the same questions with
@@ -319,6 +343,8 @@ def main():
                     help="GEMM precision mode of the bf16 models (see Session; default: the library default)")
     ap.add_argument("--no-serial", action="store_true",
                     help="skip the serial-vs-batched section (one call per suffix)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the score call")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
@@ -383,6 +409,19 @@ def main():
     ms_score = timed(score_only, args.steps)
     ms_prefill = timed(prefill_only, max(1, args.steps // 2))
     log(f"[bench] score-only {ms_score:.3f} ms, prefill-only {ms_prefill:.3f} ms")
+
+    # the score call replayed from a HIP graph (its launch-only entry point captured once; no
+    # host planning or metadata copy per replay), on a stream of its own
+    graph = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream()
+        cap = sess.capture_score_suffixes(suf, gstream)
+        ms_graph = timed_on(gstream, cap.replay, args.steps, warm=2)
+        graph = {"score_ms": round(ms_graph, 4), "candidates_per_s": round(n_cand / (ms_graph * 1e-3), 2),
+                 "speedup_vs_eager_score": round(ms_score / ms_graph, 3),
+                 "bitwise_equal_to_eager": bool(torch.equal(cap.outs[0], out))}
+        log(f"[bench] graph replay of the score call: {ms_graph:.3f} ms (eager {ms_score:.3f} ms)")
+        del cap
 
     # the same suffixes scored one call per suffix over the same prefix (the serial baseline
     # the method replaces), and with a fresh prefill per question (image-per-question)
@@ -497,6 +536,7 @@ def main():
         "prefill_ms": round(ms_prefill, 4),
         "roofline": roof,
         "attention": attn,
+        "graph_replay": graph,
         "serial_vs_batched": serial,
         "block_skipping": skip,
         "kernels": kernels,

@@ -238,6 +238,34 @@ jev_status jev_score_tree(const jev_prefix *p,
                           float *out_score, float *out_norm,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* ---- launch-only scoring (HIP graph capture) -----------------------------------
+ * jev_score_suffixes_launch and jev_score_tree_launch take the arguments of
+ * jev_score_suffixes and jev_score_tree, make the same checks and build the
+ * same plan on the host, but do not copy the plan's metadata (row tokens,
+ * positions, sequence starts, masks, readout tables) into the workspace: the
+ * workspace must still hold what the last jev_score_suffixes / jev_score_tree
+ * / jev_prefill_prefix call on this model staged into it, for identical
+ * arguments, and no call on another model may have used the workspace since.
+ * The library keeps, per model and workspace address, a 64-bit
+ * digest of the metadata it last staged there; a mismatch (other arguments,
+ * another call in between, no staging call yet) returns JEV_E_INVALID and
+ * launches nothing.  Everything these calls enqueue is a kernel launch (no
+ * copy, memset, allocation or synchronisation), so a caller can capture them
+ * on a stream into a HIP graph and replay it; each replay recomputes the
+ * outputs from the prefix store and the workspace as they are when it runs.
+ * Calls that share a workspace must not overlap.
+ * Errors: as the staging calls. */
+jev_status jev_score_suffixes_launch(const jev_prefix *p,
+                                     const int32_t *ids, const int32_t *lens, int32_t B, int32_t S_max,
+                                     const int32_t *cand_ids, const int32_t *n_cands, int32_t C_max,
+                                     float *out_logp, void *ws, size_t ws_bytes, void *stream);
+jev_status jev_score_tree_launch(const jev_prefix *p,
+                                 const int32_t *stem_ids, const int32_t *stem_lens, int32_t Q, int32_t S_max,
+                                 const int32_t *cand_tok, const int32_t *cand_lens, const int32_t *n_cands,
+                                 int32_t C_max, int32_t K_max, int32_t mode,
+                                 float *out_score, float *out_norm,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* Rows the tree layout `mode` runs for this request (host-only planning; no
  * HIP call).  Useful to size the workspace exactly.  Returns JEV_OK and sets
  * *rows, *seqs and *targets, or an error as jev_score_tree would. */

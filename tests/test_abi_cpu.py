@@ -188,6 +188,35 @@ def test_score_validation_before_any_launch(model):
     J.jev_prefix_destroy(p)
 
 
+def test_launch_only_calls_need_staged_metadata(model):
+    """The launch-only (graph-capturable) scoring calls refuse a workspace whose staged
+    metadata is not this request's; nothing is launched (no HIP call on this path)."""
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    p = J.jev_prefix_create(m, 10, _FakeDev(J.jev_prefix_bytes(m, 10)))
+    ws, out = _FakeDev(1 << 30, ptr=0x9000), _FakeDev(1 << 20)
+    ids = np.zeros((2, 4), np.int32)
+    lens = np.array([4, 2], np.int32)
+    cands = np.array([[1, 2], [3, 4]], np.int32)
+    nc = np.array([2, 2], np.int32)
+    with pytest.raises(J.JevError) as e:
+        J.jev_score_suffixes_launch(p, ids, lens, cands, nc, out, ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID and "metadata" in J.jev_last_error()
+    tree = dict(stem_ids=np.ones((1, 3), np.int32), stem_lens=np.array([3], np.int32),
+                cand_tok=np.array([[[1, 2], [1, 3]]], np.int32), cand_lens=np.array([[2, 2]], np.int32),
+                n_cands=np.array([2], np.int32))
+    with pytest.raises(J.JevError) as e:
+        J.jev_score_tree_launch(p, tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                                tree["n_cands"], 0, out, None, ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID
+    # argument checks come first, as in the staging calls
+    with pytest.raises(J.JevError) as e:
+        J.jev_score_suffixes_launch(p, ids, np.array([5, 2], np.int32), cands, nc, out, ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID and "metadata" not in J.jev_last_error()
+    assert J.jev_get_stats(m)["launches"] == 0
+    J.jev_prefix_destroy(p)
+
+
 # ---------------------------------------------------------------- tree planning
 def reference_trie(tree, mode):
     """Independent pure-Python packer: rows (token, depth, group), visibility and predictor rows."""

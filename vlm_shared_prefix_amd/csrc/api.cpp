@@ -11,7 +11,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/jev.h"
@@ -60,6 +62,9 @@ struct jev_model {
   std::vector<uint8_t> skip;
   std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
   Profiler prof;
+  // digest of the metadata last staged into each workspace address (launch-only calls check it)
+  std::mutex staged_mu;
+  std::unordered_map<const void*, uint64_t> staged;
 };
 
 struct jev_prefix {
@@ -732,8 +737,17 @@ struct Forward {
   int tree_C = 0, tree_K = 0;
 };
 
-// Copy the plan's metadata into the workspace with one host->device copy.
-jev_status stage_meta(const Plan& p, const Layout& L, void* ws, hipStream_t s) {
+// 64-bit FNV-1a of the staged metadata bytes.
+uint64_t meta_digest(const std::vector<char>& b) {
+  uint64_t h = 1469598103934665603ull;
+  for (char c : b) h = (h ^ (uint8_t)c) * 1099511628211ull;
+  return h ^ (uint64_t)b.size();
+}
+
+// Copy the plan's metadata into the workspace with one host->device copy and record its
+// digest for the workspace address; with stage == false copy nothing and check instead that
+// the workspace holds this plan's metadata (launch-only calls).
+jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hipStream_t s, bool stage) {
   std::vector<char> buf(L.meta_end, 0);
   auto put = [&](size_t off, const void* src, size_t bytes) {
     if (bytes) std::memcpy(buf.data() + off, src, bytes);
@@ -746,7 +760,16 @@ jev_status stage_meta(const Plan& p, const Layout& L, void* ws, hipStream_t s) {
   put(L.tgt_tok, p.tgt_tok.data(), 4 * p.tgt_tok.size());
   put(L.out_n, p.out_n.data(), 4 * p.out_n.size());
   put(L.mask, p.mask.data(), 8 * p.mask.size());
+  const uint64_t h = meta_digest(buf);
+  std::lock_guard<std::mutex> lock(m->staged_mu);
+  if (!stage) {
+    auto it = m->staged.find(ws);
+    if (it == m->staged.end() || it->second != h)
+      return fail(JEV_E_INVALID, "workspace does not hold this call's metadata: stage it with the copying call first");
+    return JEV_OK;
+  }
   HIP_OK(hipMemcpyAsync(ws, buf.data(), L.meta_end, hipMemcpyHostToDevice, s));
+  m->staged[ws] = h;
   return JEV_OK;
 }
 }  // namespace
@@ -779,7 +802,7 @@ extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, 
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (jev_status st = stage_meta(plan, L, ws, s)) return st;
+  if (jev_status st = stage_meta(p->m, plan, L, ws, s, true)) return st;
   Forward f(p, plan, L, ws, s, Mode::Prefill);
   jev_status st = f.run(vis_embeds, n_vis);
   p->m->launches += f.launches;
@@ -788,9 +811,9 @@ extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, 
   return JEV_OK;
 }
 
-extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
-                                         int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands,
-                                         int32_t C_max, float* out_logp, void* ws, size_t ws_bytes, void* stream) {
+static jev_status score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
+                                 int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands, int32_t C_max,
+                                 float* out_logp, void* ws, size_t ws_bytes, void* stream, bool stage) {
   if (!p) return fail(JEV_E_INVALID, "null prefix");
   jev_model* m = p->m;
   Plan plan;
@@ -804,7 +827,7 @@ extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (jev_status e = stage_meta(plan, L, ws, s)) return e;
+  if (jev_status e = stage_meta(m, plan, L, ws, s, stage)) return e;
   Forward f(p, plan, L, ws, s, Mode::Score);
   jev_status e = f.run(nullptr, 0);
   if (!e) e = f.readout(out_logp, nullptr);
@@ -815,10 +838,23 @@ extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids
   return JEV_OK;
 }
 
-extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens,
-                                     int32_t Q, int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens,
-                                     const int32_t* n_cands, int32_t C_max, int32_t K_max, int32_t mode,
-                                     float* out_score, float* out_norm, void* ws, size_t ws_bytes, void* stream) {
+extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
+                                         int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands,
+                                         int32_t C_max, float* out_logp, void* ws, size_t ws_bytes, void* stream) {
+  return score_suffixes(p, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes, stream, true);
+}
+
+extern "C" jev_status jev_score_suffixes_launch(const jev_prefix* p, const int32_t* ids, const int32_t* lens,
+                                                int32_t B, int32_t S_max, const int32_t* cand_ids,
+                                                const int32_t* n_cands, int32_t C_max, float* out_logp, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  return score_suffixes(p, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes, stream, false);
+}
+
+static jev_status score_tree(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens, int32_t Q,
+                             int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens, const int32_t* n_cands,
+                             int32_t C_max, int32_t K_max, int32_t mode, float* out_score, float* out_norm, void* ws,
+                             size_t ws_bytes, void* stream, bool stage) {
   if (!p) return fail(JEV_E_INVALID, "null prefix");
   jev_model* m = p->m;
   Plan plan;
@@ -834,7 +870,7 @@ extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_id
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (jev_status e = stage_meta(plan, L, ws, s)) return e;
+  if (jev_status e = stage_meta(m, plan, L, ws, s, stage)) return e;
   Forward f(p, plan, L, ws, s, Mode::Tree);
   f.tree_C = C_max;
   f.tree_K = K_max;
@@ -845,6 +881,23 @@ extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_id
   m->forwards++;
   m->rows += (uint64_t)plan.T;
   return JEV_OK;
+}
+
+extern "C" jev_status jev_score_tree(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens,
+                                     int32_t Q, int32_t S_max, const int32_t* cand_tok, const int32_t* cand_lens,
+                                     const int32_t* n_cands, int32_t C_max, int32_t K_max, int32_t mode,
+                                     float* out_score, float* out_norm, void* ws, size_t ws_bytes, void* stream) {
+  return score_tree(p, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands, C_max, K_max, mode, out_score,
+                    out_norm, ws, ws_bytes, stream, true);
+}
+
+extern "C" jev_status jev_score_tree_launch(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens,
+                                            int32_t Q, int32_t S_max, const int32_t* cand_tok,
+                                            const int32_t* cand_lens, const int32_t* n_cands, int32_t C_max,
+                                            int32_t K_max, int32_t mode, float* out_score, float* out_norm, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  return score_tree(p, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands, C_max, K_max, mode, out_score,
+                    out_norm, ws, ws_bytes, stream, false);
 }
 
 extern "C" jev_status jev_tree_plan_size(const int32_t* stem_ids, const int32_t* stem_lens, int32_t Q,

@@ -79,6 +79,10 @@ _sig = {
                                        _vp, _vp, C.c_size_t, _vp]),
     "jev_score_tree": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                    C.c_int32, C.c_int32, _vp, _vp, _vp, C.c_size_t, _vp]),
+    "jev_score_suffixes_launch": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32,
+                                              _vp, _vp, C.c_size_t, _vp]),
+    "jev_score_tree_launch": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p,
+                                          C.c_int32, C.c_int32, C.c_int32, _vp, _vp, _vp, C.c_size_t, _vp]),
     "jev_tree_plan_size": (C.c_int32, [_i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p]),
     "jev_tree_plan_rows": (C.c_int32, [_i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
@@ -213,15 +217,26 @@ def jev_prefill_prefix(prefix: int, vis_embeds, n_vis: int, text_ids, ws, stream
            "jev_prefill_prefix")
 
 
-def jev_score_suffixes(prefix: int, ids, lens, cand_ids, n_cands, out_logp, ws, stream=None) -> None:
+def _score_suffixes(fn, name, prefix, ids, lens, cand_ids, n_cands, out_logp, ws, stream):
     ids, lens, cand_ids, n_cands = _i32(ids), _i32(lens), _i32(cand_ids), _i32(n_cands)
     B = int(lens.shape[0])
     S_max = int(ids.shape[1]) if ids.ndim == 2 else 1
     C_max = int(cand_ids.shape[1]) if cand_ids.ndim == 2 else 1
-    _check(_lib.jev_score_suffixes(prefix, _ptr_i32(ids), _ptr_i32(lens), B, S_max, _ptr_i32(cand_ids),
-                                   _ptr_i32(n_cands), C_max, _dptr(out_logp), _dptr(ws),
-                                   ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)),
-           "jev_score_suffixes")
+    _check(fn(prefix, _ptr_i32(ids), _ptr_i32(lens), B, S_max, _ptr_i32(cand_ids), _ptr_i32(n_cands), C_max,
+              _dptr(out_logp), _dptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+              _stream(stream)), name)
+
+
+def jev_score_suffixes(prefix: int, ids, lens, cand_ids, n_cands, out_logp, ws, stream=None) -> None:
+    _score_suffixes(_lib.jev_score_suffixes, "jev_score_suffixes", prefix, ids, lens, cand_ids, n_cands,
+                    out_logp, ws, stream)
+
+
+def jev_score_suffixes_launch(prefix: int, ids, lens, cand_ids, n_cands, out_logp, ws, stream=None) -> None:
+    """Kernel launches of jev_score_suffixes only (the workspace must hold the metadata a
+    jev_score_suffixes call with the same arguments staged); capturable into a HIP graph."""
+    _score_suffixes(_lib.jev_score_suffixes_launch, "jev_score_suffixes_launch", prefix, ids, lens, cand_ids,
+                    n_cands, out_logp, ws, stream)
 
 
 def _tree_args(stem_ids, stem_lens, cand_tok, cand_lens, n_cands):
@@ -233,13 +248,25 @@ def _tree_args(stem_ids, stem_lens, cand_tok, cand_lens, n_cands):
     return stem_ids, stem_lens, cand_tok, cand_lens, n_cands, Q, S_max, C_max, K_max
 
 
+def _score_tree(fn, name, prefix, stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode, out_score, out_norm,
+                ws, stream):
+    si, sl, ct, cl, nc, Q, S_max, C_max, K_max = _tree_args(stem_ids, stem_lens, cand_tok, cand_lens, n_cands)
+    _check(fn(prefix, _ptr_i32(si), _ptr_i32(sl), Q, S_max, _ptr_i32(ct), _ptr_i32(cl), _ptr_i32(nc), C_max,
+              K_max, mode, _dptr(out_score), _dptr(out_norm), _dptr(ws),
+              ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)), name)
+
+
 def jev_score_tree(prefix: int, stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode: int,
                    out_score, out_norm, ws, stream=None) -> None:
-    si, sl, ct, cl, nc, Q, S_max, C_max, K_max = _tree_args(stem_ids, stem_lens, cand_tok, cand_lens, n_cands)
-    _check(_lib.jev_score_tree(prefix, _ptr_i32(si), _ptr_i32(sl), Q, S_max, _ptr_i32(ct), _ptr_i32(cl),
-                               _ptr_i32(nc), C_max, K_max, mode, _dptr(out_score), _dptr(out_norm), _dptr(ws),
-                               ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)),
-           "jev_score_tree")
+    _score_tree(_lib.jev_score_tree, "jev_score_tree", prefix, stem_ids, stem_lens, cand_tok, cand_lens, n_cands,
+                mode, out_score, out_norm, ws, stream)
+
+
+def jev_score_tree_launch(prefix: int, stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode: int,
+                          out_score, out_norm, ws, stream=None) -> None:
+    """Kernel launches of jev_score_tree only (see jev_score_suffixes_launch)."""
+    _score_tree(_lib.jev_score_tree_launch, "jev_score_tree_launch", prefix, stem_ids, stem_lens, cand_tok,
+                cand_lens, n_cands, mode, out_score, out_norm, ws, stream)
 
 
 def jev_tree_plan_size(stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode: int):

@@ -151,9 +151,53 @@ class Session:
                          tree["n_cands"], mode, score, norm, ws, stream)
         return score, norm
 
+    # ------------------------------------------------------------------ graph capture
+    def capture_score_suffixes(self, suf, stream: "torch.cuda.Stream") -> "CapturedCall":
+        """Stage the request's metadata with one jev_score_suffixes call on `stream` into a
+        workspace of its own, then capture jev_score_suffixes_launch into a HIP graph.  Each
+        replay of the returned call rescores the suffixes into its `out`."""
+        B, C = suf["cands"].shape
+        out = torch.empty((B, C), dtype=torch.float32, device=self.device)
+        ws = torch.empty(max(self.suffix_ws_bytes(suf), 256), dtype=torch.uint8, device=self.device)
+        args = (self.prefix, suf["ids"], suf["lens"], suf["cands"], suf["n_cands"], out, ws)
+        with torch.cuda.stream(stream):
+            J.jev_score_suffixes(*args, stream=stream.cuda_stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            J.jev_score_suffixes_launch(*args, stream=stream.cuda_stream)
+        return CapturedCall(g, ws, (out,))
+
+    def capture_score_tree(self, tree, mode, stream: "torch.cuda.Stream") -> "CapturedCall":
+        """As capture_score_suffixes for jev_score_tree; outputs (score, norm)."""
+        Q, C, _ = tree["cand_tok"].shape
+        score = torch.empty((Q, C), dtype=torch.float32, device=self.device)
+        norm = torch.empty((Q, C), dtype=torch.float32, device=self.device)
+        ws = torch.empty(max(self.tree_ws_bytes(tree, mode), 256), dtype=torch.uint8, device=self.device)
+        args = (self.prefix, tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                tree["n_cands"], mode, score, norm, ws)
+        with torch.cuda.stream(stream):
+            J.jev_score_tree(*args, stream=stream.cuda_stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            J.jev_score_tree_launch(*args, stream=stream.cuda_stream)
+        return CapturedCall(g, ws, (score, norm))
+
     def set_skip(self, skip) -> None:
         """Blocks the candidate rows of scoring calls bypass (None clears); prefills keep every block."""
         J.jev_model_set_skip(self.model, skip)
 
     def stats(self) -> dict:
         return J.jev_get_stats(self.model)
+
+
+class CapturedCall:
+    """A captured scoring call: the graph, the workspace holding its staged metadata and its
+    outputs, kept alive together.  replay() enqueues the graph on the current stream."""
+
+    def __init__(self, graph, ws, outs):
+        self.graph, self.ws, self.outs = graph, ws, outs
+
+    def replay(self):
+        self.graph.replay()
