@@ -238,6 +238,47 @@ jev_status jev_score_tree(const jev_prefix *p,
                           float *out_score, float *out_norm,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* ---- one question over several images ----------------------------------------
+ * ("Ochevid Jev-VL 2B", One question, multiple images: up to eight images and
+ * one typed question; every image is encoded, the images' rows stay
+ * independent, and each image gets its own answer.)  A segmented prefix
+ * stores n_seg independent prefixes back to back in one KV store, segment i
+ * occupying store rows [off_i, off_i + seg_lens[i]) with off_i the sum of the
+ * earlier lengths.  One batched prefill runs all of them; each suffix of a
+ * scoring call continues one segment and never sees another.
+ *
+ * jev_prefix_create_segments: as jev_prefix_create for prefix_len = the sum of
+ *   seg_lens (each >= 0; n_seg in [1, 64]; the sum <= 32768); size kv_buf with
+ *   jev_prefix_bytes(m, sum).  A plain prefix is the one-segment case.
+ *   jev_prefill_prefix, jev_score_suffixes and jev_score_tree reject a prefix of
+ *   more than one segment (JEV_E_INVALID).
+ * jev_prefill_segments: segment i's rows are its n_vis[i] visual embeddings
+ *   then the embedding rows of its n_text[i] text ids, at positions
+ *   0..seg_lens[i]-1, causal within the segment only.  n_vis[i] + n_text[i] must
+ *   equal seg_lens[i].
+ *     vis_embeds  dev  [sum n_vis, H] of the model dtype, segment-major
+ *     text_ids    host [sum n_text], segment-major, each in [0, V)
+ *     n_vis, n_text host [n_seg]
+ *   Workspace: jev_workspace_bytes(m, sum, sum, 1, 0).
+ * jev_score_segments: jev_score_suffixes where suffix b continues segment
+ *   seg[b] (host [B], each in [0, n_seg)): its token j sits at position
+ *   seg_lens[seg[b]] + j and it sees that segment's rows and its own earlier
+ *   rows only.  The one-question case passes the same question for every
+ *   segment with seg[b] = b.  Suffixes of the same segment should be adjacent
+ *   and segments in ascending order: the attention visits, for each block of
+ *   rows, the keys between the first and the last segment its rows name.
+ *   Workspace: jev_workspace_bytes(m, sum, sum of lens, B, B * C_max).
+ * Errors: as jev_prefix_create / jev_prefill_prefix / jev_score_suffixes. */
+jev_status jev_prefix_create_segments(jev_model *m, const int32_t *seg_lens, int32_t n_seg,
+                                      void *kv_buf, size_t kv_bytes, jev_prefix **out);
+jev_status jev_prefill_segments(jev_prefix *p, const void *vis_embeds, const int32_t *n_vis,
+                                const int32_t *text_ids, const int32_t *n_text,
+                                void *ws, size_t ws_bytes, void *stream);
+jev_status jev_score_segments(const jev_prefix *p, const int32_t *seg,
+                              const int32_t *ids, const int32_t *lens, int32_t B, int32_t S_max,
+                              const int32_t *cand_ids, const int32_t *n_cands, int32_t C_max,
+                              float *out_logp, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- launch-only scoring (HIP graph capture) -----------------------------------
  * jev_score_suffixes_launch and jev_score_tree_launch take the arguments of
  * jev_score_suffixes and jev_score_tree, make the same checks and build the

@@ -44,6 +44,7 @@ STREAM_LAYER0 = 1
 STREAM_PREFIX = 1000
 STREAM_SUFFIX = 2000
 STREAM_TREE = 3000
+STREAM_IMAGES = 4000
 
 
 @dataclasses.dataclass(frozen=True)
@@ -76,6 +77,10 @@ class Config:
     cand_len_lo: int = 1
     cand_len_hi: int = 1
     overlap: bool = False         # force shared candidate prefixes (trie merges fire)
+    # one question over several images: n_images prefixes of n_vis visual rows each
+    # (drawn in [vis_lo, n_vis] per image when vis_lo > 0: mixed image sizes) + n_text
+    n_images: int = 0
+    vis_lo: int = 0
 
     @property
     def prefix_len(self) -> int:
@@ -128,6 +133,17 @@ CONFIGS: Dict[str, Config] = {
                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
                  n_vis=150, n_text=0, n_questions=4, stem_len=5, tree_cands=4,
                  cand_len_lo=1, cand_len_hi=4, s_max=8, overlap=True),
+    # one question over 8 images on the 7B shape: 8 prefixes of 1000 visual + 24 text rows
+    "c6": Config("c6", **_Q7B, n_vis=1000, n_text=24, n_images=8, len_lo=6, len_hi=16, s_max=16,
+                 n_cands=3),
+    # one question over 3 images of mixed sizes, 7B head structure, 2 layers
+    "mi7": Config("mi7", n_layers=2, hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
+                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
+                  n_vis=230, n_text=10, n_images=3, vis_lo=60, len_lo=1, len_hi=16, s_max=16, n_cands=3),
+    # one question over 3 images of mixed sizes on the tiny fp32 decoder
+    "mi1": Config("mi1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                  mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",
+                  n_vis=48, n_text=16, n_images=3, vis_lo=10, len_lo=5, len_hi=7, s_max=8, n_cands=3),
     # fp32 tree workload on the tiny decoder (oracle pins and fp32 parity)
     "t1": Config("t1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                  mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",
@@ -322,6 +338,33 @@ def suffix_inputs(cfg: Config, seed: int, n: Optional[int] = None) -> Dict[str, 
         ids, lens, cands, n_cands = ids[:n], lens[:n], cands[:n], n_cands[:n]
     return {"ids": np.ascontiguousarray(ids), "lens": np.ascontiguousarray(lens),
             "cands": np.ascontiguousarray(cands), "n_cands": np.ascontiguousarray(n_cands)}
+
+
+def images_inputs(cfg: Config, seed: int) -> Dict[str, object]:
+    """One typed question over cfg.n_images images.
+
+    images[i] = {"vis": [n_vis_i, H], "text_ids": [n_text]} (the instruction text is the
+    same for every image; n_vis_i = n_vis, or drawn in [vis_lo, n_vis]); seg_lens [n];
+    the question as a suffix batch of n identical rows (ids [n, S_max], lens, cands,
+    n_cands) with seg = [0, 1, ..., n-1]: row i asks it of image i.
+    """
+    n = cfg.n_images
+    rng = _rng(seed, STREAM_IMAGES, 0)
+    text = rng.integers(0, cfg.vocab, size=cfg.n_text).astype(np.int32)
+    nv = [cfg.n_vis if cfg.vis_lo <= 0 else int(rng.integers(cfg.vis_lo, cfg.n_vis + 1)) for _ in range(n)]
+    images = []
+    for i in range(n):
+        vis = _normal((nv[i], cfg.hidden), seed, STREAM_IMAGES, 1 + i, 1.0, 0.0, cfg.dtype) \
+            if nv[i] > 0 else np.zeros((0, cfg.hidden), np.float32)
+        images.append({"vis": vis, "text_ids": text.copy()})
+    q = _rng(seed, STREAM_IMAGES, 100000)
+    L = int(q.integers(cfg.len_lo, cfg.len_hi + 1))
+    ids = q.integers(0, cfg.vocab, size=cfg.s_max).astype(np.int32)      # junk past L
+    cands = q.choice(cfg.vocab, size=cfg.n_cands, replace=False).astype(np.int32)
+    suf = {"ids": np.ascontiguousarray(np.tile(ids, (n, 1))), "lens": np.full(n, L, np.int32),
+           "cands": np.ascontiguousarray(np.tile(cands, (n, 1))), "n_cands": np.full(n, cfg.n_cands, np.int32)}
+    return {"images": images, "seg_lens": np.array([v + cfg.n_text for v in nv], np.int32),
+            "seg": np.arange(n, dtype=np.int32), "suf": suf}
 
 
 def tree_inputs(cfg: Config, seed: int) -> Dict[str, np.ndarray]:

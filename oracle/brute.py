@@ -128,6 +128,16 @@ def score_suffixes(cfg, W, prefix, suf, skip=None):
     return out
 
 
+def score_segments(cfg, W, images, suf, seg):
+    """float64 out[b]: suffix b evaluated over the prefix of image seg[b] only."""
+    B, C = suf["cands"].shape
+    out = np.full((B, C), -np.inf)
+    for b in range(B):
+        one = {k: v[b:b + 1] for k, v in suf.items()}
+        out[b] = score_suffixes(cfg, W, images[int(seg[b])], one)[0]
+    return out
+
+
 def score_tree(cfg, W, prefix, tree, skip=None):
     """float64 flat tree scores: sum of the candidate tokens' full-vocab log-probs."""
     E = W.glob["embed"]

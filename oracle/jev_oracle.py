@@ -255,6 +255,22 @@ def score_suffixes(ws, cfg, prefix, suf, free_layers: bool = False,
     return (out, np.stack(lps)) if return_full else out
 
 
+def score_segments(ws, cfg, images, suf, seg) -> np.ndarray:
+    """One question over several images ("Ochevid Jev-VL 2B", One question, multiple
+    images): every image is encoded, the images' rows stay independent, and each image
+    gets its own answer.  Suffix b continues image seg[b] alone, so out[b] is the
+    single-prefix definition over that image's prefix: score_suffixes with
+    prefix = images[seg[b]] and the suffixes of that image."""
+    seg = np.asarray(seg)
+    B, C = suf["cands"].shape
+    out = np.full((B, C), -np.inf, dtype=F32)
+    for i, pre in enumerate(images):
+        sel = np.nonzero(seg == i)[0]
+        if len(sel):
+            out[sel] = score_suffixes(ws, cfg, pre, {k: v[sel] for k, v in suf.items()})
+    return out
+
+
 def _tree_sequences(tree):
     """Per (question, candidate): the fed ids stem ‖ w_0..w_{K-2} and the targets w."""
     Q, C, _ = tree["cand_tok"].shape

@@ -188,6 +188,50 @@ def test_score_validation_before_any_launch(model):
     J.jev_prefix_destroy(p)
 
 
+def test_segment_validation(model):
+    """Segmented prefixes (one question over several images): argument checks, and the
+    single-prefix calls refuse a store of several segments (no HIP call on these paths)."""
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    kv = _FakeDev(J.jev_prefix_bytes(m, 30))
+    for lens, code in (([], J.JEV_E_INVALID), ([4, -1], J.JEV_E_INVALID), ([1] * 65, J.JEV_E_UNSUPPORTED),
+                       ([20000, 20000], J.JEV_E_UNSUPPORTED)):
+        with pytest.raises(J.JevError) as e:
+            J.jev_prefix_create_segments(m, np.array(lens, np.int32), _FakeDev(1 << 40))
+        assert e.value.code == code, lens
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefix_create_segments(m, np.array([10, 60], np.int32), kv)   # 70 rows: a larger store
+    assert e.value.code == J.JEV_E_WORKSPACE
+    p = J.jev_prefix_create_segments(m, np.array([10, 0, 20], np.int32), kv)
+    ws, out = _FakeDev(1 << 30), _FakeDev(1 << 20)
+    ids = np.zeros((2, 4), np.int32)
+    lens = np.array([4, 2], np.int32)
+    cands = np.array([[1, 2], [3, 4]], np.int32)
+    nc = np.array([2, 2], np.int32)
+    with pytest.raises(J.JevError) as e:                      # single-prefix calls refuse it
+        J.jev_score_suffixes(p, ids, lens, cands, nc, out, ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID and "jev_score_segments" in J.jev_last_error()
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefill_prefix(p, _FakeDev(1), 10, np.zeros(20, np.int32), ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID
+    for seg in ([0, 3], [-1, 0]):                             # segment index out of range
+        with pytest.raises(J.JevError) as e:
+            J.jev_score_segments(p, np.array(seg, np.int32), ids, lens, cands, nc, out, ws, stream=0)
+        assert e.value.code == J.JEV_E_INVALID, seg
+    with pytest.raises(J.JevError) as e:                      # counts must fill every segment
+        J.jev_prefill_segments(p, _FakeDev(1), np.array([5, 0, 20], np.int32), np.zeros(5, np.int32),
+                               np.array([4, 0, 0], np.int32), ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID
+    with pytest.raises(J.JevError) as e:
+        J.jev_prefill_segments(p, _FakeDev(1), np.array([5, 0, 20], np.int32), np.full(5, 5000, np.int32),
+                               np.array([5, 0, 0], np.int32), ws, stream=0)
+    assert e.value.code == J.JEV_E_INVALID                    # text id >= V
+    J.jev_score_segments(p, np.zeros(0, np.int32), np.zeros((0, 4), np.int32), np.zeros(0, np.int32),
+                         np.zeros((0, 2), np.int32), np.zeros(0, np.int32), None, None, stream=0)   # B = 0
+    assert J.jev_get_stats(m)["launches"] == 0
+    J.jev_prefix_destroy(p)
+
+
 def test_launch_only_calls_need_staged_metadata(model):
     """The launch-only (graph-capturable) scoring calls refuse a workspace whose staged
     metadata is not this request's; nothing is launched (no HIP call on this path)."""

@@ -219,6 +219,37 @@ def test_skipping_every_block_is_textbook_readout():
 
 
 # ---------------------------------------------------------------- method invariants
+@pytest.mark.parametrize("seed", [0, 1])
+def test_segments_match_brute_force(seed):
+    """One question over several images (Ochevid, One question, multiple images): each
+    image's answer is the plain definition over that image's prefix alone, checked against
+    the float64 brute force; images of different sizes, several suffixes per image in a
+    shuffled order, and an image with no suffix."""
+    cfg = S.CONFIGS["mi1"]
+    src = S.WeightSource(cfg, seed)
+    inp = S.images_inputs(cfg, seed)
+    images = inp["images"] + [S.images_inputs(cfg, seed + 5)["images"][0]]
+    suf = S.suffix_inputs(_small("c1", n_suffix=5, fixed_lens=(3, 8, 1, 6, 5)), seed)
+    seg = np.array([2, 0, 2, 1, 0], np.int32)       # image 3 gets no suffix
+    got = O.score_segments(src, cfg, images, suf, seg)
+    ref = brute.score_segments(cfg, src, images, suf, seg)
+    np.testing.assert_allclose(got, ref, atol=2e-5)
+    # the one-question layout of the generator: the same question of every image
+    got1 = O.score_segments(src, cfg, inp["images"], inp["suf"], inp["seg"])
+    ref1 = brute.score_segments(cfg, src, inp["images"], inp["suf"], inp["seg"])
+    np.testing.assert_allclose(got1, ref1, atol=2e-5)
+    assert np.ptp(got1[:, 0]) > 1e-4                   # different images, different answers
+
+
+def test_one_segment_is_the_single_prefix_call():
+    cfg = S.CONFIGS["mi1"]
+    src = S.WeightSource(cfg, 0)
+    inp = S.images_inputs(cfg, 0)
+    suf = S.suffix_inputs(_small("c1", n_suffix=3, fixed_lens=(2, 8, 4)), 0)
+    np.testing.assert_array_equal(O.score_segments(src, cfg, inp["images"][:1], suf, np.zeros(3, np.int32)),
+                                  O.score_suffixes(src, cfg, inp["images"][0], suf))
+
+
 @pytest.fixture(scope="module")
 def m2_small():
     cfg = _small("m2", hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128, mlp=256, vocab=512)

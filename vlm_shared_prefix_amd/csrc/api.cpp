@@ -69,10 +69,12 @@ struct jev_model {
 
 struct jev_prefix {
   jev_model* m;
-  int P;
+  int P;        // rows of the store: the sum of the segments
   int Pc;
   void* kv;
   size_t kv_bytes;
+  // independent prefixes stored back to back (one per image); a plain prefix is one segment
+  std::vector<int> seg_off, seg_len;
 };
 
 static thread_local std::string g_err;
@@ -244,6 +246,28 @@ extern "C" jev_status jev_prefix_create(jev_model* m, int32_t prefix_len, void* 
   p->Pc = round64(prefix_len);
   p->kv = kv_buf;
   p->kv_bytes = kv_bytes;
+  p->seg_off = {0};
+  p->seg_len = {prefix_len};
+  *out = p;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_prefix_create_segments(jev_model* m, const int32_t* seg_lens, int32_t n_seg, void* kv_buf,
+                                                 size_t kv_bytes, jev_prefix** out) {
+  if (!m || !out || !seg_lens) return fail(JEV_E_INVALID, "null argument");
+  if (n_seg < 1) return fail(JEV_E_INVALID, "n_seg must be >= 1");
+  if (n_seg > jevp::kMaxSegments) return fail(JEV_E_UNSUPPORTED, "more than 64 segments");
+  long total = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    if (seg_lens[i] < 0) return fail(JEV_E_INVALID, "seg_lens[" + std::to_string(i) + "] < 0");
+    total += seg_lens[i];
+  }
+  if (total > jevp::kMaxPrefix) return fail(JEV_E_UNSUPPORTED, "segments hold more than 32768 rows");
+  jev_prefix* p = nullptr;
+  if (jev_status st = jev_prefix_create(m, (int32_t)total, kv_buf, kv_bytes, &p)) return st;
+  p->seg_off.assign(n_seg, 0);
+  p->seg_len.assign(seg_lens, seg_lens + n_seg);
+  for (int i = 1; i < n_seg; ++i) p->seg_off[i] = p->seg_off[i - 1] + seg_lens[i - 1];
   *out = p;
   return JEV_OK;
 }
@@ -258,7 +282,7 @@ constexpr size_t kGemmPartFloats = 16ull << 20;        // bound of split-K parti
 
 struct Layout {
   // metadata (staged from the host in one copy)
-  size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, meta_end;
+  size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, pseg, ptile, meta_end;
   // float buffers
   size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, logits, rope;
   size_t total;
@@ -300,6 +324,8 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.tgt_tok = take(4ull * NT);
   L.out_n = take(4ull * NG);
   L.mask = take(has_mask ? 8ull * T : 0);
+  L.pseg = take(8ull * T);
+  L.ptile = take(16ull * ((c.n_q_heads / c.n_kv_heads * (size_t)T + 127) / 128));
   L.meta_end = o;
   const int HqD = c.n_q_heads * c.head_dim;
   const int wide = std::max(std::max(c.hidden, HqD), c.mlp);
@@ -383,7 +409,8 @@ struct Forward {
   Mode mode;
   Profiler* prof;
   int launches = 0;
-  double own_pairs = 0;   // (row, own visible key) pairs of the attention
+  double own_pairs = 0;      // (row, own visible key) pairs of the attention
+  double prefix_pairs = 0;   // (row, prefix key) pairs
 
   Forward(const jev_prefix* p, const Plan& pl, const Layout& lay, void* w, hipStream_t st, Mode md)
       : pf(p), m(p->m), c(p->m->cfg), plan(pl), L(lay), ws(w), s(st), mode(md),
@@ -391,6 +418,12 @@ struct Forward {
     for (int t = 0; t < plan.T; ++t)
       own_pairs += plan.mask.empty() ? (double)(t - plan.seq_start[t] + 1)
                                      : (double)__builtin_popcountll(plan.mask[t]);
+    if (mode != Mode::Prefill) {
+      if (plan.pseg.empty())
+        prefix_pairs = (double)plan.T * pf->P;
+      else
+        for (int t = 0; t < plan.T; ++t) prefix_pairs += plan.pseg[2 * t + 1] - plan.pseg[2 * t];
+    }
   }
 
   // Launch one kernel through `fn`, timing it with events when profiling is on.
@@ -470,7 +503,7 @@ struct Forward {
   }
 
   // Forward of a bf16 model: every GEMM consumer fused with the split-K reduction.
-  jev_status run_bf16(const void* vis, int n_vis) {
+  jev_status run_bf16(const void* vis) {
     const int T = plan.T;
     const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
     const int HqD = Hq * D, NQKV = nqkv(c);
@@ -498,7 +531,7 @@ struct Forward {
     const double rowbytes = 4.0 * T * H;
 
     if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 1.5,
-                              [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
+                              [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, x, s); }))
       return st;
     const std::vector<int> layers = run_layers(m, mode);
     if (layers.empty()) return JEV_OK;
@@ -514,8 +547,10 @@ struct Forward {
 
     // attention splits: about one block per compute unit (partials merged when > 1)
     const int own_tiles = attn_own_tiles(plan.seq_start.data(), T, Hq / Hkv);
-    const int n_split = attn_splits(T, Hq / Hkv, Hkv, P, own_tiles);
-    const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
+    const int n_split = attn_splits(T, Hq / Hkv, Hkv, plan.seg_keys >= 0 ? plan.seg_keys : P, own_tiles);
+    const int2* pseg = plan.pseg.empty() ? nullptr : at<int2>(ws, L.pseg);
+    const int4* ptile = plan.pseg.empty() ? nullptr : at<int4>(ws, L.ptile);
+    const double attn_flops = 4.0 * D * Hq * (prefix_pairs + own_pairs);
     const double attn_bytes = 2.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + 2.0 * T * HqD) + 4.0 * T * HqD;
 
     for (size_t li = 0; li < layers.size(); ++li) {
@@ -562,6 +597,7 @@ struct Forward {
       a.vts = static_cast<const _Float16*>(vdst);
       a.lds = kld;
       a.seq_start = seq_start; a.mask = mask;
+      a.pseg = pseg; a.ptile = ptile;
       a.n_split = n_split;
       a.own_tiles = own_tiles;
       a.o_part = at<float>(ws, L.o_part);
@@ -607,10 +643,10 @@ struct Forward {
     return JEV_OK;
   }
 
-  jev_status run(const void* vis, int n_vis) { return is_bf16(m) ? run_bf16(vis, n_vis) : run_f32(vis, n_vis); }
+  jev_status run(const void* vis) { return is_bf16(m) ? run_bf16(vis) : run_f32(vis); }
 
   // float32 models: every step in float32 (VALU GEMMs, one-thread-per-row attention).
-  jev_status run_f32(const void* vis, int n_vis) {
+  jev_status run_f32(const void* vis) {
     const int T = plan.T;
     const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.mlp;
     const int HqD = Hq * D, NQKV = nqkv(c);
@@ -628,9 +664,10 @@ struct Forward {
     const double rowbytes = 4.0 * T * H;
 
     if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 2.0,
-                              [&] { return launch_embed(false, m->w.embed, tok, T, H, vis, n_vis, x, s); }))
+                              [&] { return launch_embed(false, m->w.embed, tok, T, H, vis, x, s); }))
       return st;
-    const double attn_flops = 4.0 * D * Hq * ((double)T * P + own_pairs);
+    const int2* pseg = plan.pseg.empty() ? nullptr : at<int2>(ws, L.pseg);
+    const double attn_flops = 4.0 * D * Hq * (prefix_pairs + own_pairs);
     const double attn_bytes = 4.0 * (2.0 * Hkv * P * D + 2.0 * Hkv * T * D + (double)T * HqD) + 4.0 * T * HqD;
 
     for (int l : run_layers(m, mode)) {
@@ -677,6 +714,7 @@ struct Forward {
       a.vts = static_cast<const float*>(vdst);
       a.lds = kld;
       a.seq_start = seq_start; a.mask = mask;
+      a.pseg = pseg;
       a.scale = (float)(1.0 / std::sqrt((double)D));
       a.o = act;
       if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f32(a, D, s); })) return st;
@@ -760,6 +798,8 @@ jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hi
   put(L.tgt_tok, p.tgt_tok.data(), 4 * p.tgt_tok.size());
   put(L.out_n, p.out_n.data(), 4 * p.out_n.size());
   put(L.mask, p.mask.data(), 8 * p.mask.size());
+  put(L.pseg, p.pseg.data(), 4 * p.pseg.size());
+  put(L.ptile, p.ptile.data(), 4 * p.ptile.size());
   const uint64_t h = meta_digest(buf);
   std::lock_guard<std::mutex> lock(m->staged_mu);
   if (!stage) {
@@ -777,26 +817,24 @@ jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hi
 // ---------------------------------------------------------------------------
 // entry points
 // ---------------------------------------------------------------------------
-extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, int32_t n_vis,
-                                         const int32_t* text_ids, int32_t n_text, void* ws, size_t ws_bytes,
-                                         void* stream) {
-  if (!p) return fail(JEV_E_INVALID, "null prefix");
+// The causal forward over every row of the store: segment i's rows sit at positions 0..P_i-1
+// and see only the rows of their own segment (sequence start = the segment's first row).
+// Row sources: tok >= 0 an embedding row, tok = -1 - j row j of vis.
+static jev_status prefill_rows(jev_prefix* p, const void* vis, std::vector<int32_t> tok, void* ws, size_t ws_bytes,
+                               void* stream) {
   const jev_model* m = p->m;
-  if (n_vis < 0 || n_text < 0) return fail(JEV_E_INVALID, "negative counts");
-  if (n_vis + n_text != p->P) return fail(JEV_E_INVALID, "n_vis + n_text must equal prefix_len");
-  if (n_vis > 0 && !vis_embeds) return fail(JEV_E_INVALID, "null vis_embeds");
-  if (n_text > 0 && !text_ids) return fail(JEV_E_INVALID, "null text_ids");
-  for (int i = 0; i < n_text; ++i)
-    if (text_ids[i] < 0 || text_ids[i] >= m->cfg.vocab) return fail(JEV_E_INVALID, "text id out of range");
   if (p->P == 0 || m->cfg.n_layers == 0) return JEV_OK;
   Plan plan;
   plan.T = p->P;
-  plan.n_groups = 1;
-  plan.tok.assign(p->P, 0);
-  for (int i = 0; i < n_text; ++i) plan.tok[n_vis + i] = text_ids[i];
+  plan.n_groups = (int)p->seg_len.size();
+  plan.tok = std::move(tok);
   plan.pos.resize(p->P);
-  for (int i = 0; i < p->P; ++i) plan.pos[i] = i;
-  plan.seq_start.assign(p->P, 0);
+  plan.seq_start.resize(p->P);
+  for (size_t i = 0; i < p->seg_len.size(); ++i)
+    for (int j = 0; j < p->seg_len[i]; ++j) {
+      plan.pos[p->seg_off[i] + j] = j;
+      plan.seq_start[p->seg_off[i] + j] = p->seg_off[i];
+    }
   const Layout L = make_layout(m, plan.T, 0, 0, 1, false, false, 0);
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
   if (ws_bytes < L.total)
@@ -804,23 +842,93 @@ extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (jev_status st = stage_meta(p->m, plan, L, ws, s, true)) return st;
   Forward f(p, plan, L, ws, s, Mode::Prefill);
-  jev_status st = f.run(vis_embeds, n_vis);
+  jev_status st = f.run(vis);
   p->m->launches += f.launches;
   if (st) return st;
   p->m->prefills++;
   return JEV_OK;
 }
 
-static jev_status score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
-                                 int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands, int32_t C_max,
-                                 float* out_logp, void* ws, size_t ws_bytes, void* stream, bool stage) {
+extern "C" jev_status jev_prefill_prefix(jev_prefix* p, const void* vis_embeds, int32_t n_vis,
+                                         const int32_t* text_ids, int32_t n_text, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  if (!p) return fail(JEV_E_INVALID, "null prefix");
+  const jev_model* m = p->m;
+  if (p->seg_len.size() != 1) return fail(JEV_E_INVALID, "segmented prefix: use jev_prefill_segments");
+  if (n_vis < 0 || n_text < 0) return fail(JEV_E_INVALID, "negative counts");
+  if (n_vis + n_text != p->P) return fail(JEV_E_INVALID, "n_vis + n_text must equal prefix_len");
+  if (n_vis > 0 && !vis_embeds) return fail(JEV_E_INVALID, "null vis_embeds");
+  if (n_text > 0 && !text_ids) return fail(JEV_E_INVALID, "null text_ids");
+  for (int i = 0; i < n_text; ++i)
+    if (text_ids[i] < 0 || text_ids[i] >= m->cfg.vocab) return fail(JEV_E_INVALID, "text id out of range");
+  std::vector<int32_t> tok(p->P);
+  for (int i = 0; i < n_vis; ++i) tok[i] = -1 - i;
+  for (int i = 0; i < n_text; ++i) tok[n_vis + i] = text_ids[i];
+  return prefill_rows(p, vis_embeds, std::move(tok), ws, ws_bytes, stream);
+}
+
+extern "C" jev_status jev_prefill_segments(jev_prefix* p, const void* vis_embeds, const int32_t* n_vis,
+                                           const int32_t* text_ids, const int32_t* n_text, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  if (!p) return fail(JEV_E_INVALID, "null prefix");
+  const jev_model* m = p->m;
+  const int n = (int)p->seg_len.size();
+  if (!n_vis || !n_text) return fail(JEV_E_INVALID, "null n_vis / n_text");
+  long nv = 0, nt = 0;
+  for (int i = 0; i < n; ++i) {
+    if (n_vis[i] < 0 || n_text[i] < 0) return fail(JEV_E_INVALID, "negative counts");
+    if (n_vis[i] + n_text[i] != p->seg_len[i])
+      return fail(JEV_E_INVALID, "n_vis[" + std::to_string(i) + "] + n_text[" + std::to_string(i) +
+                                     "] must equal the segment's length");
+    nv += n_vis[i];
+    nt += n_text[i];
+  }
+  if (nv > 0 && !vis_embeds) return fail(JEV_E_INVALID, "null vis_embeds");
+  if (nt > 0 && !text_ids) return fail(JEV_E_INVALID, "null text_ids");
+  for (long i = 0; i < nt; ++i)
+    if (text_ids[i] < 0 || text_ids[i] >= m->cfg.vocab) return fail(JEV_E_INVALID, "text id out of range");
+  std::vector<int32_t> tok(p->P);
+  long vi = 0, ti = 0;
+  for (int i = 0; i < n; ++i) {
+    int r = p->seg_off[i];
+    for (int j = 0; j < n_vis[i]; ++j) tok[r++] = (int32_t)(-1 - vi++);
+    for (int j = 0; j < n_text[i]; ++j) tok[r++] = text_ids[ti++];
+  }
+  return prefill_rows(p, vis_embeds, std::move(tok), ws, ws_bytes, stream);
+}
+
+// segmented == false: every suffix over the one prefix.  Otherwise suffix b continues
+// segment seg[b] of a segmented store: positions P_seg + j, prefix keys the segment's rows only.
+static jev_status score_suffixes(const jev_prefix* p, bool segmented, const int32_t* seg, const int32_t* ids,
+                                 const int32_t* lens, int32_t B, int32_t S_max, const int32_t* cand_ids,
+                                 const int32_t* n_cands, int32_t C_max, float* out_logp, void* ws, size_t ws_bytes,
+                                 void* stream, bool stage) {
   if (!p) return fail(JEV_E_INVALID, "null prefix");
   jev_model* m = p->m;
+  if (!segmented && p->seg_len.size() != 1) return fail(JEV_E_INVALID, "segmented prefix: use jev_score_segments");
   Plan plan;
-  Status st = jevp::plan_suffixes(p->P, m->cfg.vocab, ids, lens, B, S_max, cand_ids, n_cands, C_max, &plan);
+  Status st = jevp::plan_suffixes(segmented ? 0 : p->P, m->cfg.vocab, ids, lens, B, S_max, cand_ids, n_cands, C_max,
+                                  &plan);
   if (!st.ok()) return fail(st.code, st.msg);
   if (B == 0) return JEV_OK;
   if (!out_logp) return fail(JEV_E_INVALID, "null out_logp");
+  if (segmented) {
+    if (!seg) return fail(JEV_E_INVALID, "null seg");
+    const int n = (int)p->seg_len.size();
+    for (int b = 0; b < B; ++b)
+      if (seg[b] < 0 || seg[b] >= n) return fail(JEV_E_INVALID, "seg[" + std::to_string(b) + "] out of range");
+    plan.pseg.resize(2 * (size_t)plan.T);
+    for (int b = 0, row = 0; b < B; ++b)
+      for (int j = 0; j < lens[b]; ++j, ++row) {
+        const int off = p->seg_off[seg[b]], len = p->seg_len[seg[b]];
+        plan.pos[row] = len + j;
+        plan.pseg[2 * row] = off;
+        plan.pseg[2 * row + 1] = off + len;
+      }
+    const int G = m->cfg.n_q_heads / m->cfg.n_kv_heads;
+    plan.ptile.resize(4 * (((size_t)G * plan.T + 127) / 128));
+    plan.seg_keys = 64 * attn_seg_tiles(plan.pseg.data(), plan.T, G, plan.ptile.data());
+  }
   const Layout L = make_layout(m, plan.T, (int)plan.read_rows.size(), (int)plan.tgt_tok.size(),
                                (int)plan.out_n.size(), false, false, p->P);
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
@@ -829,7 +937,7 @@ static jev_status score_suffixes(const jev_prefix* p, const int32_t* ids, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (jev_status e = stage_meta(m, plan, L, ws, s, stage)) return e;
   Forward f(p, plan, L, ws, s, Mode::Score);
-  jev_status e = f.run(nullptr, 0);
+  jev_status e = f.run(nullptr);
   if (!e) e = f.readout(out_logp, nullptr);
   m->launches += f.launches;
   if (e) return e;
@@ -841,14 +949,24 @@ static jev_status score_suffixes(const jev_prefix* p, const int32_t* ids, const 
 extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids, const int32_t* lens, int32_t B,
                                          int32_t S_max, const int32_t* cand_ids, const int32_t* n_cands,
                                          int32_t C_max, float* out_logp, void* ws, size_t ws_bytes, void* stream) {
-  return score_suffixes(p, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes, stream, true);
+  return score_suffixes(p, false, nullptr, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes,
+                        stream, true);
+}
+
+extern "C" jev_status jev_score_segments(const jev_prefix* p, const int32_t* seg, const int32_t* ids,
+                                         const int32_t* lens, int32_t B, int32_t S_max, const int32_t* cand_ids,
+                                         const int32_t* n_cands, int32_t C_max, float* out_logp, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  return score_suffixes(p, true, seg, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes, stream,
+                        true);
 }
 
 extern "C" jev_status jev_score_suffixes_launch(const jev_prefix* p, const int32_t* ids, const int32_t* lens,
                                                 int32_t B, int32_t S_max, const int32_t* cand_ids,
                                                 const int32_t* n_cands, int32_t C_max, float* out_logp, void* ws,
                                                 size_t ws_bytes, void* stream) {
-  return score_suffixes(p, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes, stream, false);
+  return score_suffixes(p, false, nullptr, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes,
+                        stream, false);
 }
 
 static jev_status score_tree(const jev_prefix* p, const int32_t* stem_ids, const int32_t* stem_lens, int32_t Q,
@@ -857,6 +975,7 @@ static jev_status score_tree(const jev_prefix* p, const int32_t* stem_ids, const
                              size_t ws_bytes, void* stream, bool stage) {
   if (!p) return fail(JEV_E_INVALID, "null prefix");
   jev_model* m = p->m;
+  if (p->seg_len.size() != 1) return fail(JEV_E_INVALID, "segmented prefix: jev_score_tree takes one prefix");
   Plan plan;
   Status st = jevp::plan_tree(p->P, m->cfg.vocab, stem_ids, stem_lens, Q, S_max, cand_tok, cand_lens, n_cands,
                               C_max, K_max, mode, &plan);
@@ -874,7 +993,7 @@ static jev_status score_tree(const jev_prefix* p, const int32_t* stem_ids, const
   Forward f(p, plan, L, ws, s, Mode::Tree);
   f.tree_C = C_max;
   f.tree_K = K_max;
-  jev_status e = f.run(nullptr, 0);
+  jev_status e = f.run(nullptr);
   if (!e) e = f.readout(out_score, out_norm);
   m->launches += f.launches;
   if (e) return e;

@@ -42,6 +42,11 @@ struct AttnArgs {
   int lds;
   const int* seq_start;    // [T] first row of the row's sequence / group
   const uint64_t* mask;    // [T] visibility over the group (nullptr: causal)
+  // segmented prefixes (nullptr: every row sees prefix keys [0, P)): the row's prefix keys
+  // [x, y), and per 128-row tile (attn_seg_tiles) its prefix key tiles [x, y) and the keys
+  // [z, w) every row of the tile sees
+  const int2* pseg;        // [T]
+  const int4* ptile;       // [ceil(G*T / 128)]
   int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
   int own_tiles;           // bound on any row tile's own-key tiles (attn_own_tiles); the splits
                            // divide ceil(P/64) + own_tiles tiles
@@ -65,12 +70,14 @@ struct AttnArgsF {
   int lds;
   const int* seq_start;
   const uint64_t* mask;
+  const int2* pseg;        // [T] the row's prefix keys [x, y) (nullptr: [0, P))
   float scale;             // 1 / sqrt(D)
   float* o;                // [T][Hq*D]
 };
 
-hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, int n_vis,
-                        float* x, hipStream_t s);
+// Row t: E[tok[t]] for tok[t] >= 0, vis[-1 - tok[t]] otherwise.
+hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, float* x,
+                        hipStream_t s);
 // y (float32) and/or yh/yl (bfloat16 hi/lo planes) may be null.
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
                           float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
@@ -131,6 +138,11 @@ int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
 // Own-key tiles (64 keys) of the 128-row tile that needs the most, from the host copy of
 // the rows' sequence starts.
 int attn_own_tiles(const int* seq_start, int T, int G);
+// Segmented prefixes: from the rows' prefix key ranges pseg (host, [T] pairs), per 128-row
+// tile of the G*T query rows its prefix key tiles [x, y) (the hull of its rows' ranges) and
+// the keys [z, w) every one of its rows sees (z >= w when there are none); returns the largest
+// tile count y - x.
+int attn_seg_tiles(const int* pseg, int T, int G, int* ptile);
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, bool f16out, hipStream_t s);

@@ -7,6 +7,7 @@
 // and attention runs on float16 MFMA with float32 softmax; norms, softmax
 // merge and readout are float32.  float32 models run every step in float32.
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 #include <math.h>
 
@@ -61,15 +62,16 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 }
 
 // ----------------------------------------------------------------------------
-// K1: embedding rows.  Row t < n_vis copies vis[t]; other rows gather E[tok[t]].
+// K1: embedding rows.  Row t with tok[t] >= 0 gathers E[tok[t]]; tok[t] = -1 - j copies
+// the given embedding row vis[j] (a visual token).
 // ----------------------------------------------------------------------------
 template <typename WT>
 __global__ void __launch_bounds__(256) embed_rows(const WT* __restrict__ E, const int* __restrict__ tok, int T,
-                                                  int H, const WT* __restrict__ vis, int n_vis,
-                                                  float* __restrict__ x) {
+                                                  int H, const WT* __restrict__ vis, float* __restrict__ x) {
   const int t = blockIdx.x;
   if (t >= T) return;
-  const WT* src = (t < n_vis) ? vis + (size_t)t * H : E + (size_t)tok[t] * H;
+  const int k = tok[t];
+  const WT* src = (k < 0) ? vis + (size_t)(-1 - k) * H : E + (size_t)k * H;
   float* dst = x + (size_t)t * H;
   for (int i = threadIdx.x; i < H; i += 256) dst[i] = ldw(src, i);
 }
@@ -697,17 +699,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int t = rc / G;
   const int hq = hk * G + rc % G;
 
+  // Prefix key tiles of this row tile: [ptb, ptb + ntp), every one of them visible in full to
+  // all of its rows when inside [vis_lo, vis_hi).  One shared prefix: all ceil(P/64) tiles,
+  // visible below P.  Segmented prefixes: the hull of the rows' segments (host table).
+  const int4 pt = a.ptile ? a.ptile[x] : make_int4(0, (a.P + AT_BK - 1) / AT_BK, 0, a.P);
+  const int ptb = pt.x, ntp = pt.y - pt.x, vis_lo = pt.z, vis_hi = pt.w;
   // The splits divide ntp + own_tiles key tiles (own_tiles: the host's bound on any row
   // tile's own-key tiles), so a block whose range starts on a prefix tile issues that
   // tile's loads before the sequence starts it depends on for the rest have arrived.
-  const int ntp = (a.P + AT_BK - 1) / AT_BK;
   const int nt_u = ntp + a.own_tiles;
   const int vb = (int)(((long)z * nt_u) / ns), ve_u = (int)(((long)(z + 1) * nt_u) / ns);
   const bool early = vb < ntp && vb < ve_u;
   if (early) {
     const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
     const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
-    const int k0 = vb * AT_BK;
+    const int k0 = (ptb + vb) * AT_BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = i * 256 + tid;
@@ -730,6 +736,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int my_start = a.seq_start[t];
   const bool use_mask = a.mask != nullptr;
   const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
+  const int2 my_pk = a.pseg ? a.pseg[t] : make_int2(0, a.P);   // the row's prefix keys
 
   // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
   // of q, which would shift every score of the row coherently, stays out.
@@ -756,7 +763,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     AttnTile s;
     if (v < ntp) {
       s.K = a.kp + (size_t)hk * a.ldp * 128; s.V = a.vtp + (size_t)hk * 128 * a.ldp; s.ld = a.ldp;
-      s.k0 = v * AT_BK; s.ke = a.P; s.own = false;
+      s.k0 = (ptb + v) * AT_BK; s.ke = a.P; s.own = false;
     } else {
       s.K = a.ks + (size_t)hk * a.lds * 128; s.V = a.vts + (size_t)hk * 128 * a.lds; s.ld = a.lds;
       s.k0 = own0 + (v - ntp) * AT_BK; s.ke = own_end; s.own = true;
@@ -811,13 +818,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qlo[c], s[1], 0, 0, 0);
     }
     // Masks only where some row of the block does not see the whole tile (uniform test):
-    // a partial last prefix tile, and own-key tiles not fully visible to every row.
+    // a prefix tile reaching outside [vis_lo, vis_hi) (the partial last tile, segment
+    // edges), and own-key tiles not fully visible to every row.
     const AttnTile ts = tile(vb + i);
     const bool need = ts.own ? (use_mask || ts.k0 < max_start || ts.k0 + AT_BK > t_first + 1)
-                             : (ts.k0 + AT_BK > ts.ke);
+                             : (ts.k0 < vis_lo || ts.k0 + AT_BK > vis_hi);
     if (need) {
-      const int lo = ts.own ? my_start : 0;
-      const int hi = ts.own ? t + 1 : ts.ke;
+      const int lo = ts.own ? my_start : my_pk.x;
+      const int hi = ts.own ? t + 1 : my_pk.y;
       const uint64_t mm = (ts.own && use_mask) ? my_mask : ~0ull;
       const int base = ts.k0 + 8 * hl;
 #pragma unroll
@@ -1192,7 +1200,8 @@ __global__ void __launch_bounds__(64) attn_fwd_f32(AttnArgsF a) {
   };
   const float* Kp = a.kp + (size_t)hk * a.ldp * D;
   const float* Vp = a.vtp + (size_t)hk * D * a.ldp;
-  for (int j = 0; j < a.P; ++j) visit(Kp + (size_t)j * D, Vp + j, a.ldp);
+  const int pb = a.pseg ? a.pseg[t].x : 0, pe = a.pseg ? a.pseg[t].y : a.P;
+  for (int j = pb; j < pe; ++j) visit(Kp + (size_t)j * D, Vp + j, a.ldp);
   const float* Ks = a.ks + (size_t)hk * a.lds * D;
   const float* Vs = a.vts + (size_t)hk * D * a.lds;
   const int st = a.seq_start[t];
@@ -1330,13 +1339,13 @@ using namespace jevk;
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, int n_vis,
-                        float* x, hipStream_t s) {
+hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, float* x,
+                        hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (bf16)
-    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, n_vis, x);
+    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, x);
   else
-    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, n_vis, x);
+    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, x);
   return hipGetLastError();
 }
 
@@ -1558,6 +1567,31 @@ int attn_own_tiles(const int* seq_start, int T, int G) {
   for (int r0 = 0; r0 < R; r0 += AT_BR) {
     const int t_first = r0 / G, t_last = std::min(R - 1, r0 + AT_BR - 1) / G;
     mx = std::max(mx, cdiv(t_last + 1 - (seq_start[t_first] & ~7), AT_BK));
+  }
+  return mx;
+}
+
+int attn_seg_tiles(const int* pseg, int T, int G, int* ptile) {
+  const int R = G * T;
+  int mx = 0, x = 0;
+  for (int r0 = 0; r0 < R; r0 += AT_BR, ++x) {
+    const int t_first = r0 / G, t_last = std::min(R - 1, r0 + AT_BR - 1) / G;
+    int lo = INT_MAX, hi = INT_MIN, vlo = INT_MIN, vhi = INT_MAX;
+    for (int t = t_first; t <= t_last; ++t) {
+      const int b = pseg[2 * t], e = pseg[2 * t + 1];
+      if (e > b) {
+        lo = std::min(lo, b);
+        hi = std::max(hi, e);
+      }
+      vlo = std::max(vlo, b);
+      vhi = std::min(vhi, e);
+    }
+    const int tb = (hi > lo) ? lo / AT_BK : 0, te = (hi > lo) ? cdiv(hi, AT_BK) : 0;
+    ptile[4 * x] = tb;
+    ptile[4 * x + 1] = te;
+    ptile[4 * x + 2] = vlo;
+    ptile[4 * x + 3] = vhi;
+    mx = std::max(mx, te - tb);
   }
   return mx;
 }

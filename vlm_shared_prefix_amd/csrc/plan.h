@@ -25,6 +25,12 @@ struct Plan {
   std::vector<int32_t> tgt_ridx;      // [NT] target -> index into read_rows
   std::vector<int32_t> tgt_tok;       // [NT] target token (-1: unused slot)
   std::vector<int32_t> out_n;         // [B or Q] valid candidates per output row
+  // segmented prefixes (empty otherwise): per row its prefix keys [2t, 2t+1]; per 128-row
+  // attention tile its prefix key tiles and fully visible keys (4 ints); seg_keys: 64 x the
+  // largest tile count (the attention split rule's prefix length)
+  std::vector<int32_t> pseg;
+  std::vector<int32_t> ptile;
+  int seg_keys = -1;
 };
 
 // Validation result.
@@ -47,5 +53,6 @@ constexpr int kMaxCands = 64;
 constexpr int kMaxRows = 65536;
 constexpr int kMaxGroupRows = 64;
 constexpr int kMaxPrefix = 32768;
+constexpr int kMaxSegments = 64;   // independent prefixes in one segmented store
 
 }  // namespace jevp

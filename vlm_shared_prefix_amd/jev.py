@@ -73,6 +73,10 @@ _sig = {
     "jev_prefix_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_prefix_create": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, C.POINTER(_vp)]),
     "jev_prefix_destroy": (None, [_vp]),
+    "jev_prefix_create_segments": (C.c_int32, [_vp, _i32p, C.c_int32, _vp, C.c_size_t, C.POINTER(_vp)]),
+    "jev_prefill_segments": (C.c_int32, [_vp, _vp, _i32p, _i32p, _i32p, _vp, C.c_size_t, _vp]),
+    "jev_score_segments": (C.c_int32, [_vp, _i32p, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32,
+                                       _vp, _vp, C.c_size_t, _vp]),
     "jev_workspace_bytes": (C.c_size_t, [_vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "jev_prefill_prefix": (C.c_int32, [_vp, _vp, C.c_int32, _i32p, C.c_int32, _vp, C.c_size_t, _vp]),
     "jev_score_suffixes": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32,
@@ -237,6 +241,28 @@ def jev_score_suffixes_launch(prefix: int, ids, lens, cand_ids, n_cands, out_log
     jev_score_suffixes call with the same arguments staged); capturable into a HIP graph."""
     _score_suffixes(_lib.jev_score_suffixes_launch, "jev_score_suffixes_launch", prefix, ids, lens, cand_ids,
                     n_cands, out_logp, ws, stream)
+
+
+def jev_prefix_create_segments(model: int, seg_lens, kv_buf) -> int:
+    sl = _i32(seg_lens)
+    out = _vp()
+    _check(_lib.jev_prefix_create_segments(model, _ptr_i32(sl), len(sl), _dptr(kv_buf),
+                                           kv_buf.numel() * kv_buf.element_size() if kv_buf is not None else 0,
+                                           C.byref(out)), "jev_prefix_create_segments")
+    return out.value
+
+
+def jev_prefill_segments(prefix: int, vis_embeds, n_vis, text_ids, n_text, ws, stream=None) -> None:
+    nv, ti, nt = _i32(n_vis), _i32(text_ids), _i32(n_text)
+    _check(_lib.jev_prefill_segments(prefix, _dptr(vis_embeds), _ptr_i32(nv), _ptr_i32(ti), _ptr_i32(nt),
+                                     _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "jev_prefill_segments")
+
+
+def jev_score_segments(prefix: int, seg, ids, lens, cand_ids, n_cands, out_logp, ws, stream=None) -> None:
+    sg = _i32(seg)
+    _score_suffixes(lambda p, *a: _lib.jev_score_segments(p, _ptr_i32(sg), *a), "jev_score_segments", prefix,
+                    ids, lens, cand_ids, n_cands, out_logp, ws, stream)
 
 
 def _tree_args(stem_ids, stem_lens, cand_tok, cand_lens, n_cands):

@@ -124,6 +124,35 @@ class Session:
         ws = self.workspace(J.jev_workspace_bytes(self.model, P, max(P, 1), 1, 0))
         J.jev_prefill_prefix(self.prefix, self.vis, int(vis.shape[0]), text_ids, ws, stream)
 
+    def prefill_segments(self, images, stream=None):
+        """One segmented prefix holding every image's prefix (images[i]: "vis", "text_ids"),
+        prefilled in one batched forward."""
+        if self.prefix:
+            J.jev_prefix_destroy(self.prefix)
+            self.prefix = None
+        n_vis = np.array([im["vis"].shape[0] for im in images], np.int32)
+        n_text = np.array([len(im["text_ids"]) for im in images], np.int32)
+        seg_lens = n_vis + n_text
+        P = int(seg_lens.sum())
+        self.kv = torch.empty(max(J.jev_prefix_bytes(self.model, P), 256), dtype=torch.uint8, device=self.device)
+        self.prefix = J.jev_prefix_create_segments(self.model, seg_lens, self.kv)
+        self.P = P
+        vis = np.concatenate([im["vis"] for im in images], axis=0)
+        self.vis = to_device(vis, self.cfg.dtype, self.device) if vis.shape[0] else None
+        text = np.concatenate([np.asarray(im["text_ids"], np.int32) for im in images])
+        ws = self.workspace(J.jev_workspace_bytes(self.model, P, max(P, 1), 1, 0))
+        J.jev_prefill_segments(self.prefix, self.vis, n_vis, text, n_text, ws, stream)
+
+    def score_segments(self, seg, suf, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """Suffix b continues segment seg[b] of the segmented prefix."""
+        B, C = suf["cands"].shape
+        if out is None:
+            out = torch.empty((B, C), dtype=torch.float32, device=self.device)
+        ws = self.workspace(self.suffix_ws_bytes(suf))
+        J.jev_score_segments(self.prefix, seg, suf["ids"], suf["lens"], suf["cands"], suf["n_cands"], out, ws,
+                             stream)
+        return out
+
     def suffix_ws_bytes(self, suf) -> int:
         B, C = suf["cands"].shape
         T = int(np.sum(suf["lens"]))
