@@ -217,6 +217,100 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     return out
 
 
+def images_section(seed, dev, name="c6"):
+    """Secondary measurement: one typed question over 8 images ("Ochevid Jev-VL 2B", One
+    question, multiple images) on the 7B shape.  Batched: every image's prefix in one
+    segmented store, prefilled in one forward, then one scoring call that asks the question
+    of every image.  Separate: one prefix, one prefill and one scoring call per image (the
+    same kernels).  Not the headline value."""
+    import torch
+    import jev_synth as S
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    cfg = S.CONFIGS[name]
+    t = time.time()
+    sess = Session.generated(cfg, seed, dev, precision=PRECISION)
+    inp = S.images_inputs(cfg, seed)
+    log(f"[bench] {name}: weights drawn and uploaded in {time.time() - t:.1f} s")
+    images, suf, seg = inp["images"], inp["suf"], inp["seg"]
+    n = len(images)
+    sess.prefill_segments(images)
+    out = sess.score_segments(seg, suf)
+    n_vis = np.array([im["vis"].shape[0] for im in images], np.int32)
+    n_text = np.array([len(im["text_ids"]) for im in images], np.int32)
+    text = np.concatenate([im["text_ids"] for im in images]).astype(np.int32)
+    P = int(sess.P)
+    ws = sess.workspace(max(J.jev_workspace_bytes(sess.model, P, P, 1, 0), sess.suffix_ws_bytes(suf)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    def batched_prefill():
+        J.jev_prefill_segments(sess.prefix, sess.vis, n_vis, text, n_text, ws)
+
+    def batched_score():
+        J.jev_score_segments(sess.prefix, seg, suf["ids"], suf["lens"], suf["cands"], suf["n_cands"], out, ws)
+
+    # one plain prefix per image over the same device inputs
+    offs = np.concatenate([[0], np.cumsum(n_vis)])
+    kvs, pfx, outs = [], [], []
+    for i in range(n):
+        Pi = int(n_vis[i] + n_text[i])
+        kv = torch.empty(J.jev_prefix_bytes(sess.model, Pi), dtype=torch.uint8, device=dev)
+        kvs.append(kv)
+        pfx.append(J.jev_prefix_create(sess.model, Pi, kv))
+        outs.append(torch.empty((1, suf["cands"].shape[1]), dtype=torch.float32, device=dev))
+    singles = [{k: np.ascontiguousarray(v[i:i + 1]) for k, v in suf.items()} for i in range(n)]
+
+    def separate_prefill():
+        for i in range(n):
+            J.jev_prefill_prefix(pfx[i], sess.vis[int(offs[i]):int(offs[i + 1])], int(n_vis[i]),
+                                 images[i]["text_ids"], ws)
+
+    def separate_score():
+        for i in range(n):
+            sb = singles[i]
+            J.jev_score_suffixes(pfx[i], sb["ids"], sb["lens"], sb["cands"], sb["n_cands"], outs[i], ws)
+
+    batched_prefill(); batched_score(); separate_prefill(); separate_score()
+    ms_bp = timed(batched_prefill, 2)
+    ms_bs = timed(batched_score, 5)
+    ms_sp = timed(separate_prefill, 1)
+    ms_ss = timed(separate_score, 3)
+    diff = max(float((outs[i][0] - out[i]).abs().max()) for i in range(n))
+    J.jev_profile_start(sess.model)
+    batched_score()
+    prof = J.jev_profile_stop(sess.model)
+    for p in pfx:
+        J.jev_prefix_destroy(p)
+    desc = (f"{name}: {cfg.n_layers}-layer decoder, hidden {cfg.hidden}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads x "
+            f"{cfg.head_dim}, MLP {cfg.mlp}, vocab {cfg.vocab}, {cfg.dtype}; {n} images of "
+            f"{int(n_vis[0])} visual + {int(n_text[0])} text rows; one question of {int(suf['lens'][0])} tokens, "
+            f"{cfg.n_cands} options")
+    res = {"workload": desc, "images": n,
+           "batched": {"prefill_ms": round(ms_bp, 3), "score_ms": round(ms_bs, 3),
+                       "answers_per_s": round(n / ((ms_bp + ms_bs) * 1e-3), 2)},
+           "separate": {"prefill_ms": round(ms_sp, 3), "score_ms": round(ms_ss, 3),
+                        "answers_per_s": round(n / ((ms_sp + ms_ss) * 1e-3), 2)},
+           "speedup_batched_vs_separate": round((ms_sp + ms_ss) / (ms_bp + ms_bs), 3),
+           "max_abs_diff_batched_vs_separate": round(diff, 6),
+           "attention": attention_entry(prof, P * cfg.n_kv_heads * cfg.head_dim * 4,
+                                        f"each suffix over its own image's {int(n_vis[0] + n_text[0])} keys")}
+    log(f"[bench] {name}: batched prefill {ms_bp:.1f} ms + score {ms_bs:.2f} ms vs separate "
+        f"{ms_sp:.1f} ms + {ms_ss:.2f} ms")
+    sess.close()
+    return res
+
+
 def _timer(dev):
     import torch
     stream = torch.cuda.current_stream(dev)
@@ -343,6 +437,8 @@ def main():
                     help="GEMM precision mode of the bf16 models (see Session; default: the library default)")
     ap.add_argument("--no-serial", action="store_true",
                     help="skip the serial-vs-batched section (one call per suffix)")
+    ap.add_argument("--no-images", action="store_true",
+                    help="skip the one-question-over-8-images measurement (config c6)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the score call")
     ap.add_argument("--calib-copy", action="store_true",
@@ -509,6 +605,16 @@ def main():
         torch.cuda.empty_cache()
         tree = tree_section(args.seed, dev, args.profile_steps)
 
+    images = None
+    if not args.no_images:
+        if not args.no_tree:
+            torch.cuda.empty_cache()
+        else:
+            sess.close()
+            del sess
+            torch.cuda.empty_cache()
+        images = images_section(args.seed, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline on a bounded sample ...")
@@ -541,6 +647,7 @@ def main():
         "block_skipping": skip,
         "kernels": kernels,
         "long_prefix_tree": tree,
+        "one_question_many_images": images,
         "configs": configs,
         "cpu_baseline": cpu,
     }

@@ -5,7 +5,7 @@ tests/golden/<config>_s<seed>.json holds the oracle's float32 results plus a
 fingerprint of the generated inputs, so a consumer can check that it rebuilt
 the same inputs before comparing.
 
-    python tests/golden/make_golden.py c2 c3 c4 c5        # all seeds listed below
+    python tests/golden/make_golden.py c2 c3 c4 c5 c6     # all seeds listed below
 """
 import hashlib
 import json
@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 import jev_synth as S                      # noqa: E402
 from oracle import jev_oracle as O         # noqa: E402
 
-SEEDS = {"c2": (0, 1, 2), "c3": (0,), "c4": (0,), "c5": (0,)}
+SEEDS = {"c2": (0, 1, 2), "c3": (0,), "c4": (0,), "c5": (0,), "c6": (0,)}
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -37,6 +37,14 @@ def fingerprint(cfg, seed):
     if cfg.n_questions:
         for v in S.tree_inputs(cfg, seed).values():
             h.update(v.tobytes())
+    if cfg.n_images:
+        inp = S.images_inputs(cfg, seed)
+        for im in inp["images"]:
+            h.update(im["vis"][:4].tobytes())
+            h.update(im["text_ids"].tobytes())
+        for v in inp["suf"].values():
+            h.update(v.tobytes())
+        h.update(inp["seg_lens"].tobytes())
     w = S.weights_layer(S.with_overrides(cfg, hidden=cfg.hidden), seed, 0)
     h.update(w["wq"][:2].tobytes())
     return h.hexdigest()
@@ -49,7 +57,12 @@ def run(name, seed):
     t0 = time.time()
     rec = {"config": name, "seed": seed, "fingerprint": fingerprint(cfg, seed),
            "method": "oracle prefix-once (layer-major), float32 numpy"}
-    if cfg.n_questions:
+    if cfg.n_images:
+        inp = S.images_inputs(cfg, seed)
+        out = O.score_segments(ws, cfg, inp["images"], inp["suf"], inp["seg"])
+        rec["out"] = out.astype(float).tolist()
+        rec["margin"] = O.margins(out, inp["suf"]["n_cands"]).astype(float).tolist()
+    elif cfg.n_questions:
         tree = S.tree_inputs(cfg, seed)
         r = O.score_tree(ws, cfg, pre, tree, free_layers=True)
         rec["score"] = r["score"].astype(float).tolist()

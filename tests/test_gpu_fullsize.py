@@ -136,3 +136,18 @@ def test_fullsize_tree(mode, precision):
     sel = m >= 0.05
     assert np.array_equal(O.argmax_first(ref, tree["n_cands"])[sel],
                           O.argmax_first(norm.cpu().numpy(), tree["n_cands"])[sel])
+
+
+def test_fullsize_segments():
+    """One question over 8 images at the 7B shape (8 prefixes of 1024 rows in one segmented
+    store, one batched prefill, one scoring call): every answer against the stored oracle
+    output, which scores each image over its own prefix alone."""
+    g = load_golden("c6", 0)
+    cfg = S.CONFIGS["c6"]
+    sess = session("c6", 0)
+    inp = S.images_inputs(cfg, 0)
+    say(f"[fullsize] c6: {len(inp['images'])} images, question length {int(inp['suf']['lens'][0])}")
+    sess.prefill_segments(inp["images"])
+    got = sess.score_segments(inp["seg"], inp["suf"]).cpu().numpy()
+    check_suffix_out(got, np.array(g["out"], dtype=np.float64), inp["suf"]["n_cands"], cfg.dtype, "c6/s0")
+    _SESS.pop(("c6", 0, "f16_down")).close()   # its prefix is now the segmented one
