@@ -391,12 +391,12 @@ T* at(void* ws, size_t off) {
 // Profiled launch kinds, named after the kernels they launch.
 enum Kind {
   K_EMBED, K_RMSNORM, K_RESNORM, K_ROPETAB, K_QKVPOST, K_GEMM, K_SWIGLU, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE,
-  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_GEMM16, K_SWIGLU16, K_NKINDS
+  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_GEMM16, K_SWIGLU16, K_SPLITSWIGLU, K_NKINDS
 };
 const char* const kKindName[K_NKINDS] = {
     "embed_rows", "rmsnorm_rows", "residual_norm", "rope_table", "qkv_post", "gemm", "gemm_swiglu",
     "splitk_reduce", "rope_qk", "v_transpose", "attn_fwd", "attn_merge", "silu_mul", "target_logits",
-    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize", "gemm_f16", "gemm_swiglu_f16"};
+    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize", "gemm_f16", "gemm_swiglu_f16", "splitk_swiglu"};
 
 struct Forward {
   const jev_prefix* pf;
@@ -621,7 +621,18 @@ struct Forward {
         return st;
       // activation bytes per element: two bf16 planes, or one float16 plane
       const double in_b = fg ? 2.0 : 4.0, out_b = fd ? 2.0 : 4.0;
-      if (jev_status st = run_k(fg ? K_SWIGLU16 : K_SWIGLU, 2.0 * T * 2 * I * H,
+      if (swiglu_use_split(T, I, kGemmPartFloats)) {
+        // few rows: a split-K GEMM over [W_gate | W_up] streams the weights with more blocks,
+        // then the SwiGLU is applied while the partials are summed
+        int sg = 1;
+        const AOp A_g{nullptr, a_hi, a_lo, fg};
+        if (jev_status st = gemm_deferred(A_g, wide, T, H, WG.w_gate, I, WG.w_up, I, nullptr, 0, part, 2 * I, 0, &sg))
+          return st;
+        if (jev_status st = run_k(K_SPLITSWIGLU, 0.0, 4.0 * sg * T * 2 * I + out_b * T * I, [&] {
+              return launch_splitk_swiglu(part, sg, T, I, u_hi, fd ? nullptr : u_lo, I, s);
+            }))
+          return st;
+      } else if (jev_status st = run_k(fg ? K_SWIGLU16 : K_SWIGLU, 2.0 * T * 2 * I * H,
                                 2.0 * 2 * I * H + in_b * T * H + out_b * T * I, [&] {
             uint16_t* ul = fd ? nullptr : u_lo;   // u as one float16 plane for a float16 down GEMM
             return fg ? launch_gemm_swiglu_f16(a_hi, wide, T, H, static_cast<const uint16_t*>(WG.w_gate),

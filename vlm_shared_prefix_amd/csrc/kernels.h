@@ -105,6 +105,12 @@ hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmS
 // launch_gemm_swiglu (hi/lo planes, or one float16 plane when ul is null).
 hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, const uint16_t* w_gate,
                                   const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+// gate|up with few output tiles (the fused kernel would fill under one block per compute
+// unit): run it as a plain split-K GEMM over [W_gate | W_up] into [splits][M][2I] partials (or
+// [M][2I] when one split), then launch_splitk_swiglu writes u as launch_gemm_swiglu would.
+bool swiglu_use_split(int M, int I, size_t part_cap);
+hipError_t launch_splitk_swiglu(const float* part, int splits, int M, int I, uint16_t* uh, uint16_t* ul, int ldu,
+                                hipStream_t s);
 // float16 copy of n bfloat16 values (n % 8 == 0); sets *bad = 1 if a finite value exceeds the
 // float16 range (*bad is not cleared).
 hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int* bad, hipStream_t s);

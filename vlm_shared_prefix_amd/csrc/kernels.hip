@@ -499,6 +499,48 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ p
 }
 
 // ----------------------------------------------------------------------------
+// SwiGLU from split-K partials of the gate|up product (few output tiles): part[s] is
+// [M][2I] with the gate columns first; u = silu(sum_s gate) * (sum_s up), splits summed in
+// order, written as bf16 hi/lo planes or (ul == nullptr) one float16 plane [M][ldu].
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) splitk_swiglu(const float* __restrict__ part, size_t split_stride,
+                                                     int splits, int M, int I, u16* __restrict__ uh,
+                                                     u16* __restrict__ ul, int ldu) {
+  const int I4 = I >> 2;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)M * I4) return;
+  const int row = (int)(i / I4), c = (int)(i % I4) * 4;
+  const float* p = part + (size_t)row * 2 * I + c;
+  float4 g = *reinterpret_cast<const float4*>(p), u = *reinterpret_cast<const float4*>(p + I);
+  for (int k = 1; k < splits; ++k) {
+    const float4 a = *reinterpret_cast<const float4*>(p + k * split_stride);
+    const float4 b = *reinterpret_cast<const float4*>(p + k * split_stride + I);
+    g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+    u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+  }
+  const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+  const size_t o = (size_t)row * ldu + c;
+  if (ul == nullptr) {
+    f16x4 v4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v4[j] = (f16)(gv[j] / (1.0f + expf(-gv[j])) * uv[j]);
+    *reinterpret_cast<f16x4*>(uh + o) = v4;
+    return;
+  }
+  u16 h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = gv[j] / (1.0f + expf(-gv[j])) * uv[j];
+    h[j] = f32_to_bf16(v);
+    l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
+  }
+  *reinterpret_cast<uint2*>(uh + o) =
+      make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  *reinterpret_cast<uint2*>(ul + o) =
+      make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+
+// ----------------------------------------------------------------------------
 // K3 (float32 models): tiled VALU GEMM, 64x64 tile, 4x4 outputs per thread.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ const float* seg_row_f(const GemmSegsF& s, int n, int K) {
@@ -1428,7 +1470,8 @@ GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap) {
   p.wide = true;
   const long t = (long)cdiv(M, G2M) * cdiv(N, G2N);
   long sp = (448 + t / 2) / t;
-  sp = std::min<long>(sp, std::min(16, std::max(1, K / 256)));
+  // one row tile (few rows: streaming the weights bounds it) may split K up to 32 ways
+  sp = std::min<long>(sp, std::min(M <= G2M ? 32 : 16, std::max(1, K / 256)));
   p.splits = (int)std::max<long>(1, sp);
   while (p.splits > 1 && (size_t)p.splits * M * N > part_cap) --p.splits;
   return p;
@@ -1484,6 +1527,19 @@ __global__ void __launch_bounds__(256) bf16_to_f16(const u16* __restrict__ src, 
     reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
     if (out_of_range) *bad = 1;
   }
+}
+
+bool swiglu_use_split(int M, int I, size_t part_cap) {
+  const long fused_blocks = (long)cdiv(M, G2M) * cdiv(I, G2N / 2);
+  return fused_blocks < 256 && (size_t)M * 2 * I <= part_cap && I % 4 == 0;
+}
+
+hipError_t launch_splitk_swiglu(const float* part, int splits, int M, int I, uint16_t* uh, uint16_t* ul, int ldu,
+                                hipStream_t s) {
+  if (M <= 0 || I <= 0) return hipSuccess;
+  if (I % 4 || ldu % 4 || splits < 1) return hipErrorInvalidValue;
+  splitk_swiglu<<<cdiv((long)M * (I / 4), 256), 256, 0, s>>>(part, (size_t)M * 2 * I, splits, M, I, uh, ul, ldu);
+  return hipGetLastError();
 }
 
 hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int* bad, hipStream_t s) {
