@@ -14,6 +14,7 @@ the kernel sources, so a stored figure can be dropped once they change.
 
     python -m vlm_shared_prefix_amd.profiling <fetch_dir> <write_dir> <kernel-substring> [out.md]
     python -m vlm_shared_prefix_amd.profiling --stats <kernel_trace_dir> [out.md]
+    python -m vlm_shared_prefix_amd.profiling --mfma <MfmaUtil/MfmaFlops counter dir> [out.md]
 """
 import csv
 import glob
@@ -150,7 +151,50 @@ def kernel_stats_markdown(run_dir: str, title: str, command: str = "") -> str:
     return "\n".join(lines) + "\n"
 
 
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsF16", "MfmaFlopsBF16")
+
+
+def mfma_markdown(run_dir: str, title: str, command: str = "", kernels=("attn_fwd_f16", "gemm_bf16w", "gemm_bf16s")) -> str:
+    """Per kernel and launch shape: mean MfmaUtil (percent of SIMD cycles with the MFMA unit
+    busy) and executed MFMA flops per dispatch (f16 + bf16) from one counter run."""
+    paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] not in MFMA_COUNTERS or not any(k in r["Kernel_Name"] for k in kernels):
+                    continue
+                blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                key = (_short(r["Kernel_Name"]), blocks)
+                d = per.setdefault(key, {})
+                d.setdefault(r["Counter_Name"], {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    lines = [f"# {title}", ""]
+    if command:
+        lines += ["Command (from the repository root):", "", "```", command, "```", ""]
+    lines += ["| kernel | blocks | dispatches | MfmaUtil % | executed MFMA GFLOP / dispatch (f16 + bf16) |",
+              "|---|---|---|---|---|"]
+    for (name, blocks), d in sorted(per.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        util = d.get("MfmaUtil", {})
+        n = len(util)
+        f16 = d.get("MfmaFlopsF16", {})
+        b16 = d.get("MfmaFlopsBF16", {})
+        fl = [(f16.get(i, 0.0) + b16.get(i, 0.0)) for i in util]
+        lines.append(f"| {name} | {blocks} | {n} | {sum(util.values()) / max(1, n):.1f} | "
+                     f"{sum(fl) / max(1, n) / 1e9:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "--mfma":
+        md = mfma_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 MFMA counters"),
+                           os.environ.get("JEV_STATS_COMMAND", ""))
+        if len(sys.argv) > 3:
+            with open(sys.argv[3], "w") as f:
+                f.write(md)
+        print(md)
+        sys.exit(0)
     if len(sys.argv) >= 3 and sys.argv[1] == "--stats":
         md = kernel_stats_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 kernel statistics"),
                                    os.environ.get("JEV_STATS_COMMAND", ""))
