@@ -239,9 +239,10 @@ jev_status jev_score_tree(const jev_prefix *p,
                           void *ws, size_t ws_bytes, void *stream);
 
 /* ---- one question over several images ----------------------------------------
- * ("Ochevid Jev-VL 2B", One question, multiple images: up to eight images and
- * one typed question; every image is encoded, the images' rows stay
- * independent, and each image gets its own answer.)  A segmented prefix
+ * ("Ochevid Jev-VL 2B", One question, multiple images: a single typed
+ * question asked of up to eight images, each image run through the model on
+ * its own and answered separately, with nothing shared between the images'
+ * rows.)  A segmented prefix
  * stores n_seg independent prefixes back to back in one KV store, segment i
  * occupying store rows [off_i, off_i + seg_lens[i]) with off_i the sum of the
  * earlier lengths.  One batched prefill runs all of them; each suffix of a
@@ -284,9 +285,9 @@ jev_status jev_score_segments(const jev_prefix *p, const int32_t *seg,
  * jev_score_suffixes and jev_score_tree, make the same checks and build the
  * same plan on the host, but do not copy the plan's metadata (row tokens,
  * positions, sequence starts, masks, readout tables) into the workspace: the
- * workspace must still hold what the last jev_score_suffixes / jev_score_tree
- * / jev_prefill_prefix call on this model staged into it, for identical
- * arguments, and no call on another model may have used the workspace since.
+ * workspace must still hold what the last staging call on this model (any
+ * hot-path call other than these two) put into it, for identical arguments,
+ * and no call on another model may have used the workspace since.
  * The library keeps, per model and workspace address, a 64-bit
  * digest of the metadata it last staged there; a mismatch (other arguments,
  * another call in between, no staging call yet) returns JEV_E_INVALID and

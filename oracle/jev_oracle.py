@@ -257,9 +257,9 @@ def score_suffixes(ws, cfg, prefix, suf, free_layers: bool = False,
 
 def score_segments(ws, cfg, images, suf, seg) -> np.ndarray:
     """One question over several images ("Ochevid Jev-VL 2B", One question, multiple
-    images): every image is encoded, the images' rows stay independent, and each image
-    gets its own answer.  Suffix b continues image seg[b] alone, so out[b] is the
-    single-prefix definition over that image's prefix: score_suffixes with
+    images): each image goes through the model on its own and is answered separately,
+    nothing passing between images.  Suffix b continues image seg[b] alone, so out[b] is
+    the single-prefix definition over that image's prefix: score_suffixes with
     prefix = images[seg[b]] and the suffixes of that image."""
     seg = np.asarray(seg)
     B, C = suf["cands"].shape
