@@ -103,6 +103,18 @@ def attention_entry(prof, prefix_kv_bytes, what):
     return e
 
 
+def _prefill_flops(cfg):
+    """Algorithmic flops of a prefill: 2 x decoder matrix parameters x rows for every layer but
+    the last (which only writes K/V: q|k|v), plus the causal attention 4·D·Hq·P(P+1)/2 per layer
+    that runs it (all but the last)."""
+    P, H, D, I = cfg.prefix_len, cfg.hidden, cfg.head_dim, cfg.mlp
+    qkv = H * (cfg.n_q_heads + 2 * cfg.n_kv_heads) * D
+    per = qkv + cfg.n_q_heads * D * H + 3 * H * I
+    L = cfg.n_layers
+    attn = 4.0 * D * cfg.n_q_heads * P * (P + 1) / 2
+    return 2.0 * P * (per * (L - 1) + qkv) + attn * (L - 1)
+
+
 def timed_on(stream, fn, k, warm=0):
     """ms per call of fn() enqueued k times on `stream`, between events recorded on that stream."""
     import torch
@@ -156,6 +168,17 @@ def tree_section(seed, dev, profile_steps, name="c5"):
                   "bitwise_equal_to_eager": bool(torch.equal(cap.outs[0], e_score))}
     del cap
     ms_prefill = timed(lambda: sess.prefill(pre["vis"], pre["text_ids"]), 1)
+    # the long-prefix prefill's kernels (causal attention over 8192 rows, GEMMs of 8192 rows)
+    J.jev_profile_start(sess.model)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    prof_pre = J.jev_profile_stop(sess.model)
+    prefill_kernels = {"attention": attention_entry(prof_pre, 0, f"causal self-attention of the {cfg.prefix_len} "
+                                                                  f"prefix rows")}
+    for kind in ("gemm_swiglu", "gemm_f16", "gemm"):
+        if prof_pre.get(kind):
+            k = prof_pre[kind]
+            prefill_kernels[kind] = {"launches": k["launches"], "avg_launch_us": round(k["ms"] * 1e3 / k["launches"], 1),
+                                     "algorithmic_tflops": round(k["flops"] / (k["ms"] * 1e-3) / 1e12, 1)}
     J.jev_profile_start(sess.model)
     for _ in range(max(1, profile_steps)):
         sess.score_tree(tree, J.JEV_TREE_TRIE)
@@ -170,6 +193,8 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     out = {"workload": desc, "tree_rows": int(rows),
            "tree_call_ms": round(ms_tree, 3), "candidates_per_s": round(n_c / (ms_tree * 1e-3), 1),
            "graph_replay": tree_graph, "prefill_ms": round(ms_prefill, 3),
+           "prefill_algorithmic_tflops": round(_prefill_flops(cfg) / (ms_prefill * 1e-3) / 1e12, 1),
+           "prefill_kernels": prefill_kernels,
            "attention": attention_entry(prof, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                         f"shared prefix ({cfg.prefix_len} keys) + tree rows ({rows})")}
     # trie vs stem-only vs flat schedules ("FastJEV" §4.7, Table 5): the same questions with
