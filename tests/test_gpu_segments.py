@@ -65,3 +65,24 @@ def test_segments_match_separate_prefixes(name, seed):
         say(f"  image {i}: max |d| vs its own prefix = {err:.3e}")
         assert err <= tol, (i, err)
     sess.close()
+
+
+@pytest.mark.parametrize("name,seed", [("mi1", 2), ("mi7", 3)])
+def test_segments_edge_cases(name, seed):
+    """Degenerate segments: one with no rows at all (its suffix sees only its own rows, the
+    P = 0 case) and one of text only; suffixes of length 1 included."""
+    cfg = S.CONFIGS[name]
+    say(f"[parity] segment edge cases {name} seed {seed}")
+    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "f16_down")
+    inp = S.images_inputs(cfg, seed)
+    H = cfg.hidden
+    empty = np.zeros((0, H), np.float32)
+    images = [inp["images"][0], {"vis": empty, "text_ids": np.zeros(0, np.int32)},
+              {"vis": empty, "text_ids": inp["images"][1]["text_ids"]}, inp["images"][2]]
+    sess.prefill_segments(images)
+    suf, seg = _mixed_suffixes(cfg, seed, len(images), [0, 1, 1, 2, 3, 3])
+    suf["lens"][1] = 1
+    ref = O.score_segments(src, cfg, images, suf, seg)
+    got = sess.score_segments(seg, suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"{name}/s{seed}/edge segments")
+    sess.close()
