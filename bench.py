@@ -36,6 +36,9 @@ PRECISION_NOTE = {
     "f16_down": "f16_down: down projection as one float16 pass on a float16 weight mirror; q|k|v, o and "
                 "gate|up as two bfloat16 passes (hi + lo of the float32 activation); float32 accumulation",
     "split": "split: every decoder GEMM as two bfloat16 passes (hi + lo of the float32 activation)",
+    "f16_down_gup": "f16_down_gup: down projection as one float16 pass on a float16 weight mirror; gate|up as "
+                    "one float16 pass in the prefill and two bfloat16 passes (hi + lo of the float32 "
+                    "activation) in the scoring call; q|k|v and o as two bfloat16 passes; float32 accumulation",
 }
 
 

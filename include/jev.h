@@ -128,6 +128,7 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 #define JEV_F16_QKV     2
 #define JEV_F16_DOWN    4
 #define JEV_F16_O       8
+#define JEV_F16_GATE_UP_PREFILL 16  /* w_gate, w_up mirrored, the f16 pass used by prefills only */
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
 

@@ -18,12 +18,21 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_session(cfg, seed, src=None, precision="f16_down"):
-    """precision (bf16 models): "split" = two-term bfloat16 GEMMs; "f16_down" / "f16" = single-pass
-    float16 GEMMs on a float16 weight mirror for the down projection / every decoder matrix."""
+def resolve_precision(precision):
+    """"default" -> the library's default GEMM precision mode."""
+    if precision == "default":
+        from vlm_shared_prefix_amd.session import DEFAULT_PRECISION
+        return DEFAULT_PRECISION
+    return precision
+
+
+def gpu_session(cfg, seed, src=None, precision="default"):
+    """precision (bf16 models): "default" = the library default; "split" = two-term bfloat16
+    GEMMs; "f16_down" / "f16" = single-pass float16 GEMMs on a float16 weight mirror for the
+    down projection / every decoder matrix."""
     from vlm_shared_prefix_amd.session import Session
     src = src or S.WeightSource(cfg, seed)
-    return Session(cfg, src.glob, src.layer, precision=precision), src
+    return Session(cfg, src.glob, src.layer, precision=resolve_precision(precision)), src
 
 
 def check_suffix_out(got, ref, n_cands, dtype, label=""):

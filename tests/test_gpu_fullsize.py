@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import jev_synth as S
-from tests.gpu_common import TOL, check_suffix_out, say
+from tests.gpu_common import TOL, check_suffix_out, resolve_precision, say
 
 pytestmark = pytest.mark.gpu
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -34,7 +34,7 @@ def load_golden(name, seed):
 _SESS = {}
 
 
-def session(name, seed, precision="f16_down"):
+def session(name, seed, precision="default"):
     """One uploaded model per (config, seed, precision), kept while consecutive tests use it."""
     from vlm_shared_prefix_amd.session import Session
     key = (name, seed, precision)
@@ -43,7 +43,7 @@ def session(name, seed, precision="f16_down"):
             _SESS.pop(k).close()
         say(f"[fullsize] drawing and uploading {name} seed {seed} ({precision})")
         cfg = S.CONFIGS[name]
-        sess = Session.generated(cfg, seed, precision=precision)
+        sess = Session.generated(cfg, seed, precision=resolve_precision(precision))
         pre = S.prefix_inputs(cfg, seed)
         sess.prefill(pre["vis"], pre["text_ids"])
         _SESS[key] = sess
@@ -57,8 +57,9 @@ def _cleanup():
         _SESS.pop(k).close()
 
 
-@pytest.mark.parametrize("name,seed,precision", [("c2", 0, "f16_down"), ("c2", 1, "f16_down"), ("c2", 2, "f16_down"),
-                                                 ("c2", 0, "split"), ("c2", 0, "f16"), ("c3", 0, "f16_down"),
+@pytest.mark.parametrize("name,seed,precision", [("c2", 0, "default"), ("c2", 1, "default"), ("c2", 2, "default"),
+                                                 ("c2", 0, "split"), ("c2", 0, "f16"), ("c3", 0, "default"),
+                                                 ("c3", 0, "f16_down"),
                                                  ("c3", 0, "split")])
 def test_fullsize_suffixes(name, seed, precision):
     g = load_golden(name, seed)
@@ -114,7 +115,7 @@ def test_fullsize_tree_few_questions(q, mode):
         assert np.all(np.isneginf(got[~valid]))
 
 
-@pytest.mark.parametrize("mode,precision", [(0, "f16_down"), (1, "f16_down"), (2, "f16_down"), (0, "split"),
+@pytest.mark.parametrize("mode,precision", [(0, "default"), (1, "default"), (2, "default"), (0, "f16_down"), (0, "split"),
                                             (2, "split")])
 def test_fullsize_tree(mode, precision):
     g = load_golden("c5", 0)
@@ -150,4 +151,4 @@ def test_fullsize_segments():
     sess.prefill_segments(inp["images"])
     got = sess.score_segments(inp["seg"], inp["suf"]).cpu().numpy()
     check_suffix_out(got, np.array(g["out"], dtype=np.float64), inp["suf"]["n_cands"], cfg.dtype, "c6/s0")
-    _SESS.pop(("c6", 0, "f16_down")).close()   # its prefix is now the segmented one
+    _SESS.pop(("c6", 0, "default")).close()   # its prefix is now the segmented one

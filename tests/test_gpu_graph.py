@@ -15,7 +15,7 @@ from tests.gpu_common import TOL, check_suffix_out, gpu_session, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,seed,precision", [("m7", 0, "f16_down"), ("m2", 0, "split"), ("c1", 0, "f32")])
+@pytest.mark.parametrize("name,seed,precision", [("m7", 0, "default"), ("m2", 0, "split"), ("c1", 0, "f32")])
 def test_graph_replay_suffixes(name, seed, precision):
     cfg = S.CONFIGS[name]
     say(f"[graph] score_suffixes {name} seed {seed} ({precision})")
@@ -46,7 +46,7 @@ def test_graph_replay_suffixes(name, seed, precision):
 def test_graph_replay_tree(name, seed, mode):
     cfg = S.CONFIGS[name]
     say(f"[graph] score_tree {name} seed {seed} mode {mode}")
-    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "f16_down")
+    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "default")
     pre, tree = S.prefix_inputs(cfg, seed), S.tree_inputs(cfg, seed)
     ref = O.score_tree(src, cfg, pre, tree)
     sess.prefill(pre["vis"], pre["text_ids"])

@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,seed,precision", [("c1", 0, "f32"), ("c1", 1, "f32"), ("c1", 2, "f32"),
-                                                 ("m2", 0, "f16_down"), ("m7", 0, "f16_down"), ("m2", 3, "f16_down"),
-                                                 ("m7l", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
+                                                 ("m2", 0, "default"), ("m7", 0, "default"), ("m2", 3, "default"),
+                                                 ("m7l", 0, "default"), ("m7", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
                                                  ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16")])
 def test_score_suffixes_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
@@ -30,7 +30,7 @@ def test_score_suffixes_vs_oracle(name, seed, precision):
     sess.close()
 
 
-@pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "f16_down"), ("m5", 0, "split"),
+@pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "default"), ("m5", 0, "split"),
                                                  ("m5", 0, "f16")])
 def test_score_tree_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]

@@ -23,7 +23,7 @@ def _mixed_suffixes(cfg, seed, n_images, order):
     return S.suffix_inputs(base, seed), np.asarray(order, np.int32)
 
 
-@pytest.mark.parametrize("name,seed,precision", [("mi1", 0, "f32"), ("mi7", 0, "f16_down"), ("mi7", 1, "split"),
+@pytest.mark.parametrize("name,seed,precision", [("mi1", 0, "f32"), ("mi7", 0, "default"), ("mi7", 1, "split"),
                                                  ("mi7", 2, "f16")])
 def test_segments_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
@@ -52,7 +52,7 @@ def test_segments_match_separate_prefixes(name, seed):
     same device path (each image prefilled and scored on its own)."""
     cfg = S.CONFIGS[name]
     say(f"[parity] segments vs separate prefixes {name} seed {seed}")
-    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "f16_down")
+    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "default")
     inp = S.images_inputs(cfg, seed)
     sess.prefill_segments(inp["images"])
     got = sess.score_segments(inp["seg"], inp["suf"]).cpu().numpy()
@@ -73,7 +73,7 @@ def test_segments_edge_cases(name, seed):
     P = 0 case) and one of text only; suffixes of length 1 included."""
     cfg = S.CONFIGS[name]
     say(f"[parity] segment edge cases {name} seed {seed}")
-    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "f16_down")
+    sess, src = gpu_session(cfg, seed, precision="split" if cfg.dtype == "f32" else "default")
     inp = S.images_inputs(cfg, seed)
     H = cfg.hidden
     empty = np.zeros((0, H), np.float32)

@@ -34,8 +34,9 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOWN,
               "f16_o": J.JEV_F16_O, "f16_out": J.JEV_F16_DOWN | J.JEV_F16_O,
               "f16_mlp": J.JEV_F16_GATE_UP | J.JEV_F16_DOWN,
+              "f16_down_gup": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL,
               "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
-DEFAULT_PRECISION = "f16_down"
+DEFAULT_PRECISION = "f16_down_gup"
 
 
 class Session:
@@ -43,8 +44,10 @@ class Session:
 
     def __init__(self, cfg, glob: Dict[str, np.ndarray], layers, device="cuda:0", precision: str = DEFAULT_PRECISION):
         """precision (bf16 models): "split" runs every GEMM on two bfloat16 terms of the activation;
-        "f16_gu", "f16_down", "f16_down" run the gate|up, the down, or both MLP GEMMs as single
-        float16 passes on a float16 mirror of their weights; "f16" does so for every decoder GEMM."""
+        "f16_gu", "f16_down", "f16_mlp" run the gate|up, the down, or both MLP GEMMs as single
+        float16 passes on a float16 mirror of their weights; "f16" does so for every decoder GEMM;
+        "f16_down_gup" (the default) runs the down projection on one float16 pass everywhere and
+        gate|up on one float16 pass in prefills only (scoring calls keep its two terms)."""
         if precision not in PRECISIONS:
             raise ValueError(f"precision must be one of {PRECISIONS}, not {precision!r}")
         self.cfg = cfg
