@@ -113,7 +113,11 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
  * Activations entering a mirrored GEMM must then stay below 65504 in magnitude.
  *
  * groups: any OR of JEV_F16_GATE_UP (w_gate, w_up), JEV_F16_QKV (wq, wk, wv),
- *   JEV_F16_DOWN (w_down) and JEV_F16_O (wo).
+ *   JEV_F16_DOWN (w_down) and JEV_F16_O (wo), each used by every call, and of
+ *   JEV_F16_GATE_UP_PREFILL, JEV_F16_QKV_PREFILL and JEV_F16_O_PREFILL, which
+ *   mirror the same matrices but use the single f16 pass in prefills only:
+ *   the prefix rows feed nothing but the float16 KV store, while the rows of
+ *   scoring calls, whose logits are read, keep the two bfloat16 terms.
  * jev_model_f16_bytes: size of the mirror buffer for those groups (0 for JEV_F32
  *   models or unknown bits).
  * jev_model_attach_f16: buf dev [bytes >= jev_model_f16_bytes(m, groups)],
@@ -129,6 +133,8 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 #define JEV_F16_DOWN    4
 #define JEV_F16_O       8
 #define JEV_F16_GATE_UP_PREFILL 16  /* w_gate, w_up mirrored, the f16 pass used by prefills only */
+#define JEV_F16_QKV_PREFILL     32  /* wq, wk, wv mirrored, used by prefills only            */
+#define JEV_F16_O_PREFILL       64  /* wo mirrored, used by prefills only                    */
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
 

@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,seed,precision", [("c1", 0, "f32"), ("c1", 1, "f32"), ("c1", 2, "f32"),
                                                  ("m2", 0, "default"), ("m7", 0, "default"), ("m2", 3, "default"),
                                                  ("m7l", 0, "default"), ("m7", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
-                                                 ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16")])
+                                                 ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16"),
+                                                 ("m7", 0, "f16_prefill"), ("m2", 1, "f16_prefill")])
 def test_score_suffixes_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
     say(f"[parity] score_suffixes {name} seed {seed} ({precision})")

@@ -55,7 +55,8 @@ struct jev_model {
   // groups run as single float16 passes on float16 activations
   std::vector<jev_layer> layers16;
   bool f16_gu = false;     // w_gate, w_up mirrored
-  bool f16_gu_prefill = false;   // ... and used by prefills only
+  // groups mirrored for prefills only (scoring calls keep their two bfloat16 terms)
+  bool f16_gu_prefill = false, f16_qkv_prefill = false, f16_o_prefill = false;
   bool f16_down = false;   // w_down mirrored
   bool f16_qkv = false;    // wq, wk, wv mirrored
   bool f16_o = false;      // wo mirrored
@@ -140,11 +141,13 @@ void layer_matrix_elems(const jev_config& c, size_t n[7]) {
 size_t mirror_align(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
-constexpr int32_t kAllGroups = JEV_F16_GATE_UP | JEV_F16_QKV | JEV_F16_DOWN | JEV_F16_O | JEV_F16_GATE_UP_PREFILL;
+constexpr int32_t kAllGroups = JEV_F16_GATE_UP | JEV_F16_QKV | JEV_F16_DOWN | JEV_F16_O | JEV_F16_GATE_UP_PREFILL |
+                                JEV_F16_QKV_PREFILL | JEV_F16_O_PREFILL;
 // group of matrix i of a layer (wq, wk, wv, wo, w_gate, w_up, w_down)
 static bool mirrored(int i, int32_t groups) {
-  constexpr int32_t gu = JEV_F16_GATE_UP | JEV_F16_GATE_UP_PREFILL;
-  static const int32_t group_of[7] = {JEV_F16_QKV, JEV_F16_QKV, JEV_F16_QKV, JEV_F16_O, gu, gu, JEV_F16_DOWN};
+  constexpr int32_t gu = JEV_F16_GATE_UP | JEV_F16_GATE_UP_PREFILL, qkv = JEV_F16_QKV | JEV_F16_QKV_PREFILL,
+                    o = JEV_F16_O | JEV_F16_O_PREFILL;
+  static const int32_t group_of[7] = {qkv, qkv, qkv, o, gu, gu, JEV_F16_DOWN};
   return (groups & group_of[i]) != 0;
 }
 
@@ -163,7 +166,8 @@ extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* b
   if (!m) return fail(JEV_E_INVALID, "null model");
   if (groups & ~kAllGroups) return fail(JEV_E_INVALID, "unknown matrix group bits");
   if (!buf || groups == 0) {   // detach: back to the two-term bf16 path
-    m->f16_gu = m->f16_gu_prefill = m->f16_down = m->f16_qkv = m->f16_o = false;
+    m->f16_gu = m->f16_down = m->f16_qkv = m->f16_o = false;
+    m->f16_gu_prefill = m->f16_qkv_prefill = m->f16_o_prefill = false;
     m->layers16.clear();
     return JEV_OK;
   }
@@ -198,6 +202,8 @@ extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* b
   m->layers16 = std::move(l16);
   m->f16_gu = (groups & JEV_F16_GATE_UP) != 0;
   m->f16_gu_prefill = !m->f16_gu && (groups & JEV_F16_GATE_UP_PREFILL) != 0;
+  m->f16_qkv_prefill = !m->f16_qkv && (groups & JEV_F16_QKV_PREFILL) != 0;
+  m->f16_o_prefill = !m->f16_o && (groups & JEV_F16_O_PREFILL) != 0;
   m->f16_down = (groups & JEV_F16_DOWN) != 0;
   m->f16_qkv = (groups & JEV_F16_QKV) != 0;
   m->f16_o = (groups & JEV_F16_O) != 0;
@@ -514,8 +520,9 @@ struct Forward {
     // GEMMs of a mirrored group take one float16 plane (in the hi slot), and the kernels that
     // produce their inputs write that plane: the input norm and attention output for the
     // q|k|v and o projections, the post-attention norm for gate|up, the SwiGLU output for down
-    const bool fq = m->f16_qkv, fo = m->f16_o, fd = m->f16_down;
-    const bool fg = m->f16_gu || (m->f16_gu_prefill && mode == Mode::Prefill);
+    const bool pre = mode == Mode::Prefill;
+    const bool fq = m->f16_qkv || (m->f16_qkv_prefill && pre), fo = m->f16_o || (m->f16_o_prefill && pre);
+    const bool fd = m->f16_down, fg = m->f16_gu || (m->f16_gu_prefill && pre);
     uint16_t* a_hi = at<uint16_t>(ws, L.act);                 // normalised activations / attention output
     uint16_t* a_lo = a_hi + (size_t)T * wide;
     const AOp A_qkv{nullptr, a_hi, a_lo, fq};

@@ -63,6 +63,8 @@ JEV_F16_QKV = 2       # wq, wk, wv
 JEV_F16_DOWN = 4      # w_down
 JEV_F16_O = 8         # wo
 JEV_F16_GATE_UP_PREFILL = 16   # w_gate, w_up; the f16 pass in prefills only
+JEV_F16_QKV_PREFILL = 32       # wq, wk, wv; prefills only
+JEV_F16_O_PREFILL = 64         # wo; prefills only
 
 _sig = {
     "jev_model_create": (C.c_int32, [C.POINTER(jev_config), C.POINTER(jev_weights), C.POINTER(_vp)]),

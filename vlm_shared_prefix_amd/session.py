@@ -35,6 +35,9 @@ PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOW
               "f16_o": J.JEV_F16_O, "f16_out": J.JEV_F16_DOWN | J.JEV_F16_O,
               "f16_mlp": J.JEV_F16_GATE_UP | J.JEV_F16_DOWN,
               "f16_down_gup": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL,
+              "f16_prefill": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL | J.JEV_F16_O_PREFILL,
+              "f16_down_gup_o": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_O_PREFILL,
+              "f16_down_gup_qkv": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL,
               "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
 DEFAULT_PRECISION = "f16_down_gup"
 
