@@ -425,6 +425,9 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
   auto step = [&](int s, const u16* cA, const u16* cL, const u16* cW, u16* nA, u16* nL, u16* nW) {
     if (s + 1 < nst) load_stage(kbeg + (s + 1) * G2K, nA, nL, nW);
     compute(cA, cL, cW);
+    // every MFMA of the stage is issued before the wait: left alone, the scheduler hoists the
+    // wait for the next stage's loads above most of them, leaving the loads little cover
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
