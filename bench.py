@@ -177,7 +177,7 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     prof_pre = J.jev_profile_stop(sess.model)
     prefill_kernels = {"attention": attention_entry(prof_pre, 0, f"causal self-attention of the {cfg.prefix_len} "
                                                                   f"prefix rows")}
-    for kind in ("gemm_swiglu", "gemm_f16", "gemm"):
+    for kind in ("gemm_swiglu", "gemm_swiglu_f16", "gemm_f16", "gemm"):
         if prof_pre.get(kind):
             k = prof_pre[kind]
             prefill_kernels[kind] = {"launches": k["launches"], "avg_launch_us": round(k["ms"] * 1e3 / k["launches"], 1),
