@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 import jev_synth as S                      # noqa: E402
 from oracle import jev_oracle as O         # noqa: E402
 
-SEEDS = {"c2": (0, 1, 2), "c3": (0,), "c4": (0,), "c5": (0,), "c6": (0,)}
+SEEDS = {"c2": (0, 1, 2), "c3": (0,), "c4": (0,), "c5": (0, 1), "c6": (0,)}
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 

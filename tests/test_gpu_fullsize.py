@@ -115,14 +115,15 @@ def test_fullsize_tree_few_questions(q, mode):
         assert np.all(np.isneginf(got[~valid]))
 
 
-@pytest.mark.parametrize("mode,precision", [(0, "default"), (1, "default"), (2, "default"), (0, "f16_down"), (0, "split"),
-                                            (2, "split")])
-def test_fullsize_tree(mode, precision):
-    g = load_golden("c5", 0)
+@pytest.mark.parametrize("seed,mode,precision", [(0, 0, "default"), (0, 1, "default"), (0, 2, "default"),
+                                                 (0, 0, "f16_down"), (0, 0, "split"), (0, 2, "split"),
+                                                 (1, 0, "default"), (1, 2, "default")])
+def test_fullsize_tree(seed, mode, precision):
+    g = load_golden("c5", seed)
     cfg = S.CONFIGS["c5"]
-    tree = S.tree_inputs(cfg, 0)
-    say(f"[fullsize] c5 tree mode {mode} ({precision})")
-    score, norm = session("c5", 0, precision).score_tree(tree, mode)
+    tree = S.tree_inputs(cfg, seed)
+    say(f"[fullsize] c5 seed {seed} tree mode {mode} ({precision})")
+    score, norm = session("c5", seed, precision).score_tree(tree, mode)
     for key, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
         ref = np.array(g[key], np.float32)
         valid = np.isfinite(ref)
