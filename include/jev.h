@@ -295,8 +295,9 @@ jev_status jev_score_segments(const jev_prefix *p, const int32_t *seg,
  * workspace must still hold what the last staging call on this model (any
  * hot-path call other than these two) put into it, for identical arguments,
  * and no call on another model may have used the workspace since.
- * The library keeps, per model and workspace address, a 64-bit
- * digest of the metadata it last staged there; a mismatch (other arguments,
+ * The library keeps, per model and workspace address (up to 1024 addresses;
+ * beyond that the remembered digests are dropped), a 64-bit digest of the
+ * metadata it last staged there; a mismatch (other arguments,
  * another call in between, no staging call yet) returns JEV_E_INVALID and
  * launches nothing.  Everything these calls enqueue is a kernel launch (no
  * copy, memset, allocation or synchronisation), so a caller can capture them

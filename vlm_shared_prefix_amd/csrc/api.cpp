@@ -796,6 +796,8 @@ struct Forward {
   int tree_C = 0, tree_K = 0;
 };
 
+constexpr size_t kMaxStagedWorkspaces = 1024;   // digests remembered per model
+
 // 64-bit FNV-1a of the staged metadata bytes.
 uint64_t meta_digest(const std::vector<char>& b) {
   uint64_t h = 1469598103934665603ull;
@@ -830,6 +832,9 @@ jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hi
     return JEV_OK;
   }
   HIP_OK(hipMemcpyAsync(ws, buf.data(), L.meta_end, hipMemcpyHostToDevice, s));
+  // bounded: a caller cycling through many workspaces forgets the oldest digests (a
+  // launch-only call on such a workspace then asks for a fresh staging call)
+  if (m->staged.size() >= kMaxStagedWorkspaces && !m->staged.count(ws)) m->staged.clear();
   m->staged[ws] = h;
   return JEV_OK;
 }
