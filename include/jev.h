@@ -336,6 +336,16 @@ jev_status jev_tree_plan_rows(const int32_t *stem_ids, const int32_t *stem_lens,
                               int32_t *row_tok, int32_t *row_depth, int32_t *row_group,
                               uint64_t *row_mask, int32_t *target_row);
 
+/* Host-only introspection of the attention's segment table (no HIP call), for
+ * tests: pseg host [T][2] holds each row's prefix key range [x, y); for every
+ * 128-row block of the G*T query rows (row r = t*G + g) ptile host
+ * [ceil(G*T/128)][4] receives the block's prefix key tiles [x, y) of 64 keys
+ * (the hull of its rows' ranges; 0, 0 when they are all empty) and the keys
+ * [z, w) every one of its rows sees (z >= w when there are none); *max_tiles
+ * the largest tile count.  JEV_E_INVALID for negative or reversed ranges. */
+jev_status jev_segment_plan_tiles(const int32_t *pseg, int32_t T, int32_t G, int32_t *ptile,
+                                  int32_t *max_tiles);
+
 /* ---- diagnostics ----------------------------------------------------------------
  * Per-kernel timing with HIP events recorded on the call's stream around every
  * launch, plus the algorithmic work of each launch (flops counted once, i.e.

@@ -236,6 +236,50 @@ def test_segment_validation(model):
     J.jev_prefix_destroy(p)
 
 
+def _segment_tiles_reference(pseg, G):
+    """Per 128-row block of the G*T query rows: the 64-key tile hull of its rows' prefix key
+    ranges and the keys every one of its rows sees (plain loops)."""
+    T = len(pseg)
+    out = []
+    for r0 in range(0, G * T, 128):
+        rows = sorted({r // G for r in range(r0, min(G * T, r0 + 128))})
+        rng = [pseg[t] for t in rows]
+        nonempty = [(b, e) for b, e in rng if e > b]
+        if nonempty:
+            lo, hi = min(b for b, _ in nonempty), max(e for _, e in nonempty)
+            tiles = (lo // 64, -(-hi // 64))
+        else:
+            tiles = (0, 0)
+        vis = (max(b for b, _ in rng), min(e for _, e in rng))
+        out.append([tiles[0], tiles[1], vis[0], vis[1]])
+    return np.array(out, np.int32).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_segment_tile_table(seed):
+    """The attention's per-block segment table (host logic) against a plain reference, for
+    random image layouts: mixed sizes, empty segments, grouped and shuffled suffix orders."""
+    from vlm_shared_prefix_amd import jev as J
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 9))
+    lens = rng.integers(0, 400, size=n)
+    lens[rng.integers(0, n)] = 0 if n > 1 else lens[0]
+    offs = np.concatenate([[0], np.cumsum(lens)])[:-1]
+    B = int(rng.integers(1, 40))
+    seg = rng.integers(0, n, size=B)
+    if seed % 2 == 0:
+        seg = np.sort(seg)
+    L = rng.integers(1, 17, size=B)
+    pseg = [(int(offs[s]), int(offs[s] + lens[s])) for s, l in zip(seg, L) for _ in range(l)]
+    for G in (1, 6, 7):
+        got, mx = J.jev_segment_plan_tiles(pseg, G)
+        ref = _segment_tiles_reference(pseg, G)
+        np.testing.assert_array_equal(got, ref)
+        assert mx == int(np.max(ref[:, 1] - ref[:, 0]))
+    with pytest.raises(J.JevError):
+        J.jev_segment_plan_tiles([(5, 3)], 7)
+
+
 def test_launch_only_calls_need_staged_metadata(model):
     """The launch-only (graph-capturable) scoring calls refuse a workspace whose staged
     metadata is not this request's; nothing is launched (no HIP call on this path)."""

@@ -1081,6 +1081,17 @@ extern "C" jev_status jev_tree_plan_rows(const int32_t* stem_ids, const int32_t*
   return JEV_OK;
 }
 
+extern "C" jev_status jev_segment_plan_tiles(const int32_t* pseg, int32_t T, int32_t G, int32_t* ptile,
+                                             int32_t* max_tiles) {
+  if (T < 0 || G < 1) return fail(JEV_E_INVALID, "T must be >= 0 and G >= 1");
+  if (T > 0 && (!pseg || !ptile)) return fail(JEV_E_INVALID, "null array");
+  for (int t = 0; t < T; ++t)
+    if (pseg[2 * t] < 0 || pseg[2 * t + 1] < pseg[2 * t]) return fail(JEV_E_INVALID, "bad key range");
+  const int mx = T > 0 ? attn_seg_tiles(pseg, T, G, ptile) : 0;
+  if (max_tiles) *max_tiles = mx;
+  return JEV_OK;
+}
+
 extern "C" jev_status jev_profile_start(jev_model* m) {
   if (!m) return fail(JEV_E_INVALID, "null model");
   m->prof.recs.clear();

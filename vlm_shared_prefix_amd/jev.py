@@ -94,6 +94,7 @@ _sig = {
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p]),
     "jev_tree_plan_rows": (C.c_int32, [_i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _u64p, _i32p]),
+    "jev_segment_plan_tiles": (C.c_int32, [_i32p, C.c_int32, C.c_int32, _i32p, _i32p]),
     "jev_profile_start": (C.c_int32, [_vp]),
     "jev_profile_stop": (C.c_int32, [_vp, C.POINTER(jev_kernel_stat), C.c_int32, _i32p]),
     "jev_last_error": (C.c_char_p, []),
@@ -296,6 +297,18 @@ def jev_score_tree_launch(prefix: int, stem_ids, stem_lens, cand_tok, cand_lens,
     """Kernel launches of jev_score_tree only (see jev_score_suffixes_launch)."""
     _score_tree(_lib.jev_score_tree_launch, "jev_score_tree_launch", prefix, stem_ids, stem_lens, cand_tok,
                 cand_lens, n_cands, mode, out_score, out_norm, ws, stream)
+
+
+def jev_segment_plan_tiles(pseg, G: int):
+    """(ptile [blocks][4], max tiles) of the attention's segment table for rows' prefix key
+    ranges pseg [T][2] and G query heads per KV head (host only)."""
+    ps = np.ascontiguousarray(np.asarray(pseg, dtype=np.int32).reshape(-1, 2))
+    T = int(ps.shape[0])
+    nb = (G * T + 127) // 128
+    out = np.zeros((max(nb, 1), 4), np.int32)
+    mx = C.c_int32()
+    _check(_lib.jev_segment_plan_tiles(_ptr_i32(ps), T, G, _ptr_i32(out), C.byref(mx)), "jev_segment_plan_tiles")
+    return out[:nb], mx.value
 
 
 def jev_tree_plan_size(stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode: int):
