@@ -24,7 +24,10 @@
  *     while a handle that names them is used.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream).  Outputs are valid once the stream has synchronised.
- *     Hot-path calls allocate no device memory and never block on the GPU.
+ *     Hot-path calls allocate no device memory and never synchronise the
+ *     stream themselves; their one host->device copy (the call's metadata,
+ *     from a pageable host buffer) is staged by the HIP runtime before the
+ *     call returns, so host buffers may be reused as soon as it has.
  *   - A model or prefix may be used from several host threads or streams at
  *     once provided each call has its own workspace and output buffers.
  */
