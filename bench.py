@@ -215,6 +215,21 @@ def tree_section(seed, dev, profile_steps, name="c5"):
             runs[mname] = {"rows": int(r), "call_ms": round(ms, 3)}
         schedules[label] = runs
     out["schedules"] = schedules
+    # the same comparison at a controlled shared fraction: every candidate has cand_len_hi
+    # tokens and a question's candidates agree on their first s of them
+    sweep = []
+    for shared in range(cfg.cand_len_hi):
+        tt = S.shared_tree_inputs(cfg, seed, shared)
+        e = {"shared_tokens": shared, "shared_fraction": round(shared / cfg.cand_len_hi, 3)}
+        for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat")):
+            sess.score_tree(tt, mode)
+            ms = timed(lambda: sess.score_tree(tt, mode), 3)
+            r = J.jev_tree_plan_size(tt["stem_ids"], tt["stem_lens"], tt["cand_tok"], tt["cand_lens"],
+                                     tt["n_cands"], mode)[0]
+            e[mname] = {"rows": int(r), "call_ms": round(ms, 3)}
+        e["fastest"] = min(("trie", "stem_only", "flat"), key=lambda k: e[k]["call_ms"])
+        sweep.append(e)
+    out["shared_fraction_sweep"] = sweep
 
     # the memory-bound end: the same prefix with only the first q question stems (few query
     # rows per KV head), where the attention is bound by streaming the prefix KV

@@ -398,3 +398,27 @@ def tree_inputs(cfg: Config, seed: int) -> Dict[str, np.ndarray]:
     n_cands = np.full(Q, C, dtype=np.int32)
     return {"stem_ids": np.ascontiguousarray(stem_ids), "stem_lens": stem_lens,
             "cand_tok": np.ascontiguousarray(cand_tok), "cand_lens": cand_lens, "n_cands": n_cands}
+
+
+def shared_tree_inputs(cfg: Config, seed: int, shared: int) -> Dict[str, np.ndarray]:
+    """Trees with a controlled shared fraction: every candidate has cand_len_hi tokens and
+    the candidates of a question agree on their first `shared` tokens (0 <= shared <
+    cand_len_hi) and differ at the next one, so merging common histories saves exactly
+    shared * (C - 1) rows per question.  Same layout as tree_inputs; stems as there."""
+    Q, C, K = cfg.n_questions, cfg.tree_cands, cfg.cand_len_hi
+    if not 0 <= shared < K:
+        raise ValueError(f"shared must be in [0, {K})")
+    if C > cfg.vocab:
+        raise ValueError("more candidates than vocabulary ids")
+    rng = _rng(seed, STREAM_TREE, 1 + shared)
+    stem_lens = np.full(Q, cfg.stem_len, dtype=np.int32)
+    stem_ids = rng.integers(0, cfg.vocab, size=(Q, max(cfg.s_max, cfg.stem_len))).astype(np.int32)
+    cand_tok = rng.integers(0, cfg.vocab, size=(Q, C, K)).astype(np.int32)
+    for q in range(Q):
+        cand_tok[q, 1:, :shared] = cand_tok[q, 0, :shared]
+        # first differing token: distinct across the question's candidates
+        cand_tok[q, :, shared] = rng.choice(cfg.vocab, size=C, replace=False)
+    cand_lens = np.full((Q, C), K, dtype=np.int32)
+    n_cands = np.full(Q, C, dtype=np.int32)
+    return {"stem_ids": np.ascontiguousarray(stem_ids), "stem_lens": stem_lens,
+            "cand_tok": np.ascontiguousarray(cand_tok), "cand_lens": cand_lens, "n_cands": n_cands}

@@ -388,6 +388,24 @@ def test_tree_plan_matches_reference(name, seed, mode):
                 assert plan["target_row"][q, c, k] == want
 
 
+@pytest.mark.parametrize("shared", [0, 1, 2, 3])
+def test_tree_plan_sizes_shared_fraction(shared):
+    """Trees whose candidates share their first `shared` tokens (the 7B tree workload's
+    shape): a candidate of K tokens is predicted by its stem's last row and K - 1 rows of its
+    own tokens, so per question the trie feeds stem + shared + C (K - 1 - shared) rows,
+    stem-only stem + C (K - 1) and flat C (stem + K - 1)."""
+    from vlm_shared_prefix_amd import jev as J
+    cfg = S.CONFIGS["c5"]
+    tree = S.shared_tree_inputs(cfg, 0, shared)
+    Q, C, K, st = cfg.n_questions, cfg.tree_cands, cfg.cand_len_hi, cfg.stem_len
+    want = {0: Q * (st + shared + C * (K - 1 - shared)), 1: Q * (st + C * (K - 1)), 2: Q * C * (st + K - 1)}
+    got = {m: J.jev_tree_plan_size(tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                                   tree["n_cands"], m)[0] for m in (0, 1, 2)}
+    assert got == want
+    rows, _ = reference_trie(tree, 0)
+    assert len(rows) == want[0]
+
+
 def test_trie_merges_only_same_parent_and_token():
     """Equal tokens after different histories stay separate ("FastJEV" §3.3)."""
     from vlm_shared_prefix_amd import jev as J

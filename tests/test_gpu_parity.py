@@ -53,6 +53,24 @@ def test_score_tree_vs_oracle(name, seed, precision):
     sess.close()
 
 
+@pytest.mark.parametrize("shared", [0, 2, 3])
+def test_score_tree_shared_fraction_vs_oracle(shared):
+    """Trees whose candidates share their first `shared` of 4 tokens, every schedule."""
+    cfg = S.CONFIGS["m5"]
+    say(f"[parity] score_tree m5 seed 0, candidates sharing {shared} of {cfg.cand_len_hi} tokens")
+    sess, src = gpu_session(cfg, 0)
+    pre, tree = S.prefix_inputs(cfg, 0), S.shared_tree_inputs(cfg, 0, shared)
+    ref = O.score_tree(src, cfg, pre, tree)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    for mode in (0, 1, 2):
+        score, norm = sess.score_tree(tree, mode)
+        for k, got in (("score", score.cpu().numpy()), ("norm", norm.cpu().numpy())):
+            err = float(np.max(np.abs(got - ref[k])))
+            say(f"  mode {mode} {k}: max |d| = {err:.3e}")
+            assert err <= TOL[cfg.dtype], (mode, k, err)
+    sess.close()
+
+
 @pytest.mark.parametrize("name,seed,skip", [("c1", 0, (1,)), ("m2", 0, (0, 1)), ("m7", 0, (1, 0)),
                                             ("m7l", 0, (1, 0))])
 def test_block_skipping_vs_oracle(name, seed, skip):
