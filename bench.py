@@ -221,12 +221,20 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     for shared in range(cfg.cand_len_hi):
         tt = S.shared_tree_inputs(cfg, seed, shared)
         e = {"shared_tokens": shared, "shared_fraction": round(shared / cfg.cand_len_hi, 3)}
-        for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat")):
+        modes = ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat"))
+        for mode, _ in modes:
             sess.score_tree(tt, mode)
-            ms = timed(lambda: sess.score_tree(tt, mode), 3)
+        # two interleaved passes over the modes, 5 calls each: call_ms is their mean,
+        # pass_ms both pass means (the spread between them is the run's noise)
+        passes = {mname: [] for _, mname in modes}
+        for _ in range(2):
+            for mode, mname in modes:
+                passes[mname].append(timed(lambda: sess.score_tree(tt, mode), 5))
+        for mode, mname in modes:
             r = J.jev_tree_plan_size(tt["stem_ids"], tt["stem_lens"], tt["cand_tok"], tt["cand_lens"],
                                      tt["n_cands"], mode)[0]
-            e[mname] = {"rows": int(r), "call_ms": round(ms, 3)}
+            e[mname] = {"rows": int(r), "call_ms": round(float(np.mean(passes[mname])), 3),
+                        "pass_ms": [round(x, 3) for x in passes[mname]]}
         e["fastest"] = min(("trie", "stem_only", "flat"), key=lambda k: e[k]["call_ms"])
         sweep.append(e)
     out["shared_fraction_sweep"] = sweep

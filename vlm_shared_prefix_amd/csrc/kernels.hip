@@ -1655,6 +1655,8 @@ int attn_seg_tiles(const int* pseg, int T, int G, int* ptile) {
   return mx;
 }
 
+constexpr long kAttnResidentBlocks = 512;   // 256 CUs x 2 blocks of 4 waves
+
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
   const long base = (long)cdiv((long)G * T, AT_BR) * Hkv;
   const int tiles = cdiv(P, AT_BK) + own_tiles;
@@ -1663,6 +1665,9 @@ int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
   // P = 8192 two).
   const long target = tiles >= 64 ? 512 : 256;
   long ns = (target + base / 2) / base;
+  // never past the blocks the chip holds at once (two per CU): a few blocks over it run
+  // as a second round of their own (532 blocks took 21% longer than 504)
+  ns = std::min<long>(ns, std::max(1L, kAttnResidentBlocks / base));
   ns = std::min<long>(ns, std::max(1, tiles / 2));     // at least two tiles per split
   return (int)std::max<long>(1, std::min<long>(ns, kAttnMaxSplits));
 }
