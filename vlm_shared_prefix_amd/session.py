@@ -39,7 +39,7 @@ PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOW
               "f16_down_gup_o": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_O_PREFILL,
               "f16_down_gup_qkv": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL,
               "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
-DEFAULT_PRECISION = "f16_down_gup"
+DEFAULT_PRECISION = "f16_down_gup_o"
 
 
 class Session:
@@ -49,8 +49,10 @@ class Session:
         """precision (bf16 models): "split" runs every GEMM on two bfloat16 terms of the activation;
         "f16_gu", "f16_down", "f16_mlp" run the gate|up, the down, or both MLP GEMMs as single
         float16 passes on a float16 mirror of their weights; "f16" does so for every decoder GEMM;
-        "f16_down_gup" (the default) runs the down projection on one float16 pass everywhere and
-        gate|up on one float16 pass in prefills only (scoring calls keep its two terms)."""
+        "f16_down_gup" runs the down projection on one float16 pass everywhere and gate|up on
+        one float16 pass in prefills only (scoring calls keep its two terms); "f16_down_gup_o"
+        (the default) also runs o on one float16 pass in prefills; "f16_prefill" every prefill
+        GEMM."""
         if precision not in PRECISIONS:
             raise ValueError(f"precision must be one of {PRECISIONS}, not {precision!r}")
         self.cfg = cfg
