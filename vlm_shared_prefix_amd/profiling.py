@@ -186,7 +186,60 @@ def mfma_markdown(run_dir: str, title: str, command: str = "", kernels=("attn_fw
     return "\n".join(lines) + "\n"
 
 
+LDS_TA_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+                   "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE", "TA_TA_BUSY_sum", "TA_FLAT_READ_WAVEFRONTS_sum")
+
+
+def lds_ta_markdown(run_dir: str, title: str, command: str = "", kernels=("attn_fwd_f16", "gemm_bf16w"),
+                    xcds: int = 8, cus: int = 256) -> str:
+    """Per kernel and launch shape, from one counter run: LDS bank conflicts per LDS-active
+    cycle, the fraction of wave cycles spent waiting on LDS instructions, and the texture
+    address (TA) units' busy fraction.  GRBM_GUI_ACTIVE reads as the sum over the XCDs and
+    TA_TA_BUSY_sum as the sum over the CUs' TA units, so TA busy = TA_TA_BUSY_sum /
+    (GRBM_GUI_ACTIVE / xcds * cus)."""
+    paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] not in LDS_TA_COUNTERS or not any(k in r["Kernel_Name"] for k in kernels):
+                    continue
+                blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                d = per.setdefault((_short(r["Kernel_Name"]), blocks), {})
+                c = d.setdefault(r["Counter_Name"], {})
+                c[int(r["Dispatch_Id"])] = c.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    lines = [f"# {title}", ""]
+    if command:
+        lines += ["Command (from the repository root):", "", "```", command, "```", ""]
+    lines += ["| kernel | blocks | dispatches | LDS bank conflicts / LDS-active cycle | LDS wait / wave cycle | "
+              "TA busy | TA read wavefronts / dispatch |", "|---|---|---|---|---|---|---|"]
+
+    def mean(d, k):
+        v = d.get(k, {})
+        return sum(v.values()) / max(1, len(v))
+
+    for (name, blocks), d in sorted(per.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        n = len(d.get("GRBM_GUI_ACTIVE", {}))
+        gui = mean(d, "GRBM_GUI_ACTIVE")
+        conf = mean(d, "SQ_LDS_BANK_CONFLICT") / max(1.0, mean(d, "SQ_LDS_IDX_ACTIVE"))
+        wait = mean(d, "SQ_WAIT_INST_LDS") / max(1.0, mean(d, "SQ_WAVE_CYCLES"))
+        ta = mean(d, "TA_TA_BUSY_sum") / max(1.0, gui / xcds * cus)
+        lines.append(f"| {name} | {blocks} | {n} | {conf:.3f} | {wait:.3f} | {ta:.2f} | "
+                     f"{mean(d, 'TA_FLAT_READ_WAVEFRONTS_sum'):.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "--lds-ta":
+        md = lds_ta_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 LDS and TA counters"),
+                             os.environ.get("JEV_STATS_COMMAND", ""))
+        if len(sys.argv) > 3:
+            with open(sys.argv[3], "w") as f:
+                f.write(md)
+        print(md)
+        sys.exit(0)
     if len(sys.argv) >= 3 and sys.argv[1] == "--mfma":
         md = mfma_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 MFMA counters"),
                            os.environ.get("JEV_STATS_COMMAND", ""))
