@@ -84,3 +84,19 @@ def test_lds_ta_table(tmp_path):
     write_run(tmp_path, rows)
     md = PR.lds_ta_markdown(str(tmp_path), "t")
     assert "| gemm_bf16w<true, true> | 1184 | 2 | 0.250 | 0.020 | 0.50 | 77 |" in md
+
+
+def test_committed_summaries_are_whole():
+    """Every committed summary opens with its title and the command that made it; the traffic
+    summaries still carry the figure and the source digest the bench reads."""
+    root = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+    names = sorted(n for n in os.listdir(root) if n.endswith(".md"))
+    assert names
+    for n in names:
+        with open(os.path.join(root, n)) as f:
+            text = f.read()
+        assert text.startswith("# "), n
+        assert "```\ncd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT\nrocprofv3 " in text, n
+        if n.endswith("_traffic.md"):
+            t, d = PR.stored_traffic(os.path.join(root, n))
+            assert t > 0 and len(d) == 16, n
