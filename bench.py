@@ -60,7 +60,7 @@ def roofline(kind, d):
     """Roofline entry of one kernel kind from the library's event timing.
 
     achieved = algorithmic flops per launch (each product counted once) / average
-    launch time.  The two-term bf16 GEMMs (gemm, gemm_swiglu, lm_head_gemm) run every
+    launch time.  The two-term bf16 GEMMs (gemm, gemm_swiglu, lm_head_lse) run every
     product twice (hi and lo planes of the float32 activations), so the MFMA pipes
     execute 2x the algorithmic flops: reported as executed_tflops / executed_frac.
     The float16 GEMMs (gemm_f16, gemm_swiglu_f16) execute each product once.
@@ -78,8 +78,8 @@ def roofline(kind, d):
              "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
              "avg_launch_us": round(avg_s * 1e6, 2), "launches": n,
              "algorithmic_flops_per_launch": d["flops"] / n}
-        passes = 2 if kind in ("gemm", "gemm_swiglu", "lm_head_gemm") else 1
-        if kind.startswith("gemm") or kind == "lm_head_gemm":
+        passes = 2 if kind in ("gemm", "gemm_swiglu", "lm_head_lse") else 1
+        if kind.startswith("gemm") or kind == "lm_head_lse":
             r["executed_tflops"] = round(passes * ach, 2)
             r["executed_frac"] = round(passes * ach / PEAK_BF16_TFLOPS, 4)
         return r
@@ -119,6 +119,23 @@ def _prefill_flops(cfg):
     L = cfg.n_layers
     attn = 4.0 * D * cfg.n_q_heads * P * (P + 1) / 2
     return 2.0 * P * (per * (L - 1) + qkv) + attn * (L - 1)
+
+
+def step_stats(stream, fn, k):
+    """fn() enqueued k times on `stream` with an event pair around each call: the total time
+    between the first and the last event (ms per call, the mean) and the median, p10 and p90
+    of the per-call times."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(k):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(k)])
+    return {"mean_ms": round(float(ev[0].elapsed_time(ev[k]) / k), 4), "median_ms": round(float(np.median(per)), 4),
+            "p10_ms": round(float(np.percentile(per, 10)), 4), "p90_ms": round(float(np.percentile(per, 90)), 4)}
 
 
 def timed_on(stream, fn, k, warm=0):
@@ -218,6 +235,23 @@ def tree_section(seed, dev, profile_steps, name="c5"):
             runs[mname] = {"rows": int(r), "call_ms": round(ms, 3)}
         schedules[label] = runs
     out["schedules"] = schedules
+    # the flat schedule's attention (64 sequences of 12-15 rows: the largest shared-prefix
+    # attention launch of the workload)
+    sess.score_tree(tree, J.JEV_TREE_FLAT)
+    J.jev_profile_start(sess.model)
+    for _ in range(max(1, profile_steps)):
+        sess.score_tree(tree, J.JEV_TREE_FLAT)
+    flat_rows = J.jev_tree_plan_size(tree["stem_ids"], tree["stem_lens"], tree["cand_tok"], tree["cand_lens"],
+                                     tree["n_cands"], J.JEV_TREE_FLAT)[0]
+    out["attention_flat"] = attention_entry(J.jev_profile_stop(sess.model),
+                                            cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
+                                            f"shared prefix ({cfg.prefix_len} keys) + flat rows ({flat_rows})")
+    modes_ms = {}
+    for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat")):
+        st = step_stats(stream, lambda: sess.score_tree(tree, mode), 5)
+        modes_ms[mname] = {"ms": st["median_ms"], "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+                           "candidates_per_s": round(n_c / (st["median_ms"] * 1e-3), 1)}
+    out["modes"] = modes_ms
     # the same comparison at a controlled shared fraction: every candidate has cand_len_hi
     # tokens and a question's candidates agree on their first s of them
     sweep = []
@@ -381,16 +415,18 @@ def _timer(dev):
     return timed
 
 
-def configs_report(seed, dev, reps=5):
+def configs_report(seed, dev, reps=5, names=("c1", "c2", "c4")):
     """Per-config call times: c1, c2 (scoring), c4 (each B, one batched call vs B single-suffix
-    calls on the same prefix), c5 (trie, stem-only, flat).  ms per call, candidates per second."""
+    calls on the same prefix; the shared-prefix attention's MFMA utilisation at B = 32 and 100),
+    c5 (trie, stem-only, flat).  ms per call (median, p10/p90), candidates per second."""
     import torch
     import jev_synth as S
     from vlm_shared_prefix_amd import jev as J
     from vlm_shared_prefix_amd.session import Session
     timed = _timer(dev)
     rep = {}
-    for name in ("c1", "c2", "c4", "c5"):
+    stream = torch.cuda.current_stream(dev)
+    for name in names:
         cfg = S.CONFIGS[name]
         sess = Session.generated(cfg, seed, dev, precision=PRECISION)
         pre = S.prefix_inputs(cfg, seed)
@@ -413,9 +449,18 @@ def configs_report(seed, dev, reps=5):
                 n_c = int(np.sum(suf["n_cands"]))
                 out = sess.score_suffixes(suf)
                 sess.workspace(sess.suffix_ws_bytes(suf))
-                ms = timed(lambda: sess.score_suffixes(suf, out), reps)
-                e = {"B": nb, "rows": int(np.sum(suf["lens"])), "ms": round(ms, 3),
-                     "candidates_per_s": round(n_c / (ms * 1e-3), 1)}
+                st = step_stats(stream, lambda: sess.score_suffixes(suf, out), reps)
+                ms = st["median_ms"]
+                e = {"B": nb, "rows": int(np.sum(suf["lens"])), "ms": round(ms, 3), "p10_ms": st["p10_ms"],
+                     "p90_ms": st["p90_ms"], "candidates_per_s": round(n_c / (ms * 1e-3), 1)}
+                if name == "c4" and nb >= 32:
+                    J.jev_profile_start(sess.model)
+                    for _ in range(2):
+                        sess.score_suffixes(suf, out)
+                    e["attention"] = attention_entry(J.jev_profile_stop(sess.model),
+                                                     cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
+                                                     f"shared prefix ({cfg.prefix_len} keys) + own rows of "
+                                                     f"{nb} suffixes")
                 if name == "c4":
                     singles = [{k: v[b:b + 1] for k, v in suf.items()} for b in range(nb)]
                     o1 = torch.empty((1, out.shape[1]), dtype=torch.float32, device=dev)
@@ -433,6 +478,33 @@ def configs_report(seed, dev, reps=5):
         del sess
         torch.cuda.empty_cache()
     return rep
+
+
+def host_info():
+    """CPU model, memory and the BLAS NumPy calls (with its thread count) of this host."""
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["ram_gib"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 0))
+    except Exception:
+        pass
+    return info
 
 
 def cpu_baseline(cfg, seed, budget_layers=2):
@@ -466,12 +538,33 @@ def cpu_baseline(cfg, seed, budget_layers=2):
     per_layer = max(tk - t0, 0.0) / budget_layers
     est = t0 + cfg.n_layers * per_layer
     n_c = int(np.sum(suf["n_cands"]))
-    return {"value": n_c / est, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
+    return {"value": n_c / est, "unit": "candidates/s", "cores": int(cores), "kind": "oracle", "host": host_info(),
+            "seconds_per_question": est / cfg.n_suffix,
             "sample": (f"jev_oracle.score_suffixes (prefix once, layer-major, float32 numpy) on all "
                        f"{cfg.n_suffix} suffixes with the model cut to 0 and {budget_layers} of "
                        f"{cfg.n_layers} layers; measured {t0:.2f} s and {tk:.2f} s, scaled to "
                        f"{cfg.n_layers} layers = {est:.1f} s per step"),
             "seconds_per_step": est}
+
+
+def cpu_crosscheck(name, seed):
+    """Host only: the oracle's full scoring call on one configuration (every layer, all
+    suffixes) against the bounded-sample estimate cpu_baseline reports for it."""
+    import jev_synth as S
+    from oracle import jev_oracle as O
+    cfg = S.CONFIGS[name]
+    est = cpu_baseline(cfg, seed)
+    ws = S.WeightSource(cfg, seed, cache_layers=False)
+    pre, suf = S.prefix_inputs(cfg, seed), S.suffix_inputs(cfg, seed)
+    t = time.perf_counter()
+    O.score_suffixes(ws, cfg, pre, suf, free_layers=True)
+    full = time.perf_counter() - t
+    n_c = int(np.sum(suf["n_cands"]))
+    print(json.dumps({"config": name, "host": host_info(), "full_seconds": round(full, 2),
+                      "full_candidates_per_s": round(n_c / full, 3),
+                      "estimate_seconds": round(est["seconds_per_step"], 2),
+                      "estimate_candidates_per_s": round(est["value"], 3),
+                      "estimate_over_full": round(est["seconds_per_step"] / full, 3)}), flush=True)
 
 
 def main():
@@ -485,8 +578,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true",
                     help="skip the secondary long-prefix tree measurement (config c5)")
-    ap.add_argument("--all-configs", action="store_true",
-                    help="also time configs c1, c2, c4 (every B, batched and serial) and c5 (every mode)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config calls of c1, c2 and c4 (every B, batched and serial)")
+    ap.add_argument("--cpu-crosscheck", default=None, metavar="CONFIG",
+                    help="host only: time the oracle's full scoring call on CONFIG and the bounded-sample "
+                         "estimate the bench reports, then exit (no GPU needed)")
     ap.add_argument("--precision", default=None,
                     help="GEMM precision mode of the bf16 models (see Session; default: the library default)")
     ap.add_argument("--no-serial", action="store_true",
@@ -498,6 +594,9 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of a known size (the counter calibration for traffic)")
     args = ap.parse_args()
+    if args.cpu_crosscheck:
+        cpu_crosscheck(args.cpu_crosscheck, args.seed)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
               f"requested). Run with --gpus 1.", file=sys.stderr)
@@ -553,11 +652,15 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
     t_wall = time.perf_counter()
-    ms_step = timed(step, args.steps)
+    step_st = step_stats(stream, step, args.steps)
+    ms_step = step_st["mean_ms"]
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall_ms:.3f})")
-    ms_score = timed(score_only, args.steps)
-    ms_prefill = timed(prefill_only, max(1, args.steps // 2))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall_ms:.3f}); median "
+        f"{step_st['median_ms']:.3f}, p10 {step_st['p10_ms']:.3f}, p90 {step_st['p90_ms']:.3f}")
+    score_st = step_stats(stream, score_only, args.steps)
+    ms_score = score_st["median_ms"]
+    prefill_st = step_stats(stream, prefill_only, max(3, args.steps // 2))
+    ms_prefill = prefill_st["median_ms"]
     log(f"[bench] score-only {ms_score:.3f} ms, prefill-only {ms_prefill:.3f} ms")
 
     # the score call replayed from a HIP graph (its launch-only entry point captured once; no
@@ -647,26 +750,25 @@ def main():
         del src, dst
 
     configs = None
-    if args.all_configs:
+    if not args.no_configs:
         sess.close()
         torch.cuda.empty_cache()
-        configs = configs_report(args.seed, dev)
+        configs = configs_report(args.seed, dev, reps=max(3, args.steps // 4))
 
     tree = None
     if not args.no_tree:
-        sess.close()
+        if args.no_configs:
+            sess.close()
         del sess
         torch.cuda.empty_cache()
         tree = tree_section(args.seed, dev, args.profile_steps)
 
     images = None
     if not args.no_images:
-        if not args.no_tree:
-            torch.cuda.empty_cache()
-        else:
+        if args.no_tree and args.no_configs:
             sess.close()
             del sess
-            torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
         images = images_section(args.seed, dev)
 
     cpu = None
@@ -683,6 +785,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_st,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -692,8 +795,10 @@ def main():
                    "suffix_rows": T, "candidates": n_cand, "seed": args.seed,
                    "gemm_precision": PRECISION_NOTE.get(PRECISION, PRECISION),
                    "step": "jev_prefill_prefix + jev_score_suffixes"},
-        "score_only": {"ms": round(ms_score, 4), "candidates_per_s": round(n_cand / (ms_score * 1e-3), 2)},
+        "score_only": {"ms": round(ms_score, 4), "p10_ms": score_st["p10_ms"], "p90_ms": score_st["p90_ms"],
+                       "candidates_per_s": round(n_cand / (ms_score * 1e-3), 2)},
         "prefill_ms": round(ms_prefill, 4),
+        "prefill_p10_p90_ms": [prefill_st["p10_ms"], prefill_st["p90_ms"]],
         "roofline": roof,
         "attention": attn,
         "graph_replay": graph,

@@ -25,9 +25,13 @@
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream).  Outputs are valid once the stream has synchronised.
  *     Hot-path calls allocate no device memory and never synchronise the
- *     stream themselves; their one host->device copy (the call's metadata,
- *     from a pageable host buffer) is staged by the HIP runtime before the
- *     call returns, so host buffers may be reused as soon as it has.
+ *     stream themselves.  Their one host->device copy (the call's packed
+ *     metadata) goes through a ring of pinned host slots that the model
+ *     creates on its first staging call (8 x 1 MiB of pinned host memory,
+ *     freed by jev_model_destroy); a slot is refilled only once the copy that
+ *     last read it has completed, so the caller's host arrays may be reused as
+ *     soon as a call returns.  A host that runs more than eight staging calls
+ *     ahead of the device waits for the oldest copy at that point.
  *   - A model or prefix may be used from several host threads or streams at
  *     once provided each call has its own workspace and output buffers.
  */
@@ -127,8 +131,12 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
  *   caller-owned and kept alive while the model is used.  Converts the groups'
  *   matrices of every layer into it on `stream`, then synchronises the stream to
  *   read the range check: JEV_E_UNSUPPORTED if a weight exceeds the float16
- *   range (the model stays on the two-term path), JEV_E_WORKSPACE if bytes is
- *   too small.  buf == NULL or groups == 0 detaches the mirror.  Not a hot-path
+ *   range, JEV_E_WORKSPACE if bytes is too small (nothing changes then).  Any
+ *   failure after the conversion has begun (a range error, a HIP error) leaves
+ *   the model detached, every GEMM on the two-term path: a mirror attached
+ *   earlier is dropped, since the buffer may hold it and is being rewritten.
+ *   Each call replaces the previous mirror; its groups alone decide which
+ *   GEMMs run on the float16 pass.  buf == NULL or groups == 0 detaches the mirror.  Not a hot-path
  *   call (it blocks); do not call it while another call on this model is in
  *   flight.  The LM head and embeddings are never mirrored. */
 #define JEV_F16_GATE_UP 1
@@ -140,6 +148,9 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 #define JEV_F16_O_PREFILL       64  /* wo mirrored, used by prefills only                    */
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
+/* The groups whose float16 pass is in effect (0: none; a prefill-only bit is
+ * reported only when its every-call bit is not set). */
+int32_t    jev_model_f16_groups(const jev_model *m);
 
 /* ---- decision-guided block skipping ("FastJEV", §2.3 and §3.4) -----------------
  * The candidate rows of jev_score_suffixes and jev_score_tree bypass the decoder
@@ -152,6 +163,28 @@ jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t 
  * copied; it applies to calls enqueued after this returns (do not change it
  * while another call on this model is being enqueued). */
 jev_status jev_model_set_skip(jev_model *m, const uint8_t *skip, int32_t n);
+
+/* ---- attention precision ---------------------------------------------------------
+ * The scores q.k of the attention run on float16 matrix cores.  q is rounded to
+ * float16 once (terms = 1) or carried as two float16 terms, f16(q) and the rounding
+ * remainder q - f16(q) (terms = 2, twice the matrix-core work of the score
+ * product).  q's rounding moves every score of a row coherently; its weight grows
+ * with the number of keys a row sees.  terms = 0 (the default) takes two terms when
+ * a call's rows see more than 2048 prefix keys (the longest segment of the store),
+ * one otherwise.  Applies to calls enqueued after this returns. */
+jev_status jev_model_set_attn_q_terms(jev_model *m, int32_t terms);
+
+/* ---- range flag of a call ---------------------------------------------------------
+ * Float16 activation planes (q, k and v; the normalised input of a float16
+ * mirrored GEMM; the SwiGLU output feeding a float16 down projection) hold
+ * magnitudes up to 65504.  Every forward clears a flag word at the start of its
+ * workspace and each kernel writing such a plane sets bit JEV_FLAG_F16_RANGE when
+ * a value is out of range or not finite; the scores of that call are then not
+ * reliable.  jev_workspace_flags enqueues a read of the word on `stream`,
+ * synchronises the stream and returns it in *flags: it reports the last call that
+ * used the workspace (not a hot-path call: it blocks). */
+#define JEV_FLAG_F16_RANGE 1
+jev_status jev_workspace_flags(const void *ws, int32_t *flags, void *stream);
 
 /* ---- prefix KV store ---------------------------------------------------------
  * Layout per layer l (element type float16 for JEV_BF16, float32 for JEV_F32),

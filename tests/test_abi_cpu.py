@@ -141,6 +141,7 @@ def test_mirror_and_skip_arguments(model):
         J.jev_model_attach_f16(m, J.JEV_F16_DOWN, _FakeDev(100), stream=0)
     assert e.value.code == J.JEV_E_WORKSPACE
     J.jev_model_attach_f16(m, J.JEV_F16_DOWN, None, stream=0)   # detach: no HIP call
+    assert J.jev_model_f16_groups(m) == 0
     with pytest.raises(J.JevError) as e:
         J.jev_model_set_skip(m, [1, 0, 1])                  # 3 flags for 2 layers
     assert e.value.code == J.JEV_E_INVALID
@@ -442,4 +443,33 @@ def test_tree_validation():
     with pytest.raises(J.JevError) as e:
         J.jev_tree_plan_size(stem, np.array([60], np.int32), cand, np.full((1, 3), 4, np.int32),
                              np.array([3], np.int32), 5)
+    assert e.value.code == J.JEV_E_INVALID
+
+
+def test_failed_attach_leaves_model_detached(model):
+    """An attach that fails once the conversion has begun (here: no device to convert on)
+    leaves every GEMM on the two-term path."""
+    import torch
+    from vlm_shared_prefix_amd import jev as J
+    if torch.cuda.device_count() > 0:
+        pytest.skip("exercises the failure of the conversion launch on a host without a GPU")
+    m, _ = model
+    nb = J.jev_model_f16_bytes(m, J.JEV_F16_DOWN | J.JEV_F16_QKV)
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_attach_f16(m, J.JEV_F16_DOWN | J.JEV_F16_QKV, _FakeDev(nb), stream=0)
+    assert e.value.code == J.JEV_E_HIP
+    assert J.jev_model_f16_groups(m) == 0
+
+
+def test_attn_q_terms_and_flags_arguments(model):
+    """The q-terms setting takes 0, 1 or 2; the flag read rejects null arguments (no HIP call)."""
+    from vlm_shared_prefix_amd import jev as J
+    m, _ = model
+    for t in (0, 1, 2, 0):
+        J.jev_model_set_attn_q_terms(m, t)
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_set_attn_q_terms(m, 3)
+    assert e.value.code == J.JEV_E_INVALID
+    with pytest.raises(J.JevError) as e:
+        J.jev_workspace_flags(None, stream=0)
     assert e.value.code == J.JEV_E_INVALID

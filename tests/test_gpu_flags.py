@@ -1,0 +1,106 @@
+"""GPU checks of the call-level controls: the float16 range flag, re-attaching the float16
+mirror, and the attention's q terms.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+
+import jev_synth as S
+from oracle import jev_oracle as O
+from tests.gpu_common import check_suffix_out, gpu_session, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _scaled_layers(src, key, factor):
+    """The seeded layers with one matrix multiplied by a power of two (exact in bfloat16)."""
+    def get(l):
+        W = dict(src.layer(l))
+        W[key] = (W[key] * np.float32(factor)).astype(np.float32)
+        return W
+    return get
+
+
+def test_f16_range_flag():
+    """A SwiGLU output beyond 65504 feeding the float16 down projection is reported by the
+    workspace flag instead of passing silently; in-range calls leave the flag clear."""
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    cfg = S.CONFIGS["m2"]
+    src = S.WeightSource(cfg, 0)
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    say("[flags] m2 seed 0: in-range weights")
+    sess = Session(cfg, src.glob, src.layer, precision="f16_down")
+    sess.prefill(pre["vis"], pre["text_ids"])
+    assert J.jev_workspace_flags(sess.ws) == 0
+    sess.score_suffixes(suf)
+    assert J.jev_workspace_flags(sess.ws) == 0
+    sess.close()
+    # w_up x 2^17: |w| stays far below 65504 (the mirror accepts it) but the up projection,
+    # hence silu(gate) * up, reaches ~1e5 on the float16 plane of the down GEMM
+    say("[flags] m2 seed 0: w_up x 2^17")
+    sess = Session(cfg, src.glob, _scaled_layers(src, "w_up", 2.0 ** 17), precision="f16_down")
+    sess.prefill(pre["vis"], pre["text_ids"])
+    assert J.jev_workspace_flags(sess.ws) & J.JEV_FLAG_F16_RANGE
+    sess.score_suffixes(suf)
+    assert J.jev_workspace_flags(sess.ws) & J.JEV_FLAG_F16_RANGE
+    sess.close()
+
+
+def test_reattach_and_failed_attach():
+    """A second attach replaces the first by its groups alone; an attach that fails while
+    converting leaves the model detached, scoring as the two-term path does."""
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    import torch
+    cfg = S.CONFIGS["m2"]
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    src = S.WeightSource(cfg, 0)
+    ref = O.score_suffixes(src, cfg, pre, suf)
+    # two-term reference on the library
+    sess = Session(cfg, src.glob, src.layer, precision="split")
+    sess.prefill(pre["vis"], pre["text_ids"])
+    two_term = sess.score_suffixes(suf).cpu().numpy()
+    assert J.jev_model_f16_groups(sess.model) == 0
+    # attach q|k|v for every call, then re-attach q|k|v for prefills only
+    buf = torch.empty(J.jev_model_f16_bytes(sess.model, J.JEV_F16_QKV), dtype=torch.uint8, device="cuda:0")
+    J.jev_model_attach_f16(sess.model, J.JEV_F16_QKV, buf)
+    assert J.jev_model_f16_groups(sess.model) == J.JEV_F16_QKV
+    J.jev_model_attach_f16(sess.model, J.JEV_F16_QKV_PREFILL, buf)
+    assert J.jev_model_f16_groups(sess.model) == J.JEV_F16_QKV_PREFILL
+    sess.prefill(pre["vis"], pre["text_ids"])
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, "m2 after re-attach (q|k|v prefill-only)")
+    sess.close()
+    # a weight beyond the float16 range fails the attach: the model runs two-term again
+    say("[attach] w_down x 2^22 (beyond float16): attach fails, model detached")
+    big = Session(cfg, src.glob, _scaled_layers(src, "w_down", 2.0 ** 22), precision="split")
+    buf = torch.empty(J.jev_model_f16_bytes(big.model, J.JEV_F16_DOWN | J.JEV_F16_QKV), dtype=torch.uint8,
+                      device="cuda:0")
+    J.jev_model_attach_f16(big.model, J.JEV_F16_QKV, buf)
+    with pytest.raises(J.JevError) as e:
+        J.jev_model_attach_f16(big.model, J.JEV_F16_DOWN | J.JEV_F16_QKV, buf)
+    assert e.value.code == J.JEV_E_UNSUPPORTED
+    assert J.jev_model_f16_groups(big.model) == 0
+    big.close()
+    # the unscaled model detached the same way scores bit-identically to the two-term path
+    sess = Session(cfg, src.glob, src.layer, precision="split")
+    J.jev_model_attach_f16(sess.model, J.JEV_F16_QKV, buf)
+    J.jev_model_attach_f16(sess.model, 0, None)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    assert np.array_equal(sess.score_suffixes(suf).cpu().numpy(), two_term)
+    sess.close()
+
+
+@pytest.mark.parametrize("terms", [1, 2])
+def test_attn_q_terms_vs_oracle(terms):
+    """Both q forms of the attention meet the bar on a live configuration."""
+    from vlm_shared_prefix_amd import jev as J
+    cfg = S.CONFIGS["m7l"]
+    say(f"[q terms] m7l seed 0, {terms} term(s)")
+    sess, src = gpu_session(cfg, 0)
+    J.jev_model_set_attn_q_terms(sess.model, terms)
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    ref = O.score_suffixes(src, cfg, pre, suf)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"m7l q terms {terms}")
+    sess.close()

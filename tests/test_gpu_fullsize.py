@@ -70,6 +70,33 @@ def test_fullsize_suffixes(name, seed, precision):
     check_suffix_out(got, np.array(g["out"], np.float32), suf["n_cands"], cfg.dtype, f"{name}/s{seed}/{precision}")
 
 
+def test_fullsize_block_skipping():
+    """Config 3 with the candidate rows bypassing 12 of the 28 blocks (15-26; the prefix keeps
+    every block, "FastJEV", §2.3 and §3.4) against the oracle run with the same mask."""
+    path = os.path.join(GOLD, "c3_skip_s0.json")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle output {path}")
+    with open(path) as f:
+        g = json.load(f)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(GOLD, "make_golden.py"))
+    mg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mg)
+    cfg = S.CONFIGS["c3"]
+    assert g["fingerprint"] == mg.fingerprint(cfg, 0), "generated inputs differ from the stored ones"
+    mask = mg.skip_mask(cfg)
+    assert [int(v) for v in mask] == g["skip"]
+    suf = S.suffix_inputs(cfg, 0)
+    sess = session("c3", 0)
+    say(f"[fullsize] c3 seed 0 skipping blocks {np.nonzero(mask)[0].tolist()}")
+    sess.set_skip(mask)
+    try:
+        got = sess.score_suffixes(suf).cpu().numpy()
+    finally:
+        sess.set_skip(None)
+    check_suffix_out(got, np.array(g["out"], np.float32), suf["n_cands"], cfg.dtype, "c3/s0/skip 12 of 28")
+
+
 @pytest.mark.parametrize("B", S.C4_BATCHES)
 def test_fullsize_batch_sweep(B):
     """Config 4: every batch size B gives the answers of the same suffixes in the pool."""

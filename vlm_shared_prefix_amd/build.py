@@ -30,6 +30,45 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host sanitizers: only the host passes of the ABI and planner sources are instrumented (each
+# -fsanitize= sits right after -Xarch_host); device code is built as usual.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_DIR = os.path.join(BUILD_DIR, "sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libjev.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime a host process must preload."""
+    clang = os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libjev.so with AddressSanitizer + UndefinedBehaviorSanitizer on the host code of
+    api.cpp and plan.cpp (kernels.hip unchanged), for the CPU tests of the ABI."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+            cmd[1:1] = SAN_FLAGS
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        objs.append(obj)
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libasan", *SAN_FLAGS, *objs,
+                        "-o", SAN_LIB], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:

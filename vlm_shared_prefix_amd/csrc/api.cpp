@@ -47,6 +47,69 @@ struct Profiler {
   }
 };
 
+// Pinned host staging of each call's metadata.  hipMemcpyAsync from pageable memory may be
+// carried out by the runtime after the call has returned (the source is read when the stream
+// reaches the copy), so the packed metadata is first written into one of kSlots pinned slots
+// and copied from there.  A slot is rewritten only after the copy that last read it has
+// completed (its event), so no pending copy ever sees its bytes change.  Metadata larger
+// than a slot goes through the slots in slot-sized pieces.
+struct StageRing {
+  static constexpr int kSlots = 8;
+  static constexpr size_t kSlotBytes = 1u << 20;
+  bool ready = false;
+  char* host[kSlots] = {};
+  hipEvent_t done[kSlots] = {};
+  bool pending[kSlots] = {};
+  int next = 0;
+  hipError_t init() {
+    if (ready) return hipSuccess;
+    for (int i = 0; i < kSlots; ++i) {
+      hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&host[i]), kSlotBytes, hipHostMallocDefault);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&done[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        release();
+        return e;
+      }
+    }
+    ready = true;
+    return hipSuccess;
+  }
+  // enqueue the host->device copy of bytes [0, n) of src into dst on stream s
+  hipError_t copy(void* dst, const char* src, size_t n, hipStream_t s) {
+    for (size_t off = 0; off < n; off += kSlotBytes) {
+      const size_t len = std::min(kSlotBytes, n - off);
+      const int k = next;
+      next = (next + 1) % kSlots;
+      if (pending[k]) {
+        hipError_t e = hipEventSynchronize(done[k]);
+        if (e != hipSuccess) return e;
+        pending[k] = false;
+      }
+      std::memcpy(host[k], src + off, len);
+      hipError_t e = hipMemcpyAsync(static_cast<char*>(dst) + off, host[k], len, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(done[k], s);
+      if (e != hipSuccess) return e;
+      pending[k] = true;
+    }
+    return hipSuccess;
+  }
+  void release() {
+    for (int i = 0; i < kSlots; ++i) {
+      if (done[i]) {
+        if (pending[i]) (void)hipEventSynchronize(done[i]);
+        (void)hipEventDestroy(done[i]);
+        done[i] = nullptr;
+      }
+      if (host[i]) {
+        (void)hipHostFree(host[i]);
+        host[i] = nullptr;
+      }
+      pending[i] = false;
+    }
+    ready = false;
+  }
+};
+
 struct jev_model {
   jev_config cfg;
   jev_weights w;
@@ -62,11 +125,17 @@ struct jev_model {
   bool f16_o = false;      // wo mirrored
   // blocks the candidate rows bypass in scoring calls (empty: none); prefills run every block
   std::vector<uint8_t> skip;
+  // float16 terms of q in the attention: 0 = by prefix length, 1 or 2 (jev_model_set_attn_q_terms)
+  int q_terms = 0;
   std::atomic<uint64_t> prefills{0}, forwards{0}, rows{0}, launches{0};
   Profiler prof;
   // digest of the metadata last staged into each workspace address (launch-only calls check it)
   std::mutex staged_mu;
   std::unordered_map<const void*, uint64_t> staged;
+  // pinned host slots the calls' metadata is copied from (created by the first staging call;
+  // guarded by staged_mu)
+  StageRing ring;
+  ~jev_model() { ring.release(); }
 };
 
 struct jev_prefix {
@@ -161,19 +230,27 @@ extern "C" size_t jev_model_f16_bytes(const jev_model* m, int32_t groups) {
   return total + 256;   // + the range flag
 }
 
+// Back to the two-term bfloat16 path for every GEMM.
+static void detach_f16(jev_model* m) {
+  m->f16_gu = m->f16_down = m->f16_qkv = m->f16_o = false;
+  m->f16_gu_prefill = m->f16_qkv_prefill = m->f16_o_prefill = false;
+  m->layers16.clear();
+}
+
 extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* buf, size_t bytes, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!m) return fail(JEV_E_INVALID, "null model");
   if (groups & ~kAllGroups) return fail(JEV_E_INVALID, "unknown matrix group bits");
   if (!buf || groups == 0) {   // detach: back to the two-term bf16 path
-    m->f16_gu = m->f16_down = m->f16_qkv = m->f16_o = false;
-    m->f16_gu_prefill = m->f16_qkv_prefill = m->f16_o_prefill = false;
-    m->layers16.clear();
+    detach_f16(m);
     return JEV_OK;
   }
   if (m->cfg.dtype != JEV_BF16) return fail(JEV_E_UNSUPPORTED, "a float16 mirror applies to bf16 models only");
   const size_t need = jev_model_f16_bytes(m, groups);
   if (bytes < need) return fail(JEV_E_WORKSPACE, "mirror buffer smaller than jev_model_f16_bytes");
+  // From here on the buffer is being rewritten: a failure leaves the model detached (a mirror
+  // attached earlier may live in this same buffer and no longer holds its matrices).
+  detach_f16(m);
   size_t n[7];
   layer_matrix_elems(m->cfg, n);
   char* at = static_cast<char*>(buf);
@@ -199,15 +276,24 @@ extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* b
       hipStreamSynchronize(s) != hipSuccess)
     return fail(JEV_E_HIP, "mirror conversion failed");
   if (h_bad) return fail(JEV_E_UNSUPPORTED, "a weight exceeds the float16 range");
+  // every flag follows from `groups` alone; a group mirrored for every call needs no
+  // prefill-only bit
   m->layers16 = std::move(l16);
   m->f16_gu = (groups & JEV_F16_GATE_UP) != 0;
+  m->f16_qkv = (groups & JEV_F16_QKV) != 0;
+  m->f16_o = (groups & JEV_F16_O) != 0;
+  m->f16_down = (groups & JEV_F16_DOWN) != 0;
   m->f16_gu_prefill = !m->f16_gu && (groups & JEV_F16_GATE_UP_PREFILL) != 0;
   m->f16_qkv_prefill = !m->f16_qkv && (groups & JEV_F16_QKV_PREFILL) != 0;
   m->f16_o_prefill = !m->f16_o && (groups & JEV_F16_O_PREFILL) != 0;
-  m->f16_down = (groups & JEV_F16_DOWN) != 0;
-  m->f16_qkv = (groups & JEV_F16_QKV) != 0;
-  m->f16_o = (groups & JEV_F16_O) != 0;
   return JEV_OK;
+}
+
+extern "C" int32_t jev_model_f16_groups(const jev_model* m) {
+  if (!m) return 0;
+  return (m->f16_gu ? JEV_F16_GATE_UP : 0) | (m->f16_qkv ? JEV_F16_QKV : 0) | (m->f16_down ? JEV_F16_DOWN : 0) |
+         (m->f16_o ? JEV_F16_O : 0) | (m->f16_gu_prefill ? JEV_F16_GATE_UP_PREFILL : 0) |
+         (m->f16_qkv_prefill ? JEV_F16_QKV_PREFILL : 0) | (m->f16_o_prefill ? JEV_F16_O_PREFILL : 0);
 }
 
 extern "C" jev_status jev_get_stats(const jev_model* m, jev_stats* out) {
@@ -230,6 +316,24 @@ extern "C" jev_status jev_model_set_skip(jev_model* m, const uint8_t* skip, int3
   bool any = false;
   for (uint8_t b : v) any |= b != 0;
   if (any) m->skip = std::move(v); else m->skip.clear();
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_model_set_attn_q_terms(jev_model* m, int32_t terms) {
+  if (!m) return fail(JEV_E_INVALID, "null model");
+  if (terms < 0 || terms > 2) return fail(JEV_E_INVALID, "terms must be 0, 1 or 2");
+  m->q_terms = terms;
+  return JEV_OK;
+}
+
+extern "C" jev_status jev_workspace_flags(const void* ws, int32_t* flags, void* stream) {
+  if (!ws || !flags) return fail(JEV_E_INVALID, "null argument");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  // the flag word sits at the start of every call's workspace layout
+  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return fail(JEV_E_HIP, "reading the workspace flags failed");
+  *flags = v;
   return JEV_OK;
 }
 
@@ -289,10 +393,10 @@ namespace {
 constexpr size_t kGemmPartFloats = 16ull << 20;        // bound of split-K partials (gemm_bf16_plan)
 
 struct Layout {
-  // metadata (staged from the host in one copy)
-  size_t tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, pseg, ptile, meta_end;
+  // range flag word, then metadata (staged from the host in one copy)
+  size_t flags, tok, pos, seq_start, read_rows, tgt_ridx, tgt_tok, out_n, mask, pseg, ptile, meta_end;
   // float buffers
-  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, logits, rope;
+  size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, lse_slices, rope;
   size_t total;
   int Tc;
 };
@@ -324,6 +428,7 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
     o = align256(o + bytes);
     return at;
   };
+  L.flags = take(4);
   L.tok = take(4ull * T);
   L.pos = take(4ull * T);
   L.seq_start = take(4ull * T);
@@ -355,7 +460,8 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.hsplit = take(bf && need_logits ? 4ull * R * c.hidden : 0);
   L.z = take(4ull * NT);
   L.lse_rows = take(4ull * R);
-  L.logits = take(need_logits ? 4ull * R * c.vocab : 0);
+  // full-vocabulary readout: per row one (max, sum of exp) pair per 128 logits, never the logits
+  L.lse_slices = take(need_logits ? 8ull * R * ((c.vocab + 127) / 128) : 0);
   L.rope = take(bf ? 8ull * T * 64 : 0);
   L.total = o;
   return L;
@@ -374,6 +480,16 @@ extern "C" size_t jev_workspace_bytes(const jev_model* m, int32_t prefix_len, in
 // ---------------------------------------------------------------------------
 namespace {
 enum class Mode { Prefill, Score, Tree };
+
+// Terms of q in the attention's QK^T products: with one term q is rounded once to float16;
+// the second term (q - f16(q)) removes that rounding, which shifts every score of a row
+// coherently and grows in weight with the number of keys a row sees.
+constexpr int kAttnQ2Keys = 2048;   // the automatic choice takes two terms above this many prefix keys
+// keys: the most prefix keys (the longest segment) a row of the call sees.
+int attn_q_terms(const jev_model* m, int keys) {
+  if (m->q_terms == 1 || m->q_terms == 2) return m->q_terms;
+  return keys > kAttnQ2Keys ? 2 : 1;
+}
 
 // Layers a forward runs: all of them for a prefill; in scoring calls the candidate rows bypass
 // the blocks of the model's skip mask ("FastJEV", §2.3 and §3.4: the shared context keeps every
@@ -404,7 +520,7 @@ enum Kind {
 const char* const kKindName[K_NKINDS] = {
     "embed_rows", "rmsnorm_rows", "residual_norm", "rope_table", "qkv_post", "gemm", "gemm_swiglu",
     "splitk_reduce", "rope_qk", "v_transpose", "attn_fwd", "attn_merge", "silu_mul", "target_logits",
-    "cand_logsoftmax", "lm_head_gemm", "row_lse", "tree_finalize", "gemm_f16", "gemm_swiglu_f16", "splitk_swiglu"};
+    "cand_logsoftmax", "lm_head_lse", "lse_merge", "tree_finalize", "gemm_f16", "gemm_swiglu_f16", "splitk_swiglu"};
 
 struct Forward {
   const jev_prefix* pf;
@@ -517,6 +633,7 @@ struct Forward {
     const int HqD = Hq * D, NQKV = nqkv(c);
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
+    int* flags = at<int>(ws, L.flags);
     // GEMMs of a mirrored group take one float16 plane (in the hi slot), and the kernels that
     // produce their inputs write that plane: the input norm and attention output for the
     // q|k|v and o projections, the post-attention norm for gate|up, the SwiGLU output for down
@@ -541,7 +658,7 @@ struct Forward {
     const double rowbytes = 4.0 * T * H;
 
     if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 1.5,
-                              [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, x, s); }))
+                              [&] { return launch_embed(true, m->w.embed, tok, T, H, vis, x, flags, s); }))
       return st;
     const std::vector<int> layers = run_layers(m, mode);
     if (layers.empty()) return JEV_OK;
@@ -551,10 +668,13 @@ struct Forward {
       return st;
     if (jev_status st = run_k(K_RESNORM, 0.0, 2 * rowbytes, [&] {
           return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[layers[0]].attn_norm, c.rms_eps, a_hi,
-                                      a_lo, wide, fq, s);
+                                      a_lo, wide, fq, flags, s);
         }))
       return st;
 
+    // q as one float16 term, or two (q_hi + q_lo) when rows see long prefixes (jev_model_set_attn_q_terms)
+    const int q_terms = attn_q_terms(m, *std::max_element(pf->seg_len.begin(), pf->seg_len.end()));
+    const float qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
     // attention splits: about one block per compute unit (partials merged when > 1)
     const int own_tiles = attn_own_tiles(plan.seq_start.data(), T, Hq / Hkv);
     const int n_split = attn_splits(T, Hq / Hkv, Hkv, plan.seg_keys >= 0 ? plan.seg_keys : P, own_tiles);
@@ -586,10 +706,10 @@ struct Forward {
         kld = L.Tc;
       }
       _Float16* q_hi = at<_Float16>(ws, L.q);
-      _Float16* q_lo = q_hi + attn_q_plane_elems(T, Hq, Hkv);
-      if (jev_status st = run_k(K_QKVPOST, 0.0, (double)T * NQKV * 4 * sp + (double)T * (2 * HqD + 2 * Hkv * D) * 2, [&] {
+      _Float16* q_lo = q_terms == 2 ? q_hi + attn_q_plane_elems(T, Hq, Hkv) : nullptr;
+      if (jev_status st = run_k(K_QKVPOST, 0.0, (double)T * NQKV * 4 * sp + (double)T * (q_terms * HqD + 2 * Hkv * D) * 2, [&] {
             return launch_qkv_post(sp > 1 ? part : big, NQKV, (size_t)T * NQKV, sp, T, Hq, Hkv, rope, q_hi, q_lo,
-                                   kdst, kld, vdst, kld, s);
+                                   kdst, kld, vdst, kld, qscale, flags, s);
           }))
         return st;
       if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
@@ -614,8 +734,8 @@ struct Forward {
       a.lse_part = at<float>(ws, L.lse_part);
       a.oh = a_hi; a.ol = a_lo;
       a.o_f16 = fo ? 1 : 0;
-      a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, s); })) return st;
+      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, q_terms, 1, s); }))
+        return st;
       if (n_split > 1) {
         if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 1) * T * HqD, [&] {
               return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, fo, s);
@@ -626,7 +746,7 @@ struct Forward {
       if (jev_status st = gemm_deferred(A_o, HqD, T, HqD, WO.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H, W.mlp_norm, c.rms_eps,
-                                        a_hi, a_lo, wide, fg, s);
+                                        a_hi, a_lo, wide, fg, flags, s);
           }))
         return st;
       // activation bytes per element: two bf16 planes, or one float16 plane
@@ -639,16 +759,16 @@ struct Forward {
         if (jev_status st = gemm_deferred(A_g, wide, T, H, WG.w_gate, I, WG.w_up, I, nullptr, 0, part, 2 * I, 0, &sg))
           return st;
         if (jev_status st = run_k(K_SPLITSWIGLU, 0.0, 4.0 * sg * T * 2 * I + out_b * T * I, [&] {
-              return launch_splitk_swiglu(part, sg, T, I, u_hi, fd ? nullptr : u_lo, I, s);
+              return launch_splitk_swiglu(part, sg, T, I, u_hi, fd ? nullptr : u_lo, I, flags, s);
             }))
           return st;
       } else if (jev_status st = run_k(fg ? K_SWIGLU16 : K_SWIGLU, 2.0 * T * 2 * I * H,
                                 2.0 * 2 * I * H + in_b * T * H + out_b * T * I, [&] {
             uint16_t* ul = fd ? nullptr : u_lo;   // u as one float16 plane for a float16 down GEMM
             return fg ? launch_gemm_swiglu_f16(a_hi, wide, T, H, static_cast<const uint16_t*>(WG.w_gate),
-                                               static_cast<const uint16_t*>(WG.w_up), I, u_hi, ul, I, s)
+                                               static_cast<const uint16_t*>(WG.w_up), I, u_hi, ul, I, flags, s)
                       : launch_gemm_swiglu(a_hi, a_lo, wide, T, H, static_cast<const uint16_t*>(W.w_gate),
-                                           static_cast<const uint16_t*>(W.w_up), I, u_hi, ul, I, s);
+                                           static_cast<const uint16_t*>(W.w_up), I, u_hi, ul, I, flags, s);
           }))
         return st;
       // down: x += u·W_dᵀ, then the next layer's input norm
@@ -657,7 +777,7 @@ struct Forward {
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
                                         next_g ? next_g : W.mlp_norm, c.rms_eps, next_g ? a_hi : nullptr,
-                                        next_g ? a_lo : nullptr, wide, fq, s);
+                                        next_g ? a_lo : nullptr, wide, fq, flags, s);
           }))
         return st;
     }
@@ -673,6 +793,7 @@ struct Forward {
     const int HqD = Hq * D, NQKV = nqkv(c);
     const int wide = std::max(std::max(H, HqD), I);
     float* x = at<float>(ws, L.x);
+    int* flags = at<int>(ws, L.flags);
     float* act = at<float>(ws, L.act);
     const AOp A_act{act, nullptr, nullptr};
     float* big = at<float>(ws, L.big);
@@ -685,7 +806,7 @@ struct Forward {
     const double rowbytes = 4.0 * T * H;
 
     if (jev_status st = run_k(K_EMBED, 0.0, rowbytes * 2.0,
-                              [&] { return launch_embed(false, m->w.embed, tok, T, H, vis, x, s); }))
+                              [&] { return launch_embed(false, m->w.embed, tok, T, H, vis, x, flags, s); }))
       return st;
     const int2* pseg = plan.pseg.empty() ? nullptr : at<int2>(ws, L.pseg);
     const double attn_flops = 4.0 * D * Hq * (prefix_pairs + own_pairs);
@@ -780,12 +901,16 @@ struct Forward {
       return run_k(K_CANDSM, 0.0, 8.0 * NT,
                [&] { return launch_cand_logsoftmax(z, at<int>(ws, L.out_n), B, NT / std::max(B, 1), out_a, s); });
     }
-    float* logits = at<float>(ws, L.logits);
-    if (jev_status st = gemm(AOp{h, h_hi, h_lo}, H, R, H, m->w.lm_head, c.vocab, nullptr, 0, nullptr, 0, logits,
-                             c.vocab, 0, K_LMHEAD))
+    // LSE over all V logits of every readout row, the logits never leaving the GEMM's registers
+    float2* slices = at<float2>(ws, L.lse_slices);
+    const double slice_bytes = 8.0 * R * ((c.vocab + 127) / 128);
+    if (jev_status st = run_k(K_LMHEAD, 2.0 * R * c.vocab * H, (double)c.vocab * H * we + slice_bytes, [&] {
+          return launch_lmhead_lse(bf, h, h_hi, h_lo, H, R, m->w.lm_head, c.vocab, slices, s);
+        }))
       return st;
-    if (jev_status st = run_k(K_ROWLSE, 0.0, 4.0 * R * c.vocab,
-                          [&] { return launch_row_lse(logits, c.vocab, R, at<float>(ws, L.lse_rows), s); }))
+    if (jev_status st = run_k(K_ROWLSE, 0.0, slice_bytes + 4.0 * R, [&] {
+          return launch_lse_merge(slices, R, c.vocab, at<float>(ws, L.lse_rows), s);
+        }))
       return st;
     const int Q = (int)plan.out_n.size();
     return run_k(K_TREEFIN, 0.0, 8.0 * NT, [&] {
@@ -831,7 +956,8 @@ jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hi
       return fail(JEV_E_INVALID, "workspace does not hold this call's metadata: stage it with the copying call first");
     return JEV_OK;
   }
-  HIP_OK(hipMemcpyAsync(ws, buf.data(), L.meta_end, hipMemcpyHostToDevice, s));
+  HIP_OK(m->ring.init());
+  HIP_OK(m->ring.copy(ws, buf.data(), L.meta_end, s));
   // bounded: a caller cycling through many workspaces forgets the oldest digests (a
   // launch-only call on such a workspace then asks for a fresh staging call)
   if (m->staged.size() >= kMaxStagedWorkspaces && !m->staged.count(ws)) m->staged.clear();

@@ -31,8 +31,8 @@ inline size_t attn_q_plane_elems(int T, int Hq, int Hkv) {
   return (size_t)Hkv * attn_q_rows(T, Hq / Hkv) * 128;
 }
 struct AttnArgs {
-  const _Float16* q;       // q rounded to f16 (hi), layout above
-  const _Float16* q_lo;    // q - hi, rounded to f16, same layout
+  const _Float16* q;       // q * log2(e)/sqrt(128) rounded to f16 (hi), layout above
+  const _Float16* q_lo;    // the rounding remainder as f16, same layout (two-term q only)
   int T, Hq, Hkv, G;
   const _Float16* kp;      // prefix K  [Hkv][ldp][128]
   const _Float16* vtp;     // prefix Vt [Hkv][128][ldp], columns [P, round8(P)) zero
@@ -55,7 +55,6 @@ struct AttnArgs {
   uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1) ...
   uint16_t* ol;
   int o_f16;               // ... or (non-zero) one float16 plane of o in oh
-  float scale_log2;        // log2(e) / sqrt(128)
 };
 
 // float32 attention (head_dim 64 or 128).
@@ -75,9 +74,13 @@ struct AttnArgsF {
   float* o;                // [T][Hq*D]
 };
 
-// Row t: E[tok[t]] for tok[t] >= 0, vis[-1 - tok[t]] otherwise.
+// Range flag of a forward (nullable everywhere): bit 0 is set by any kernel that writes a
+// float16 activation plane (q/k/v, a norm's float16 output, the SwiGLU output) and meets a
+// value outside the float16 range or not finite.
+constexpr int kFlagF16Range = 1;
+// Row t: E[tok[t]] for tok[t] >= 0, vis[-1 - tok[t]] otherwise.  Clears *flags.
 hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, float* x,
-                        hipStream_t s);
+                        int* flags, hipStream_t s);
 // y (float32) and/or yh/yl (bfloat16 hi/lo planes) may be null.
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
                           float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s);
@@ -95,7 +98,8 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
 // gate|up GEMM with the SwiGLU epilogue: u = silu(A·W_gateᵀ) * (A·W_upᵀ) as bf16 hi/lo planes [M][ldu],
 // or as one float16 plane into uh when ul is null.
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
-                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, int* flags,
+                              hipStream_t s);
 // Single-pass float16 GEMM: A is one float16 plane, seg holds float16 weights; otherwise as
 // launch_gemm_bf16 (split partials when *eff_splits > 1).
 GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap);
@@ -104,13 +108,14 @@ hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmS
 // gate|up GEMM with the SwiGLU epilogue on a float16 activation plane and float16 weights; u as in
 // launch_gemm_swiglu (hi/lo planes, or one float16 plane when ul is null).
 hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, const uint16_t* w_gate,
-                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s);
+                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, int* flags,
+                                  hipStream_t s);
 // gate|up with few output tiles (the fused kernel would fill under one block per compute
 // unit): run it as a plain split-K GEMM over [W_gate | W_up] into [splits][M][2I] partials (or
 // [M][2I] when one split), then launch_splitk_swiglu writes u as launch_gemm_swiglu would.
 bool swiglu_use_split(int M, int I, size_t part_cap);
 hipError_t launch_splitk_swiglu(const float* part, int splits, int M, int I, uint16_t* uh, uint16_t* ul, int ldu,
-                                hipStream_t s);
+                                int* flags, hipStream_t s);
 // float16 copy of n bfloat16 values (n % 8 == 0); sets *bad = 1 if a finite value exceeds the
 // float16 range (*bad is not cleared).
 hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int* bad, hipStream_t s);
@@ -118,15 +123,16 @@ hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int*
 // planes, or one float16 plane into yh when f16out (skipped when yh is null).  H % 4 == 0, H <= 8192.
 hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
                                 int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, bool f16out,
-                                hipStream_t s);
-// Sum of `splits` projection partials (row stride lds) -> RoPE (table cs) -> q hi/lo [T][Hq][128] f16,
+                                int* flags, hipStream_t s);
+// Sum of `splits` projection partials (row stride lds) -> RoPE (table cs) -> q * qscale as f16 hi (and
+// lo = the rounding remainder, when q_lo is not null) in the attention's operand order,
 // K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1 and zeros in
 // columns T..round8(T)-1 (ldv >= round8(T)).
 // cs[t][i] = (cos, sin) of pos[t] * theta^(-2i/128), i < 64 (head_dim 128).
 hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s);
 hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
                            const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
-                           hipStream_t s);
+                           float qscale, int* flags, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
                                 hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
@@ -149,7 +155,10 @@ int attn_own_tiles(const int* seq_start, int T, int G);
 // the keys [z, w) every one of its rows sees (z >= w when there are none); returns the largest
 // tile count y - x.
 int attn_seg_tiles(const int* pseg, int T, int G, int* ptile);
-hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
+// q_terms 1: q as one float16 term (q_lo unused); 2: q = q_hi + q_lo.  q is pre-scaled by
+// log2(e)/sqrt(128) (qkv_post's qscale), so the kernel's scores are in log2 units.
+// kg 1: 128-row blocks; kg 2: 64-row blocks whose two wave pairs take alternate key tiles.
+hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, int kg, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, bool f16out, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);
@@ -157,7 +166,13 @@ hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh
 hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,
                                 int NT, float* z, hipStream_t s);
 hipError_t launch_cand_logsoftmax(const float* z, const int* n_cands, int B, int C, float* out, hipStream_t s);
-hipError_t launch_row_lse(const float* logits, int V, int R, float* lse, hipStream_t s);
+// Full-vocabulary log-sum-exp of R rows without storing the [R][V] logits: the LM-head GEMM
+// (bf16 models: h as bf16 hi/lo planes, two matrix-core passes; float32 models: h in float32)
+// leaves per-row (max, sum of exp) pairs of each 128-column slice in part [R][ceil(V/128)];
+// launch_lse_merge combines them in a fixed order into lse[R].
+hipError_t launch_lmhead_lse(bool bf16, const float* h, const uint16_t* h_hi, const uint16_t* h_lo, int H, int R,
+                             const void* W, int V, float2* part, hipStream_t s);
+hipError_t launch_lse_merge(const float2* part, int R, int V, float* lse, hipStream_t s);
 hipError_t launch_tree_finalize(const float* z, const float* lse_rows, const int* ridx, const int* tok,
                                 const int* n_cands, int Q, int C, int K, float* score, float* norm,
                                 hipStream_t s);

@@ -18,6 +18,8 @@
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
@@ -51,6 +53,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Range flag of the float16 activation planes: bit 0 of *flags is set when a value written
+// to a float16 plane lies outside the float16 range (|v| > 65504) or is not finite.
+__device__ __forceinline__ bool f16_out_of_range(float v) { return !(fabsf(v) <= 65504.f); }
+__device__ __forceinline__ void flag_f16_range(int* flags, bool bad) {
+  if (bad && flags) atomicOr(flags, 1);
+}
+
 // block of 256 threads: sum over the block, result broadcast to all threads
 __device__ __forceinline__ float block_sum256(float v, float* red) {
   v = wave_sum(v);
@@ -67,8 +76,10 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // ----------------------------------------------------------------------------
 template <typename WT>
 __global__ void __launch_bounds__(256) embed_rows(const WT* __restrict__ E, const int* __restrict__ tok, int T,
-                                                  int H, const WT* __restrict__ vis, float* __restrict__ x) {
+                                                  int H, const WT* __restrict__ vis, float* __restrict__ x,
+                                                  int* __restrict__ flags) {
   const int t = blockIdx.x;
+  if (t == 0 && threadIdx.x == 0 && flags) *flags = 0;   // the forward's range flag starts clear
   if (t >= T) return;
   const int k = tok[t];
   const WT* src = (k < 0) ? vis + (size_t)(-1 - k) * H : E + (size_t)k * H;
@@ -282,12 +293,12 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
 #define G2M 128
 #define G2N 256
 #define G2K 32
-template <bool SWIGLU, bool F16>
+template <bool SWIGLU, bool F16, bool LSE = false>
 __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah, const u16* __restrict__ Al, int lda,
                                                 int M, int K, GemmSegs seg, int N, int m_tiles, int n_tiles,
                                                 int splits, int k_chunk, float* __restrict__ C, int ldc,
                                                 size_t split_stride, int accum, u16* __restrict__ oh,
-                                                u16* __restrict__ ol) {
+                                                u16* __restrict__ ol, int* __restrict__ flags) {
   __shared__ __attribute__((aligned(16))) u16 sAh0[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sAl0[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sW0[G2N * G2K];
@@ -442,7 +453,38 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
   }
 
   if (m0 + wm * 64 >= M) return;
+  if (LSE) {
+    // Full-vocabulary readout: the logits stay in registers.  Per row of the wave's 64, the
+    // max and the sum of exp over its 128 columns (those past N excluded), reduced across
+    // the 32 lanes that hold the row's columns: one (max, sum) pair per row and 128-column
+    // slice, in C viewed as float2 [M][ldc].
+    float2* part = reinterpret_cast<float2*>(C);
+    const int slice = ntile * 2 + wn;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        float mx = NEG_INF;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n0 + wn * 128 + j * 32 + ql < N) mx = fmaxf(mx, acc[i][j][r]);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float se = 0.f;
+        if (mx != NEG_INF) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (n0 + wn * 128 + j * 32 + ql < N) se += expf(acc[i][j][r] - mx);
+        }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (ql == 0 && row < M) part[(size_t)row * ldc + slice] = make_float2(mx, se);
+      }
+    return;
+  }
   if (SWIGLU) {
+    bool bad = false;
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
       const int col = n0 + wn * 64 + jp * 32 + ql;
@@ -455,6 +497,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
             const float g = acc[i][2 * jp][r], u = acc[i][2 * jp + 1][r];
             const float val = g / (1.0f + expf(-g)) * u;
             if (ol == nullptr) {   // one float16 plane
+              bad |= f16_out_of_range(val);
               reinterpret_cast<f16*>(oh)[(size_t)row * ldc + col] = (f16)val;
             } else {
               const u16 h = f32_to_bf16(val);
@@ -464,6 +507,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
           }
         }
     }
+    flag_f16_range(flags, bad);
     return;
   }
   float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
@@ -508,7 +552,7 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ p
 // ----------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) splitk_swiglu(const float* __restrict__ part, size_t split_stride,
                                                      int splits, int M, int I, u16* __restrict__ uh,
-                                                     u16* __restrict__ ul, int ldu) {
+                                                     u16* __restrict__ ul, int ldu, int* __restrict__ flags) {
   const int I4 = I >> 2;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)M * I4) return;
@@ -525,9 +569,15 @@ __global__ void __launch_bounds__(256) splitk_swiglu(const float* __restrict__ p
   const size_t o = (size_t)row * ldu + c;
   if (ul == nullptr) {
     f16x4 v4;
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v4[j] = (f16)(gv[j] / (1.0f + expf(-gv[j])) * uv[j]);
+    for (int j = 0; j < 4; ++j) {
+      const float v = gv[j] / (1.0f + expf(-gv[j])) * uv[j];
+      bad |= f16_out_of_range(v);
+      v4[j] = (f16)v;
+    }
     *reinterpret_cast<f16x4*>(uh + o) = v4;
+    flag_f16_range(flags, bad);
     return;
   }
   u16 h[4], l[4];
@@ -683,13 +733,20 @@ __global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src
 // Key tiles of 64: a row tile sees the prefix tiles [0, ceil(P/64)) followed by
 // the tiles of its own keys (from the first row's sequence start, causal within
 // the row's sequence, or the row's 64-bit ancestor mask over its group).
-// blockIdx.z = split takes the contiguous share [z*n/S, (z+1)*n/S) of those n
-// tiles.  Tiles arrive by direct global->LDS loads (16 B per lane) into a
-// double buffer, the next tile's loads in flight while the current one is
-// computed.  LDS rows are XOR-swizzled by 16 B chunk so the operand reads are
-// bank-conflict free.  With S == 1 the block writes o as bf16 hi/lo planes;
-// otherwise it writes a normalised partial o and its log2-sum-exp for
-// attn_merge.
+// Split z takes the contiguous share [z*n/S, (z+1)*n/S) of those n tiles.  Tiles
+// arrive by direct global->LDS loads (16 B per lane) into a double buffer, the
+// next tile's loads in flight while the current one is computed.  LDS rows are
+// XOR-swizzled by 16 B chunk so the operand reads are bank-conflict free.  With
+// S == 1 the block writes o as bf16 hi/lo planes (or one f16 plane); otherwise a
+// normalised partial o and its log2-sum-exp for attn_merge.
+//
+// Arithmetic: q arrives multiplied by log2(e)/sqrt(D) (qkv_post), so a score is in
+// log2 units; the score accumulators start at -m (the row's reference max), so the
+// MFMAs leave score - m and a weight is exp2 of it with no further arithmetic.
+// QT = 1 takes q rounded once to f16; QT = 2 adds the second term q - f16(q)
+// (twice the score MFMAs), for rows that see long prefixes.  The weights are
+// rounded to f16 in pairs (v_cvt_pk) and the row sum adds exactly those rounded
+// values (v_dot2 against 1, 1).
 // ----------------------------------------------------------------------------
 #define AT_BR 128
 #define AT_BK 64
@@ -724,21 +781,39 @@ struct AttnTile {
   bool own;
 };
 
+template <int QT, int KG>
 __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16 sK0[AT_BK * 128];
-  __shared__ __attribute__((aligned(16))) f16 sK1[AT_BK * 128];
-  __shared__ __attribute__((aligned(16))) f16 sV0[128 * AT_BK];
-  __shared__ __attribute__((aligned(16))) f16 sV1[128 * AT_BK];
+  // KG key groups: with KG = 2 the waves w and w + 2 hold the same rows (64 per block) and
+  // take alternate key tiles, each group with its own double buffer; group 1 hands its
+  // softmax state to group 0 through LDS at the end
+  constexpr int RB = AT_BR / KG;    // query rows per block
+  constexpr int NWR = 4 / KG;       // waves (of 32 rows) per key group
+  __shared__ __attribute__((aligned(16))) f16 smem[KG * 2 * 2 * AT_BK * 128];
+  // group g, buffer b: K tile at smem + (g * 2 + b) * 2 tiles, V^T tile right after it
+  auto sk = [&](int g, int b) { return smem + (size_t)((g * 2 + b) * 2) * (AT_BK * 128); };
+  auto sv = [&](int g, int b) { return smem + (size_t)((g * 2 + b) * 2 + 1) * (AT_BK * 128); };
 
   // row tiles in reverse order: with long causal sequences the later tiles see the most keys
   // and are dispatched first
-  const int x = gridDim.x - 1 - blockIdx.x, hk = blockIdx.y, z = blockIdx.z, ns = a.n_split;
-  const int G = a.G, T = a.T, Hq = a.Hq;
+  const int G = a.G, T = a.T, Hq = a.Hq, ns = a.n_split;
   const int R = G * T;
-  const int r0 = x * AT_BR;
+  const int n_rt = (R + RB - 1) / RB;
+  // Block order.  With prefix keys (scoring calls) each XCD (blocks are dispatched to the 8
+  // XCDs round-robin) takes a contiguous run of (KV head, row tile, split) items, so the row
+  // tiles of a KV head share its prefix K/V through one L2.  Without them (prefills: causal
+  // rows whose work grows with the row) consecutive items go to different XCDs, which keeps
+  // the heavy and the light row tiles spread over all of them.
+  const int per = gridDim.x >> 3;
+  const int vv = a.P > 0 ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
+  if (vv >= n_rt * a.Hkv * ns) return;
+  const int z = vv % ns;
+  const int x = n_rt - 1 - (vv / ns) % n_rt;   // row tiles of most keys first
+  const int hk = vv / (ns * n_rt);
+  const int r0 = x * RB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hl = lane >> 5;
-  const int r = r0 + wave * 32 + ql;
+  const int wr = wave % NWR, kgrp = wave / NWR;
+  const int r = r0 + wr * 32 + ql;
   const bool rvalid = r < R;
   const int rc = rvalid ? r : R - 1;          // clamped row: loads stay in bounds
   const int t = rc / G;
@@ -747,35 +822,45 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   // Prefix key tiles of this row tile: [ptb, ptb + ntp), every one of them visible in full to
   // all of its rows when inside [vis_lo, vis_hi).  One shared prefix: all ceil(P/64) tiles,
   // visible below P.  Segmented prefixes: the hull of the rows' segments (host table).
-  const int4 pt = a.ptile ? a.ptile[x] : make_int4(0, (a.P + AT_BK - 1) / AT_BK, 0, a.P);
+  // (the host's table is per 128-row tile; a smaller row tile takes its tile's entry)
+  const int4 pt = a.ptile ? a.ptile[r0 / AT_BR] : make_int4(0, (a.P + AT_BK - 1) / AT_BK, 0, a.P);
   const int ptb = pt.x, ntp = pt.y - pt.x, vis_lo = pt.z, vis_hi = pt.w;
   // The splits divide ntp + own_tiles key tiles (own_tiles: the host's bound on any row
   // tile's own-key tiles), so a block whose range starts on a prefix tile issues that
   // tile's loads before the sequence starts it depends on for the rest have arrived.
   const int nt_u = ntp + a.own_tiles;
   const int vb = (int)(((long)z * nt_u) / ns), ve_u = (int)(((long)(z + 1) * nt_u) / ns);
-  const bool early = vb < ntp && vb < ve_u;
-  if (early) {
-    const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
-    const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
-    const int k0 = (ptb + vb) * AT_BK;
+  const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
+  const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
+  // K tile: 64 rows of 256 B, chunk c (16 B) of key row k at chunk position c ^ (k & 15).
+  // V^T tile: 128 dim rows of 128 B, key chunk c of dim d at position c ^ ((d >> 1) & 7).
+  // Rows / chunks at or past ke load row / column 0 instead (finite, never weighted);
+  // a V chunk straddling ke holds later rows of this call or zeroed padding.
+  auto load_kv = [&](const f16* K, const f16* V, int ld, int k0, int ke, f16* dk, f16* dv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = i * 256 + tid;
       const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
       const int key = k0 + row;
-      dma16(Kp, ((key < a.P ? key : 0) * 128 + c * 8) * 2, sK0 + (i * 256 + wave * 64) * 8);
+      dma16(K, ((key < ke ? key : 0) * 128 + c * 8) * 2, dk + (i * 256 + wave * 64) * 8);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = i * 256 + tid;
       const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
       const int key = k0 + c * 8;
-      dma16(Vp, (d * a.ldp + (key < a.P ? key : 0)) * 2, sV0 + (i * 256 + wave * 64) * 8);
+      dma16(V, (d * ld + (key < ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
     }
+  };
+  // the first iteration's prefix tiles go out before the sequence metadata they do not need
+  bool early[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    early[g] = vb + g < ntp && vb + g < ve_u;
+    if (early[g]) load_kv(Kp, Vp, a.ldp, (ptb + vb + g) * AT_BK, a.P, sk(g, 0), sv(g, 0));
   }
 
-  const int t_first = r0 / G, t_last = min(R - 1, r0 + AT_BR - 1) / G;
+  const int t_first = r0 / G, t_last = min(R - 1, r0 + RB - 1) / G;
   const int s_first = a.seq_start[t_first];
   const int max_start = a.seq_start[t_last];
   const int my_start = a.seq_start[t];
@@ -785,14 +870,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 
   // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
   // of q, which would shift every score of the row coherently, stays out.
-  f16x8 qreg[8], qlo[8];
+  f16x8 qreg[8], qlo[QT == 2 ? 8 : 1];
   {
     // operand-ordered q: slice c of the wave's 32 rows is one contiguous 1 KB run
     const size_t qo = ((size_t)hk * attn_q_rows(T, G) + (rc & ~31)) * 128 + (size_t)(hl * 32 + (rc & 31)) * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 512);
-      qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 512);
+      if (QT == 2) qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 512);
     }
   }
 
@@ -807,7 +892,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   auto tile = [&](int v) {
     AttnTile s;
     if (v < ntp) {
-      s.K = a.kp + (size_t)hk * a.ldp * 128; s.V = a.vtp + (size_t)hk * 128 * a.ldp; s.ld = a.ldp;
+      s.K = Kp; s.V = Vp; s.ld = a.ldp;
       s.k0 = (ptb + v) * AT_BK; s.ke = a.P; s.own = false;
     } else {
       s.K = a.ks + (size_t)hk * a.lds * 128; s.V = a.vts + (size_t)hk * 128 * a.lds; s.ld = a.lds;
@@ -815,29 +900,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     }
     return s;
   };
-  // K tile: 64 rows of 256 B, chunk c (16 B) of key row k at chunk position c ^ (k & 15).
-  // V^T tile: 128 dim rows of 128 B, key chunk c of dim d at position c ^ ((d >> 1) & 7).
-  // Rows / chunks at or past ke load row / column 0 instead (finite, never weighted);
-  // a V chunk straddling ke holds later rows of this call or zeroed padding.
-  auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = i * 256 + tid;
-      const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
-      const int key = s.k0 + row;
-      dma16(s.K, ((key < s.ke ? key : 0) * 128 + c * 8) * 2, dk + (i * 256 + wave * 64) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = i * 256 + tid;
-      const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
-      const int key = s.k0 + c * 8;
-      dma16(s.V, (d * s.ld + (key < s.ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
-    }
-  };
+  auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) { load_kv(s.K, s.V, s.ld, s.k0, s.ke, dk, dv); };
+  const int n_it = (nt + KG - 1) / KG;   // iteration it: group g takes tile vb + it * KG + g
 
   const int prow = attn_key_perm(ql);
-  const float sl = a.scale_log2;
   float m_ref = NEG_INF, l_run = 0.f;   // m_ref: reference max of the row, in scaled log2 units
   f32x16 acc[4];
 #pragma unroll
@@ -845,22 +911,45 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
 
-  auto step = [&](int i, const f16* sk, const f16* sv, f16* nk, f16* nv) {
-    if (i + 1 < nt) load_tile(tile(vb + i + 1), nk, nv);   // in flight during this tile
+  auto step = [&](int it, int b) {
+#pragma unroll
+    for (int g = 0; g < KG; ++g)   // the next iteration's tiles, in flight during this one
+      if ((it + 1) * KG + g < nt) load_tile(tile(vb + (it + 1) * KG + g), sk(g, b ^ 1), sv(g, b ^ 1));
+    const int i = it * KG + kgrp;
+    if (i < nt) {
+    const f16* skb = sk(kgrp, b);
+    const f16* svb = sv(kgrp, b);
+    // scores start at -m_use (q carries the log2(e)/sqrt(D) scale): the MFMAs leave
+    // score - m_use, in log2 units, and a weight is exp2 of it
     f32x16 s[2];
+    const float m_init = (m_ref == NEG_INF) ? 0.f : -m_ref;
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[hs][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[hs][e] = m_init;
+    // the K operands of half the tile's dims are read ahead of their MFMAs (one LDS round
+    // trip per half instead of one per 16-dim step)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int ch = (2 * c + hl) ^ (prow & 15);
-      const f16x8 k0op = *reinterpret_cast<const f16x8*>(sk + prow * 128 + ch * 8);
-      const f16x8 k1op = *reinterpret_cast<const f16x8*>(sk + (32 + prow) * 128 + ch * 8);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qreg[c], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qreg[c], s[1], 0, 0, 0);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op, qlo[c], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op, qlo[c], s[1], 0, 0, 0);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f16x8 k0op[4], k1op[4];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int ch = (2 * (4 * h2 + c4) + hl) ^ (prow & 15);
+        k0op[c4] = *reinterpret_cast<const f16x8*>(skb + prow * 128 + ch * 8);
+        k1op[c4] = *reinterpret_cast<const f16x8*>(skb + (32 + prow) * 128 + ch * 8);
+      }
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int c = 4 * h2 + c4;
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qreg[c], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qreg[c], s[1], 0, 0, 0);
+        if (QT == 2) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qlo[c], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qlo[c], s[1], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);            // the 8 LDS reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, QT == 2 ? 16 : 8, 0);   // then their MFMAs
     }
     // Masks only where some row of the block does not see the whole tile (uniform test):
     // a prefix tile reaching outside [vis_lo, vis_hi) (the partial last tile, segment
@@ -887,23 +976,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hs][e]);
-    mx = halves_max(mx) * sl;
-    // The reference max moves only when a tile max exceeds it by more than 8: the
-    // weights p = 2^(s*scale - m_ref) stay below 2^8 (exact to f16's relative
+    mx = halves_max(mx);
+    // The reference max moves only when a score exceeds it by more than 8 (log2 units):
+    // the weights p = 2^(score - m_ref) stay below 2^8 (exact to f16's relative
     // precision), and the accumulators are rescaled on few tiles.
-    const bool grow = mx > m_ref + 8.f;
+    const bool first = m_ref == NEG_INF;
+    const bool grow = first ? (mx != NEG_INF) : (mx > 8.f);
     if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_ref;
-      const float alpha = (m_ref == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      const float d = grow ? mx : 0.f;
+      const float alpha = grow ? (first ? 0.f : __builtin_amdgcn_exp2f(-mx)) : 1.f;
+      if (grow) m_ref = (first ? 0.f : m_ref) + mx;
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
-      m_ref = m_new;
+        for (int e = 0; e < 16; ++e) acc[dd][e] *= alpha;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[hs][e] -= d;
     }
-    const float m_use = (m_ref == NEG_INF) ? 0.f : m_ref;
-    // the row sum is taken in f32 and p is rounded to nearest f16 for the P·V product
+    // p is rounded to nearest f16 in pairs; the row sum adds exactly the rounded weights
     float rs = 0.f;
     f16x8 pops[2][2];
 #pragma unroll
@@ -911,10 +1004,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[hs][8 * p + j], sl, -m_use));
-          rs += pv;
-          pops[hs][p][j] = (f16)pv;
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 e2 = {__builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j]), __builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j + 1])};
+          const f16x2 h2 = __builtin_convertvector(e2, f16x2);
+          rs = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.0f, (f16)1.0f}, rs, false);
+          pops[hs][p][2 * j] = h2[0];
+          pops[hs][p][2 * j + 1] = h2[1];
         }
     l_run += halves_sum(rs);
     // O^T += V^T · P^T, four 16-key steps
@@ -926,72 +1021,110 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d = dt * 32 + ql;
-          const f16x8 vop = *reinterpret_cast<const f16x8*>(sv + d * AT_BK + ((c ^ ((d >> 1) & 7)) * 8));
+          const f16x8 vop = *reinterpret_cast<const f16x8*>(svb + d * AT_BK + ((c ^ ((d >> 1) & 7)) * 8));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pops[hs][p], acc[dt], 0, 0, 0);
         }
       }
-    // The next tile's loads have landed and every wave is done with this tile's buffers.
+    }
+    // The next tiles' loads have landed and every wave is done with this tile's buffers.
     // (The wait is a builtin so the compiler knows the loads are complete; the barrier is
     // asm with a memory clobber so no LDS access moves across it.)
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
-  if (nt > 0 && !early) load_tile(tile(vb), sK0, sV0);
-  // the first tile has landed (or, with no tile to process, the early loads are done
+#pragma unroll
+  for (int g = 0; g < KG; ++g)
+    if (g < nt && !early[g]) load_tile(tile(vb + g), sk(g, 0), sv(g, 0));
+  // the first tiles have landed (or, with no tile to process, the early loads are done
   // before the block's LDS is released)
   __builtin_amdgcn_s_waitcnt(0x70);
   if (nt > 0) asm volatile("s_barrier" ::: "memory");
-  for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
-    step(i, sK0, sV0, sK1, sV1);
-    if (i + 1 < nt) step(i + 1, sK1, sV1, sK0, sV0);
+  for (int it = 0; it < n_it; it += 2) {   // two iterations per trip: buffers named statically
+    step(it, 0);
+    if (it + 1 < n_it) step(it + 1, 1);
+  }
+  if (KG == 2) {
+    // key group 1 hands (m_ref, l_run, acc) to group 0 through LDS (the loop's last barrier
+    // has released the tile buffers)
+    float* xs = reinterpret_cast<float*>(smem) + (size_t)wr * (66 * 64);
+    if (kgrp == 1) {
+      xs[lane] = m_ref;
+      xs[64 + lane] = l_run;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xs[(2 + dt * 16 + e) * 64 + lane] = acc[dt][e];
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+    const float m1 = xs[lane], l1 = xs[64 + lane];
+    const float M = fmaxf(m_ref, m1);
+    const float a0 = (m_ref == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float a1 = (m1 == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    if (M != NEG_INF) {
+      l_run = l_run * a0 + l1 * a1;
+      m_ref = M;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] = acc[dt][e] * a0 + xs[(2 + dt * 16 + e) * 64 + lane] * a1;
+    }
   }
 
-  if (!rvalid) return;
+  // this block's normalised partial o (acc / l) and its log2-sum-exp
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-  if (ns == 1) {
-    const size_t ob = ((size_t)t * Hq + hq) * 128;
-    if (a.o_f16) {   // one float16 plane
+  float lse = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] *= inv;
+  if (ns > 1) {
+    float* op = a.o_part + (((size_t)z * T + t) * Hq + hq) * 128;
+    if (rvalid) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int d = dt * 32 + 8 * ii + 4 * hl;
-          f16x4 v4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = (f16)(acc[dt][4 * ii + j] * inv);
-          *reinterpret_cast<f16x4*>(a.oh + ob + d) = v4;
+          *reinterpret_cast<float4*>(op + d) =
+              make_float4(acc[dt][4 * ii], acc[dt][4 * ii + 1], acc[dt][4 * ii + 2], acc[dt][4 * ii + 3]);
         }
-      return;
+      if (hl == 0) a.lse_part[((size_t)z * T + t) * Hq + hq] = lse;
     }
+    return;   // attn_merge combines the splits
+  }
+  if (!rvalid) return;
+  const size_t ob = ((size_t)t * Hq + hq) * 128;
+  if (a.o_f16) {   // one float16 plane
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int d = dt * 32 + 8 * ii + 4 * hl;
-        u16 h[4], l[4];
+        f16x4 v4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = acc[dt][4 * ii + j] * inv;
-          h[j] = f32_to_bf16(v);
-          l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
-        }
-        *reinterpret_cast<uint2*>(a.oh + ob + d) =
-            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-        *reinterpret_cast<uint2*>(a.ol + ob + d) =
-            make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+        for (int j = 0; j < 4; ++j) v4[j] = (f16)acc[dt][4 * ii + j];
+        *reinterpret_cast<f16x4*>(a.oh + ob + d) = v4;
       }
     return;
   }
-  float* op = a.o_part + (((size_t)z * T + t) * Hq + hq) * 128;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int d = dt * 32 + 8 * ii + 4 * hl;
-      *reinterpret_cast<float4*>(op + d) = make_float4(acc[dt][4 * ii] * inv, acc[dt][4 * ii + 1] * inv,
-                                                       acc[dt][4 * ii + 2] * inv, acc[dt][4 * ii + 3] * inv);
+      u16 h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = acc[dt][4 * ii + j];
+        h[j] = f32_to_bf16(v);
+        l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
+      }
+      *reinterpret_cast<uint2*>(a.oh + ob + d) =
+          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      *reinterpret_cast<uint2*>(a.ol + ob + d) =
+          make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
     }
-  if (hl == 0) a.lse_part[((size_t)z * T + t) * Hq + hq] = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
 }
 
 // ----------------------------------------------------------------------------
@@ -1005,7 +1138,7 @@ template <typename WT>
 __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
                                                      float* __restrict__ x, int H, const WT* __restrict__ g,
                                                      float eps, u16* __restrict__ yh, u16* __restrict__ yl,
-                                                     int ldy, int f16out) {
+                                                     int ldy, int f16out, int* __restrict__ flags) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int H4 = H >> 2;
@@ -1044,9 +1177,15 @@ __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ p
       const size_t o = (size_t)row * ldy + 4 * k;
       if (f16out) {   // one float16 plane
         f16x4 y4;
+        bool bad = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y4[e] = (f16)(ldw(g, 4 * k + e) * (in[e] * r));
+        for (int e = 0; e < 4; ++e) {
+          const float y = ldw(g, 4 * k + e) * (in[e] * r);
+          bad |= f16_out_of_range(y);
+          y4[e] = (f16)y;
+        }
         *reinterpret_cast<f16x4*>(yh + o) = y4;
+        flag_f16_range(flags, bad);
         continue;
       }
       u16 h[4], l[4];
@@ -1090,8 +1229,9 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
                                                 const float2* __restrict__ cs,
                                                 f16* __restrict__ q_hi, f16* __restrict__ q_lo,
                                                 f16* __restrict__ kdst, int ldk, f16* __restrict__ vtdst,
-                                                int ldv) {
+                                                int ldv, float qscale, int* __restrict__ flags) {
   __shared__ float vt[16][129];
+  bool bad = false;
   const int t0 = blockIdx.x * 16;
   const int nqk = Hq + Hkv;
   const int h = blockIdx.y;
@@ -1118,16 +1258,21 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       const float a = ld(t, h * 128 + i), b = ld(t, h * 128 + i + 64);
       const float2 e = cs[t * 64 + i];
       const float ra = a * e.x - b * e.y, rb = b * e.x + a * e.y;
+      bad |= f16_out_of_range(ra) || f16_out_of_range(rb);
       if (h < Hq) {
         // operand-ordered layout (see AttnArgs): row r = t*G + g of KV head h / G
         const int G = Hq / Hkv, r = t * G + h % G;
         const size_t base = ((size_t)(h / G) * attn_q_rows(T, G) + (r & ~31)) * 128 + (size_t)(r & 31) * 8;
         auto at = [&](int d) { return base + (size_t)(((d >> 4) * 2 + ((d >> 3) & 1)) * 256) + (d & 7); };
-        const f16 qa = (f16)ra, qb = (f16)rb;
+        // q carries the softmax scale log2(e)/sqrt(D): scores come out in log2 units
+        const float sa = ra * qscale, sb = rb * qscale;
+        const f16 qa = (f16)sa, qb = (f16)sb;
         q_hi[at(i)] = qa;
         q_hi[at(i + 64)] = qb;
-        q_lo[at(i)] = (f16)(ra - (float)qa);
-        q_lo[at(i + 64)] = (f16)(rb - (float)qb);
+        if (q_lo) {
+          q_lo[at(i)] = (f16)(sa - (float)qa);
+          q_lo[at(i + 64)] = (f16)(sb - (float)qb);
+        }
       } else {
         f16* kd = kdst + ((size_t)(h - Hq) * ldk + t) * 128;
         kd[i] = (f16)ra;
@@ -1143,6 +1288,7 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       const int rr = idx >> 7, d = idx & 127;
       const int t = t0 + rr;
       vt[rr][d] = (t < T) ? ld(t, c0 + d) : 0.f;
+      bad |= f16_out_of_range(vt[rr][d]);
     }
     __syncthreads();
 #pragma unroll
@@ -1154,6 +1300,7 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       if (t < ((T + 7) & ~7)) vtdst[((size_t)hk * 128 + d) * ldv + t] = (f16)vt[rr][d];
     }
   }
+  flag_f16_range(flags, bad);
 }
 
 // Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), written as
@@ -1320,24 +1467,59 @@ __global__ void cand_logsoftmax(const float* __restrict__ z, const int* __restri
   for (int c = 0; c < C; ++c) out[(size_t)b * C + c] = (c < n) ? zb[c] - lse : NEG_INF;
 }
 
-// Row-wise logsumexp of logits [R][V] (natural log), one block per row.
-__global__ void __launch_bounds__(256) row_lse(const float* __restrict__ logits, int V, int R,
-                                               float* __restrict__ lse) {
+// Row-wise log-sum-exp (natural log) from 128-column slice partials (max, sum of exp):
+// lse = M + log(sum_p s_p * exp(m_p - M)), M the largest slice max; one block per row,
+// slices combined in a fixed order.
+__global__ void __launch_bounds__(256) lse_merge(const float2* __restrict__ part, int nparts, int R,
+                                                 float* __restrict__ lse) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (r >= R) return;
-  const float* z = logits + (size_t)r * V;
+  const float2* p = part + (size_t)r * nparts;
   float m = NEG_INF;
-  for (int k = threadIdx.x; k < V; k += 256) m = fmaxf(m, z[k]);
+  for (int k = threadIdx.x; k < nparts; k += 256) m = fmaxf(m, p[k].x);
   m = wave_max(m);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (l == 0) red[w] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float s = 0.f;
-  for (int k = threadIdx.x; k < V; k += 256) s += expf(z[k] - m);
+  if (m != NEG_INF)
+    for (int k = threadIdx.x; k < nparts; k += 256) {
+      const float2 v = p[k];
+      if (v.x != NEG_INF) s += v.y * expf(v.x - m);
+    }
   s = block_sum256(s, red);
   if (threadIdx.x == 0) lse[r] = m + logf(s);
+}
+
+// float32 models: the same slice partials straight from h and the float32 LM head, one
+// block of 128 threads per (slice, row), one column per thread.
+__global__ void __launch_bounds__(128) lmhead_lse_f32(const float* __restrict__ h, int H,
+                                                      const float* __restrict__ W, int V, int nparts,
+                                                      float2* __restrict__ part) {
+  __shared__ float red[2];
+  const int slice = blockIdx.x, r = blockIdx.y;
+  const int col = slice * 128 + threadIdx.x;
+  const float* hr = h + (size_t)r * H;
+  float z = NEG_INF;
+  if (col < V) {
+    const float* wr = W + (size_t)col * H;
+    float acc = 0.f;
+    for (int k = 0; k < H; ++k) acc = fmaf(hr[k], wr[k], acc);
+    z = acc;
+  }
+  float m = wave_max(z);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = m;
+  __syncthreads();
+  m = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float e = (col < V && m != NEG_INF) ? expf(z - m) : 0.f;
+  e = wave_sum(e);
+  if (l == 0) red[w] = e;
+  __syncthreads();
+  if (threadIdx.x == 0) part[(size_t)r * nparts + slice] = make_float2(m, red[0] + red[1]);
 }
 
 // Tree readout: score[q][c] = sum_k (z[t] - lse[ridx[t]]) over targets t = (q*C + c)*K + k
@@ -1385,12 +1567,12 @@ using namespace jevk;
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, float* x,
-                        hipStream_t s) {
+                        int* flags, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (bf16)
-    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, x);
+    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, x, flags);
   else
-    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, x);
+    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, x, flags);
   return hipGetLastError();
 }
 
@@ -1446,7 +1628,7 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
   const int acc = splits == 1 ? accum : 0;
   if (pl.wide)
     gemm_bf16w<false, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
-                                           (size_t)M * N, acc, nullptr, nullptr);
+                                           (size_t)M * N, acc, nullptr, nullptr, nullptr);
   else
     gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo, (size_t)M * N,
                                     acc);
@@ -1454,13 +1636,15 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
 }
 
 hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const uint16_t* w_gate,
-                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s) {
+                              const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, int* flags,
+                              hipStream_t s) {
   if (M <= 0 || I <= 0) return hipSuccess;
   if (K % G2K) return hipErrorInvalidValue;
   const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
   const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
-  gemm_bf16w<true, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul);
+  gemm_bf16w<true, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul,
+                                                flags);
   return hipGetLastError();
 }
 
@@ -1495,19 +1679,20 @@ hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmS
   const int ldo = splits == 1 ? ldc : N;
   const int acc = splits == 1 ? accum : 0;
   gemm_bf16w<false, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
-                                               (size_t)M * N, acc, nullptr, nullptr);
+                                               (size_t)M * N, acc, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, const uint16_t* w_gate,
-                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, hipStream_t s) {
+                                  const uint16_t* w_up, int I, uint16_t* uh, uint16_t* ul, int ldu, int* flags,
+                                  hipStream_t s) {
   if (M <= 0 || I <= 0) return hipSuccess;
   if (K % G2K) return hipErrorInvalidValue;
   const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
   const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
   gemm_bf16w<true, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh,
-                                              ul);
+                                              ul, flags);
   return hipGetLastError();
 }
 
@@ -1538,10 +1723,10 @@ bool swiglu_use_split(int M, int I, size_t part_cap) {
 }
 
 hipError_t launch_splitk_swiglu(const float* part, int splits, int M, int I, uint16_t* uh, uint16_t* ul, int ldu,
-                                hipStream_t s) {
+                                int* flags, hipStream_t s) {
   if (M <= 0 || I <= 0) return hipSuccess;
   if (I % 4 || ldu % 4 || splits < 1) return hipErrorInvalidValue;
-  splitk_swiglu<<<cdiv((long)M * (I / 4), 256), 256, 0, s>>>(part, (size_t)M * 2 * I, splits, M, I, uh, ul, ldu);
+  splitk_swiglu<<<cdiv((long)M * (I / 4), 256), 256, 0, s>>>(part, (size_t)M * 2 * I, splits, M, I, uh, ul, ldu, flags);
   return hipGetLastError();
 }
 
@@ -1556,13 +1741,13 @@ hipError_t launch_bf16_to_f16(const uint16_t* src, size_t n, uint16_t* dst, int*
 
 hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_stride, int splits, float* x, int M,
                                 int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, bool f16out,
-                                hipStream_t s) {
+                                int* flags, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (bf16)
-    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy, f16out);
+    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy, f16out, flags);
   else
     residual_norm<float><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl, ldy,
-                                           f16out);
+                                           f16out, flags);
   return hipGetLastError();
 }
 
@@ -1574,11 +1759,11 @@ hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* c
 
 hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
                            const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
-                           hipStream_t s) {
+                           float qscale, int* flags, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   dim3 grid(cdiv(T, 16), Hq + 2 * Hkv);
   qkv_post<<<grid, 256, 0, s>>>(src, lds, split_stride, splits, T, Hq, Hkv, cs, (f16*)q_hi, (f16*)q_lo, (f16*)kdst,
-                                ldk, (f16*)vtdst, ldv);
+                                ldk, (f16*)vtdst, ldv, qscale, flags);
   return hipGetLastError();
 }
 
@@ -1672,11 +1857,20 @@ int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
   return (int)std::max<long>(1, std::min<long>(ns, kAttnMaxSplits));
 }
 
-hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
+
+hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, int kg, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (a.n_split < 1 || a.n_split > kAttnMaxSplits) return hipErrorInvalidValue;
-  dim3 grid(cdiv((long)a.G * a.T, AT_BR), a.Hkv, a.n_split);
-  attn_fwd_f16<<<grid, 256, 0, s>>>(a);
+  if (a.n_split < 1 || a.n_split > kAttnMaxSplits || (q_terms != 1 && q_terms != 2) || (kg != 1 && kg != 2))
+    return hipErrorInvalidValue;
+  const long nb = (long)cdiv((long)a.G * a.T, AT_BR / kg) * a.Hkv * a.n_split;
+  const int grid = (int)(cdiv(nb, 8) * 8);
+  if (kg == 1) {
+    if (q_terms == 1) attn_fwd_f16<1, 1><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_f16<2, 1><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (q_terms == 1) attn_fwd_f16<1, 2><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_f16<2, 2><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1723,9 +1917,29 @@ hipError_t launch_cand_logsoftmax(const float* z, const int* n_cands, int B, int
   return hipGetLastError();
 }
 
-hipError_t launch_row_lse(const float* logits, int V, int R, float* lse, hipStream_t s) {
+// Full-vocabulary LSE of R rows without storing their logits: slice partials [R][nparts]
+// (nparts = ceil(V / 128)); launch_lse_merge combines them in a fixed order into lse[R].
+hipError_t launch_lmhead_lse(bool bf16, const float* h, const uint16_t* h_hi, const uint16_t* h_lo, int H, int R,
+                             const void* W, int V, float2* part, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  row_lse<<<R, 256, 0, s>>>(logits, V, R, lse);
+  const int nparts = cdiv(V, 128);
+  if (bf16) {
+    if (H % G2K) return hipErrorInvalidValue;
+    const int mt = cdiv(R, G2M), nt = cdiv(V, G2N);
+    const int grid = cdiv((long)mt * nt, 8) * 8;
+    GemmSegs seg{{static_cast<const uint16_t*>(W), nullptr, nullptr}, {V, V, V}};
+    gemm_bf16w<false, false, true><<<grid, 256, 0, s>>>(h_hi, h_lo, H, R, H, seg, V, mt, nt, 1, H,
+                                                         reinterpret_cast<float*>(part), nparts, 0, 0, nullptr,
+                                                         nullptr, nullptr);
+  } else {
+    lmhead_lse_f32<<<dim3(nparts, R), 128, 0, s>>>(h, H, static_cast<const float*>(W), V, nparts, part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const float2* part, int R, int V, float* lse, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  lse_merge<<<R, 256, 0, s>>>(part, cdiv(V, 128), R, lse);
   return hipGetLastError();
 }
 

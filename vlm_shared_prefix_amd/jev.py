@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libjev.so")
+# JEV_LIBRARY names another build of the same library (the host-sanitized one of the CPU tests)
+LIB_PATH = os.environ.get("JEV_LIBRARY") or os.path.join(HERE, "libjev.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with `python -m vlm_shared_prefix_amd.build`")
@@ -72,7 +73,10 @@ _sig = {
     "jev_get_stats": (C.c_int32, [_vp, C.POINTER(jev_stats)]),
     "jev_model_f16_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_model_attach_f16": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, _vp]),
+    "jev_model_f16_groups": (C.c_int32, [_vp]),
     "jev_model_set_skip": (C.c_int32, [_vp, C.POINTER(C.c_uint8), C.c_int32]),
+    "jev_model_set_attn_q_terms": (C.c_int32, [_vp, C.c_int32]),
+    "jev_workspace_flags": (C.c_int32, [_vp, _i32p, _vp]),
     "jev_prefix_bytes": (C.c_size_t, [_vp, C.c_int32]),
     "jev_prefix_create": (C.c_int32, [_vp, C.c_int32, _vp, C.c_size_t, C.POINTER(_vp)]),
     "jev_prefix_destroy": (None, [_vp]),
@@ -172,6 +176,11 @@ def jev_model_attach_f16(model: int, groups: int, buf, stream=None) -> None:
     _check(_lib.jev_model_attach_f16(model, groups, _dptr(buf), nbytes, _stream(stream)), "jev_model_attach_f16")
 
 
+def jev_model_f16_groups(model: int) -> int:
+    """Mirror groups whose float16 pass is in effect."""
+    return int(_lib.jev_model_f16_groups(model))
+
+
 def jev_model_set_skip(model: int, skip) -> None:
     """Blocks the candidate rows of scoring calls bypass (host array of n_layers flags; None clears)."""
     if skip is None:
@@ -180,6 +189,21 @@ def jev_model_set_skip(model: int, skip) -> None:
     arr = np.ascontiguousarray(np.asarray(skip, dtype=np.uint8))
     _check(_lib.jev_model_set_skip(model, arr.ctypes.data_as(C.POINTER(C.c_uint8)), int(arr.size)),
            "jev_model_set_skip")
+
+
+def jev_model_set_attn_q_terms(model: int, terms: int) -> None:
+    """Float16 terms of q in the attention (0: by prefix length, 1 or 2)."""
+    _check(_lib.jev_model_set_attn_q_terms(model, terms), "jev_model_set_attn_q_terms")
+
+
+JEV_FLAG_F16_RANGE = 1
+
+
+def jev_workspace_flags(ws, stream=None) -> int:
+    """Range flag word of the last call that used the workspace (synchronises the stream)."""
+    v = C.c_int32(0)
+    _check(_lib.jev_workspace_flags(_dptr(ws), C.byref(v), _stream(stream)), "jev_workspace_flags")
+    return int(v.value)
 
 
 def jev_prefix_bytes(model: int, prefix_len: int) -> int:
