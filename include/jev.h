@@ -250,6 +250,24 @@ jev_status jev_score_suffixes(const jev_prefix *p,
                               const int32_t *cand_ids, const int32_t *n_cands, int32_t C_max,
                               float *out_logp, void *ws, size_t ws_bytes, void *stream);
 
+/* Scoring for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): jev_score_suffixes without a
+ * workspace argument.  The workspace is a file-scope device array of
+ * jev_static_scratch_bytes() bytes (256 MiB) inside the library, one copy per GPU,
+ * held until the process ends.  The call allocates nothing: no device memory, no
+ * pinned host memory.  Its metadata goes through the model's pinned staging ring
+ * if an earlier call created it, otherwise it is copied and the stream
+ * synchronised before the call returns.  A request whose workspace would exceed
+ * the scratch returns JEV_E_WORKSPACE with the size it needs.  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (other streams or
+ * host threads) race and must be serialised by the caller.  jev_workspace_flags
+ * does not reach the scratch.  Otherwise as jev_score_suffixes. */
+size_t     jev_static_scratch_bytes(void);
+jev_status jev_score_suffixes_noalloc(const jev_prefix *p,
+                                      const int32_t *ids, const int32_t *lens, int32_t B, int32_t S_max,
+                                      const int32_t *cand_ids, const int32_t *n_cands, int32_t C_max,
+                                      float *out_logp, void *stream);
+
 /* Tree layouts of jev_score_tree. */
 #define JEV_TREE_TRIE      0  /* stem + candidate tokens merged on (parent, token)   */
 #define JEV_TREE_STEM_ONLY 1  /* stem shared, each candidate's tokens its own chain  */

@@ -933,7 +933,8 @@ uint64_t meta_digest(const std::vector<char>& b) {
 // Copy the plan's metadata into the workspace with one host->device copy and record its
 // digest for the workspace address; with stage == false copy nothing and check instead that
 // the workspace holds this plan's metadata (launch-only calls).
-jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hipStream_t s, bool stage) {
+jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hipStream_t s, bool stage,
+                      bool may_alloc = true) {
   std::vector<char> buf(L.meta_end, 0);
   auto put = [&](size_t off, const void* src, size_t bytes) {
     if (bytes) std::memcpy(buf.data() + off, src, bytes);
@@ -956,8 +957,14 @@ jev_status stage_meta(jev_model* m, const Plan& p, const Layout& L, void* ws, hi
       return fail(JEV_E_INVALID, "workspace does not hold this call's metadata: stage it with the copying call first");
     return JEV_OK;
   }
-  HIP_OK(m->ring.init());
-  HIP_OK(m->ring.copy(ws, buf.data(), L.meta_end, s));
+  if (may_alloc) HIP_OK(m->ring.init());
+  if (m->ring.ready) {
+    HIP_OK(m->ring.copy(ws, buf.data(), L.meta_end, s));
+  } else {
+    // no pinned ring and none may be made: copy and wait, so the host buffer outlives the copy
+    HIP_OK(hipMemcpyAsync(ws, buf.data(), L.meta_end, hipMemcpyHostToDevice, s));
+    HIP_OK(hipStreamSynchronize(s));
+  }
   // bounded: a caller cycling through many workspaces forgets the oldest digests (a
   // launch-only call on such a workspace then asks for a fresh staging call)
   if (m->staged.size() >= kMaxStagedWorkspaces && !m->staged.count(ws)) m->staged.clear();
@@ -1051,10 +1058,14 @@ extern "C" jev_status jev_prefill_segments(jev_prefix* p, const void* vis_embeds
 
 // segmented == false: every suffix over the one prefix.  Otherwise suffix b continues
 // segment seg[b] of a segmented store: positions P_seg + j, prefix keys the segment's rows only.
+static void* static_scratch(jev_status* st);
+static constexpr size_t kStaticScratchBytes = 256ull << 20;
+
+// ws == nullptr with use_static: the library's static device scratch (no allocation anywhere)
 static jev_status score_suffixes(const jev_prefix* p, bool segmented, const int32_t* seg, const int32_t* ids,
                                  const int32_t* lens, int32_t B, int32_t S_max, const int32_t* cand_ids,
                                  const int32_t* n_cands, int32_t C_max, float* out_logp, void* ws, size_t ws_bytes,
-                                 void* stream, bool stage) {
+                                 void* stream, bool stage, bool use_static = false) {
   if (!p) return fail(JEV_E_INVALID, "null prefix");
   jev_model* m = p->m;
   if (!segmented && p->seg_len.size() != 1) return fail(JEV_E_INVALID, "segmented prefix: use jev_score_segments");
@@ -1083,11 +1094,20 @@ static jev_status score_suffixes(const jev_prefix* p, bool segmented, const int3
   }
   const Layout L = make_layout(m, plan.T, (int)plan.read_rows.size(), (int)plan.tgt_tok.size(),
                                (int)plan.out_n.size(), false, false, p->P);
+  if (use_static) {
+    if (L.total > kStaticScratchBytes)
+      return fail(JEV_E_WORKSPACE, "request needs " + std::to_string(L.total) + " bytes of scratch; the static "
+                                   "scratch holds " + std::to_string(kStaticScratchBytes));
+    jev_status st2 = JEV_OK;
+    ws = static_scratch(&st2);
+    if (st2) return st2;
+    ws_bytes = kStaticScratchBytes;
+  }
   if (!ws) return fail(JEV_E_INVALID, "null workspace");
   if (ws_bytes < L.total)
     return fail(JEV_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (jev_status e = stage_meta(m, plan, L, ws, s, stage)) return e;
+  if (jev_status e = stage_meta(m, plan, L, ws, s, stage, !use_static)) return e;
   Forward f(p, plan, L, ws, s, Mode::Score);
   jev_status e = f.run(nullptr);
   if (!e) e = f.readout(out_logp, nullptr);
@@ -1103,6 +1123,45 @@ extern "C" jev_status jev_score_suffixes(const jev_prefix* p, const int32_t* ids
                                          int32_t C_max, float* out_logp, void* ws, size_t ws_bytes, void* stream) {
   return score_suffixes(p, false, nullptr, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, ws, ws_bytes,
                         stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// scoring without allocation: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+// Each device that runs the library holds its own copy of `scratch` until the process ends.
+// In host code its name is only a stand-in: the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever handed to kernels or copies.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};
+
+static void* static_scratch(jev_status* st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *st = fail(JEV_E_HIP, "no current HIP device for the static scratch");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *st = fail(JEV_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" size_t jev_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" jev_status jev_score_suffixes_noalloc(const jev_prefix* p, const int32_t* ids, const int32_t* lens,
+                                                 int32_t B, int32_t S_max, const int32_t* cand_ids,
+                                                 const int32_t* n_cands, int32_t C_max, float* out_logp,
+                                                 void* stream) {
+  return score_suffixes(p, false, nullptr, ids, lens, B, S_max, cand_ids, n_cands, C_max, out_logp, nullptr, 0,
+                        stream, true, true);
 }
 
 extern "C" jev_status jev_score_segments(const jev_prefix* p, const int32_t* seg, const int32_t* ids,

@@ -90,6 +90,9 @@ _sig = {
                                        _vp, _vp, C.c_size_t, _vp]),
     "jev_score_tree": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                    C.c_int32, C.c_int32, _vp, _vp, _vp, C.c_size_t, _vp]),
+    "jev_static_scratch_bytes": (C.c_size_t, []),
+    "jev_score_suffixes_noalloc": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32,
+                                               _vp, _vp]),
     "jev_score_suffixes_launch": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32,
                                               _vp, _vp, C.c_size_t, _vp]),
     "jev_score_tree_launch": (C.c_int32, [_vp, _i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p,
@@ -269,6 +272,21 @@ def jev_score_suffixes_launch(prefix: int, ids, lens, cand_ids, n_cands, out_log
     jev_score_suffixes call with the same arguments staged); capturable into a HIP graph."""
     _score_suffixes(_lib.jev_score_suffixes_launch, "jev_score_suffixes_launch", prefix, ids, lens, cand_ids,
                     n_cands, out_logp, ws, stream)
+
+
+def jev_static_scratch_bytes() -> int:
+    return int(_lib.jev_static_scratch_bytes())
+
+
+def jev_score_suffixes_noalloc(prefix: int, ids, lens, cand_ids, n_cands, out_logp, stream=None) -> None:
+    """jev_score_suffixes on the library's static device scratch (no workspace, no allocation)."""
+    ids, lens, cand_ids, n_cands = _i32(ids), _i32(lens), _i32(cand_ids), _i32(n_cands)
+    B = int(lens.shape[0])
+    S_max = int(ids.shape[1]) if ids.ndim == 2 else 1
+    C_max = int(cand_ids.shape[1]) if cand_ids.ndim == 2 else 1
+    _check(_lib.jev_score_suffixes_noalloc(prefix, _ptr_i32(ids), _ptr_i32(lens), B, S_max, _ptr_i32(cand_ids),
+                                           _ptr_i32(n_cands), C_max, _dptr(out_logp), _stream(stream)),
+           "jev_score_suffixes_noalloc")
 
 
 def jev_prefix_create_segments(model: int, seg_lens, kv_buf) -> int:
