@@ -154,7 +154,7 @@ def timed_on(stream, fn, k, warm=0):
     return a.elapsed_time(b) / k
 
 
-def tree_section(seed, dev, profile_steps, name="c5"):
+def tree_section(seed, dev, profile_steps, name="c5", sweep=True):
     """Secondary measurement: the long-prefix tree workload (prefix 8192, 16 questions with
     4 multi-token candidates each, trie sharing) on the same 7B shape; not the headline value."""
     import torch
@@ -224,7 +224,7 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     # independent candidates and with overlapping ones (candidate k+1 repeating a leading run
     # of candidate k half the time), rows fed and call time per mode
     schedules = {}
-    for label, tcfg in (("independent", cfg), ("overlapping", S.with_overrides(cfg, overlap=True))):
+    for label, tcfg in (("independent", cfg), ("overlapping", S.with_overrides(cfg, overlap=True)))[:2 if sweep else 0]:
         tt = S.tree_inputs(tcfg, seed)
         runs = {}
         for mode, mname in ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat")):
@@ -254,8 +254,8 @@ def tree_section(seed, dev, profile_steps, name="c5"):
     out["modes"] = modes_ms
     # the same comparison at a controlled shared fraction: every candidate has cand_len_hi
     # tokens and a question's candidates agree on their first s of them
-    sweep = []
-    for shared in range(cfg.cand_len_hi):
+    sweep_out = []
+    for shared in range(cfg.cand_len_hi if sweep else 0):
         tt = S.shared_tree_inputs(cfg, seed, shared)
         e = {"shared_tokens": shared, "shared_fraction": round(shared / cfg.cand_len_hi, 3)}
         modes = ((J.JEV_TREE_TRIE, "trie"), (J.JEV_TREE_STEM_ONLY, "stem_only"), (J.JEV_TREE_FLAT, "flat"))
@@ -273,8 +273,8 @@ def tree_section(seed, dev, profile_steps, name="c5"):
             e[mname] = {"rows": int(r), "call_ms": round(float(np.mean(passes[mname])), 3),
                         "pass_ms": [round(x, 3) for x in passes[mname]]}
         e["fastest"] = min(("trie", "stem_only", "flat"), key=lambda k: e[k]["call_ms"])
-        sweep.append(e)
-    out["shared_fraction_sweep"] = sweep
+        sweep_out.append(e)
+    out["shared_fraction_sweep"] = sweep_out
 
     # the memory-bound end: the same prefix with only the first q question stems (few query
     # rows per KV head), where the attention is bound by streaming the prefix KV
@@ -556,11 +556,18 @@ def cpu_crosscheck(name, seed):
     est = cpu_baseline(cfg, seed)
     ws = S.WeightSource(cfg, seed, cache_layers=False)
     pre, suf = S.prefix_inputs(cfg, seed), S.suffix_inputs(cfg, seed)
+    # the full call draws each layer's weights as it reaches it; drawing them alone is timed
+    # too and taken out, as the estimate's runs use weights drawn beforehand
+    t = time.perf_counter()
+    for l in range(cfg.n_layers):
+        S.WeightSource(cfg, seed, cache_layers=False).layer(l)
+    draw = time.perf_counter() - t
     t = time.perf_counter()
     O.score_suffixes(ws, cfg, pre, suf, free_layers=True)
-    full = time.perf_counter() - t
+    full = time.perf_counter() - t - draw
     n_c = int(np.sum(suf["n_cands"]))
     print(json.dumps({"config": name, "host": host_info(), "full_seconds": round(full, 2),
+                      "weight_draw_seconds_excluded": round(draw, 2),
                       "full_candidates_per_s": round(n_c / full, 3),
                       "estimate_seconds": round(est["seconds_per_step"], 2),
                       "estimate_candidates_per_s": round(est["value"], 3),
@@ -578,6 +585,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true",
                     help="skip the secondary long-prefix tree measurement (config c5)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the tree section's schedule comparisons (shorter profiled runs)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config calls of c1, c2 and c4 (every B, batched and serial)")
     ap.add_argument("--cpu-crosscheck", default=None, metavar="CONFIG",
@@ -761,7 +770,7 @@ def main():
             sess.close()
         del sess
         torch.cuda.empty_cache()
-        tree = tree_section(args.seed, dev, args.profile_steps)
+        tree = tree_section(args.seed, dev, args.profile_steps, sweep=not args.no_sweep)
 
     images = None
     if not args.no_images:

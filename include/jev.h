@@ -64,7 +64,7 @@ typedef struct {
     int32_t hidden;       /* H; multiple of 64 and <= 8192 for JEV_BF16                 */
     int32_t n_q_heads;    /* Hq                                                         */
     int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0; q head h reads kv head h / (Hq/Hkv)    */
-    int32_t head_dim;     /* D; 128 for JEV_BF16, 64 or 128 for JEV_F32                 */
+    int32_t head_dim;     /* D; 64 or 128                                               */
     int32_t mlp;          /* I; multiple of 64 for JEV_BF16                             */
     int32_t vocab;        /* V                                                          */
     float   rope_theta;   /* angle of pair t at position p: p * theta^(-2t/D)           */
@@ -188,9 +188,11 @@ jev_status jev_workspace_flags(const void *ws, int32_t *flags, void *stream);
 
 /* ---- prefix KV store ---------------------------------------------------------
  * Layout per layer l (element type float16 for JEV_BF16, float32 for JEV_F32),
- * with Pc = prefix_len rounded up to a multiple of 64:
- *     K  [Hkv][Pc][D]   rotated keys, row p = prefix position p
- *     Vt [Hkv][D][Pc]   values, transposed (position fastest)
+ * with Pc = prefix_len rounded up to a multiple of 64 and Dk the stored head
+ * width (128 for JEV_BF16, whose float16 attention runs on 128-dim heads: a
+ * 64-dim head is stored and computed zero-padded; D for JEV_F32):
+ *     K  [Hkv][Pc][Dk]  rotated keys, row p = prefix position p
+ *     Vt [Hkv][Dk][Pc]  values, transposed (position fastest)
  * and layers stacked: store = { K_0, Vt_0, K_1, Vt_1, ... }.  Columns
  * [prefix_len, Pc) are padding and never read as values.  The buffer is
  * written by jev_prefill_prefix and only read afterwards ("FastJEV", §3.2:

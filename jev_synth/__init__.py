@@ -144,6 +144,11 @@ CONFIGS: Dict[str, Config] = {
     "mi1": Config("mi1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                   mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",
                   n_vis=48, n_text=16, n_images=3, vis_lo=10, len_lo=5, len_hi=7, s_max=8, n_cands=3),
+    # bf16 decoder with 64-dim heads (G=4), 2 layers: suffixes and a tree workload
+    "m64": Config("m64", n_layers=2, hidden=1024, n_q_heads=16, n_kv_heads=4, head_dim=64,
+                  mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
+                  n_vis=150, n_text=10, n_suffix=6, len_lo=1, len_hi=20, s_max=24, n_cands=3,
+                  n_questions=4, stem_len=5, tree_cands=4, cand_len_lo=1, cand_len_hi=4, overlap=True),
     # fp32 tree workload on the tiny decoder (oracle pins and fp32 parity)
     "t1": Config("t1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                  mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",

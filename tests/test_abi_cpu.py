@@ -61,7 +61,7 @@ def test_model_create_validation():
     J.jev_model_destroy(m)
     cases = [
         (dict(n_q_heads=5), J.JEV_E_UNSUPPORTED),          # Hq % Hkv
-        (dict(head_dim=64), J.JEV_E_UNSUPPORTED),          # bf16 needs D = 128
+        (dict(head_dim=96), J.JEV_E_UNSUPPORTED),          # D in {64, 128}
         (dict(hidden=250), J.JEV_E_UNSUPPORTED),           # bf16 needs H % 64 == 0
         (dict(vocab=0), J.JEV_E_INVALID),
         (dict(dtype=7), J.JEV_E_INVALID),
@@ -73,6 +73,11 @@ def test_model_create_validation():
         assert e.value.code == code, kw
     # float32 models accept head_dim 64 and any hidden size
     m = J.jev_model_create(_cfg(dtype=J.JEV_F32, head_dim=64, hidden=250, mlp=688), w)
+    assert J.jev_prefix_bytes(m, 100) == 2 * 2 * 2 * 128 * 64 * 4
+    J.jev_model_destroy(m)
+    # bf16 models take head_dim 64 too; their float16 store keeps 128-dim heads (zero-padded)
+    m = J.jev_model_create(_cfg(head_dim=64), w)
+    assert J.jev_prefix_bytes(m, 100) == 2 * 2 * 2 * 128 * 128 * 2
     J.jev_model_destroy(m)
     bad = J.jev_weights(0, 0x200, 0x300, keep)
     with pytest.raises(J.JevError) as e:
@@ -473,3 +478,16 @@ def test_attn_q_terms_and_flags_arguments(model):
     with pytest.raises(J.JevError) as e:
         J.jev_workspace_flags(None, stream=0)
     assert e.value.code == J.JEV_E_INVALID
+
+
+def test_one_hip_runtime_in_process():
+    """Importing the binding before torch must not leave two HIP runtimes in the process (the
+    library's runtime would not know torch's device buffers)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); from vlm_shared_prefix_amd import jev; import torch; "
+            "print(sorted(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)))" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
                                                  ("m2", 0, "default"), ("m7", 0, "default"), ("m2", 3, "default"),
                                                  ("m7l", 0, "default"), ("m7", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
                                                  ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16"),
-                                                 ("m7", 0, "f16_prefill"), ("m2", 1, "f16_prefill")])
+                                                 ("m7", 0, "f16_prefill"), ("m2", 1, "f16_prefill"),
+                                                 ("m64", 0, "default"), ("m64", 1, "split")])
 def test_score_suffixes_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
     say(f"[parity] score_suffixes {name} seed {seed} ({precision})")
@@ -31,8 +32,27 @@ def test_score_suffixes_vs_oracle(name, seed, precision):
     sess.close()
 
 
+@pytest.mark.parametrize("name,n,precision", [("m2", 1, "default"), ("m2", 2, "split"), ("m7", 1, "default"),
+                                              ("m7", 2, "f16"), ("m7", 3, "split"), ("m7", 1, "f16_down"),
+                                              ("m64", 1, "default"), ("m64", 2, "f16_prefill")])
+def test_few_rows_vs_oracle(name, n, precision):
+    """Scoring calls of one to three suffixes: at most 32 rows take the weight-streaming GEMM
+    (one float16 plane or two bf16 planes, split K), more rows the tiled one."""
+    cfg = S.CONFIGS[name]
+    suf = S.suffix_inputs(cfg, 0, n)
+    rows = int(suf["lens"].sum())
+    say(f"[parity] score_suffixes {name} seed 0, {n} suffix(es), {rows} rows ({precision})")
+    sess, src = gpu_session(cfg, 0, precision=precision)
+    pre = S.prefix_inputs(cfg, 0)
+    ref = O.score_suffixes(src, cfg, pre, suf)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"{name}/n{n}/{precision}")
+    sess.close()
+
+
 @pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "default"), ("m5", 0, "split"),
-                                                 ("m5", 0, "f16")])
+                                                 ("m5", 0, "f16"), ("m64", 0, "default")])
 def test_score_tree_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
     say(f"[parity] score_tree {name} seed {seed} ({precision})")

@@ -163,6 +163,9 @@ static inline int round64(int x) { return (x + 63) & ~63; }
 static bool is_bf16(const jev_model* m) { return m->cfg.dtype == JEV_BF16; }
 static size_t kv_elem(const jev_model* m) { return is_bf16(m) ? 2 : 4; }
 static int nqkv(const jev_config& c) { return (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; }
+// Head width of the KV store and of the attention's operands: bf16 models run their float16
+// attention on 128-dim heads (a 64-dim head zero-padded); float32 models use head_dim itself.
+static int kv_dim(const jev_model* m) { return is_bf16(m) ? 128 : m->cfg.head_dim; }
 
 // ---------------------------------------------------------------------------
 // model / prefix
@@ -179,9 +182,7 @@ extern "C" jev_status jev_model_create(const jev_config* cfg, const jev_weights*
   if (c.dtype == JEV_BF16 && (c.hidden % 64 || c.mlp % 64))
     return fail(JEV_E_UNSUPPORTED, "bf16 models need hidden and mlp multiples of 64");
   if (c.dtype == JEV_BF16 && c.hidden > 8192) return fail(JEV_E_UNSUPPORTED, "bf16 models need hidden <= 8192");
-  if (c.dtype == JEV_BF16 && c.head_dim != 128) return fail(JEV_E_UNSUPPORTED, "bf16 models need head_dim 128");
-  if (c.dtype == JEV_F32 && c.head_dim != 64 && c.head_dim != 128)
-    return fail(JEV_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(JEV_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (!w->embed || !w->final_norm || !w->lm_head || (c.n_layers > 0 && !w->layers))
     return fail(JEV_E_INVALID, "null weight pointer");
   for (int l = 0; l < c.n_layers; ++l) {
@@ -341,7 +342,7 @@ extern "C" size_t jev_prefix_bytes(const jev_model* m, int32_t prefix_len) {
   if (!m || prefix_len < 0) return 0;
   const jev_config& c = m->cfg;
   const size_t Pc = (size_t)round64(prefix_len);
-  return (size_t)c.n_layers * 2 * c.n_kv_heads * Pc * c.head_dim * kv_elem(m);
+  return (size_t)c.n_layers * 2 * c.n_kv_heads * Pc * kv_dim(m) * kv_elem(m);
 }
 
 extern "C" jev_status jev_prefix_create(jev_model* m, int32_t prefix_len, void* kv_buf, size_t kv_bytes,
@@ -450,10 +451,10 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.big = take(4ull * T * bigw);
   L.q = take(bf ? 2 * 2 * attn_q_plane_elems(T, c.n_q_heads, c.n_kv_heads)   // bf16 models: q hi and lo planes
                 : e * T * HqD);
-  L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
-  L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * c.head_dim);
+  L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * kv_dim(m));
+  L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * kv_dim(m));
   const size_t prow = bf ? attn_part_rows(c, T, P) : 0;
-  L.o_part = take(4ull * prow * HqD);
+  L.o_part = take(4ull * prow * c.n_q_heads * kv_dim(m));
   L.lse_part = take(4ull * prow * c.n_q_heads);
   L.gpart = take(bf ? 4ull * kGemmPartFloats : 0);
   L.h = take(4ull * R * c.hidden);
@@ -573,10 +574,10 @@ struct Forward {
 
   // layer l's K / Vt in the prefix store
   char* store_k(int l) const {
-    const size_t per = (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m);
+    const size_t per = (size_t)c.n_kv_heads * pf->Pc * kv_dim(m) * kv_elem(m);
     return static_cast<char*>(pf->kv) + (size_t)l * 2 * per;
   }
-  char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * c.head_dim * kv_elem(m); }
+  char* store_vt(int l) const { return store_k(l) + (size_t)c.n_kv_heads * pf->Pc * kv_dim(m) * kv_elem(m); }
 
 
   // A operand: float32 rows (float32 models), bfloat16 hi/lo planes, or one float16 plane
@@ -664,7 +665,7 @@ struct Forward {
     if (layers.empty()) return JEV_OK;
     float2* rope = at<float2>(ws, L.rope);
     if (jev_status st = run_k(K_ROPETAB, 0.0, 8.0 * T * 64,
-                              [&] { return launch_rope_table(pos, T, log2_theta, rope, s); }))
+                              [&] { return launch_rope_table(pos, T, D, log2_theta, rope, s); }))
       return st;
     if (jev_status st = run_k(K_RESNORM, 0.0, 2 * rowbytes, [&] {
           return launch_residual_norm(true, nullptr, 0, 0, x, T, H, m->layers[layers[0]].attn_norm, c.rms_eps, a_hi,
@@ -709,7 +710,7 @@ struct Forward {
       _Float16* q_lo = q_terms == 2 ? q_hi + attn_q_plane_elems(T, Hq, Hkv) : nullptr;
       if (jev_status st = run_k(K_QKVPOST, 0.0, (double)T * NQKV * 4 * sp + (double)T * (q_terms * HqD + 2 * Hkv * D) * 2, [&] {
             return launch_qkv_post(sp > 1 ? part : big, NQKV, (size_t)T * NQKV, sp, T, Hq, Hkv, rope, q_hi, q_lo,
-                                   kdst, kld, vdst, kld, qscale, flags, s);
+                                   kdst, kld, vdst, kld, D, qscale, flags, s);
           }))
         return st;
       if (last_prefill) break;   // the prefix store is complete; later rows of this layer are unused
@@ -734,7 +735,8 @@ struct Forward {
       a.lse_part = at<float>(ws, L.lse_part);
       a.oh = a_hi; a.ol = a_lo;
       a.o_f16 = fo ? 1 : 0;
-      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, q_terms, 1, s); }))
+      a.D = D;
+      if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, q_terms, s); }))
         return st;
       if (n_split > 1) {
         if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 1) * T * HqD, [&] {

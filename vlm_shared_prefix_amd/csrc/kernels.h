@@ -50,11 +50,13 @@ struct AttnArgs {
   int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
   int own_tiles;           // bound on any row tile's own-key tiles (attn_own_tiles); the splits
                            // divide ceil(P/64) + own_tiles tiles
-  float* o_part;           // [n_split][T][Hq][128]  (n_split > 1)
+  float* o_part;           // [n_split][T][Hq][128]  (n_split > 1; always 128 dims)
   float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1)
   uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1) ...
   uint16_t* ol;
   int o_f16;               // ... or (non-zero) one float16 plane of o in oh
+  int D;                   // the model's head dim (64 or 128): o is [T][Hq][D], the first D of
+                           // the 128 computed dims (a 64-dim head runs zero-padded to 128)
 };
 
 // float32 attention (head_dim 64 or 128).
@@ -128,11 +130,11 @@ hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_strid
 // lo = the rounding remainder, when q_lo is not null) in the attention's operand order,
 // K [Hkv][ldk][128] f16 at rows 0..T-1, Vt [Hkv][128][ldv] f16 at columns 0..T-1 and zeros in
 // columns T..round8(T)-1 (ldv >= round8(T)).
-// cs[t][i] = (cos, sin) of pos[t] * theta^(-2i/128), i < 64 (head_dim 128).
-hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s);
+// cs[t][i] = (cos, sin) of pos[t] * theta^(-2i/D), i < D/2 of 64 slots per row (D = 64 or 128).
+hipError_t launch_rope_table(const int* pos, int T, int D, double log2_theta, float2* cs, hipStream_t s);
 hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
                            const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
-                           float qscale, int* flags, hipStream_t s);
+                           int D, float qscale, int* flags, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, int ldc, int accum,
                                 hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int K, const GemmSegsF& seg, int N, float* C, int ldc,
@@ -157,8 +159,7 @@ int attn_own_tiles(const int* seq_start, int T, int G);
 int attn_seg_tiles(const int* pseg, int T, int G, int* ptile);
 // q_terms 1: q as one float16 term (q_lo unused); 2: q = q_hi + q_lo.  q is pre-scaled by
 // log2(e)/sqrt(128) (qkv_post's qscale), so the kernel's scores are in log2 units.
-// kg 1: 128-row blocks; kg 2: 64-row blocks whose two wave pairs take alternate key tiles.
-hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, int kg, hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
                              uint16_t* ol, bool f16out, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);

@@ -279,8 +279,9 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
 // ----------------------------------------------------------------------------
 // K3 wide (bf16 models): the same product on a 128 x 256 block tile, 4 waves of
 // 64 x 128 (8 MFMA tiles each, half the LDS bytes per MFMA of the 64 x 64 wave
-// tile), K stages of 32 staged by direct global->LDS loads into a double buffer
-// (the next stage in flight while the current one is multiplied).  LDS rows are
+// tile), K stages of 32 staged by direct global->LDS loads into a ring of buffers
+// (one float16 plane: three, the next two stages in flight while the current one is
+// multiplied; two bf16 planes: two).  LDS rows are
 // 64 B with the 16 B chunk c of row r at position c ^ ((r / 4) % 4), which makes
 // the operand reads bank-conflict free.  All hi-plane MFMAs of a k-step are
 // issued before the lo-plane ones, so no two consecutive MFMAs share an
@@ -299,12 +300,20 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
                                                 int splits, int k_chunk, float* __restrict__ C, int ldc,
                                                 size_t split_stride, int accum, u16* __restrict__ oh,
                                                 u16* __restrict__ ol, int* __restrict__ flags) {
+  // K stages in the LDS ring: three for the float16 SwiGLU (72 KiB of LDS, two blocks per CU;
+  // 14% faster than two on the 1024-row prefill shape), two elsewhere (the plain float16
+  // product measured 2% slower with three; for two bf16 planes a third would leave one
+  // block per CU).  Each buffer is its own array so that the compiler can
+  // tell the direct-to-LDS loads of later stages from the reads of the current one.
+  constexpr int NS = (F16 && SWIGLU && !LSE) ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u16 sAh0[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sAl0[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sW0[G2N * G2K];
   __shared__ __attribute__((aligned(16))) u16 sAh1[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sAl1[G2M * G2K];
   __shared__ __attribute__((aligned(16))) u16 sW1[G2N * G2K];
+  __shared__ __attribute__((aligned(16))) u16 sAh2[NS > 2 ? G2M * G2K : 8];
+  __shared__ __attribute__((aligned(16))) u16 sW2[NS > 2 ? G2N * G2K : 8];
 
   const int nb = m_tiles * n_tiles * splits;
   const int per = gridDim.x >> 3;
@@ -433,23 +442,55 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs of k-step 1
     }
   };
+  // Stage s: wait for this thread's loads of stage s (the NS - 2 later stages already issued
+  // stay in flight), a barrier (every thread's stage-s bytes are in LDS and every wave is done
+  // reading stage s - 1), then the loads of stage s + NS - 1 into the buffer stage s - 1 used,
+  // then stage s's MFMAs.
+  constexpr int LPS = F16 ? 6 : 8;   // direct-to-LDS loads per thread per stage
   auto step = [&](int s, const u16* cA, const u16* cL, const u16* cW, u16* nA, u16* nL, u16* nW) {
-    if (s + 1 < nst) load_stage(kbeg + (s + 1) * G2K, nA, nL, nW);
+    if (NS > 2 && s + 1 < nst)
+      __builtin_amdgcn_s_waitcnt(0x70 | (LPS & 15) | ((LPS >> 4) << 14));   // vmcnt(LPS) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x70);                                       // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (s + NS - 1 < nst) load_stage(kbeg + (s + NS - 1) * G2K, nA, nL, nW);
     compute(cA, cL, cW);
-    // every MFMA of the stage is issued before the wait: left alone, the scheduler hoists the
-    // wait for the next stage's loads above most of them, leaving the loads little cover
+    // every MFMA of the stage is issued before the next wait: left alone, the scheduler
+    // hoists that wait above most of them, leaving the loads little cover
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
   };
-  if (nst > 0) {
-    load_stage(kbeg, sAh0, sAl0, sW0);
-    __builtin_amdgcn_s_waitcnt(0x70);
+  // a stage with a later stage in flight and a stage to load (the three-stage ring only)
+  auto full_step = [&](const u16* cA, const u16* cW, u16* nA, u16* nW, int knext) {
+    __builtin_amdgcn_s_waitcnt(0x70 | (LPS & 15) | ((LPS >> 4) << 14));   // vmcnt(LPS) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-  }
-  for (int s = 0; s < nst; s += 2) {
-    step(s, sAh0, sAl0, sW0, sAh1, sAl1, sW1);
-    if (s + 1 < nst) step(s + 1, sAh1, sAl1, sW1, sAh0, sAl0, sW0);
+    load_stage(knext, nA, nullptr, nW);
+    compute(cA, nullptr, cW);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NS == 2) {
+    if (nst > 0) load_stage(kbeg, sAh0, sAl0, sW0);
+    for (int s = 0; s < nst; s += 2) {
+      step(s, sAh0, sAl0, sW0, sAh1, sAl1, sW1);
+      if (s + 1 < nst) step(s + 1, sAh1, sAl1, sW1, sAh0, sAl0, sW0);
+    }
+  } else {
+    // the prologue loads are unconditional, which keeps the compiler's count of loads in
+    // flight exact where the loop starts; with one stage (a short last split) the second is
+    // clamped into the chunk and left unused
+    load_stage(kbeg, sAh0, nullptr, sW0);
+    load_stage(min(kbeg + G2K, kend - G2K), sAh1, nullptr, sW1);
+    // whole groups of three stages whose loads all exist, then the tail with its checks
+    int s = 0;
+    for (; s + 4 < nst; s += 3) {
+      full_step(sAh0, sW0, sAh2, sW2, kbeg + (s + 2) * G2K);
+      full_step(sAh1, sW1, sAh0, sW0, kbeg + (s + 3) * G2K);
+      full_step(sAh2, sW2, sAh1, sW1, kbeg + (s + 4) * G2K);
+    }
+    for (; s < nst; s += 3) {
+      step(s, sAh0, sAl0, sW0, sAh2, nullptr, sW2);
+      if (s + 1 < nst) step(s + 1, sAh1, sAl1, sW1, sAh0, sAl0, sW0);
+      if (s + 2 < nst) step(s + 2, sAh2, nullptr, sW2, sAh1, sAl1, sW1);
+    }
   }
 
   if (m0 + wm * 64 >= M) return;
@@ -530,6 +571,136 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
         if (row < M && col < N) Cb[(size_t)row * ldc + col] = old[r] + acc[i][j][r];
       }
     }
+}
+
+// ----------------------------------------------------------------------------
+// K3 for few rows (M <= 32): a weight-streaming product.  Block = 4 waves and 128 output
+// columns (32 per wave) over one K chunk, walked in stages of 64 of K.  A stage's weight
+// tile (128 rows x 128 B) is staged in LDS by direct global->LDS loads in which a wave's
+// instruction covers 8 whole 128 B row segments (fully used cache lines; loading the MFMA
+// operand layout straight into registers touches 32 rows per instruction and streamed
+// ~30% slower); the 16 B chunk c of row r sits at position c ^ ((r / 2) % 8), so the
+// operand reads (a column wave's 32 rows, one chunk each) are bank-conflict free.  A ring
+// of three stages keeps two stages of loads in flight.  The M activation rows go straight
+// to registers as the A operand of v_mfma 32x32x16 (rows past M clamped, their outputs
+// dropped).  F16: one f16 activation plane x the f16 weight mirror; else two bf16 planes x
+// bf16 weights (W·hi + W·lo).  The chunk's sum goes to C (splits == 1) or to partials
+// [split][M][N].
+// ----------------------------------------------------------------------------
+#define SKS 64   // K per stage of the few-row product
+template <bool F16>
+__global__ void __launch_bounds__(256, 3) gemm_skinny(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+                                                     int lda, int M, int K, GemmSegs seg, int N, int n_tiles,
+                                                     int splits, int k_chunk, float* __restrict__ C, int ldc,
+                                                     size_t split_stride, int accum) {
+  constexpr int NB = F16 ? 1 : 2;   // activation planes
+  __shared__ __attribute__((aligned(16))) u16 sW0[128 * SKS];
+  __shared__ __attribute__((aligned(16))) u16 sW1[128 * SKS];
+  __shared__ __attribute__((aligned(16))) u16 sW2[128 * SKS];
+  const int v = blockIdx.x;
+  if (v >= n_tiles * splits) return;
+  const int ntile = v % n_tiles, ks = v / n_tiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ql = lane & 31, hl = lane >> 5;
+  const int kb = ks * k_chunk, ke = min(K, kb + k_chunk);
+  const int nst = (ke - kb) / SKS;   // >= 1
+  // the thread's 4 weight loads per stage: slot = q * 256 + tid, row slot / 8, chunk slot % 8
+  const u16* srcW[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int slot = q * 256 + tid, row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+    const int n = ntile * 128 + row;
+    srcW[q] = seg_row(seg, n < N ? n : 0, K) + c * 8;
+  }
+  auto load_w = [&](int k0, u16* dst) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(srcW[q] + k0, dst + (q * 256 + wave * 64) * 8, 16, 0, 0);
+  };
+  const int m = ql < M ? ql : M - 1;
+  const u16* arow[NB];
+  arow[0] = Ah + (size_t)m * lda + hl * 8;
+  if (!F16) arow[NB - 1] = Al + (size_t)m * lda + hl * 8;
+  typedef u16 u16x8 __attribute__((ext_vector_type(8)));
+  u16x8 a0[NB][4], a1[NB][4], a2[NB][4];
+  auto load_a = [&](int k0, u16x8 (*av)[4]) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[p][j] = *reinterpret_cast<const u16x8*>(arow[p] + k0 + 16 * j);
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int wr = wave * 32 + ql;   // the lane's weight row (output column) in the tile
+  auto compute = [&](const u16* sw, const u16x8 (*av)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = 2 * j + hl;
+      const u16x8 b = *reinterpret_cast<const u16x8*>(sw + wr * SKS + ((g ^ ((wr >> 1) & 7)) * 8));
+#pragma unroll
+      for (int p = 0; p < NB; ++p) {
+        if (F16)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av[p][j]),
+                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[p][j]),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      }
+    }
+  };
+  // Issue order: W(0), A(0), W(1), then per stage s: A(s + 1), W(s + 2) -- the same order at
+  // the loop's entry and on its back edge, so the compiler's count of loads in flight stays
+  // exact.  The prologue's second stage is clamped into the chunk (unused when nst == 1).
+  // Stage s waits until only W(s + 1) may be in flight (its 4 loads), then a barrier (every
+  // thread's W(s) is in LDS, every wave is done reading stage s - 1's buffer).
+  constexpr int LPS = 4;
+  load_w(kb, sW0);
+  load_a(kb, a0);
+  load_w(min(kb + SKS, ke - SKS), sW1);
+  auto full = [&](int s, const u16* cw, u16* nw, const u16x8 (*ca)[4], u16x8 (*na)[4]) {
+    __builtin_amdgcn_s_waitcnt(0x70 | LPS);   // vmcnt(4) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    load_a(kb + (s + 1) * SKS, na);
+    load_w(kb + (s + 2) * SKS, nw);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cw, ca);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto tail = [&](int s, const u16* cw, u16* nw, const u16x8 (*ca)[4], u16x8 (*na)[4]) {
+    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x70 | LPS);
+    else __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (s + 1 < nst) load_a(kb + (s + 1) * SKS, na);
+    if (s + 2 < nst) load_w(kb + (s + 2) * SKS, nw);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cw, ca);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 4 < nst; s += 3) {
+    full(s, sW0, sW2, a0, a1);
+    full(s + 1, sW1, sW0, a1, a2);
+    full(s + 2, sW2, sW1, a2, a0);
+  }
+  for (; s < nst; s += 3) {
+    tail(s, sW0, sW2, a0, a1);
+    if (s + 1 < nst) tail(s + 1, sW1, sW0, a1, a2);
+    if (s + 2 < nst) tail(s + 2, sW2, sW1, a2, a0);
+  }
+  const int n = ntile * 128 + wr;
+  if (n >= N) return;
+  // acc[r]: row 8 (r / 4) + 4 hl + r % 4 of the 32, column n
+  float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
+  const bool add = (splits == 1) && accum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (row < M) {
+      float* o = Cb + (size_t)row * ldc + n;
+      *o = add ? *o + acc[r] : acc[r];
+    }
+  }
 }
 
 // Deterministic split-K reduction: out = (accum ? out : 0) + sum_s part[s] (fixed order).
@@ -781,17 +952,13 @@ struct AttnTile {
   bool own;
 };
 
-template <int QT, int KG>
+template <int QT>
 __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
-  // KG key groups: with KG = 2 the waves w and w + 2 hold the same rows (64 per block) and
-  // take alternate key tiles, each group with its own double buffer; group 1 hands its
-  // softmax state to group 0 through LDS at the end
-  constexpr int RB = AT_BR / KG;    // query rows per block
-  constexpr int NWR = 4 / KG;       // waves (of 32 rows) per key group
-  __shared__ __attribute__((aligned(16))) f16 smem[KG * 2 * 2 * AT_BK * 128];
-  // group g, buffer b: K tile at smem + (g * 2 + b) * 2 tiles, V^T tile right after it
-  auto sk = [&](int g, int b) { return smem + (size_t)((g * 2 + b) * 2) * (AT_BK * 128); };
-  auto sv = [&](int g, int b) { return smem + (size_t)((g * 2 + b) * 2 + 1) * (AT_BK * 128); };
+  constexpr int RB = AT_BR;         // query rows per block, 32 per wave
+  __shared__ __attribute__((aligned(16))) f16 smem[2 * 2 * AT_BK * 128];
+  // buffer b: K tile at smem + 2 b tiles, V^T tile right after it
+  auto sk = [&](int b) { return smem + (size_t)(b * 2) * (AT_BK * 128); };
+  auto sv = [&](int b) { return smem + (size_t)(b * 2 + 1) * (AT_BK * 128); };
 
   // row tiles in reverse order: with long causal sequences the later tiles see the most keys
   // and are dispatched first
@@ -812,8 +979,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   const int r0 = x * RB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hl = lane >> 5;
-  const int wr = wave % NWR, kgrp = wave / NWR;
-  const int r = r0 + wr * 32 + ql;
+  const int r = r0 + wave * 32 + ql;
   const bool rvalid = r < R;
   const int rc = rvalid ? r : R - 1;          // clamped row: loads stay in bounds
   const int t = rc / G;
@@ -852,13 +1018,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
       dma16(V, (d * ld + (key < ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
     }
   };
-  // the first iteration's prefix tiles go out before the sequence metadata they do not need
-  bool early[KG];
-#pragma unroll
-  for (int g = 0; g < KG; ++g) {
-    early[g] = vb + g < ntp && vb + g < ve_u;
-    if (early[g]) load_kv(Kp, Vp, a.ldp, (ptb + vb + g) * AT_BK, a.P, sk(g, 0), sv(g, 0));
-  }
+  // the first prefix tile goes out before the sequence metadata it does not need
+  const bool early = vb < ntp && vb < ve_u;
+  if (early) load_kv(Kp, Vp, a.ldp, (ptb + vb) * AT_BK, a.P, sk(0), sv(0));
 
   const int t_first = r0 / G, t_last = min(R - 1, r0 + RB - 1) / G;
   const int s_first = a.seq_start[t_first];
@@ -901,7 +1063,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     return s;
   };
   auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) { load_kv(s.K, s.V, s.ld, s.k0, s.ke, dk, dv); };
-  const int n_it = (nt + KG - 1) / KG;   // iteration it: group g takes tile vb + it * KG + g
 
   const int prow = attn_key_perm(ql);
   float m_ref = NEG_INF, l_run = 0.f;   // m_ref: reference max of the row, in scaled log2 units
@@ -911,14 +1072,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
 
-  auto step = [&](int it, int b) {
-#pragma unroll
-    for (int g = 0; g < KG; ++g)   // the next iteration's tiles, in flight during this one
-      if ((it + 1) * KG + g < nt) load_tile(tile(vb + (it + 1) * KG + g), sk(g, b ^ 1), sv(g, b ^ 1));
-    const int i = it * KG + kgrp;
-    if (i < nt) {
-    const f16* skb = sk(kgrp, b);
-    const f16* svb = sv(kgrp, b);
+  auto step = [&](int i, int b) {
+    if (i + 1 < nt) load_tile(tile(vb + i + 1), sk(b ^ 1), sv(b ^ 1));   // in flight during this tile
+    const f16* skb = sk(b);
+    const f16* svb = sv(b);
     // scores start at -m_use (q carries the log2(e)/sqrt(D) scale): the MFMAs leave
     // score - m_use, in log2 units, and a weight is exp2 of it
     f32x16 s[2];
@@ -1025,52 +1182,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pops[hs][p], acc[dt], 0, 0, 0);
         }
       }
-    }
-    // The next tiles' loads have landed and every wave is done with this tile's buffers.
+    // The next tile's loads have landed and every wave is done with this tile's buffers.
     // (The wait is a builtin so the compiler knows the loads are complete; the barrier is
     // asm with a memory clobber so no LDS access moves across it.)
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
-#pragma unroll
-  for (int g = 0; g < KG; ++g)
-    if (g < nt && !early[g]) load_tile(tile(vb + g), sk(g, 0), sv(g, 0));
-  // the first tiles have landed (or, with no tile to process, the early loads are done
-  // before the block's LDS is released)
+  if (nt > 0 && !early) load_tile(tile(vb), sk(0), sv(0));
+  // the first tile has landed (or, with no tile to process, the early load is done before
+  // the block's LDS is released)
   __builtin_amdgcn_s_waitcnt(0x70);
   if (nt > 0) asm volatile("s_barrier" ::: "memory");
-  for (int it = 0; it < n_it; it += 2) {   // two iterations per trip: buffers named statically
-    step(it, 0);
-    if (it + 1 < n_it) step(it + 1, 1);
+  for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
+    step(i, 0);
+    if (i + 1 < nt) step(i + 1, 1);
   }
-  if (KG == 2) {
-    // key group 1 hands (m_ref, l_run, acc) to group 0 through LDS (the loop's last barrier
-    // has released the tile buffers)
-    float* xs = reinterpret_cast<float*>(smem) + (size_t)wr * (66 * 64);
-    if (kgrp == 1) {
-      xs[lane] = m_ref;
-      xs[64 + lane] = l_run;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xs[(2 + dt * 16 + e) * 64 + lane] = acc[dt][e];
-    }
-    __syncthreads();
-    if (kgrp == 1) return;
-    const float m1 = xs[lane], l1 = xs[64 + lane];
-    const float M = fmaxf(m_ref, m1);
-    const float a0 = (m_ref == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
-    const float a1 = (m1 == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    if (M != NEG_INF) {
-      l_run = l_run * a0 + l1 * a1;
-      m_ref = M;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[dt][e] = acc[dt][e] * a0 + xs[(2 + dt * 16 + e) * 64 + lane] * a1;
-    }
-  }
-
   // this block's normalised partial o (acc / l) and its log2-sum-exp
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
   float lse = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
@@ -1094,13 +1220,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
     return;   // attn_merge combines the splits
   }
   if (!rvalid) return;
-  const size_t ob = ((size_t)t * Hq + hq) * 128;
+  // o [T][Hq][D]: the first D of the 128 dims (a 64-dim head runs zero-padded)
+  const int Do = a.D;
+  const size_t ob = ((size_t)t * Hq + hq) * Do;
   if (a.o_f16) {   // one float16 plane
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int d = dt * 32 + 8 * ii + 4 * hl;
+        if (d >= Do) continue;
         f16x4 v4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v4[j] = (f16)acc[dt][4 * ii + j];
@@ -1113,6 +1242,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int d = dt * 32 + 8 * ii + 4 * hl;
+      if (d >= Do) continue;
       u16 h[4], l[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1204,22 +1334,26 @@ __global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ p
 }
 
 // ----------------------------------------------------------------------------
-// RoPE table for the rows of one forward: cs[t][i] = (cos, sin)(pos[t] * theta^(-2i/128)),
-// angle and sin/cos in float64; shared by every layer of the forward.
+// RoPE table for the rows of one forward: cs[t][i] = (cos, sin)(pos[t] * theta^(-2i/D)) for
+// the D/2 pairs of a head (i < D/2 of 64 slots), angle and sin/cos in float64; shared by
+// every layer of the forward.
 // ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) rope_table(const int* __restrict__ pos, int T, double log2_theta,
+__global__ void __launch_bounds__(256) rope_table(const int* __restrict__ pos, int T, int D, double log2_theta,
                                                   float2* __restrict__ cs) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= T * 64) return;
   const int t = idx >> 6, i = idx & 63;
+  if (2 * i >= D) return;
   double sd, cd;
-  sincos((double)pos[t] * exp2(-(2.0 * i / 128.0) * log2_theta), &sd, &cd);
+  sincos((double)pos[t] * exp2(-(2.0 * i / D) * log2_theta), &sd, &cd);
   cs[idx] = make_float2((float)cd, (float)sd);
 }
 
 // ----------------------------------------------------------------------------
-// Fused split-K reduce + RoPE + KV layout for the q|k|v projection (head_dim 128).
-// src: projection output [T][(Hq+2Hkv)*128] (splits == 1) or its split partials.
+// Fused split-K reduce + RoPE + KV layout for the q|k|v projection.
+// src: projection output [T][(Hq+2Hkv)*D] (splits == 1) or its split partials, D = 64 or
+// 128.  The attention's heads are 128 wide: a 64-dim head is written zero-padded (q and K
+// dims [D, 128), V^T rows [D, 128)).
 // Grid (ceil(T/16), Hq + 2 Hkv): y < Hq + Hkv rotates head y over 16 rows (q as
 // f16 hi + lo, k as f16 into K[hk][ldk][128]); the last Hkv values of y
 // transpose one kv head's V over 16 rows into Vt[hk][128][ldv] via LDS.
@@ -1229,7 +1363,7 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
                                                 const float2* __restrict__ cs,
                                                 f16* __restrict__ q_hi, f16* __restrict__ q_lo,
                                                 f16* __restrict__ kdst, int ldk, f16* __restrict__ vtdst,
-                                                int ldv, float qscale, int* __restrict__ flags) {
+                                                int ldv, int D, float qscale, int* __restrict__ flags) {
   __shared__ float vt[16][129];
   bool bad = false;
   const int t0 = blockIdx.x * 16;
@@ -1249,15 +1383,24 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
     return a;
   };
   if (h < nqk) {
+    const int half = D >> 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = threadIdx.x + 256 * j;
       const int rr = idx >> 6, i = idx & 63;
       const int t = t0 + rr;
       if (t >= T) continue;
-      const float a = ld(t, h * 128 + i), b = ld(t, h * 128 + i + 64);
-      const float2 e = cs[t * 64 + i];
-      const float ra = a * e.x - b * e.y, rb = b * e.x + a * e.y;
+      // slot i < D/2: the rotated pair (i, i + D/2); slots past it zero dims [D, 128)
+      float ra = 0.f, rb = 0.f;
+      int da = D + (i - half), db = D + half + (i - half);
+      if (i < half) {
+        const float a = ld(t, h * D + i), b = ld(t, h * D + i + half);
+        const float2 e = cs[t * 64 + i];
+        ra = a * e.x - b * e.y;
+        rb = b * e.x + a * e.y;
+        da = i;
+        db = i + half;
+      }
       bad |= f16_out_of_range(ra) || f16_out_of_range(rb);
       if (h < Hq) {
         // operand-ordered layout (see AttnArgs): row r = t*G + g of KV head h / G
@@ -1267,27 +1410,27 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
         // q carries the softmax scale log2(e)/sqrt(D): scores come out in log2 units
         const float sa = ra * qscale, sb = rb * qscale;
         const f16 qa = (f16)sa, qb = (f16)sb;
-        q_hi[at(i)] = qa;
-        q_hi[at(i + 64)] = qb;
+        q_hi[at(da)] = qa;
+        q_hi[at(db)] = qb;
         if (q_lo) {
-          q_lo[at(i)] = (f16)(sa - (float)qa);
-          q_lo[at(i + 64)] = (f16)(sb - (float)qb);
+          q_lo[at(da)] = (f16)(sa - (float)qa);
+          q_lo[at(db)] = (f16)(sb - (float)qb);
         }
       } else {
         f16* kd = kdst + ((size_t)(h - Hq) * ldk + t) * 128;
-        kd[i] = (f16)ra;
-        kd[i + 64] = (f16)rb;
+        kd[da] = (f16)ra;
+        kd[db] = (f16)rb;
       }
     }
   } else {
     const int hk = h - nqk;
-    const int c0 = nqk * 128 + hk * 128;
+    const int c0 = nqk * D + hk * D;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = threadIdx.x + 256 * j;
       const int rr = idx >> 7, d = idx & 127;
       const int t = t0 + rr;
-      vt[rr][d] = (t < T) ? ld(t, c0 + d) : 0.f;
+      vt[rr][d] = (t < T && d < D) ? ld(t, c0 + d) : 0.f;
       bad |= f16_out_of_range(vt[rr][d]);
     }
     __syncthreads();
@@ -1308,7 +1451,8 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
 template <int MAXS>
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
-                                                  int D, u16* __restrict__ oh, u16* __restrict__ ol, int f16out) {
+                                                  int D, int Dp, u16* __restrict__ oh, u16* __restrict__ ol,
+                                                  int f16out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one (t, hq)
   const int d4 = D >> 2;
   if (i >= (size_t)T * Hq * d4) return;
@@ -1322,7 +1466,7 @@ __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_pa
   for (int s = 0; s < MAXS; ++s) {
     if (s < S) {
       lse[s] = lse_part[(size_t)s * T * Hq + th];
-      part[s] = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * D)[c];
+      part[s] = reinterpret_cast<const float4*>(o_part + ((size_t)s * T * Hq + th) * Dp)[c];
     }
   }
   float M = NEG_INF;
@@ -1610,12 +1754,51 @@ GemmPlan gemm_bf16_plan(int M, int N, int K, size_t part_cap) {
   return p;
 }
 
+// Few-row plan (measured on the 7B and 2B projection shapes): about 1024 blocks of 128
+// columns at first, each chunk at least 3 stages, at most 32 splits; then, while the grid
+// exceeds 512 blocks and chunks are shorter than 1024 of K, fewer splits (long chunks keep
+// the split partials, written here and read by the consumer, small); partials within
+// part_cap floats.
+static int skinny_splits(int M, int N, int K, size_t part_cap) {
+  const long nt = cdiv(N, 128);
+  long sp = std::max(1L, 1024 / nt);
+  sp = std::min<long>(sp, std::max(1, K / (3 * SKS)));
+  sp = std::min<long>(sp, 32);
+  while (sp > 1 && sp * nt > 512 && K / sp < 1024) --sp;
+  while (sp > 1 && (size_t)sp * M * N > part_cap) --sp;
+  return (int)sp;
+}
+
+static hipError_t launch_skinny(bool f16, const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K,
+                                const GemmSegs& seg, int N, float* C, int ldc, int accum, size_t part_cap,
+                                float* part, hipStream_t s, int* eff_splits) {
+  const int sp = skinny_splits(M, N, K, part_cap);
+  const int k_chunk = cdiv(cdiv(K, sp), SKS) * SKS;
+  const int splits = cdiv(K, k_chunk);
+  *eff_splits = splits;
+  const int nt = cdiv(N, 128);
+  float* out = splits == 1 ? C : part;
+  const int ldo = splits == 1 ? ldc : N;
+  const int acc = splits == 1 ? accum : 0;
+  if (f16)
+    gemm_skinny<true><<<nt * splits, 256, 0, s>>>(Ah, nullptr, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo,
+                                                  (size_t)M * N, acc);
+  else
+    gemm_skinny<false><<<nt * splits, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo,
+                                                   (size_t)M * N, acc);
+  return hipGetLastError();
+}
+
+// the weight-streaming kernel takes products of at most 32 rows with K a multiple of its stage
+static bool use_skinny(int M, int K) { return M <= 32 && K % SKS == 0; }
+
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
                             float* C, int ldc, int accum, size_t part_cap, float* part, hipStream_t s,
                             int* eff_splits) {
   *eff_splits = 1;
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % G2K) return hipErrorInvalidValue;
+  if (use_skinny(M, K)) return launch_skinny(false, Ah, Al, lda, M, K, seg, N, C, ldc, accum, part_cap, part, s, eff_splits);
   const GemmPlan pl = gemm_bf16_plan(M, N, K, part_cap);
   const int bk = pl.wide ? G2K : GBK;
   const int mt = cdiv(M, GBM), nt = cdiv(N, pl.wide ? G2N : GBN);
@@ -1669,6 +1852,7 @@ hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmS
   *eff_splits = 1;
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % G2K) return hipErrorInvalidValue;
+  if (use_skinny(M, K)) return launch_skinny(true, A, nullptr, lda, M, K, seg, N, C, ldc, accum, part_cap, part, s, eff_splits);
   const GemmPlan pl = gemm_f16_plan(M, N, K, part_cap);
   const int mt = cdiv(M, G2M), nt = cdiv(N, G2N);
   const int k_chunk = cdiv(cdiv(K, pl.splits), G2K) * G2K;
@@ -1751,19 +1935,21 @@ hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_strid
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(const int* pos, int T, double log2_theta, float2* cs, hipStream_t s) {
+hipError_t launch_rope_table(const int* pos, int T, int D, double log2_theta, float2* cs, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  rope_table<<<cdiv((long)T * 64, 256), 256, 0, s>>>(pos, T, log2_theta, cs);
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  rope_table<<<cdiv((long)T * 64, 256), 256, 0, s>>>(pos, T, D, log2_theta, cs);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int splits, int T, int Hq, int Hkv,
                            const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
-                           float qscale, int* flags, hipStream_t s) {
+                           int D, float qscale, int* flags, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
   dim3 grid(cdiv(T, 16), Hq + 2 * Hkv);
   qkv_post<<<grid, 256, 0, s>>>(src, lds, split_stride, splits, T, Hq, Hkv, cs, (f16*)q_hi, (f16*)q_lo, (f16*)kdst,
-                                ldk, (f16*)vtdst, ldv, qscale, flags);
+                                ldk, (f16*)vtdst, ldv, D, qscale, flags);
   return hipGetLastError();
 }
 
@@ -1858,19 +2044,13 @@ int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
 }
 
 
-hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, int kg, hipStream_t s) {
+hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (a.n_split < 1 || a.n_split > kAttnMaxSplits || (q_terms != 1 && q_terms != 2) || (kg != 1 && kg != 2))
-    return hipErrorInvalidValue;
-  const long nb = (long)cdiv((long)a.G * a.T, AT_BR / kg) * a.Hkv * a.n_split;
+  if (a.n_split < 1 || a.n_split > kAttnMaxSplits || (q_terms != 1 && q_terms != 2)) return hipErrorInvalidValue;
+  const long nb = (long)cdiv((long)a.G * a.T, AT_BR) * a.Hkv * a.n_split;
   const int grid = (int)(cdiv(nb, 8) * 8);
-  if (kg == 1) {
-    if (q_terms == 1) attn_fwd_f16<1, 1><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_f16<2, 1><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (q_terms == 1) attn_fwd_f16<1, 2><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_f16<2, 2><<<grid, 256, 0, s>>>(a);
-  }
+  if (q_terms == 1) attn_fwd_f16<1><<<grid, 256, 0, s>>>(a);
+  else attn_fwd_f16<2><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1879,9 +2059,9 @@ hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, 
   if (T <= 0) return hipSuccess;
   const int grid = cdiv((long)T * Hq * (D / 4), 256);
   if (S <= 8)
-    attn_merge<8><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
+    attn_merge<8><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out);
   else
-    attn_merge<kAttnMaxSplits><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, oh, ol, f16out);
+    attn_merge<kAttnMaxSplits><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out);
   return hipGetLastError();
 }
 

@@ -13,6 +13,11 @@ import os
 from typing import Optional, Sequence
 
 import numpy as np
+# torch brings its own HIP runtime (libamdhip64.so.7 in torch/lib).  Loading it before
+# libjev.so lets the library's libamdhip64.so.7 dependency resolve to that same, already
+# loaded runtime; loaded the other way round a process holds two HIP runtimes, and the
+# library's runtime does not know the device buffers torch's runtime allocated.
+import torch  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # JEV_LIBRARY names another build of the same library (the host-sanitized one of the CPU tests)

@@ -119,8 +119,9 @@ def _short(name: str) -> str:
     return n[:48]
 
 
-def kernel_stats_markdown(run_dir: str, title: str, command: str = "") -> str:
-    """Per-kernel totals (rocprofv3 --stats) and per-launch-shape medians (kernel trace)."""
+def kernel_stats_markdown(run_dir: str, title: str, command: str = "", always=("attn_fwd_f16", "attn_merge")) -> str:
+    """Per-kernel totals (rocprofv3 --stats) and per-launch-shape medians (kernel trace): the
+    top 16 shapes by total time plus every shape of the `always` kernels."""
     stats = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
     trace = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not stats or not trace:
@@ -142,9 +143,11 @@ def kernel_stats_markdown(run_dir: str, title: str, command: str = "") -> str:
                    int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
             groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     tot = sum(sum(v) for v in groups.values())
-    lines += ["", "Per launch shape (blocks x, y, z), top 16 by total time:", "",
+    lines += ["", "Per launch shape (blocks x, y, z), top 16 by total time, then every attention / merge shape:", "",
               "| kernel | blocks | launches | median us | total ms | % |", "|---|---|---|---|---|---|"]
-    for (n, gx, gy, gz), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:16]:
+    ranked = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    shown = ranked[:16] + [kv for kv in ranked[16:] if any(a in kv[0][0] for a in always)]
+    for (n, gx, gy, gz), v in shown:
         v.sort()
         lines.append(f"| {n} | {gx}x{gy}x{gz} | {len(v)} | {v[len(v) // 2]:.1f} | {sum(v) / 1e3:.2f} | "
                      f"{100 * sum(v) / tot:.1f} |")
