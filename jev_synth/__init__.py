@@ -149,6 +149,12 @@ CONFIGS: Dict[str, Config] = {
                   mlp=1024, vocab=4096, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
                   n_vis=150, n_text=10, n_suffix=6, len_lo=1, len_hi=20, s_max=24, n_cands=3,
                   n_questions=4, stem_len=5, tree_cands=4, cand_len_lo=1, cand_len_hi=4, overlap=True),
+    # edge shapes of the few-row product: hidden 320 (ragged 128-column tiles), MLP 832 (the
+    # down projection's last K split is a single 64-wide stage, q|k|v an odd stage count),
+    # one suffix of one token (a single row)
+    "mk": Config("mk", n_layers=2, hidden=320, n_q_heads=5, n_kv_heads=1, head_dim=64,
+                 mlp=832, vocab=1024, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
+                 n_vis=40, n_text=8, n_suffix=4, fixed_lens=(1, 7, 10, 4), s_max=10, n_cands=3),
     # fp32 tree workload on the tiny decoder (oracle pins and fp32 parity)
     "t1": Config("t1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                  mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",

@@ -34,10 +34,13 @@ def test_score_suffixes_vs_oracle(name, seed, precision):
 
 @pytest.mark.parametrize("name,n,precision", [("m2", 1, "default"), ("m2", 2, "split"), ("m7", 1, "default"),
                                               ("m7", 2, "f16"), ("m7", 3, "split"), ("m7", 1, "f16_down"),
-                                              ("m64", 1, "default"), ("m64", 2, "f16_prefill")])
+                                              ("m64", 1, "default"), ("m64", 2, "f16_prefill"),
+                                              ("mk", 1, "default"), ("mk", 1, "split"), ("mk", 2, "default"),
+                                              ("mk", 4, "split")])
 def test_few_rows_vs_oracle(name, n, precision):
-    """Scoring calls of one to three suffixes: at most 32 rows take the weight-streaming GEMM
-    (one float16 plane or two bf16 planes, split K), more rows the tiled one."""
+    """Scoring calls of one to four suffixes: at most 32 rows take the weight-streaming GEMM
+    (one float16 plane or two bf16 planes, split K), more rows the tiled one.  mk adds a
+    single-row call, ragged column tiles and a one-stage last K split."""
     cfg = S.CONFIGS[name]
     suf = S.suffix_inputs(cfg, 0, n)
     rows = int(suf["lens"].sum())

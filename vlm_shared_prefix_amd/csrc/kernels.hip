@@ -576,27 +576,30 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
 // ----------------------------------------------------------------------------
 // K3 for few rows (M <= 32): a weight-streaming product.  Block = 4 waves and 128 output
 // columns (32 per wave) over one K chunk, walked in stages of 64 of K.  A stage's weight
-// tile (128 rows x 128 B) is staged in LDS by direct global->LDS loads in which a wave's
-// instruction covers 8 whole 128 B row segments (fully used cache lines; loading the MFMA
-// operand layout straight into registers touches 32 rows per instruction and streamed
-// ~30% slower); the 16 B chunk c of row r sits at position c ^ ((r / 2) % 8), so the
-// operand reads (a column wave's 32 rows, one chunk each) are bank-conflict free.  A ring
-// of three stages keeps two stages of loads in flight.  The M activation rows go straight
-// to registers as the A operand of v_mfma 32x32x16 (rows past M clamped, their outputs
-// dropped).  F16: one f16 activation plane x the f16 weight mirror; else two bf16 planes x
-// bf16 weights (W·hi + W·lo).  The chunk's sum goes to C (splits == 1) or to partials
-// [split][M][N].
+// tile (128 rows x 128 B) and its activation tile (32 rows x 128 B per plane; rows past M
+// repeat row M - 1, their outputs dropped) are staged in LDS by direct global->LDS loads
+// in which a wave's instruction covers 8 whole 128 B row segments (fully used cache
+// lines).  Loading the MFMA operand layout straight into registers touches 32 rows per
+// instruction and issued every wave's own copy of the activations: 30-40% slower.  The
+// 16 B chunk c of row r sits at position c ^ ((r / 2) % 8), so the operand reads are
+// bank-conflict free.  A ring of three stages keeps two stages of loads in flight.  F16:
+// one f16 activation plane x the f16 weight mirror; else two bf16 planes x bf16 weights
+// (W·hi + W·lo).  The chunk's sum goes to C (splits == 1) or to partials [split][M][N].
 // ----------------------------------------------------------------------------
 #define SKS 64   // K per stage of the few-row product
 template <bool F16>
-__global__ void __launch_bounds__(256, 3) gemm_skinny(const u16* __restrict__ Ah, const u16* __restrict__ Al,
+__global__ void __launch_bounds__(256, 2) gemm_skinny(const u16* __restrict__ Ah, const u16* __restrict__ Al,
                                                      int lda, int M, int K, GemmSegs seg, int N, int n_tiles,
                                                      int splits, int k_chunk, float* __restrict__ C, int ldc,
                                                      size_t split_stride, int accum) {
   constexpr int NB = F16 ? 1 : 2;   // activation planes
+  constexpr int AS = 32 * SKS;      // one activation plane of a stage
   __shared__ __attribute__((aligned(16))) u16 sW0[128 * SKS];
   __shared__ __attribute__((aligned(16))) u16 sW1[128 * SKS];
   __shared__ __attribute__((aligned(16))) u16 sW2[128 * SKS];
+  __shared__ __attribute__((aligned(16))) u16 sA0[NB * AS];
+  __shared__ __attribute__((aligned(16))) u16 sA1[NB * AS];
+  __shared__ __attribute__((aligned(16))) u16 sA2[NB * AS];
   const int v = blockIdx.x;
   if (v >= n_tiles * splits) return;
   const int ntile = v % n_tiles, ks = v / n_tiles;
@@ -604,7 +607,8 @@ __global__ void __launch_bounds__(256, 3) gemm_skinny(const u16* __restrict__ Ah
   const int ql = lane & 31, hl = lane >> 5;
   const int kb = ks * k_chunk, ke = min(K, kb + k_chunk);
   const int nst = (ke - kb) / SKS;   // >= 1
-  // the thread's 4 weight loads per stage: slot = q * 256 + tid, row slot / 8, chunk slot % 8
+  // the thread's loads per stage: 4 weight slots q * 256 + tid (row slot / 8, chunk slot % 8)
+  // and, per plane, activation slot tid (row tid / 8)
   const u16* srcW[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -612,81 +616,81 @@ __global__ void __launch_bounds__(256, 3) gemm_skinny(const u16* __restrict__ Ah
     const int n = ntile * 128 + row;
     srcW[q] = seg_row(seg, n < N ? n : 0, K) + c * 8;
   }
-  auto load_w = [&](int k0, u16* dst) {
+  const u16* srcA[2];   // fixed size: a template-sized array of these loads drops the host stub
+  {
+    const int row = tid >> 3, c = (tid & 7) ^ ((row >> 1) & 7);
+    const size_t off = (size_t)(row < M ? row : M - 1) * lda + c * 8;
+    srcA[0] = Ah + off;
+    srcA[1] = F16 ? srcA[0] : Al + off;
+  }
+  auto load = [&](int k0, u16* dw, u16* da) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(srcW[q] + k0, dst + (q * 256 + wave * 64) * 8, 16, 0, 0);
-  };
-  const int m = ql < M ? ql : M - 1;
-  const u16* arow[NB];
-  arow[0] = Ah + (size_t)m * lda + hl * 8;
-  if (!F16) arow[NB - 1] = Al + (size_t)m * lda + hl * 8;
-  typedef u16 u16x8 __attribute__((ext_vector_type(8)));
-  u16x8 a0[NB][4], a1[NB][4], a2[NB][4];
-  auto load_a = [&](int k0, u16x8 (*av)[4]) {
+      __builtin_amdgcn_global_load_lds(srcW[q] + k0, dw + (q * 256 + wave * 64) * 8, 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < NB; ++p)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) av[p][j] = *reinterpret_cast<const u16x8*>(arow[p] + k0 + 16 * j);
+      __builtin_amdgcn_global_load_lds(srcA[p] + k0, da + p * AS + wave * 64 * 8, 16, 0, 0);
   };
+  typedef u16 u16x8 __attribute__((ext_vector_type(8)));
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int wr = wave * 32 + ql;   // the lane's weight row (output column) in the tile
-  auto compute = [&](const u16* sw, const u16x8 (*av)[4]) {
+  auto compute = [&](const u16* sw, const u16* sa) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int g = 2 * j + hl;
       const u16x8 b = *reinterpret_cast<const u16x8*>(sw + wr * SKS + ((g ^ ((wr >> 1) & 7)) * 8));
 #pragma unroll
       for (int p = 0; p < NB; ++p) {
+        const u16x8 a = *reinterpret_cast<const u16x8*>(sa + p * AS + ql * SKS + ((g ^ ((ql >> 1) & 7)) * 8));
         if (F16)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av[p][j]),
-                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      acc, 0, 0, 0);
         else
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[p][j]),
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
       }
     }
   };
-  // Issue order: W(0), A(0), W(1), then per stage s: A(s + 1), W(s + 2) -- the same order at
-  // the loop's entry and on its back edge, so the compiler's count of loads in flight stays
-  // exact.  The prologue's second stage is clamped into the chunk (unused when nst == 1).
-  // Stage s waits until only W(s + 1) may be in flight (its 4 loads), then a barrier (every
-  // thread's W(s) is in LDS, every wave is done reading stage s - 1's buffer).
-  constexpr int LPS = 4;
-  load_w(kb, sW0);
-  load_a(kb, a0);
-  load_w(min(kb + SKS, ke - SKS), sW1);
-  auto full = [&](int s, const u16* cw, u16* nw, const u16x8 (*ca)[4], u16x8 (*na)[4]) {
-    __builtin_amdgcn_s_waitcnt(0x70 | LPS);   // vmcnt(4) lgkmcnt(0)
+  // Stage s waits until only stage s + 1's loads may be in flight (4 + NB per thread), then a
+  // barrier (every thread's stage s is in LDS, every wave is done reading stage s - 1's
+  // buffers), then the loads of stage s + 2 into those buffers, then stage s's MFMAs.  Both
+  // prologue loads are unconditional (the second clamped into the chunk, unused when
+  // nst == 1), which keeps the compiler's count of loads in flight exact at the loop head.
+  auto wait_stage = [&]() {
+    if constexpr (F16) __builtin_amdgcn_s_waitcnt(0x75);   // vmcnt(5) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x76);                 // vmcnt(6) lgkmcnt(0)
+  };
+  load(kb, sW0, sA0);
+  load(min(kb + SKS, ke - SKS), sW1, sA1);
+  auto full = [&](int s, const u16* cw, const u16* ca, u16* nw, u16* na) {
+    wait_stage();
     asm volatile("s_barrier" ::: "memory");
-    load_a(kb + (s + 1) * SKS, na);
-    load_w(kb + (s + 2) * SKS, nw);
+    load(kb + (s + 2) * SKS, nw, na);
     __builtin_amdgcn_sched_barrier(0);
     compute(cw, ca);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto tail = [&](int s, const u16* cw, u16* nw, const u16x8 (*ca)[4], u16x8 (*na)[4]) {
-    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x70 | LPS);
+  auto tail = [&](int s, const u16* cw, const u16* ca, u16* nw, u16* na) {
+    if (s + 1 < nst) wait_stage();
     else __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    if (s + 1 < nst) load_a(kb + (s + 1) * SKS, na);
-    if (s + 2 < nst) load_w(kb + (s + 2) * SKS, nw);
+    if (s + 2 < nst) load(kb + (s + 2) * SKS, nw, na);
     __builtin_amdgcn_sched_barrier(0);
     compute(cw, ca);
     __builtin_amdgcn_sched_barrier(0);
   };
   int s = 0;
   for (; s + 4 < nst; s += 3) {
-    full(s, sW0, sW2, a0, a1);
-    full(s + 1, sW1, sW0, a1, a2);
-    full(s + 2, sW2, sW1, a2, a0);
+    full(s, sW0, sA0, sW2, sA2);
+    full(s + 1, sW1, sA1, sW0, sA0);
+    full(s + 2, sW2, sA2, sW1, sA1);
   }
   for (; s < nst; s += 3) {
-    tail(s, sW0, sW2, a0, a1);
-    if (s + 1 < nst) tail(s + 1, sW1, sW0, a1, a2);
-    if (s + 2 < nst) tail(s + 2, sW2, sW1, a2, a0);
+    tail(s, sW0, sA0, sW2, sA2);
+    if (s + 1 < nst) tail(s + 1, sW1, sA1, sW0, sA0);
+    if (s + 2 < nst) tail(s + 2, sW2, sA2, sW1, sA1);
   }
   const int n = ntile * 128 + wr;
   if (n >= N) return;
@@ -1262,46 +1266,85 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 //   x[row] += sum_s part[s][row]      (fixed order; nothing to add if splits == 0)
 //   y = g * x / sqrt(mean(x^2) + eps) written as bf16 hi/lo planes, or as one float16
 //   plane into yh when f16out (skipped if yh == nullptr)
-// H % 4 == 0 and H <= 8192.
+// H % 4 == 0 and H <= 8192.  NT threads per block: 256, or 1024 for few rows, where a
+// thread's (at most two) float4 columns take each group of eight split partials in one
+// round of loads.
 // ----------------------------------------------------------------------------
-template <typename WT>
-__global__ void __launch_bounds__(256) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
-                                                     float* __restrict__ x, int H, const WT* __restrict__ g,
-                                                     float eps, u16* __restrict__ yh, u16* __restrict__ yl,
-                                                     int ldy, int f16out, int* __restrict__ flags) {
-  __shared__ float red[4];
+template <typename WT, int NT>
+__global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
+                                                    float* __restrict__ x, int H, const WT* __restrict__ g,
+                                                    float eps, u16* __restrict__ yh, u16* __restrict__ yl,
+                                                    int ldy, int f16out, int* __restrict__ flags) {
+  constexpr int J = 2048 / NT;   // float4 columns per thread
+  __shared__ float red[NT / 64];
   const int row = blockIdx.x;
   const int H4 = H >> 2;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)row * H);
-  float4 v[8];
+  const float4* pr = splits > 0 ? reinterpret_cast<const float4*>(part + (size_t)row * H) : nullptr;
+  float4 v[J];
   float ss = 0.f;
+  if constexpr (J <= 2) {
+    bool ok[J];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int k = threadIdx.x + 256 * j;
-    if (k < H4) {
-      float4 a = xr[k];
-      // partials summed in split order; loaded eight at a time so their loads overlap
-      for (int s0 = 0; s0 < splits; s0 += 8) {
-        float4 b[8];
+    for (int j = 0; j < J; ++j) {
+      const int k = threadIdx.x + NT * j;
+      ok[j] = k < H4;
+      v[j] = ok[j] ? xr[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int s0 = 0; s0 < splits; s0 += 8) {   // partials summed in split order
+      float4 b[J][8];
+#pragma unroll
+      for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (s0 + u < splits)
-            b[u] = reinterpret_cast<const float4*>(part + (s0 + u) * split_stride + (size_t)row * H)[k];
+          if (ok[j] && s0 + u < splits) b[j][u] = pr[(s0 + u) * (split_stride >> 2) + threadIdx.x + NT * j];
+#pragma unroll
+      for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (s0 + u < splits) { a.x += b[u].x; a.y += b[u].y; a.z += b[u].z; a.w += b[u].w; }
+          if (ok[j] && s0 + u < splits) {
+            v[j].x += b[j][u].x; v[j].y += b[j][u].y; v[j].z += b[j][u].z; v[j].w += b[j][u].w;
+          }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (ok[j]) {
+        if (splits > 0) xr[threadIdx.x + NT * j] = v[j];
+        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
       }
-      if (splits > 0) xr[k] = a;
-      v[j] = a;
-      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = threadIdx.x + NT * j;
+      if (k < H4) {
+        float4 a = xr[k];
+        // partials summed in split order; loaded eight at a time so their loads overlap
+        for (int s0 = 0; s0 < splits; s0 += 8) {
+          float4 b[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) b[u] = pr[(s0 + u) * (split_stride >> 2) + k];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) { a.x += b[u].x; a.y += b[u].y; a.z += b[u].z; a.w += b[u].w; }
+        }
+        if (splits > 0) xr[k] = a;
+        v[j] = a;
+        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+      }
     }
   }
   if (yh == nullptr) return;
-  ss = block_sum256(ss, red);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) ss += red[w];
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int k = threadIdx.x + 256 * j;
+  for (int j = 0; j < J; ++j) {
+    const int k = threadIdx.x + NT * j;
     if (k < H4) {
       const float in[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
       const size_t o = (size_t)row * ldy + 4 * k;
@@ -1369,21 +1412,43 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
   const int t0 = blockIdx.x * 16;
   const int nqk = Hq + Hkv;
   const int h = blockIdx.y;
-  auto ld = [&](int t, int c) {   // split partials summed in order, loaded eight at a time
-    float a = src[(size_t)t * lds + c];
-    for (int s0 = 1; s0 < splits; s0 += 8) {
-      float b[8];
+  // The thread's N elements (offsets off[n] into a partial, valid ok[n]) summed over the
+  // split partials in split order; every element's loads of a group of four partials go
+  // out in one round.
+  auto ld_all = [&](auto& val, const auto& off, const auto& ok) {
+    constexpr int N = sizeof(val) / sizeof(float);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < splits) b[u] = src[(s0 + u) * split_stride + (size_t)t * lds + c];
+    for (int n = 0; n < N; ++n) val[n] = ok[n] ? src[off[n]] : 0.f;
+    for (int s0 = 1; s0 < splits; s0 += 4) {
+      float b[N][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < splits) a += b[u];
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (ok[n] && s0 + u < splits) b[n][u] = src[(s0 + u) * split_stride + off[n]];
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (ok[n] && s0 + u < splits) val[n] += b[n][u];
     }
-    return a;
   };
   if (h < nqk) {
     const int half = D >> 1;
+    // element pairs (i, i + D/2) of rows t0 + idx / 64, slot i = idx % 64, for idx = tid + 256 j
+    float val[8];
+    size_t off[8];
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int rr = idx >> 6, i = idx & 63;
+      const int t = t0 + rr;
+      ok[2 * j] = ok[2 * j + 1] = t < T && i < half;
+      off[2 * j] = (size_t)t * lds + h * D + i;
+      off[2 * j + 1] = off[2 * j] + half;
+    }
+    ld_all(val, off, ok);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = threadIdx.x + 256 * j;
@@ -1394,7 +1459,7 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
       float ra = 0.f, rb = 0.f;
       int da = D + (i - half), db = D + half + (i - half);
       if (i < half) {
-        const float a = ld(t, h * D + i), b = ld(t, h * D + i + half);
+        const float a = val[2 * j], b = val[2 * j + 1];
         const float2 e = cs[t * 64 + i];
         ra = a * e.x - b * e.y;
         rb = b * e.x + a * e.y;
@@ -1425,13 +1490,24 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
   } else {
     const int hk = h - nqk;
     const int c0 = nqk * D + hk * D;
+    float val[8];
+    size_t off[8];
+    bool ok[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = threadIdx.x + 256 * j;
       const int rr = idx >> 7, d = idx & 127;
       const int t = t0 + rr;
-      vt[rr][d] = (t < T && d < D) ? ld(t, c0 + d) : 0.f;
-      bad |= f16_out_of_range(vt[rr][d]);
+      ok[j] = t < T && d < D;
+      off[j] = (size_t)t * lds + c0 + d;
+    }
+    ld_all(val, off, ok);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int rr = idx >> 7, d = idx & 127;
+      vt[rr][d] = val[j];
+      bad |= f16_out_of_range(val[j]);
     }
     __syncthreads();
 #pragma unroll
@@ -1927,11 +2003,24 @@ hipError_t launch_residual_norm(bool bf16, const float* part, size_t split_strid
                                 int H, const void* g, float eps, uint16_t* yh, uint16_t* yl, int ldy, bool f16out,
                                 int* flags, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (bf16)
-    residual_norm<u16><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy, f16out, flags);
-  else
-    residual_norm<float><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl, ldy,
-                                           f16out, flags);
+  if (H % 4 || H > 8192 || split_stride % 4) return hipErrorInvalidValue;
+  // few rows: 1024 threads per row, so each thread's partial loads go out in one round
+  const bool wide = M <= 64;
+  if (bf16) {
+    if (wide)
+      residual_norm<u16, 1024><<<M, 1024, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy,
+                                                  f16out, flags);
+    else
+      residual_norm<u16, 256><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const u16*)g, eps, yh, yl, ldy,
+                                                f16out, flags);
+  } else {
+    if (wide)
+      residual_norm<float, 1024><<<M, 1024, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl,
+                                                    ldy, f16out, flags);
+    else
+      residual_norm<float, 256><<<M, 256, 0, s>>>(part, split_stride, splits, x, H, (const float*)g, eps, yh, yl,
+                                                  ldy, f16out, flags);
+  }
   return hipGetLastError();
 }
 
