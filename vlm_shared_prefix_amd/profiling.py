@@ -157,7 +157,8 @@ def kernel_stats_markdown(run_dir: str, title: str, command: str = "", always=("
 MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsF16", "MfmaFlopsBF16")
 
 
-def mfma_markdown(run_dir: str, title: str, command: str = "", kernels=("attn_fwd_f16", "gemm_bf16w", "gemm_bf16s")) -> str:
+def mfma_markdown(run_dir: str, title: str, command: str = "",
+                  kernels=("attn_fwd_f16", "gemm_bf16w", "gemm_bf16s", "gemm_skinny")) -> str:
     """Per kernel and launch shape: mean MfmaUtil (percent of SIMD cycles with the MFMA unit
     busy) and executed MFMA flops per dispatch (f16 + bf16) from one counter run."""
     paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -234,26 +235,33 @@ def lds_ta_markdown(run_dir: str, title: str, command: str = "", kernels=("attn_
     return "\n".join(lines) + "\n"
 
 
+def _with_notes(md: str) -> str:
+    """The summary followed by the notes in JEV_STATS_NOTES (which launch shape is which call)."""
+    notes = os.environ.get("JEV_STATS_NOTES", "").strip()
+    return md + ("\n" + notes + "\n" if notes else "")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "--lds-ta":
-        md = lds_ta_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 LDS and TA counters"),
-                             os.environ.get("JEV_STATS_COMMAND", ""))
+        md = _with_notes(lds_ta_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 LDS and TA counters"),
+                                         os.environ.get("JEV_STATS_COMMAND", "")))
         if len(sys.argv) > 3:
             with open(sys.argv[3], "w") as f:
                 f.write(md)
         print(md)
         sys.exit(0)
     if len(sys.argv) >= 3 and sys.argv[1] == "--mfma":
-        md = mfma_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 MFMA counters"),
-                           os.environ.get("JEV_STATS_COMMAND", ""))
+        md = _with_notes(mfma_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 MFMA counters"),
+                                       os.environ.get("JEV_STATS_COMMAND", "")))
         if len(sys.argv) > 3:
             with open(sys.argv[3], "w") as f:
                 f.write(md)
         print(md)
         sys.exit(0)
     if len(sys.argv) >= 3 and sys.argv[1] == "--stats":
-        md = kernel_stats_markdown(sys.argv[2], os.environ.get("JEV_STATS_TITLE", "rocprofv3 kernel statistics"),
-                                   os.environ.get("JEV_STATS_COMMAND", ""))
+        md = _with_notes(kernel_stats_markdown(sys.argv[2],
+                                               os.environ.get("JEV_STATS_TITLE", "rocprofv3 kernel statistics"),
+                                               os.environ.get("JEV_STATS_COMMAND", "")))
         if len(sys.argv) > 3:
             with open(sys.argv[3], "w") as f:
                 f.write(md)
