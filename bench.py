@@ -666,7 +666,7 @@ def main():
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall_ms:.3f}); median "
         f"{step_st['median_ms']:.3f}, p10 {step_st['p10_ms']:.3f}, p90 {step_st['p90_ms']:.3f}")
-    score_st = step_stats(stream, score_only, args.steps)
+    score_st = step_stats(stream, score_only, max(args.steps, 50))   # median / p10 / p90 over >= 50 calls
     ms_score = score_st["median_ms"]
     prefill_st = step_stats(stream, prefill_only, max(3, args.steps // 2))
     ms_prefill = prefill_st["median_ms"]

@@ -574,7 +574,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
 }
 
 // ----------------------------------------------------------------------------
-// K3 for few rows (M <= 32): a weight-streaming product.  Block = 4 waves and 128 output
+// K3 for few rows (M <= 64): a weight-streaming product.  Block = 4 waves and 128 output
 // columns (32 per wave) over one K chunk, walked in stages of 64 of K.  A stage's weight
 // tile (128 rows x 128 B) and its activation tile (32 rows x 128 B per plane; rows past M
 // repeat row M - 1, their outputs dropped) are staged in LDS by direct global->LDS loads
@@ -591,7 +591,7 @@ template <bool F16>
 __global__ void __launch_bounds__(256, 2) gemm_skinny(const u16* __restrict__ Ah, const u16* __restrict__ Al,
                                                      int lda, int M, int K, GemmSegs seg, int N, int n_tiles,
                                                      int splits, int k_chunk, float* __restrict__ C, int ldc,
-                                                     size_t split_stride, int accum) {
+                                                     size_t split_stride, int accum, int row_groups) {
   constexpr int NB = F16 ? 1 : 2;   // activation planes
   constexpr int AS = 32 * SKS;      // one activation plane of a stage
   __shared__ __attribute__((aligned(16))) u16 sW0[128 * SKS];
@@ -600,8 +600,13 @@ __global__ void __launch_bounds__(256, 2) gemm_skinny(const u16* __restrict__ Ah
   __shared__ __attribute__((aligned(16))) u16 sA0[NB * AS];
   __shared__ __attribute__((aligned(16))) u16 sA1[NB * AS];
   __shared__ __attribute__((aligned(16))) u16 sA2[NB * AS];
-  const int v = blockIdx.x;
+  // Rows past 32 (at most 64): two row groups per work item, blocks 8 apart in the grid so
+  // that both run on the same XCD (blocks go round-robin over the 8) and the second reads
+  // the weight tile from that XCD's L2.
+  const int rg = row_groups == 2 ? (blockIdx.x >> 3) & 1 : 0;
+  const int v = row_groups == 2 ? ((blockIdx.x >> 4) << 3) + (blockIdx.x & 7) : blockIdx.x;
   if (v >= n_tiles * splits) return;
+  const int m0 = rg * 32;
   const int ntile = v % n_tiles, ks = v / n_tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hl = lane >> 5;
@@ -619,7 +624,7 @@ __global__ void __launch_bounds__(256, 2) gemm_skinny(const u16* __restrict__ Ah
   const u16* srcA[2];   // fixed size: a template-sized array of these loads drops the host stub
   {
     const int row = tid >> 3, c = (tid & 7) ^ ((row >> 1) & 7);
-    const size_t off = (size_t)(row < M ? row : M - 1) * lda + c * 8;
+    const size_t off = (size_t)(m0 + row < M ? m0 + row : M - 1) * lda + c * 8;
     srcA[0] = Ah + off;
     srcA[1] = F16 ? srcA[0] : Al + off;
   }
@@ -694,12 +699,12 @@ __global__ void __launch_bounds__(256, 2) gemm_skinny(const u16* __restrict__ Ah
   }
   const int n = ntile * 128 + wr;
   if (n >= N) return;
-  // acc[r]: row 8 (r / 4) + 4 hl + r % 4 of the 32, column n
+  // acc[r]: row m0 + 8 (r / 4) + 4 hl + r % 4, column n
   float* Cb = C + (splits > 1 ? (size_t)ks * split_stride : 0);
   const bool add = (splits == 1) && accum;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+    const int row = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
     if (row < M) {
       float* o = Cb + (size_t)row * ldc + n;
       *o = add ? *o + acc[r] : acc[r];
@@ -1856,17 +1861,22 @@ static hipError_t launch_skinny(bool f16, const uint16_t* Ah, const uint16_t* Al
   float* out = splits == 1 ? C : part;
   const int ldo = splits == 1 ? ldc : N;
   const int acc = splits == 1 ? accum : 0;
+  // two row groups: work item w runs as blocks 16 (w / 8) + w % 8 and that + 8
+  const int rgs = M > 32 ? 2 : 1;
+  const int items = nt * splits;
+  const int grid = rgs == 2 ? cdiv(items, 8) * 16 : items;
   if (f16)
-    gemm_skinny<true><<<nt * splits, 256, 0, s>>>(Ah, nullptr, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo,
-                                                  (size_t)M * N, acc);
+    gemm_skinny<true><<<grid, 256, 0, s>>>(Ah, nullptr, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo,
+                                           (size_t)M * N, acc, rgs);
   else
-    gemm_skinny<false><<<nt * splits, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo,
-                                                   (size_t)M * N, acc);
+    gemm_skinny<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, nt, splits, k_chunk, out, ldo, (size_t)M * N,
+                                            acc, rgs);
   return hipGetLastError();
 }
 
-// the weight-streaming kernel takes products of at most 32 rows with K a multiple of its stage
-static bool use_skinny(int M, int K) { return M <= 32 && K % SKS == 0; }
+// the weight-streaming kernel takes products of at most 64 rows (two row groups past 32)
+// with K a multiple of its stage
+static bool use_skinny(int M, int K) { return M <= 64 && K % SKS == 0; }
 
 hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int M, int K, const GemmSegs& seg, int N,
                             float* C, int ldc, int accum, size_t part_cap, float* part, hipStream_t s,
