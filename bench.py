@@ -39,6 +39,10 @@ PRECISION_NOTE = {
     "f16_down_gup": "f16_down_gup: down projection as one float16 pass on a float16 weight mirror; gate|up as "
                     "one float16 pass in the prefill and two bfloat16 passes (hi + lo of the float32 "
                     "activation) in the scoring call; q|k|v and o as two bfloat16 passes; float32 accumulation",
+    "f16_prefill": "f16_prefill: down projection as one float16 pass on a float16 weight mirror; in prefills "
+                   "every projection as one float16 pass (q|k|v only for prefixes of at most 2048 rows, "
+                   "else two bfloat16 passes); in the scoring call gate|up, o and q|k|v as two bfloat16 "
+                   "passes (hi + lo of the float32 activation); float32 accumulation",
     "f16_down_gup_o": "f16_down_gup_o: down projection as one float16 pass on a float16 weight mirror; gate|up "
                       "and o as one float16 pass in the prefill and two bfloat16 passes (hi + lo of the float32 "
                       "activation) in the scoring call; q|k|v as two bfloat16 passes; float32 accumulation",

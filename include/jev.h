@@ -125,6 +125,10 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
  *   mirror the same matrices but use the single f16 pass in prefills only:
  *   the prefix rows feed nothing but the float16 KV store, while the rows of
  *   scoring calls, whose logits are read, keep the two bfloat16 terms.
+ *   JEV_F16_QKV_PREFILL applies to prefills whose longest segment is at most
+ *   2048 rows; longer prefixes keep q|k|v on two terms (the rounding of K and
+ *   V reaches every query's scores, and its error grows with the keys a query
+ *   sees, as for the q terms in jev_model_set_attn_q_terms).
  * jev_model_f16_bytes: size of the mirror buffer for those groups (0 for JEV_F32
  *   models or unknown bits).
  * jev_model_attach_f16: buf dev [bytes >= jev_model_f16_bytes(m, groups)],
@@ -144,7 +148,7 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 #define JEV_F16_DOWN    4
 #define JEV_F16_O       8
 #define JEV_F16_GATE_UP_PREFILL 16  /* w_gate, w_up mirrored, the f16 pass used by prefills only */
-#define JEV_F16_QKV_PREFILL     32  /* wq, wk, wv mirrored, used by prefills only            */
+#define JEV_F16_QKV_PREFILL     32  /* wq, wk, wv mirrored, used by prefills of <= 2048 rows  */
 #define JEV_F16_O_PREFILL       64  /* wo mirrored, used by prefills only                    */
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);

@@ -486,6 +486,7 @@ enum class Mode { Prefill, Score, Tree };
 // the second term (q - f16(q)) removes that rounding, which shifts every score of a row
 // coherently and grows in weight with the number of keys a row sees.
 constexpr int kAttnQ2Keys = 2048;   // the automatic choice takes two terms above this many prefix keys
+constexpr int kF16QkvPrefillKeys = 2048;   // longest prefix segment whose prefill runs q|k|v on float16
 // keys: the most prefix keys (the longest segment) a row of the call sees.
 int attn_q_terms(const jev_model* m, int keys) {
   if (m->q_terms == 1 || m->q_terms == 2) return m->q_terms;
@@ -639,7 +640,12 @@ struct Forward {
     // produce their inputs write that plane: the input norm and attention output for the
     // q|k|v and o projections, the post-attention norm for gate|up, the SwiGLU output for down
     const bool pre = mode == Mode::Prefill;
-    const bool fq = m->f16_qkv || (m->f16_qkv_prefill && pre), fo = m->f16_o || (m->f16_o_prefill && pre);
+    // the longest key segment a row of this call sees (the prefix's longest segment)
+    const int seg_max = *std::max_element(pf->seg_len.begin(), pf->seg_len.end());
+    // q|k|v of prefills on the float16 pass only up to kF16QkvPrefillKeys rows: K and V reach
+    // every query's scores, and their rounding error grows with the keys a query sees
+    const bool fq = m->f16_qkv || (m->f16_qkv_prefill && pre && seg_max <= kF16QkvPrefillKeys);
+    const bool fo = m->f16_o || (m->f16_o_prefill && pre);
     const bool fd = m->f16_down, fg = m->f16_gu || (m->f16_gu_prefill && pre);
     uint16_t* a_hi = at<uint16_t>(ws, L.act);                 // normalised activations / attention output
     uint16_t* a_lo = a_hi + (size_t)T * wide;
@@ -674,7 +680,7 @@ struct Forward {
       return st;
 
     // q as one float16 term, or two (q_hi + q_lo) when rows see long prefixes (jev_model_set_attn_q_terms)
-    const int q_terms = attn_q_terms(m, *std::max_element(pf->seg_len.begin(), pf->seg_len.end()));
+    const int q_terms = attn_q_terms(m, seg_max);
     const float qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
     // attention splits: about one block per compute unit (partials merged when > 1)
     const int own_tiles = attn_own_tiles(plan.seq_start.data(), T, Hq / Hkv);

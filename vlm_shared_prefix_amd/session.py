@@ -39,7 +39,7 @@ PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOW
               "f16_down_gup_o": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_O_PREFILL,
               "f16_down_gup_qkv": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL,
               "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
-DEFAULT_PRECISION = "f16_down_gup_o"
+DEFAULT_PRECISION = "f16_prefill"
 
 
 class Session:
@@ -51,8 +51,8 @@ class Session:
         float16 passes on a float16 mirror of their weights; "f16" does so for every decoder GEMM;
         "f16_down_gup" runs the down projection on one float16 pass everywhere and gate|up on
         one float16 pass in prefills only (scoring calls keep its two terms); "f16_down_gup_o"
-        (the default) also runs o on one float16 pass in prefills; "f16_prefill" every prefill
-        GEMM."""
+        also runs o on one float16 pass in prefills; "f16_prefill" (the default) every prefill
+        GEMM, q|k|v only for prefixes of at most 2048 rows (the library's rule)."""
         if precision not in PRECISIONS:
             raise ValueError(f"precision must be one of {PRECISIONS}, not {precision!r}")
         self.cfg = cfg
