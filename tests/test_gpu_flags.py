@@ -104,3 +104,24 @@ def test_attn_q_terms_vs_oracle(terms):
     got = sess.score_suffixes(suf).cpu().numpy()
     check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"m7l q terms {terms}")
     sess.close()
+
+
+@pytest.mark.parametrize("n_vis,same", [(2038, False), (2039, True)])
+def test_f16_qkv_prefill_length_rule(n_vis, same):
+    """JEV_F16_QKV_PREFILL runs the prefill's q|k|v on one float16 pass only while the longest
+    prefix segment is at most 2048 rows: one row past it, the default mode scores bit for
+    bit like the mode without that group; at 2048 rows it does not."""
+    import torch
+    from vlm_shared_prefix_amd.session import Session
+    cfg = S.with_overrides(S.CONFIGS["m2"], n_vis=n_vis)   # + 10 text rows: 2048 / 2049 rows
+    assert cfg.prefix_len == (2048 if not same else 2049)
+    src = S.WeightSource(cfg, 0)
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    outs = []
+    for precision in ("f16_prefill", "f16_down_gup_o"):
+        say(f"[q|k|v rule] m2 prefix {cfg.prefix_len} rows ({precision})")
+        sess = Session(cfg, src.glob, src.layer, precision=precision)
+        sess.prefill(pre["vis"], pre["text_ids"])
+        outs.append(sess.score_suffixes(suf).cpu())
+        sess.close()
+    assert torch.equal(outs[0], outs[1]) == same
