@@ -64,10 +64,11 @@ def roofline(kind, d):
     """Roofline entry of one kernel kind from the library's event timing.
 
     achieved = algorithmic flops per launch (each product counted once) / average
-    launch time.  The two-term bf16 GEMMs (gemm, gemm_swiglu, lm_head_lse) run every
-    product twice (hi and lo planes of the float32 activations), so the MFMA pipes
-    execute 2x the algorithmic flops: reported as executed_tflops / executed_frac.
-    The float16 GEMMs (gemm_f16, gemm_swiglu_f16) execute each product once.
+    launch time.  The two-term bf16 GEMMs (gemm_qkv, gemm_o, gemm_gate_up, gemm_down,
+    gemm_swiglu, lm_head_lse) run every product twice (hi and lo planes of the float32
+    activations), so the MFMA pipes execute 2x the algorithmic flops: reported as
+    executed_tflops / executed_frac.  The float16 GEMMs (kinds ending in _f16) execute
+    each product once.
     """
     from vlm_shared_prefix_amd import profiling
     n = d["launches"]
@@ -82,7 +83,8 @@ def roofline(kind, d):
              "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
              "avg_launch_us": round(avg_s * 1e6, 2), "launches": n,
              "algorithmic_flops_per_launch": d["flops"] / n}
-        passes = 2 if kind in ("gemm", "gemm_swiglu", "lm_head_lse") else 1
+        # two passes: the bf16 kinds (the float16 kinds end in _f16)
+        passes = 2 if (kind.startswith("gemm") or kind == "lm_head_lse") and not kind.endswith("_f16") else 1
         if kind.startswith("gemm") or kind == "lm_head_lse":
             r["executed_tflops"] = round(passes * ach, 2)
             r["executed_frac"] = round(passes * ach / PEAK_BF16_TFLOPS, 4)
@@ -201,7 +203,8 @@ def tree_section(seed, dev, profile_steps, name="c5", sweep=True):
     prof_pre = J.jev_profile_stop(sess.model)
     prefill_kernels = {"attention": attention_entry(prof_pre, 0, f"causal self-attention of the {cfg.prefix_len} "
                                                                   f"prefix rows")}
-    for kind in ("gemm_swiglu", "gemm_swiglu_f16", "gemm_f16", "gemm"):
+    for kind in ("gemm_swiglu", "gemm_swiglu_f16", "gemm_qkv", "gemm_qkv_f16", "gemm_o", "gemm_o_f16", "gemm_down",
+                 "gemm_down_f16"):
         if prof_pre.get(kind):
             k = prof_pre[kind]
             prefill_kernels[kind] = {"launches": k["launches"], "avg_launch_us": round(k["ms"] * 1e3 / k["launches"], 1),

@@ -514,15 +514,19 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Profiled launch kinds, named after the kernels they launch.
+// Profiled launch kinds, named after the kernels they launch; the decoder's projections are
+// told apart by role (two bf16 passes, or one float16 pass: _f16).
 enum Kind {
   K_EMBED, K_RMSNORM, K_RESNORM, K_ROPETAB, K_QKVPOST, K_GEMM, K_SWIGLU, K_SPLITK, K_ROPE, K_VT, K_ATTN, K_MERGE,
-  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_GEMM16, K_SWIGLU16, K_SPLITSWIGLU, K_NKINDS
+  K_SILU, K_TARGET, K_CANDSM, K_LMHEAD, K_ROWLSE, K_TREEFIN, K_GEMM16, K_SWIGLU16, K_SPLITSWIGLU,
+  K_QKV, K_QKV16, K_O, K_O16, K_GU, K_GU16, K_DOWN, K_DOWN16, K_NKINDS
 };
 const char* const kKindName[K_NKINDS] = {
     "embed_rows", "rmsnorm_rows", "residual_norm", "rope_table", "qkv_post", "gemm", "gemm_swiglu",
     "splitk_reduce", "rope_qk", "v_transpose", "attn_fwd", "attn_merge", "silu_mul", "target_logits",
-    "cand_logsoftmax", "lm_head_lse", "lse_merge", "tree_finalize", "gemm_f16", "gemm_swiglu_f16", "splitk_swiglu"};
+    "cand_logsoftmax", "lm_head_lse", "lse_merge", "tree_finalize", "gemm_f16", "gemm_swiglu_f16", "splitk_swiglu",
+    "gemm_qkv", "gemm_qkv_f16", "gemm_o", "gemm_o_f16", "gemm_gate_up", "gemm_gate_up_f16", "gemm_down",
+    "gemm_down_f16"};
 
 struct Forward {
   const jev_prefix* pf;
@@ -614,14 +618,15 @@ struct Forward {
 
   // bf16 GEMM whose split-K partials (if any) are left for a fused consumer:
   // on return *splits_out is 1 (C written / accumulated) or > 1 (partials in gpart, stride M*N).
-  jev_status gemm_deferred(AOp A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
+  // kind: the role's two-pass kind; its float16 kind is the next one
+  jev_status gemm_deferred(int kind, AOp A, int lda, int M, int K, const void* w0, int n0, const void* w1, int n1,
                            const void* w2, int n2, float* C, int ldc, int accum, int* splits_out) {
     const int N = n0 + n1 + n2;
     const double flops = 2.0 * M * N * K;
     const double bytes = 2.0 * N * K + (A.f16 ? 2.0 : 4.0) * M * K + 4.0 * M * N * (accum ? 2 : 1);
     GemmSegs sg{{(const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)w2}, {n0, n0 + n1, N}};
     float* part = at<float>(ws, L.gpart);
-    return run_k(A.f16 ? K_GEMM16 : K_GEMM, flops, bytes, [&] {
+    return run_k(A.f16 ? kind + 1 : kind, flops, bytes, [&] {
       return A.f16 ? launch_gemm_f16(A.hi, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s, splits_out)
                    : launch_gemm_bf16(A.hi, A.lo, lda, M, K, sg, N, C, ldc, accum, kGemmPartFloats, part, s,
                                       splits_out);
@@ -699,7 +704,7 @@ struct Forward {
       const jev_layer& WD = fd ? m->layers16[l] : W;
       const bool last_prefill = (mode == Mode::Prefill) && (l == c.n_layers - 1);
       int sp = 1;
-      if (jev_status st = gemm_deferred(A_qkv, wide, T, H, WQ.wq, HqD, WQ.wk, Hkv * D, WQ.wv, Hkv * D, big, NQKV, 0, &sp))
+      if (jev_status st = gemm_deferred(K_QKV, A_qkv, wide, T, H, WQ.wq, HqD, WQ.wk, Hkv * D, WQ.wv, Hkv * D, big, NQKV, 0, &sp))
         return st;
       void *kdst, *vdst;
       int kld;
@@ -751,7 +756,7 @@ struct Forward {
           return st;
       }
       // o-proj: x += o·W_oᵀ, then m = RMSNorm(x; g2) into the activation planes
-      if (jev_status st = gemm_deferred(A_o, HqD, T, HqD, WO.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      if (jev_status st = gemm_deferred(K_O, A_o, HqD, T, HqD, WO.wo, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H, W.mlp_norm, c.rms_eps,
                                         a_hi, a_lo, wide, fg, flags, s);
@@ -764,7 +769,7 @@ struct Forward {
         // then the SwiGLU is applied while the partials are summed
         int sg = 1;
         const AOp A_g{nullptr, a_hi, a_lo, fg};
-        if (jev_status st = gemm_deferred(A_g, wide, T, H, WG.w_gate, I, WG.w_up, I, nullptr, 0, part, 2 * I, 0, &sg))
+        if (jev_status st = gemm_deferred(K_GU, A_g, wide, T, H, WG.w_gate, I, WG.w_up, I, nullptr, 0, part, 2 * I, 0, &sg))
           return st;
         if (jev_status st = run_k(K_SPLITSWIGLU, 0.0, 4.0 * sg * T * 2 * I + out_b * T * I, [&] {
               return launch_splitk_swiglu(part, sg, T, I, u_hi, fd ? nullptr : u_lo, I, flags, s);
@@ -780,7 +785,7 @@ struct Forward {
           }))
         return st;
       // down: x += u·W_dᵀ, then the next layer's input norm
-      if (jev_status st = gemm_deferred(A_u, I, T, I, WD.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
+      if (jev_status st = gemm_deferred(K_DOWN, A_u, I, T, I, WD.w_down, H, nullptr, 0, nullptr, 0, x, H, 1, &sp)) return st;
       const void* next_g = (li + 1 < layers.size()) ? m->layers[layers[li + 1]].attn_norm : nullptr;
       if (jev_status st = run_k(K_RESNORM, 0.0, rowbytes * (2 + (sp > 1 ? sp + 1 : 0)), [&] {
             return launch_residual_norm(true, part, (size_t)T * H, sp > 1 ? sp : 0, x, T, H,
