@@ -131,6 +131,13 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x,
 #define GBK 64
 #define GLD (GBK + 8)   // LDS row stride in bf16 elements (144 B: conflict-free 16 B reads)
 
+// Direct global->LDS loads in the buffer form: a wave-uniform resource (base, 2 GB range),
+// a 32-bit byte offset per lane and a uniform byte offset in an SGPR.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
 __device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
   if (n < s.n_end[0]) return s.w[0] + (size_t)n * K;
   if (n < s.n_end[1]) return s.w[1] + (size_t)(n - s.n_end[0]) * K;
@@ -294,7 +301,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
 #define G2M 128
 #define G2N 256
 #define G2K 32
-template <bool SWIGLU, bool F16, bool LSE = false>
+template <bool SWIGLU, bool F16, bool LSE = false, bool BUF = false>
 __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah, const u16* __restrict__ Al, int lda,
                                                 int M, int K, GemmSegs seg, int N, int m_tiles, int n_tiles,
                                                 int splits, int k_chunk, float* __restrict__ C, int ldc,
@@ -363,7 +370,49 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16w(const u16* __restrict__ Ah,
     const int slot = i * 256 + tid, row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
     srcW[i] = w_row(row) + c * 8;
   }
+  // BUF (the SwiGLU products, when every byte offset fits 31 bits): the same loads in the
+  // buffer form, a 32-bit offset per lane and the K position in a scalar register (measured
+  // 1.5% faster on the float16 SwiGLU of 1024 rows; the plain products, on their two-stage
+  // ring, measured 0-2% slower and keep the global form).  A W load instruction of a wave
+  // covers 16 consecutive tile rows: all gate rows (waves 0, 1) or all up rows (waves 2, 3),
+  // so its resource is uniform.
+  static_assert(!BUF || (SWIGLU && !LSE), "buffer-form loads: the SwiGLU products only");
+  int offA[2], offW[4];
+  __amdgpu_buffer_rsrc_t rA, rL, rW;
+  if constexpr (BUF) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    rA = buf_rsrc(Ah);
+    rL = buf_rsrc(F16 ? Ah : Al);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot = i * 256 + tid, row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+      offA[i] = ((m0 + row < M ? m0 + row : 0) * lda + c * 8) * 2;
+    }
+    rW = buf_rsrc((wv >> 1) ? seg.w[1] : seg.w[0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = i * 256 + tid, nr = slot >> 2, c = (slot & 3) ^ ((nr >> 2) & 3);
+      const int gi = nr >> 5;
+      const int n = n0 + (gi >> 2) * 64 + ((gi & 3) >> 1) * 32 + (nr & 31);
+      offW[i] = ((n < N ? n : 0) * K + c * 8) * 2;
+    }
+  }
   auto load_stage = [&](int k0, u16* dA, u16* dL, u16* dW) {
+    if constexpr (BUF) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t*)(dA + (i * 256 + wave * 64) * 8), 16, offA[i],
+                                                 k0 * 2, 0, 0);
+        if (!F16)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void_t*)(dL + (i * 256 + wave * 64) * 8), 16, offA[i],
+                                                   k0 * 2, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void_t*)(dW + (i * 256 + wave * 64) * 8), 16, offW[i],
+                                                 k0 * 2, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_global_load_lds(srcA[i] + k0, dA + (i * 256 + wave * 64) * 8, 16, 0, 0);
@@ -947,11 +996,8 @@ __device__ __forceinline__ float halves_sum(float x) {
 // 16 B per lane from base + byte_off into LDS at dst + lane * 16.  The buffer form of the
 // direct load is counted by vmcnt alone, so the waits the compiler places for LDS reads
 // stay exact (the global form is also tracked as an LDS access, forcing full drains).
-typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(const void* base, int byte_off, void* dst) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, byte_off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base), (lds_void_t*)dst, 16, byte_off, 0, 0, 0);
 }
 
 struct AttnTile {
@@ -1912,8 +1958,13 @@ hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, i
   const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
   const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
-  gemm_bf16w<true, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul,
-                                                flags);
+  // buffer-form loads while every byte offset they form fits the 31-bit range
+  if ((size_t)M * lda * 2 < (1ull << 31) && (size_t)I * K * 2 < (1ull << 31))
+    gemm_bf16w<true, false, false, true><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu,
+                                                              0, 0, uh, ul, flags);
+  else
+    gemm_bf16w<true, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh, ul,
+                                                  flags);
   return hipGetLastError();
 }
 
@@ -1961,8 +2012,13 @@ hipError_t launch_gemm_swiglu_f16(const uint16_t* A, int lda, int M, int K, cons
   const int mt = cdiv(M, G2M), nt = cdiv(I, G2N / 2);
   const int grid = cdiv(mt * nt, 8) * 8;
   GemmSegs seg{{w_gate, w_up, nullptr}, {I, 2 * I, 2 * I}};
-  gemm_bf16w<true, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh,
-                                              ul, flags);
+  // buffer-form loads while every byte offset they form fits the 31-bit range
+  if ((size_t)M * lda * 2 < (1ull << 31) && (size_t)I * K * 2 < (1ull << 31))
+    gemm_bf16w<true, true, false, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu,
+                                                             0, 0, uh, ul, flags);
+  else
+    gemm_bf16w<true, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, I, mt, nt, 1, K, nullptr, ldu, 0, 0, uh,
+                                                ul, flags);
   return hipGetLastError();
 }
 
