@@ -1463,102 +1463,122 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
   const int t0 = blockIdx.x * 16;
   const int nqk = Hq + Hkv;
   const int h = blockIdx.y;
-  // The thread's N elements (offsets off[n] into a partial, valid ok[n]) summed over the
-  // split partials in split order; every element's loads of a group of four partials go
-  // out in one round.
+  // The thread's N float4 groups (offsets off[n] into a partial, valid ok[n]) summed over the
+  // split partials in split order; every group's loads of a set of four partials go out in
+  // one round.  The loads are unconditional (invalid groups read offset 0, splits past the
+  // last re-read the last), so none waits on a branch; only the sums are selected.
   auto ld_all = [&](auto& val, const auto& off, const auto& ok) {
-    constexpr int N = sizeof(val) / sizeof(float);
+    constexpr int N = sizeof(val) / sizeof(float4);
+    auto at4 = [&](size_t o) { return *reinterpret_cast<const float4*>(src + o); };
+    size_t o[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) val[n] = ok[n] ? src[off[n]] : 0.f;
+    for (int n = 0; n < N; ++n) {
+      o[n] = ok[n] ? off[n] : 0;
+      const float4 a = at4(o[n]);
+      val[n] = ok[n] ? a : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     for (int s0 = 1; s0 < splits; s0 += 4) {
-      float b[N][4];
+      float4 b[N][4];
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[n][u] = at4(min(s0 + u, splits - 1) * split_stride + o[n]);
 #pragma unroll
       for (int n = 0; n < N; ++n)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (ok[n] && s0 + u < splits) b[n][u] = src[(s0 + u) * split_stride + off[n]];
-#pragma unroll
-      for (int n = 0; n < N; ++n)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (ok[n] && s0 + u < splits) val[n] += b[n][u];
+          if (ok[n] && s0 + u < splits) {
+            val[n].x += b[n][u].x; val[n].y += b[n][u].y; val[n].z += b[n][u].z; val[n].w += b[n][u].w;
+          }
     }
   };
   if (h < nqk) {
     const int half = D >> 1;
-    // element pairs (i, i + D/2) of rows t0 + idx / 64, slot i = idx % 64, for idx = tid + 256 j
-    float val[8];
-    size_t off[8];
-    bool ok[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = threadIdx.x + 256 * j;
-      const int rr = idx >> 6, i = idx & 63;
-      const int t = t0 + rr;
-      ok[2 * j] = ok[2 * j + 1] = t < T && i < half;
-      off[2 * j] = (size_t)t * lds + h * D + i;
-      off[2 * j + 1] = off[2 * j] + half;
-    }
+    // row t0 + rr, rotation slots i0 .. i0 + 3 (the pairs (i, i + D/2)); slots at or past D/2
+    // (64-dim heads) write the zero padding of dims [D, 128)
+    const int rr = threadIdx.x >> 4, i0 = 4 * (threadIdx.x & 15);
+    const int t = t0 + rr;
+    float4 val[2];
+    size_t off[2];
+    bool ok[2];
+    ok[0] = ok[1] = t < T && i0 < half;
+    off[0] = (size_t)t * lds + h * D + i0;
+    off[1] = off[0] + half;
     ld_all(val, off, ok);
+    if (t < T) {
+      const float av[4] = {val[0].x, val[0].y, val[0].z, val[0].w};
+      const float bv[4] = {val[1].x, val[1].y, val[1].z, val[1].w};
+      float ra[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+      int da = D + (i0 - half), db = D + half + (i0 - half);
+      if (i0 < half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = threadIdx.x + 256 * j;
-      const int rr = idx >> 6, i = idx & 63;
-      const int t = t0 + rr;
-      if (t >= T) continue;
-      // slot i < D/2: the rotated pair (i, i + D/2); slots past it zero dims [D, 128)
-      float ra = 0.f, rb = 0.f;
-      int da = D + (i - half), db = D + half + (i - half);
-      if (i < half) {
-        const float a = val[2 * j], b = val[2 * j + 1];
-        const float2 e = cs[t * 64 + i];
-        ra = a * e.x - b * e.y;
-        rb = b * e.x + a * e.y;
-        da = i;
-        db = i + half;
+        for (int e = 0; e < 4; ++e) {
+          const float2 c = cs[t * 64 + i0 + e];
+          ra[e] = av[e] * c.x - bv[e] * c.y;
+          rb[e] = bv[e] * c.x + av[e] * c.y;
+        }
+        da = i0;
+        db = i0 + half;
       }
-      bad |= f16_out_of_range(ra) || f16_out_of_range(rb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bad |= f16_out_of_range(ra[e]) || f16_out_of_range(rb[e]);
       if (h < Hq) {
-        // operand-ordered layout (see AttnArgs): row r = t*G + g of KV head h / G
+        // operand-ordered layout (see AttnArgs): row r = t*G + g of KV head h / G; dims d..d+3
+        // (d % 4 == 0) are 4 consecutive elements
         const int G = Hq / Hkv, r = t * G + h % G;
         const size_t base = ((size_t)(h / G) * attn_q_rows(T, G) + (r & ~31)) * 128 + (size_t)(r & 31) * 8;
         auto at = [&](int d) { return base + (size_t)(((d >> 4) * 2 + ((d >> 3) & 1)) * 256) + (d & 7); };
         // q carries the softmax scale log2(e)/sqrt(D): scores come out in log2 units
-        const float sa = ra * qscale, sb = rb * qscale;
-        const f16 qa = (f16)sa, qb = (f16)sb;
-        q_hi[at(da)] = qa;
-        q_hi[at(db)] = qb;
+        f16x4 qa, qb, la, lb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sa = ra[e] * qscale, sb = rb[e] * qscale;
+          qa[e] = (f16)sa;
+          qb[e] = (f16)sb;
+          la[e] = (f16)(sa - (float)qa[e]);
+          lb[e] = (f16)(sb - (float)qb[e]);
+        }
+        *reinterpret_cast<f16x4*>(q_hi + at(da)) = qa;
+        *reinterpret_cast<f16x4*>(q_hi + at(db)) = qb;
         if (q_lo) {
-          q_lo[at(da)] = (f16)(sa - (float)qa);
-          q_lo[at(db)] = (f16)(sb - (float)qb);
+          *reinterpret_cast<f16x4*>(q_lo + at(da)) = la;
+          *reinterpret_cast<f16x4*>(q_lo + at(db)) = lb;
         }
       } else {
         f16* kd = kdst + ((size_t)(h - Hq) * ldk + t) * 128;
-        kd[da] = (f16)ra;
-        kd[db] = (f16)rb;
+        f16x4 ka, kb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ka[e] = (f16)ra[e];
+          kb[e] = (f16)rb[e];
+        }
+        *reinterpret_cast<f16x4*>(kd + da) = ka;
+        *reinterpret_cast<f16x4*>(kd + db) = kb;
       }
     }
   } else {
     const int hk = h - nqk;
     const int c0 = nqk * D + hk * D;
-    float val[8];
-    size_t off[8];
-    bool ok[8];
+    // rows t0 + rr and t0 + rr + 8, dims d4 .. d4 + 3
+    const int rr = threadIdx.x >> 5, d4 = 4 * (threadIdx.x & 31);
+    float4 val[2];
+    size_t off[2];
+    bool ok[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = threadIdx.x + 256 * j;
-      const int rr = idx >> 7, d = idx & 127;
-      const int t = t0 + rr;
-      ok[j] = t < T && d < D;
-      off[j] = (size_t)t * lds + c0 + d;
+    for (int j = 0; j < 2; ++j) {
+      const int t = t0 + rr + 8 * j;
+      ok[j] = t < T && d4 < D;
+      off[j] = (size_t)t * lds + c0 + d4;
     }
     ld_all(val, off, ok);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = threadIdx.x + 256 * j;
-      const int rr = idx >> 7, d = idx & 127;
-      vt[rr][d] = val[j];
-      bad |= f16_out_of_range(val[j]);
+    for (int j = 0; j < 2; ++j) {
+      const float v4[4] = {val[j].x, val[j].y, val[j].z, val[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[rr + 8 * j][d4 + e] = v4[e];
+        bad |= f16_out_of_range(v4[e]);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -2101,7 +2121,7 @@ hipError_t launch_qkv_post(const float* src, int lds, size_t split_stride, int s
                            const float2* cs, void* q_hi, void* q_lo, void* kdst, int ldk, void* vtdst, int ldv,
                            int D, float qscale, int* flags, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  if ((D != 64 && D != 128) || lds % 4 || split_stride % 4) return hipErrorInvalidValue;
   dim3 grid(cdiv(T, 16), Hq + 2 * Hkv);
   qkv_post<<<grid, 256, 0, s>>>(src, lds, split_stride, splits, T, Hq, Hkv, cs, (f16*)q_hi, (f16*)q_lo, (f16*)kdst,
                                 ldk, (f16*)vtdst, ldv, D, qscale, flags);
