@@ -54,6 +54,24 @@ def test_few_rows_vs_oracle(name, n, precision):
     sess.close()
 
 
+@pytest.mark.parametrize("name,mlp,n,precision", [("m64", 2560, 1, "default"), ("m64", 2560, 2, "split"),
+                                                  ("m2", 2560, 1, "default"), ("m2", 2560, 2, "f16_prefill")])
+def test_few_rows_norm_split_groups(name, mlp, n, precision):
+    """Few-row calls whose down projection splits K more than eight ways on a narrow hidden size
+    (1024 or 1536): the norm that sums those partials shares them out over four or two thread
+    groups per row, and the scores still meet the bar."""
+    cfg = S.with_overrides(S.CONFIGS[name], mlp=mlp)
+    suf = S.suffix_inputs(cfg, 0, n)
+    say(f"[parity] score_suffixes {name} (MLP {mlp}) seed 0, {n} suffix(es) ({precision})")
+    sess, src = gpu_session(cfg, 0, precision=precision)
+    pre = S.prefix_inputs(cfg, 0)
+    ref = O.score_suffixes(src, cfg, pre, suf)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"{name}/mlp{mlp}/n{n}/{precision}")
+    sess.close()
+
+
 @pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "default"), ("m5", 0, "split"),
                                                  ("m5", 0, "f16"), ("m64", 0, "default")])
 def test_score_tree_vs_oracle(name, seed, precision):

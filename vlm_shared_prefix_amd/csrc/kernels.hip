@@ -1336,6 +1336,43 @@ __global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ pa
   float ss = 0.f;
   if constexpr (J <= 2) {
     bool ok[J];
+    // More than one round of partials and at most half as many columns as threads: G groups
+    // of H/4 threads each sum a contiguous share of the splits (in split order), and the
+    // shares are added to x in group order, so each thread waits on fewer rounds of loads.
+    const int G = splits > 8 ? (H4 <= NT / 4 ? 4 : (H4 <= NT / 2 ? 2 : 1)) : 1;
+    if (G > 1) {
+      __shared__ float4 gsum[3 * (NT / 4)];   // shares of groups 1 .. G-1: (G - 1) * H4 <= 3 NT / 4
+      const int grp = threadIdx.x / H4, k = threadIdx.x - grp * H4;
+      const bool act = grp < G;
+      const int sb = (int)(((long)grp * splits) / G), se = (int)(((long)(grp + 1) * splits) / G);
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s0 = sb; act && s0 < se; s0 += 8) {
+        float4 b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < se) b[u] = pr[(s0 + u) * (split_stride >> 2) + k];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < se) { a.x += b[u].x; a.y += b[u].y; a.z += b[u].z; a.w += b[u].w; }
+      }
+      if (act && grp > 0) gsum[(grp - 1) * H4 + k] = a;
+      __syncthreads();
+      ok[0] = grp == 0;   // then k == threadIdx.x < H4
+      v[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok[0]) {
+        const float4 xv = xr[k];
+        v[0] = make_float4(xv.x + a.x, xv.y + a.y, xv.z + a.z, xv.w + a.w);
+        for (int gi = 1; gi < G; ++gi) {
+          const float4 c = gsum[(gi - 1) * H4 + k];
+          v[0].x += c.x; v[0].y += c.y; v[0].z += c.z; v[0].w += c.w;
+        }
+      }
+#pragma unroll
+      for (int j = 1; j < J; ++j) {
+        ok[j] = false;
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int k = threadIdx.x + NT * j;
@@ -1356,6 +1393,7 @@ __global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ pa
           if (ok[j] && s0 + u < splits) {
             v[j].x += b[j][u].x; v[j].y += b[j][u].y; v[j].z += b[j][u].z; v[j].w += b[j][u].w;
           }
+    }
     }
 #pragma unroll
     for (int j = 0; j < J; ++j)
