@@ -1336,13 +1336,14 @@ __global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ pa
   float ss = 0.f;
   if constexpr (J <= 2) {
     bool ok[J];
-    // More than one round of partials and at most half as many columns as threads: G groups
-    // of H/4 threads each sum a contiguous share of the splits (in split order), and the
-    // shares are added to x in group order, so each thread waits on fewer rounds of loads.
-    const int G = splits > 8 ? (H4 <= NT / 4 ? 4 : (H4 <= NT / 2 ? 2 : 1)) : 1;
+    // More than one round of partials and at most half as many columns as threads (whole
+    // waves of them): G groups of H/4 threads each sum a contiguous share of the splits (in
+    // split order), and the shares are added to x in group order, so each thread waits on
+    // fewer rounds of loads.  A group is whole waves, so its share is wave-uniform.
+    const int G = (splits > 8 && H4 % 64 == 0) ? (H4 <= NT / 4 ? 4 : (H4 <= NT / 2 ? 2 : 1)) : 1;
     if (G > 1) {
       __shared__ float4 gsum[3 * (NT / 4)];   // shares of groups 1 .. G-1: (G - 1) * H4 <= 3 NT / 4
-      const int grp = threadIdx.x / H4, k = threadIdx.x - grp * H4;
+      const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / H4), k = threadIdx.x - grp * H4;
       const bool act = grp < G;
       const int sb = (int)(((long)grp * splits) / G), se = (int)(((long)(grp + 1) * splits) / G);
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1366,6 +1367,31 @@ __global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ pa
           const float4 c = gsum[(gi - 1) * H4 + k];
           v[0].x += c.x; v[0].y += c.y; v[0].z += c.z; v[0].w += c.w;
         }
+      }
+#pragma unroll
+      for (int j = 1; j < J; ++j) {
+        ok[j] = false;
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else if (H4 <= NT) {
+      // every column in the thread's first slot: rounds of sixteen partials.  Whole waves past
+      // the columns skip the loads; inside a wave the loads are unconditional (lanes past the
+      // columns read the last one and drop it), so a round goes out without lane branches.
+      ok[0] = threadIdx.x < H4;
+      const int kc = ok[0] ? threadIdx.x : H4 - 1;
+      v[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if ((threadIdx.x & ~63) < H4) {
+        v[0] = xr[kc];
+        for (int s0 = 0; s0 < splits; s0 += 16) {   // partials summed in split order
+          float4 b[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (s0 + u < splits) b[u] = pr[(s0 + u) * (split_stride >> 2) + kc];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (s0 + u < splits) { v[0].x += b[u].x; v[0].y += b[u].y; v[0].z += b[u].z; v[0].w += b[u].w; }
+        }
+        if (!ok[0]) v[0] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int j = 1; j < J; ++j) {
