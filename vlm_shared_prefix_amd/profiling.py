@@ -143,7 +143,8 @@ def kernel_stats_markdown(run_dir: str, title: str, command: str = "", always=("
                    int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
             groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     tot = sum(sum(v) for v in groups.values())
-    lines += ["", "Per launch shape (blocks x, y, z), top 16 by total time, then every attention / merge shape:", "",
+    lines += ["", "Per launch shape (blocks x, y, z), top 16 by total time, then every shape of "
+              + " / ".join(f"`{a}`" for a in always) + ":", "",
               "| kernel | blocks | launches | median us | total ms | % |", "|---|---|---|---|---|---|"]
     ranked = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     shown = ranked[:16] + [kv for kv in ranked[16:] if any(a in kv[0][0] for a in always)]
@@ -259,9 +260,11 @@ if __name__ == "__main__":
         print(md)
         sys.exit(0)
     if len(sys.argv) >= 3 and sys.argv[1] == "--stats":
+        # JEV_STATS_ALWAYS: comma-separated kernel names whose every launch shape is listed
+        always = tuple(a for a in os.environ.get("JEV_STATS_ALWAYS", "attn_fwd_f16,attn_merge").split(",") if a)
         md = _with_notes(kernel_stats_markdown(sys.argv[2],
                                                os.environ.get("JEV_STATS_TITLE", "rocprofv3 kernel statistics"),
-                                               os.environ.get("JEV_STATS_COMMAND", "")))
+                                               os.environ.get("JEV_STATS_COMMAND", ""), always))
         if len(sys.argv) > 3:
             with open(sys.argv[3], "w") as f:
                 f.write(md)
