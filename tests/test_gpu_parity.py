@@ -72,6 +72,27 @@ def test_few_rows_norm_split_groups(name, mlp, n, precision):
     sess.close()
 
 
+@pytest.mark.parametrize("precision", ["default", "split"])
+def test_fused_swiglu_ragged_columns(precision):
+    """A prefill long enough for the fused SwiGLU GEMM (at least 256 tiles: 4708 rows x 7 column
+    tiles of 128) on an MLP of 832, so its last column tile is half empty: the prefix's K/V,
+    hence the scores, must still meet the bar (one float16 pass by default, two bfloat16 passes
+    with "split")."""
+    from vlm_shared_prefix_amd import jev as J
+    cfg = S.with_overrides(S.CONFIGS["mk"], n_vis=4700)
+    say(f"[parity] mk with a {cfg.prefix_len}-row prefix, MLP {cfg.mlp} ({precision})")
+    sess, src = gpu_session(cfg, 0, precision=precision)
+    pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
+    ref = O.score_suffixes(src, cfg, pre, suf)
+    J.jev_profile_start(sess.model)
+    sess.prefill(pre["vis"], pre["text_ids"])
+    kinds = J.jev_profile_stop(sess.model)
+    assert ("gemm_swiglu_f16" if precision == "default" else "gemm_swiglu") in kinds, sorted(kinds)
+    got = sess.score_suffixes(suf).cpu().numpy()
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"mk/P{cfg.prefix_len}/{precision}")
+    sess.close()
+
+
 @pytest.mark.parametrize("name,seed,precision", [("t1", 1, "f32"), ("m5", 0, "default"), ("m5", 0, "split"),
                                                  ("m5", 0, "f16"), ("m64", 0, "default")])
 def test_score_tree_vs_oracle(name, seed, precision):
