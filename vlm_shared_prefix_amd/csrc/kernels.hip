@@ -41,6 +41,7 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
 }
 
 template <typename WT> __device__ __forceinline__ float ldw(const WT* p, size_t i);
+typedef u16 u16x8_t __attribute__((ext_vector_type(8)));
 template <> __device__ __forceinline__ float ldw<float>(const float* p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ldw<u16>(const u16* p, size_t i) { return bf16_to_f32(p[i]); }
 
@@ -1784,13 +1785,14 @@ __global__ void __launch_bounds__(256) silu_mul(const float* __restrict__ gu, in
 
 // ----------------------------------------------------------------------------
 // K7: candidate logits z[p] = h[ridx[p]] · W_lm[tok[p]] (float32 accumulate),
-// one wave per target; tok < 0 marks an unused slot (z = -inf).
+// one wave per target; tok < 0 marks an unused slot (z = -inf).  bf16 rows (vec): 16 B
+// loads, eight elements per lane and step.
 // ----------------------------------------------------------------------------
 template <typename WT>
 __global__ void __launch_bounds__(256) target_logits(const float* __restrict__ h, int H,
                                                      const WT* __restrict__ W, const int* __restrict__ ridx,
                                                      const int* __restrict__ tok, int NT,
-                                                     float* __restrict__ z) {
+                                                     float* __restrict__ z, int vec) {
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (p >= NT) return;
@@ -1802,6 +1804,33 @@ __global__ void __launch_bounds__(256) target_logits(const float* __restrict__ h
   const float* hr = h + (size_t)ridx[p] * H;
   const WT* wr = W + (size_t)w * H;
   float s = 0.f;
+  if constexpr (sizeof(WT) == 2) {
+    if (vec) {   // H % 8 == 0, h and W 16 B aligned
+      // bf16 rows: 8 consecutive elements per lane and step (16 B of W, 32 B of h), the
+      // loads of up to four steps issued together
+      for (int k0 = lane * 8; k0 < H; k0 += 64 * 8 * 4) {
+        u16x8_t wv[4];
+        float4 ha[4], hb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = min(k0 + q * 512, H - 8);
+          wv[q] = *reinterpret_cast<const u16x8_t*>(wr + k);
+          ha[q] = *reinterpret_cast<const float4*>(hr + k);
+          hb[q] = *reinterpret_cast<const float4*>(hr + k + 4);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k0 + q * 512 < H) {
+            const float hv[8] = {ha[q].x, ha[q].y, ha[q].z, ha[q].w, hb[q].x, hb[q].y, hb[q].z, hb[q].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(hv[e], bf16_to_f32(wv[q][e]), s);
+          }
+      }
+      s = wave_sum(s);
+      if (lane == 0) z[p] = s;
+      return;
+    }
+  }
   for (int k = lane; k < H; k += 64) s = fmaf(hr[k], ldw(wr, k), s);
   s = wave_sum(s);
   if (lane == 0) z[p] = s;
@@ -2323,10 +2352,11 @@ hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh
 hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,
                                 int NT, float* z, hipStream_t s) {
   if (NT <= 0) return hipSuccess;
+  const int vec = H % 8 == 0 && reinterpret_cast<uintptr_t>(h) % 16 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
   if (bf16)
-    target_logits<u16><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const u16*)W, ridx, tok, NT, z);
+    target_logits<u16><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const u16*)W, ridx, tok, NT, z, vec);
   else
-    target_logits<float><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const float*)W, ridx, tok, NT, z);
+    target_logits<float><<<cdiv(NT, 4), 256, 0, s>>>(h, H, (const float*)W, ridx, tok, NT, z, 0);
   return hipGetLastError();
 }
 
