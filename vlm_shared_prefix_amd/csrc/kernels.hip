@@ -78,13 +78,25 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 template <typename WT>
 __global__ void __launch_bounds__(256) embed_rows(const WT* __restrict__ E, const int* __restrict__ tok, int T,
                                                   int H, const WT* __restrict__ vis, float* __restrict__ x,
-                                                  int* __restrict__ flags) {
+                                                  int* __restrict__ flags, int vec) {
   const int t = blockIdx.x;
   if (t == 0 && threadIdx.x == 0 && flags) *flags = 0;   // the forward's range flag starts clear
   if (t >= T) return;
   const int k = tok[t];
   const WT* src = (k < 0) ? vis + (size_t)(-1 - k) * H : E + (size_t)k * H;
   float* dst = x + (size_t)t * H;
+  if constexpr (sizeof(WT) == 2) {
+    if (vec) {   // H % 8 == 0, rows 16 B aligned: 8 elements per thread and step
+      for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+        const u16x8_t w = *reinterpret_cast<const u16x8_t*>(src + i);
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(bf16_to_f32(w[0]), bf16_to_f32(w[1]), bf16_to_f32(w[2]), bf16_to_f32(w[3]));
+        *reinterpret_cast<float4*>(dst + i + 4) =
+            make_float4(bf16_to_f32(w[4]), bf16_to_f32(w[5]), bf16_to_f32(w[6]), bf16_to_f32(w[7]));
+      }
+      return;
+    }
+  }
   for (int i = threadIdx.x; i < H; i += 256) dst[i] = ldw(src, i);
 }
 
@@ -96,13 +108,44 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const float* __restrict__ x,
                                                     const int* __restrict__ rows, int n_rows, int H,
                                                     const WT* __restrict__ g, float eps,
                                                     float* __restrict__ y, u16* __restrict__ yh,
-                                                    u16* __restrict__ yl, int ldy) {
+                                                    u16* __restrict__ yl, int ldy, int vec) {
   __shared__ float red[4];
   const int i = blockIdx.x;
   if (i >= n_rows) return;
   const int src = rows ? rows[i] : i;
   const float* xr = x + (size_t)src * ldx;
   float ss = 0.f;
+  if (vec) {   // H, ldx, ldy % 4 == 0 and x, y, g aligned: 4 elements per thread and step
+    const float4* x4 = reinterpret_cast<const float4*>(xr);
+    const int H4 = H >> 2;
+    for (int k = threadIdx.x; k < H4; k += 256) {
+      const float4 v = x4[k];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int k = threadIdx.x; k < H4; k += 256) {
+      const float4 v = x4[k];
+      const float xv[4] = {v.x, v.y, v.z, v.w};
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = ldw(g, 4 * k + e) * (xv[e] * r);
+      if (y) *reinterpret_cast<float4*>(y + (size_t)i * ldy + 4 * k) = make_float4(o[0], o[1], o[2], o[3]);
+      if (yh) {
+        u16 hh[4], ll[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hh[e] = f32_to_bf16(o[e]);
+          ll[e] = f32_to_bf16(o[e] - bf16_to_f32(hh[e]));
+        }
+        *reinterpret_cast<uint2*>(yh + (size_t)i * ldy + 4 * k) =
+            make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
+        *reinterpret_cast<uint2*>(yl + (size_t)i * ldy + 4 * k) =
+            make_uint2((uint32_t)ll[0] | ((uint32_t)ll[1] << 16), (uint32_t)ll[2] | ((uint32_t)ll[3] << 16));
+      }
+    }
+    return;
+  }
   for (int k = threadIdx.x; k < H; k += 256) { float v = xr[k]; ss += v * v; }
   ss = block_sum256(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
@@ -1953,20 +1996,24 @@ static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 hipError_t launch_embed(bool bf16, const void* E, const int* tok, int T, int H, const void* vis, float* x,
                         int* flags, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const int vec = H % 8 == 0 && al16(E) && (vis == nullptr || al16(vis)) && al16(x);
   if (bf16)
-    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, x, flags);
+    embed_rows<u16><<<T, 256, 0, s>>>((const u16*)E, tok, T, H, (const u16*)vis, x, flags, vec);
   else
-    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, x, flags);
+    embed_rows<float><<<T, 256, 0, s>>>((const float*)E, tok, T, H, (const float*)vis, x, flags, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(bool bf16, const float* x, int ldx, const int* rows, int n_rows, int H, const void* g,
                           float eps, float* y, uint16_t* yh, uint16_t* yl, int ldy, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
+  auto al16 = [](const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const int vec = H % 4 == 0 && ldx % 4 == 0 && ldy % 4 == 0 && al16(x) && al16(y) && al16(yh) && al16(yl);
   if (bf16)
-    rmsnorm_rows<u16><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const u16*)g, eps, y, yh, yl, ldy);
+    rmsnorm_rows<u16><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const u16*)g, eps, y, yh, yl, ldy, vec);
   else
-    rmsnorm_rows<float><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const float*)g, eps, y, yh, yl, ldy);
+    rmsnorm_rows<float><<<n_rows, 256, 0, s>>>(x, ldx, rows, n_rows, H, (const float*)g, eps, y, yh, yl, ldy, vec);
   return hipGetLastError();
 }
 
