@@ -832,11 +832,20 @@ __global__ void __launch_bounds__(256) splitk_swiglu(const float* __restrict__ p
   const int row = (int)(i / I4), c = (int)(i % I4) * 4;
   const float* p = part + (size_t)row * 2 * I + c;
   float4 g = *reinterpret_cast<const float4*>(p), u = *reinterpret_cast<const float4*>(p + I);
-  for (int k = 1; k < splits; ++k) {
-    const float4 a = *reinterpret_cast<const float4*>(p + k * split_stride);
-    const float4 b = *reinterpret_cast<const float4*>(p + k * split_stride + I);
-    g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
-    u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+  for (int k0 = 1; k0 < splits; k0 += 4) {   // split order; four splits' loads per round
+    float4 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + j < splits) {
+        a[j] = *reinterpret_cast<const float4*>(p + (k0 + j) * split_stride);
+        b[j] = *reinterpret_cast<const float4*>(p + (k0 + j) * split_stride + I);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + j < splits) {
+        g.x += a[j].x; g.y += a[j].y; g.z += a[j].z; g.w += a[j].w;
+        u.x += b[j].x; u.y += b[j].y; u.z += b[j].z; u.w += b[j].w;
+      }
   }
   const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
   const size_t o = (size_t)row * ldu + c;
