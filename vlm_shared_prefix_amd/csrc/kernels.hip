@@ -1372,7 +1372,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
 //   plane into yh when f16out (skipped if yh == nullptr)
 // H % 4 == 0 and H <= 8192.  NT threads per block: 256, or 1024 for few rows, where a
 // thread's (at most two) float4 columns take each group of eight split partials in one
-// round of loads.
+// round of loads, sixteen when every column fits the first pass of the threads, and narrow
+// rows with many partials share the splits out over thread groups (below).
 // ----------------------------------------------------------------------------
 template <typename WT, int NT>
 __global__ void __launch_bounds__(NT) residual_norm(const float* __restrict__ part, size_t split_stride, int splits,
