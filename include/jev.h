@@ -406,6 +406,22 @@ jev_status jev_tree_plan_rows(const int32_t *stem_ids, const int32_t *stem_lens,
 jev_status jev_segment_plan_tiles(const int32_t *pseg, int32_t T, int32_t G, int32_t *ptile,
                                   int32_t *max_tiles);
 
+/* Host-only introspection of the bf16 attention's work split (no HIP call), for tests.
+ * For T query tokens with G q heads per KV head, Hkv KV heads, P prefix keys, own_tiles
+ * own-key tiles of 64 keys (the largest any 128-row tile needs) and segmented != 0 for
+ * segmented prefixes, *n_split, *chunk and *blocks receive the schedule of the shared-prefix
+ * attention (FastJEV, §3.2: every question's rows read the shared prefix keys): chunk 0 means
+ * n_split equal key splits per 128-row tile, chunk > 0 the balanced schedule (chunk key
+ * tiles per block, n_split partial slots).  Under the balanced schedule, with spans
+ * non-null, spans [cap][7] receives block by block every run the kernel processes:
+ * (block, item, slot, first tile, end tile, last, the item's slot count as the merge
+ * reads it), the item being KV head item / n_rt and row tile n_rt - 1 - item % n_rt
+ * (n_rt = ceil(G*T/128)); *n_spans their count.
+ * JEV_E_INVALID for sizes out of range or a short cap. */
+jev_status jev_attn_schedule(int32_t T, int32_t G, int32_t Hkv, int32_t P, int32_t own_tiles, int32_t segmented,
+                             int32_t *n_split, int32_t *chunk, int32_t *blocks, int32_t *spans, int32_t cap,
+                             int32_t *n_spans);
+
 /* ---- diagnostics ----------------------------------------------------------------
  * Per-kernel timing with HIP events recorded on the call's stream around every
  * launch, plus the algorithmic work of each launch (flops counted once, i.e.

@@ -155,6 +155,15 @@ CONFIGS: Dict[str, Config] = {
     "mk": Config("mk", n_layers=2, hidden=320, n_q_heads=5, n_kv_heads=1, head_dim=64,
                  mlp=832, vocab=1024, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
                  n_vis=40, n_text=8, n_suffix=4, fixed_lens=(1, 7, 10, 4), s_max=10, n_cands=3),
+    # 7B head structure (G=7) with 64-dim heads over a 2560-key prefix and 470 suffix rows: 108
+    # row tiles of 41 key tiles, where equal key splits would leave the chip unevenly loaded,
+    # so the attention takes the balanced schedule (two-term q past 2048 keys)
+    "mb": Config("mb", n_layers=1, hidden=512, n_q_heads=28, n_kv_heads=4, head_dim=64,
+                 mlp=512, vocab=2048, rope_theta=1e6, rms_eps=1e-6, dtype="bf16",
+                 n_vis=2540, n_text=20, n_suffix=32,
+                 fixed_lens=(1, 29, 14, 23, 17, 17, 22, 15, 12, 18, 6, 25, 16, 11, 19, 8,
+                             13, 20, 2, 24, 15, 10, 21, 7, 16, 14, 23, 5, 12, 18, 9, 8),
+                 s_max=29, n_cands=3),
     # fp32 tree workload on the tiny decoder (oracle pins and fp32 parity)
     "t1": Config("t1", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                  mlp=688, vocab=1024, rope_theta=1e4, rms_eps=1e-6, dtype="f32",

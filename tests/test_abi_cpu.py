@@ -286,6 +286,55 @@ def test_segment_tile_table(seed):
         J.jev_segment_plan_tiles([(5, 3)], 7)
 
 
+@pytest.mark.parametrize("shape", [
+    (858, 7, 4, 8192, 1),    # 7B-shaped flat tree rows over an 8192-key prefix: equal splits give 376 blocks
+    (861, 7, 4, 8192, 2),
+    (470, 7, 4, 2560, 1),    # the "mb" parity workload (equal splits: 216 blocks of 256)
+    (470, 7, 4, 2560, 2),
+    (700, 6, 2, 4096, 1),
+    (2000, 6, 2, 2816, 2),
+    (378, 7, 4, 1024, 1),    # 7B scoring rows over 1024 keys: equal splits (252 blocks)
+    (282, 7, 4, 8192, 2),    # trie rows: equal splits fill the chip (512 blocks)
+    (54, 7, 4, 8192, 1),
+    (1600, 6, 2, 1296, 1),
+])
+def test_attention_balanced_schedule_covers_every_tile_once(shape):
+    """The balanced attention schedule (the enumeration the kernel runs, from the library):
+    every (KV head, row tile) item's nominal key tiles are processed exactly once, in block
+    order, its partial slots are 0.. in block order and within n_split, the merge's slot count
+    for the item is the number of blocks on it, exactly its final run is marked last, every
+    block holds `chunk` tiles (the last block fewer) and the launch fits the resident blocks."""
+    from vlm_shared_prefix_amd import jev as J
+    T, G, Hkv, P, own = shape
+    ns, chunk, blocks, spans = J.jev_attn_schedule(T, G, Hkv, P, own, False, 1 << 16)
+    n_rt = -(-G * T // 128)
+    nt_u = -(-P // 64) + own
+    if chunk == 0:
+        assert len(spans) == 0 and blocks == n_rt * Hkv * ns
+        assert T not in (858, 861, 470)   # the flat tree rows and "mb" take the balanced schedule
+        return
+    assert blocks <= 512 and 16 <= chunk < nt_u and 2 <= ns <= 32
+    seen = {}
+    per_block = np.zeros(blocks, np.int64)
+    prev = (-1, -1)
+    for b, u, z, vb, ve, last, slots in spans.tolist():
+        assert (b, u) > prev
+        prev = (b, u)
+        assert 0 <= u < n_rt * Hkv and 0 <= vb < ve <= nt_u
+        per_block[b] += ve - vb
+        seen.setdefault(u, []).append((b, z, vb, ve, last, slots))
+    assert sorted(seen) == list(range(n_rt * Hkv))
+    for u, runs in seen.items():
+        assert [r[1] for r in runs] == list(range(len(runs))), u          # slots 0.. in block order
+        assert len(runs) <= ns and all(r[5] == len(runs) for r in runs), u
+        edges = [0] + [r[3] for r in runs]
+        assert [r[2] for r in runs] == edges[:-1] and edges[-1] == nt_u, u   # tiles once, in order
+        assert [r[4] for r in runs] == [0] * (len(runs) - 1) + [1], u
+    assert np.all(per_block[:-1] == chunk) and 0 < per_block[-1] <= chunk
+    # segmented prefixes keep equal splits
+    assert J.jev_attn_schedule(T, G, Hkv, P, own, True)[1] == 0
+
+
 def test_launch_only_calls_need_staged_metadata(model):
     """The launch-only (graph-capturable) scoring calls refuse a workspace whose staged
     metadata is not this request's; nothing is launched (no HIP call on this path)."""

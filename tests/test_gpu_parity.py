@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
                                                  ("m7l", 0, "default"), ("m7", 0, "f16_down"), ("m2", 0, "split"), ("m7", 0, "split"),
                                                  ("m7l", 0, "split"), ("m7", 0, "f16"), ("m7l", 0, "f16"),
                                                  ("m7", 0, "f16_prefill"), ("m2", 1, "f16_prefill"),
-                                                 ("m64", 0, "default"), ("m64", 1, "split")])
+                                                 ("m64", 0, "default"), ("m64", 1, "split"),
+                                                 ("mb", 0, "default"), ("mb", 1, "split")])
 def test_score_suffixes_vs_oracle(name, seed, precision):
     cfg = S.CONFIGS[name]
     say(f"[parity] score_suffixes {name} seed {seed} ({precision})")

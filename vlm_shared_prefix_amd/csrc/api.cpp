@@ -399,6 +399,7 @@ struct Layout {
   // float buffers
   size_t x, act, big, q, ks, vts, o_part, lse_part, gpart, h, hsplit, z, lse_rows, lse_slices, rope;
   size_t total;
+  size_t prow;   // rows of attention partials (o_part / lse_part) the layout holds
   int Tc;
 };
 
@@ -413,7 +414,8 @@ size_t attn_part_rows(const jev_config& c, int T, int P) {
     // the split count grows with the tiles; a row tile's own keys span at most t + 7 rows,
     // and prefills (no prefix keys) count as well
     const int own = (t + 7 + AT_KEYS - 1) / AT_KEYS;
-    const int ns = std::max(attn_splits(t, G, c.n_kv_heads, P, own), attn_splits(t, G, c.n_kv_heads, 0, own));
+    const int ns = std::max({attn_splits(t, G, c.n_kv_heads, P, own), attn_splits(t, G, c.n_kv_heads, 0, own),
+                             attn_schedule(t, G, c.n_kv_heads, P, own, false).n_split});
     if (ns > 1) best = std::max(best, (size_t)ns * t);
   }
   return best;
@@ -454,6 +456,7 @@ Layout make_layout(const jev_model* m, int T, int R, int NT, int NG, bool has_ma
   L.ks = take(e * c.n_kv_heads * (size_t)L.Tc * kv_dim(m));
   L.vts = take(e * c.n_kv_heads * (size_t)L.Tc * kv_dim(m));
   const size_t prow = bf ? attn_part_rows(c, T, P) : 0;
+  L.prow = prow;
   L.o_part = take(4ull * prow * c.n_q_heads * kv_dim(m));
   L.lse_part = take(4ull * prow * c.n_q_heads);
   L.gpart = take(bf ? 4ull * kGemmPartFloats : 0);
@@ -687,9 +690,16 @@ struct Forward {
     // q as one float16 term, or two (q_hi + q_lo) when rows see long prefixes (jev_model_set_attn_q_terms)
     const int q_terms = attn_q_terms(m, seg_max);
     const float qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
-    // attention splits: about one block per compute unit (partials merged when > 1)
+    // attention splits: about one block per compute unit (partials merged when > 1), or the
+    // balanced schedule where equal splits would load the compute units unevenly (it falls
+    // back to equal splits should its partials not fit the layout's)
     const int own_tiles = attn_own_tiles(plan.seq_start.data(), T, Hq / Hkv);
-    const int n_split = attn_splits(T, Hq / Hkv, Hkv, plan.seg_keys >= 0 ? plan.seg_keys : P, own_tiles);
+    const int split_keys = plan.seg_keys >= 0 ? plan.seg_keys : P;
+    AttnSchedule sched = attn_schedule(T, Hq / Hkv, Hkv, split_keys, own_tiles, !plan.pseg.empty());
+    if (sched.chunk > 0 && (size_t)sched.n_split * T > L.prow)
+      sched = AttnSchedule{attn_splits(T, Hq / Hkv, Hkv, split_keys, own_tiles), 0};
+    const int n_split = sched.n_split;
+    const bool attn_parts = n_split > 1 || sched.chunk > 0;
     const int2* pseg = plan.pseg.empty() ? nullptr : at<int2>(ws, L.pseg);
     const int4* ptile = plan.pseg.empty() ? nullptr : at<int4>(ws, L.ptile);
     const double attn_flops = 4.0 * D * Hq * (prefix_pairs + own_pairs);
@@ -741,6 +751,7 @@ struct Forward {
       a.seq_start = seq_start; a.mask = mask;
       a.pseg = pseg; a.ptile = ptile;
       a.n_split = n_split;
+      a.sk_chunk = sched.chunk;
       a.own_tiles = own_tiles;
       a.o_part = at<float>(ws, L.o_part);
       a.lse_part = at<float>(ws, L.lse_part);
@@ -749,9 +760,10 @@ struct Forward {
       a.D = D;
       if (jev_status st = run_k(K_ATTN, attn_flops, attn_bytes, [&] { return launch_attn_f16(a, q_terms, s); }))
         return st;
-      if (n_split > 1) {
+      if (attn_parts) {
         if (jev_status st = run_k(K_MERGE, 0.0, 4.0 * (n_split + 1) * T * HqD, [&] {
-              return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, fo, s);
+              return launch_attn_merge(a.o_part, a.lse_part, n_split, T, Hq, D, a_hi, a_lo, fo, Hq / Hkv, P,
+                                       own_tiles, sched.chunk, s);
             }))
           return st;
       }
@@ -1288,6 +1300,36 @@ extern "C" jev_status jev_segment_plan_tiles(const int32_t* pseg, int32_t T, int
   const int mx = T > 0 ? attn_seg_tiles(pseg, T, G, ptile) : 0;
   if (max_tiles) *max_tiles = mx;
   return JEV_OK;
+}
+
+extern "C" jev_status jev_attn_schedule(int32_t T, int32_t G, int32_t Hkv, int32_t P, int32_t own_tiles,
+                                        int32_t segmented, int32_t* n_split, int32_t* chunk, int32_t* blocks,
+                                        int32_t* spans, int32_t cap, int32_t* n_spans) {
+  if (T < 1 || G < 1 || Hkv < 1 || P < 0 || own_tiles < 0 || (long)G * T > (1L << 24))
+    return fail(JEV_E_INVALID, "sizes out of range");
+  if (!n_split || !chunk || !blocks) return fail(JEV_E_INVALID, "null output");
+  const AttnSchedule sc = attn_schedule(T, G, Hkv, P, own_tiles, segmented != 0);
+  const int n_rt = (G * T + 127) / 128, nt_u = (P + AT_KEYS - 1) / AT_KEYS + own_tiles;
+  *n_split = sc.n_split;
+  *chunk = sc.chunk;
+  *blocks = sc.chunk > 0 ? (int)(((long)n_rt * Hkv * nt_u + sc.chunk - 1) / sc.chunk) : n_rt * Hkv * sc.n_split;
+  if (!spans || sc.chunk <= 0) {
+    if (n_spans) *n_spans = 0;
+    return JEV_OK;
+  }
+  int n = 0;
+  bool over = false;
+  for (int b = 0; b < *blocks; ++b)
+    attn_balanced_items(b, sc.chunk, nt_u, n_rt * Hkv, [&](int u, int z, int vb, int ve, bool last) {
+      if (n >= cap) {
+        over = true;
+        return;
+      }
+      const int32_t row[7] = {b, u, z, vb, ve, last ? 1 : 0, attn_balanced_item_slots(u, sc.chunk, nt_u)};
+      std::memcpy(spans + 7 * n++, row, sizeof(row));
+    });
+  if (n_spans) *n_spans = n;
+  return over ? fail(JEV_E_INVALID, "spans capacity too small") : JEV_OK;
 }
 
 extern "C" jev_status jev_profile_start(jev_model* m) {

@@ -47,17 +47,39 @@ struct AttnArgs {
   // [z, w) every row of the tile sees
   const int2* pseg;        // [T]
   const int4* ptile;       // [ceil(G*T / 128)]
-  int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits
+  int n_split;             // splits of each row tile's key tiles, 1..kAttnMaxSplits (balanced
+                           // schedule: the partial slots a row tile may need)
+  int sk_chunk;            // > 0: balanced schedule, sk_chunk key tiles per block (attn_schedule)
   int own_tiles;           // bound on any row tile's own-key tiles (attn_own_tiles); the splits
                            // divide ceil(P/64) + own_tiles tiles
-  float* o_part;           // [n_split][T][Hq][128]  (n_split > 1; always 128 dims)
-  float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1)
-  uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1) ...
+  float* o_part;           // [n_split][T][Hq][128]  (n_split > 1 or balanced; always 128 dims)
+  float* lse_part;         // [n_split][T][Hq]       (log2 units; n_split > 1 or balanced)
+  uint16_t* oh;            // [T][Hq*128] bf16 hi/lo planes of o (n_split == 1, not balanced) ...
   uint16_t* ol;
   int o_f16;               // ... or (non-zero) one float16 plane of o in oh
   int D;                   // the model's head dim (64 or 128): o is [T][Hq][D], the first D of
                            // the 128 computed dims (a 64-dim head runs zero-padded to 128)
 };
+
+// Balanced schedule (AttnArgs::sk_chunk = c > 0): the n_items (KV head, row tile) items'
+// nominal tile sequences of nt_u tiles each laid end to end, block vv taking tiles
+// [vv*c, (vv+1)*c) of them.  f(u, z, vb, ve, last) is called for each item u the block
+// touches, in order: its tiles [vb, ve), z the block's partial slot for that item (its
+// offset from the item's first block) and last whether the block ends the item.  The
+// attention kernel and the host checks run this same enumeration.
+template <typename F>
+inline JEV_HD void attn_balanced_items(int vv, int c, int nt_u, int n_items, F&& f) {
+  const int W = n_items * nt_u;
+  const int w0 = vv * c, w1 = (W < w0 + c) ? W : w0 + c;
+  for (int u = w0 / nt_u; u * nt_u < w1; ++u) {
+    const int b0 = u * nt_u;
+    f(u, vv - b0 / c, (w0 > b0 ? w0 : b0) - b0, (w1 < b0 + nt_u ? w1 : b0 + nt_u) - b0, b0 + nt_u <= w1);
+  }
+}
+// The partial slots item u holds under the balanced schedule: the blocks its tiles meet.
+inline JEV_HD int attn_balanced_item_slots(int u, int c, int nt_u) {
+  return ((u + 1) * nt_u - 1) / c - (u * nt_u) / c + 1;
+}
 
 // float32 attention (head_dim 64 or 128).
 struct AttnArgsF {
@@ -149,6 +171,15 @@ constexpr int kAttnMaxSplits = 32;
 // own_tiles tiles of own keys: about one block per compute unit (two from 64 key tiles on),
 // at least two tiles each.
 int attn_splits(int T, int G, int Hkv, int P, int own_tiles);
+// The attention's work split: n_split equal key splits per row tile (chunk 0), or the
+// balanced schedule (chunk > 0: chunk key tiles per block over the row tiles' sequences laid
+// end to end; n_split = the partial slots any row tile needs), chosen for one shared prefix
+// (not segmented) when equal splits would leave the compute units unevenly loaded.
+struct AttnSchedule {
+  int n_split;
+  int chunk;
+};
+AttnSchedule attn_schedule(int T, int G, int Hkv, int P, int own_tiles, bool segmented);
 // Own-key tiles (64 keys) of the 128-row tile that needs the most, from the host copy of
 // the rows' sequence starts.
 int attn_own_tiles(const int* seq_start, int T, int G);
@@ -160,8 +191,10 @@ int attn_seg_tiles(const int* pseg, int T, int G, int* ptile);
 // q_terms 1: q as one float16 term (q_lo unused); 2: q = q_hi + q_lo.  q is pre-scaled by
 // log2(e)/sqrt(128) (qkv_post's qscale), so the kernel's scores are in log2 units.
 hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, hipStream_t s);
+// S: the partial slots (n_split); under the balanced schedule (chunk > 0, with the launch's
+// G, P and own_tiles) each row merges the slots its row tile has.
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
-                             uint16_t* ol, bool f16out, hipStream_t s);
+                             uint16_t* ol, bool f16out, int G, int P, int own_tiles, int chunk, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgsF& a, int D, hipStream_t s);
 hipError_t launch_silu_mul(const float* gu, int T, int I, float* u, uint16_t* uh, uint16_t* ul, hipStream_t s);
 hipError_t launch_target_logits(bool bf16, const float* h, int H, const void* W, const int* ridx, const int* tok,

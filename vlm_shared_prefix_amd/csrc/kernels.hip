@@ -1015,7 +1015,10 @@ __global__ void __launch_bounds__(256) v_transpose(const float* __restrict__ src
 // Key tiles of 64: a row tile sees the prefix tiles [0, ceil(P/64)) followed by
 // the tiles of its own keys (from the first row's sequence start, causal within
 // the row's sequence, or the row's 64-bit ancestor mask over its group).
-// Split z takes the contiguous share [z*n/S, (z+1)*n/S) of those n tiles.  Tiles
+// Split z takes the contiguous share [z*n/S, (z+1)*n/S) of those n tiles; or, in the
+// balanced schedule (sk_chunk > 0), every block takes sk_chunk consecutive tiles of all
+// (KV head, row tile) sequences laid end to end, so blocks hold equal work whatever the
+// number of row tiles, and a row tile's partials sit in slots 0.. of its first block on.  Tiles
 // arrive by direct global->LDS loads (16 B per lane) into a double buffer, the
 // next tile's loads in flight while the current one is computed.  LDS rows are
 // XOR-swizzled by 16 B chunk so the operand reads are bank-conflict free.  With
@@ -1060,7 +1063,7 @@ struct AttnTile {
   bool own;
 };
 
-template <int QT>
+template <int QT, bool BAL>
 __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   constexpr int RB = AT_BR;         // query rows per block, 32 per wave
   __shared__ __attribute__((aligned(16))) f16 smem[2 * 2 * AT_BK * 128];
@@ -1080,289 +1083,312 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f16(AttnArgs a) {
   // the heavy and the light row tiles spread over all of them.
   const int per = gridDim.x >> 3;
   const int vv = a.P > 0 ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
-  if (vv >= n_rt * a.Hkv * ns) return;
-  const int z = vv % ns;
-  const int x = n_rt - 1 - (vv / ns) % n_rt;   // row tiles of most keys first
-  const int hk = vv / (ns * n_rt);
-  const int r0 = x * RB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hl = lane >> 5;
-  const int r = r0 + wave * 32 + ql;
-  const bool rvalid = r < R;
-  const int rc = rvalid ? r : R - 1;          // clamped row: loads stay in bounds
-  const int t = rc / G;
-  const int hq = hk * G + rc % G;
+  const bool parts = BAL || ns > 1;   // partials for attn_merge
 
-  // Prefix key tiles of this row tile: [ptb, ptb + ntp), every one of them visible in full to
-  // all of its rows when inside [vis_lo, vis_hi).  One shared prefix: all ceil(P/64) tiles,
-  // visible below P.  Segmented prefixes: the hull of the rows' segments (host table).
-  // (the host's table is per 128-row tile; a smaller row tile takes its tile's entry)
-  const int4 pt = a.ptile ? a.ptile[r0 / AT_BR] : make_int4(0, (a.P + AT_BK - 1) / AT_BK, 0, a.P);
-  const int ptb = pt.x, ntp = pt.y - pt.x, vis_lo = pt.z, vis_hi = pt.w;
-  // The splits divide ntp + own_tiles key tiles (own_tiles: the host's bound on any row
-  // tile's own-key tiles), so a block whose range starts on a prefix tile issues that
-  // tile's loads before the sequence starts it depends on for the rest have arrived.
-  const int nt_u = ntp + a.own_tiles;
-  const int vb = (int)(((long)z * nt_u) / ns), ve_u = (int)(((long)(z + 1) * nt_u) / ns);
-  const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
-  const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
-  // K tile: 64 rows of 256 B, chunk c (16 B) of key row k at chunk position c ^ (k & 15).
-  // V^T tile: 128 dim rows of 128 B, key chunk c of dim d at position c ^ ((d >> 1) & 7).
-  // Rows / chunks at or past ke load row / column 0 instead (finite, never weighted);
-  // a V chunk straddling ke holds later rows of this call or zeroed padding.
-  auto load_kv = [&](const f16* K, const f16* V, int ld, int k0, int ke, f16* dk, f16* dv) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = i * 256 + tid;
-      const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
-      const int key = k0 + row;
-      dma16(K, ((key < ke ? key : 0) * 128 + c * 8) * 2, dk + (i * 256 + wave * 64) * 8);
+  // One work item: KV head hk, row tile x, the key tiles [vb, ve_u) of the row tile's nominal
+  // tile sequence (last: the item's final share, which also takes any tiles past the nominal
+  // bound), its partial written to slot z.  vb < 0: share z of ns equal splits.
+  auto run = [&](const int hk, const int x, const int z, int vb, int ve_u, bool last) {
+    const int r0 = x * RB;
+    const int r = r0 + wave * 32 + ql;
+    const bool rvalid = r < R;
+    const int rc = rvalid ? r : R - 1;          // clamped row: loads stay in bounds
+    const int t = rc / G;
+    const int hq = hk * G + rc % G;
+
+    // Prefix key tiles of this row tile: [ptb, ptb + ntp), every one of them visible in full to
+    // all of its rows when inside [vis_lo, vis_hi).  One shared prefix: all ceil(P/64) tiles,
+    // visible below P.  Segmented prefixes: the hull of the rows' segments (host table).
+    // (the host's table is per 128-row tile; a smaller row tile takes its tile's entry)
+    const int4 pt = a.ptile ? a.ptile[r0 / AT_BR] : make_int4(0, (a.P + AT_BK - 1) / AT_BK, 0, a.P);
+    const int ptb = pt.x, ntp = pt.y - pt.x, vis_lo = pt.z, vis_hi = pt.w;
+    // The splits divide ntp + own_tiles key tiles (own_tiles: the host's bound on any row
+    // tile's own-key tiles), so a block whose range starts on a prefix tile issues that
+    // tile's loads before the sequence starts it depends on for the rest have arrived.
+    if (vb < 0) {
+      const int nt_u = ntp + a.own_tiles;
+      vb = (int)(((long)z * nt_u) / ns);
+      ve_u = (int)(((long)(z + 1) * nt_u) / ns);
+      last = z == ns - 1;
     }
+    const f16* Kp = a.kp + (size_t)hk * a.ldp * 128;
+    const f16* Vp = a.vtp + (size_t)hk * 128 * a.ldp;
+    // K tile: 64 rows of 256 B, chunk c (16 B) of key row k at chunk position c ^ (k & 15).
+    // V^T tile: 128 dim rows of 128 B, key chunk c of dim d at position c ^ ((d >> 1) & 7).
+    // Rows / chunks at or past ke load row / column 0 instead (finite, never weighted);
+    // a V chunk straddling ke holds later rows of this call or zeroed padding.
+    auto load_kv = [&](const f16* K, const f16* V, int ld, int k0, int ke, f16* dk, f16* dv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = i * 256 + tid;
-      const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
-      const int key = k0 + c * 8;
-      dma16(V, (d * ld + (key < ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
-    }
-  };
-  // the first prefix tile goes out before the sequence metadata it does not need
-  const bool early = vb < ntp && vb < ve_u;
-  if (early) load_kv(Kp, Vp, a.ldp, (ptb + vb) * AT_BK, a.P, sk(0), sv(0));
-
-  const int t_first = r0 / G, t_last = min(R - 1, r0 + RB - 1) / G;
-  const int s_first = a.seq_start[t_first];
-  const int max_start = a.seq_start[t_last];
-  const int my_start = a.seq_start[t];
-  const bool use_mask = a.mask != nullptr;
-  const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
-  const int2 my_pk = a.pseg ? a.pseg[t] : make_int2(0, a.P);   // the row's prefix keys
-
-  // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
-  // of q, which would shift every score of the row coherently, stays out.
-  f16x8 qreg[8], qlo[QT == 2 ? 8 : 1];
-  {
-    // operand-ordered q: slice c of the wave's 32 rows is one contiguous 1 KB run
-    const size_t qo = ((size_t)hk * attn_q_rows(T, G) + (rc & ~31)) * 128 + (size_t)(hl * 32 + (rc & 31)) * 8;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 512);
-      if (QT == 2) qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 512);
-    }
-  }
-
-  // this block's share of the tile sequence: [vb, ve) of the row tile's real tiles (the last
-  // split also takes any tiles past the bound, should the host's bound be short)
-  const int own_end = t_last + 1;
-  const int own0 = s_first & ~7;   // 16 B aligned start of the block's own keys
-  const int nt_all = ntp + (own_end - own0 + AT_BK - 1) / AT_BK;
-  const int ve = (z == ns - 1) ? nt_all : min(ve_u, nt_all);
-  const int nt = max(0, ve - vb);
-
-  auto tile = [&](int v) {
-    AttnTile s;
-    if (v < ntp) {
-      s.K = Kp; s.V = Vp; s.ld = a.ldp;
-      s.k0 = (ptb + v) * AT_BK; s.ke = a.P; s.own = false;
-    } else {
-      s.K = a.ks + (size_t)hk * a.lds * 128; s.V = a.vts + (size_t)hk * 128 * a.lds; s.ld = a.lds;
-      s.k0 = own0 + (v - ntp) * AT_BK; s.ke = own_end; s.own = true;
-    }
-    return s;
-  };
-  auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) { load_kv(s.K, s.V, s.ld, s.k0, s.ke, dk, dv); };
-
-  const int prow = attn_key_perm(ql);
-  float m_ref = NEG_INF, l_run = 0.f;   // m_ref: reference max of the row, in scaled log2 units
-  f32x16 acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
-
-  auto step = [&](int i, int b) {
-    if (i + 1 < nt) load_tile(tile(vb + i + 1), sk(b ^ 1), sv(b ^ 1));   // in flight during this tile
-    const f16* skb = sk(b);
-    const f16* svb = sv(b);
-    // scores start at -m_use (q carries the log2(e)/sqrt(D) scale): the MFMAs leave
-    // score - m_use, in log2 units, and a weight is exp2 of it
-    f32x16 s[2];
-    const float m_init = (m_ref == NEG_INF) ? 0.f : -m_ref;
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[hs][e] = m_init;
-    // the K operands of half the tile's dims are read ahead of their MFMAs (one LDS round
-    // trip per half instead of one per 16-dim step)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f16x8 k0op[4], k1op[4];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int ch = (2 * (4 * h2 + c4) + hl) ^ (prow & 15);
-        k0op[c4] = *reinterpret_cast<const f16x8*>(skb + prow * 128 + ch * 8);
-        k1op[c4] = *reinterpret_cast<const f16x8*>(skb + (32 + prow) * 128 + ch * 8);
+      for (int i = 0; i < 4; ++i) {
+        const int slot = i * 256 + tid;
+        const int row = slot >> 4, c = (slot & 15) ^ (row & 15);
+        const int key = k0 + row;
+        dma16(K, ((key < ke ? key : 0) * 128 + c * 8) * 2, dk + (i * 256 + wave * 64) * 8);
       }
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int c = 4 * h2 + c4;
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qreg[c], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qreg[c], s[1], 0, 0, 0);
-        if (QT == 2) {
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qlo[c], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qlo[c], s[1], 0, 0, 0);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int slot = i * 256 + tid;
+        const int d = slot >> 3, c = (slot & 7) ^ ((d >> 1) & 7);
+        const int key = k0 + c * 8;
+        dma16(V, (d * ld + (key < ke ? key : 0)) * 2, dv + (i * 256 + wave * 64) * 8);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);            // the 8 LDS reads first
-      __builtin_amdgcn_sched_group_barrier(0x008, QT == 2 ? 16 : 8, 0);   // then their MFMAs
+    };
+    // the first prefix tile goes out before the sequence metadata it does not need
+    const bool early = vb < ntp && vb < ve_u;
+    if (early) load_kv(Kp, Vp, a.ldp, (ptb + vb) * AT_BK, a.P, sk(0), sv(0));
+
+    const int t_first = r0 / G, t_last = min(R - 1, r0 + RB - 1) / G;
+    const int s_first = a.seq_start[t_first];
+    const int max_start = a.seq_start[t_last];
+    const int my_start = a.seq_start[t];
+    const bool use_mask = a.mask != nullptr;
+    const uint64_t my_mask = use_mask ? a.mask[t] : 0ull;
+    const int2 my_pk = a.pseg ? a.pseg[t] : make_int2(0, a.P);   // the row's prefix keys
+
+    // q = q_hi + q_lo (two f16 terms): scores are K·q_hi + K·q_lo, so the rounding
+    // of q, which would shift every score of the row coherently, stays out.
+    f16x8 qreg[8], qlo[QT == 2 ? 8 : 1];
+    {
+      // operand-ordered q: slice c of the wave's 32 rows is one contiguous 1 KB run
+      const size_t qo = ((size_t)hk * attn_q_rows(T, G) + (rc & ~31)) * 128 + (size_t)(hl * 32 + (rc & 31)) * 8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        qreg[c] = *reinterpret_cast<const f16x8*>(a.q + qo + c * 512);
+        if (QT == 2) qlo[c] = *reinterpret_cast<const f16x8*>(a.q_lo + qo + c * 512);
+      }
     }
-    // Masks only where some row of the block does not see the whole tile (uniform test):
-    // a prefix tile reaching outside [vis_lo, vis_hi) (the partial last tile, segment
-    // edges), and own-key tiles not fully visible to every row.
-    const AttnTile ts = tile(vb + i);
-    const bool need = ts.own ? (use_mask || ts.k0 < max_start || ts.k0 + AT_BK > t_first + 1)
-                             : (ts.k0 < vis_lo || ts.k0 + AT_BK > vis_hi);
-    if (need) {
-      const int lo = ts.own ? my_start : my_pk.x;
-      const int hi = ts.own ? t + 1 : my_pk.y;
-      const uint64_t mm = (ts.own && use_mask) ? my_mask : ~0ull;
-      const int base = ts.k0 + 8 * hl;
+
+    // this block's share of the tile sequence: [vb, ve) of the row tile's real tiles (the last
+    // split also takes any tiles past the bound, should the host's bound be short)
+    const int own_end = t_last + 1;
+    const int own0 = s_first & ~7;   // 16 B aligned start of the block's own keys
+    const int nt_all = ntp + (own_end - own0 + AT_BK - 1) / AT_BK;
+    const int ve = last ? nt_all : min(ve_u, nt_all);
+    const int nt = max(0, ve - vb);
+
+    auto tile = [&](int v) {
+      AttnTile s;
+      if (v < ntp) {
+        s.K = Kp; s.V = Vp; s.ld = a.ldp;
+        s.k0 = (ptb + v) * AT_BK; s.ke = a.P; s.own = false;
+      } else {
+        s.K = a.ks + (size_t)hk * a.lds * 128; s.V = a.vts + (size_t)hk * 128 * a.lds; s.ld = a.lds;
+        s.k0 = own0 + (v - ntp) * AT_BK; s.ke = own_end; s.own = true;
+      }
+      return s;
+    };
+    auto load_tile = [&](const AttnTile& s, f16* dk, f16* dv) { load_kv(s.K, s.V, s.ld, s.k0, s.ke, dk, dv); };
+
+    const int prow = attn_key_perm(ql);
+    float m_ref = NEG_INF, l_run = 0.f;   // m_ref: reference max of the row, in scaled log2 units
+    f32x16 acc[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
+
+    auto step = [&](int i, int b) {
+      if (i + 1 < nt) load_tile(tile(vb + i + 1), sk(b ^ 1), sv(b ^ 1));   // in flight during this tile
+      const f16* skb = sk(b);
+      const f16* svb = sv(b);
+      // scores start at -m_use (q carries the log2(e)/sqrt(D) scale): the MFMAs leave
+      // score - m_use, in log2 units, and a weight is exp2 of it
+      f32x16 s[2];
+      const float m_init = (m_ref == NEG_INF) ? 0.f : -m_ref;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = base + hs * 32 + 16 * (e >> 3) + (e & 7);
-          const bool in = ((unsigned)(key - lo) < (unsigned)(hi - lo)) && ((mm >> ((key - lo) & 63)) & 1ull);
-          s[hs][e] = in ? s[hs][e] : NEG_INF;
+        for (int e = 0; e < 16; ++e) s[hs][e] = m_init;
+      // the K operands of half the tile's dims are read ahead of their MFMAs (one LDS round
+      // trip per half instead of one per 16-dim step)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f16x8 k0op[4], k1op[4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int ch = (2 * (4 * h2 + c4) + hl) ^ (prow & 15);
+          k0op[c4] = *reinterpret_cast<const f16x8*>(skb + prow * 128 + ch * 8);
+          k1op[c4] = *reinterpret_cast<const f16x8*>(skb + (32 + prow) * 128 + ch * 8);
         }
-    }
-    float mx = NEG_INF;
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int c = 4 * h2 + c4;
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qreg[c], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qreg[c], s[1], 0, 0, 0);
+          if (QT == 2) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0op[c4], qlo[c], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1op[c4], qlo[c], s[1], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);            // the 8 LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, QT == 2 ? 16 : 8, 0);   // then their MFMAs
+      }
+      // Masks only where some row of the block does not see the whole tile (uniform test):
+      // a prefix tile reaching outside [vis_lo, vis_hi) (the partial last tile, segment
+      // edges), and own-key tiles not fully visible to every row.
+      const AttnTile ts = tile(vb + i);
+      const bool need = ts.own ? (use_mask || ts.k0 < max_start || ts.k0 + AT_BK > t_first + 1)
+                               : (ts.k0 < vis_lo || ts.k0 + AT_BK > vis_hi);
+      if (need) {
+        const int lo = ts.own ? my_start : my_pk.x;
+        const int hi = ts.own ? t + 1 : my_pk.y;
+        const uint64_t mm = (ts.own && use_mask) ? my_mask : ~0ull;
+        const int base = ts.k0 + 8 * hl;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hs][e]);
-    mx = halves_max(mx);
-    // The reference max moves only when a score exceeds it by more than 8 (log2 units):
-    // the weights p = 2^(score - m_ref) stay below 2^8 (exact to f16's relative
-    // precision), and the accumulators are rescaled on few tiles.
-    const bool first = m_ref == NEG_INF;
-    const bool grow = first ? (mx != NEG_INF) : (mx > 8.f);
-    if (__ballot(grow)) {
-      const float d = grow ? mx : 0.f;
-      const float alpha = grow ? (first ? 0.f : __builtin_amdgcn_exp2f(-mx)) : 1.f;
-      if (grow) m_ref = (first ? 0.f : m_ref) + mx;
-      l_run *= alpha;
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[dd][e] *= alpha;
+          for (int e = 0; e < 16; ++e) {
+            const int key = base + hs * 32 + 16 * (e >> 3) + (e & 7);
+            const bool in = ((unsigned)(key - lo) < (unsigned)(hi - lo)) && ((mm >> ((key - lo) & 63)) & 1ull);
+            s[hs][e] = in ? s[hs][e] : NEG_INF;
+          }
+      }
+      float mx = NEG_INF;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[hs][e] -= d;
-    }
-    // p is rounded to nearest f16 in pairs; the row sum adds exactly the rounded weights
-    float rs = 0.f;
-    f16x8 pops[2][2];
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hs][e]);
+      mx = halves_max(mx);
+      // The reference max moves only when a score exceeds it by more than 8 (log2 units):
+      // the weights p = 2^(score - m_ref) stay below 2^8 (exact to f16's relative
+      // precision), and the accumulators are rescaled on few tiles.
+      const bool first = m_ref == NEG_INF;
+      const bool grow = first ? (mx != NEG_INF) : (mx > 8.f);
+      if (__ballot(grow)) {
+        const float d = grow ? mx : 0.f;
+        const float alpha = grow ? (first ? 0.f : __builtin_amdgcn_exp2f(-mx)) : 1.f;
+        if (grow) m_ref = (first ? 0.f : m_ref) + mx;
+        l_run *= alpha;
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
+        for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+          for (int e = 0; e < 16; ++e) acc[dd][e] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x2 e2 = {__builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j]), __builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j + 1])};
-          const f16x2 h2 = __builtin_convertvector(e2, f16x2);
-          rs = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.0f, (f16)1.0f}, rs, false);
-          pops[hs][p][2 * j] = h2[0];
-          pops[hs][p][2 * j + 1] = h2[1];
-        }
-    l_run += halves_sum(rs);
-    // O^T += V^T · P^T, four 16-key steps
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int c = 4 * hs + 2 * p + hl;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = dt * 32 + ql;
-          const f16x8 vop = *reinterpret_cast<const f16x8*>(svb + d * AT_BK + ((c ^ ((d >> 1) & 7)) * 8));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pops[hs][p], acc[dt], 0, 0, 0);
-        }
+          for (int e = 0; e < 16; ++e) s[hs][e] -= d;
       }
-    // The next tile's loads have landed and every wave is done with this tile's buffers.
-    // (The wait is a builtin so the compiler knows the loads are complete; the barrier is
-    // asm with a memory clobber so no LDS access moves across it.)
-    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-  };
-  if (nt > 0 && !early) load_tile(tile(vb), sk(0), sv(0));
-  // the first tile has landed (or, with no tile to process, the early load is done before
-  // the block's LDS is released)
-  __builtin_amdgcn_s_waitcnt(0x70);
-  if (nt > 0) asm volatile("s_barrier" ::: "memory");
-  for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
-    step(i, 0);
-    if (i + 1 < nt) step(i + 1, 1);
-  }
-  // this block's normalised partial o (acc / l) and its log2-sum-exp
-  const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-  float lse = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
+      // p is rounded to nearest f16 in pairs; the row sum adds exactly the rounded weights
+      float rs = 0.f;
+      f16x8 pops[2][2];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+      for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[dt][e] *= inv;
-  if (ns > 1) {
-    float* op = a.o_part + (((size_t)z * T + t) * Hq + hq) * 128;
-    if (rvalid) {
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x2 e2 = {__builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j]),
+                              __builtin_amdgcn_exp2f(s[hs][8 * p + 2 * j + 1])};
+            const f16x2 h2 = __builtin_convertvector(e2, f16x2);
+            rs = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.0f, (f16)1.0f}, rs, false);
+            pops[hs][p][2 * j] = h2[0];
+            pops[hs][p][2 * j + 1] = h2[1];
+          }
+      l_run += halves_sum(rs);
+      // O^T += V^T · P^T, four 16-key steps
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int c = 4 * hs + 2 * p + hl;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int d = dt * 32 + ql;
+            const f16x8 vop = *reinterpret_cast<const f16x8*>(svb + d * AT_BK + ((c ^ ((d >> 1) & 7)) * 8));
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pops[hs][p], acc[dt], 0, 0, 0);
+          }
+        }
+      // The next tile's loads have landed and every wave is done with this tile's buffers.
+      // (The wait is a builtin so the compiler knows the loads are complete; the barrier is
+      // asm with a memory clobber so no LDS access moves across it.)
+      __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+    };
+    if (nt > 0 && !early) load_tile(tile(vb), sk(0), sv(0));
+    // the first tile has landed (or, with no tile to process, the early load is done before
+    // the block's LDS is released)
+    __builtin_amdgcn_s_waitcnt(0x70);
+    if (nt > 0) asm volatile("s_barrier" ::: "memory");
+    for (int i = 0; i < nt; i += 2) {   // two steps per trip: the buffers are named statically
+      step(i, 0);
+      if (i + 1 < nt) step(i + 1, 1);
+    }
+    // this block's normalised partial o (acc / l) and its log2-sum-exp
+    const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+    float lse = (l_run > 0.f) ? m_ref + log2f(l_run) : NEG_INF;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[dt][e] *= inv;
+    if (parts) {
+      float* op = a.o_part + (((size_t)z * T + t) * Hq + hq) * 128;
+      if (rvalid) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int d = dt * 32 + 8 * ii + 4 * hl;
+            *reinterpret_cast<float4*>(op + d) =
+                make_float4(acc[dt][4 * ii], acc[dt][4 * ii + 1], acc[dt][4 * ii + 2], acc[dt][4 * ii + 3]);
+          }
+        if (hl == 0) a.lse_part[((size_t)z * T + t) * Hq + hq] = lse;
+      }
+      return;   // attn_merge combines the splits
+    }
+    if (!rvalid) return;
+    // o [T][Hq][D]: the first D of the 128 dims (a 64-dim head runs zero-padded)
+    const int Do = a.D;
+    const size_t ob = ((size_t)t * Hq + hq) * Do;
+    if (a.o_f16) {   // one float16 plane
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int d = dt * 32 + 8 * ii + 4 * hl;
-          *reinterpret_cast<float4*>(op + d) =
-              make_float4(acc[dt][4 * ii], acc[dt][4 * ii + 1], acc[dt][4 * ii + 2], acc[dt][4 * ii + 3]);
+          if (d >= Do) continue;
+          f16x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = (f16)acc[dt][4 * ii + j];
+          *reinterpret_cast<f16x4*>(a.oh + ob + d) = v4;
         }
-      if (hl == 0) a.lse_part[((size_t)z * T + t) * Hq + hq] = lse;
+      return;
     }
-    return;   // attn_merge combines the splits
-  }
-  if (!rvalid) return;
-  // o [T][Hq][D]: the first D of the 128 dims (a 64-dim head runs zero-padded)
-  const int Do = a.D;
-  const size_t ob = ((size_t)t * Hq + hq) * Do;
-  if (a.o_f16) {   // one float16 plane
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int d = dt * 32 + 8 * ii + 4 * hl;
         if (d >= Do) continue;
-        f16x4 v4;
+        u16 h[4], l[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = (f16)acc[dt][4 * ii + j];
-        *reinterpret_cast<f16x4*>(a.oh + ob + d) = v4;
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[dt][4 * ii + j];
+          h[j] = f32_to_bf16(v);
+          l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
+        }
+        *reinterpret_cast<uint2*>(a.oh + ob + d) =
+            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(a.ol + ob + d) =
+            make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
       }
-    return;
+  };
+
+  if constexpr (BAL) {
+    // Balanced: the items' nominal tile sequences laid end to end (item u = KV head u / n_rt,
+    // row tile n_rt - 1 - u % n_rt), block vv taking the run [vv*c, (vv+1)*c) of them, which
+    // may cover the end of one item and the start of the next.  An item's partial slot is the
+    // block's offset from the first block on that item.
+    // (the host keeps n_rt * Hkv * nt_u within int)
+    attn_balanced_items(vv, a.sk_chunk, (a.P + AT_BK - 1) / AT_BK + a.own_tiles, n_rt * a.Hkv,
+                        [&](int u, int z, int vb, int ve, bool last) {
+                          run(u / n_rt, n_rt - 1 - u % n_rt, z, vb, ve, last);
+                        });
+  } else {
+    if (vv >= n_rt * a.Hkv * ns) return;
+    run(vv / (ns * n_rt), n_rt - 1 - (vv / ns) % n_rt, vv % ns, -1, 0, false);
   }
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int d = dt * 32 + 8 * ii + 4 * hl;
-      if (d >= Do) continue;
-      u16 h[4], l[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = acc[dt][4 * ii + j];
-        h[j] = f32_to_bf16(v);
-        l[j] = f32_to_bf16(v - bf16_to_f32(h[j]));
-      }
-      *reinterpret_cast<uint2*>(a.oh + ob + d) =
-          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-      *reinterpret_cast<uint2*>(a.ol + ob + d) =
-          make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
-    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1712,17 +1738,24 @@ __global__ void __launch_bounds__(256) qkv_post(const float* __restrict__ src, i
 }
 
 // Combine split partials: o = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), written as
-// bf16 hi/lo planes or (f16out) one float16 plane.
+// bf16 hi/lo planes or (f16out) one float16 plane.  chunk > 0 (balanced schedule): the row's
+// row tile holds the slots [0, number of blocks on its tile sequence), found from the same
+// layout the attention used (nt_u nominal tiles per row tile, chunk tiles per block).
 template <int MAXS>
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ o_part,
                                                   const float* __restrict__ lse_part, int S, int T, int Hq,
                                                   int D, int Dp, u16* __restrict__ oh, u16* __restrict__ ol,
-                                                  int f16out) {
+                                                  int f16out, int G, int nt_u, int chunk) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one (t, hq)
   const int d4 = D >> 2;
   if (i >= (size_t)T * Hq * d4) return;
   const size_t th = i / d4;
   const int c = (int)(i % d4);
+  if (chunk > 0) {
+    const int t = (int)(th / Hq), hq = (int)(th % Hq);
+    const int n_rt = (G * T + AT_BR - 1) / AT_BR;
+    S = attn_balanced_item_slots((hq / G) * n_rt + (n_rt - 1 - (t * G + hq % G) / AT_BR), chunk, nt_u);
+  }
   // every split's lse and partial are loaded up front (S <= MAXS), so the loads are in
   // flight together instead of one round trip per split
   float lse[MAXS];
@@ -2369,24 +2402,66 @@ int attn_splits(int T, int G, int Hkv, int P, int own_tiles) {
 }
 
 
+// Largest partial slot count of any row tile under the balanced schedule: a run of nt_u
+// tiles starting anywhere meets at most floor((nt_u - 1) / chunk) + 2 blocks of chunk tiles.
+static long attn_balanced_slots(long nt_u, long chunk) { return (nt_u - 1) / chunk + 2; }
+
+AttnSchedule attn_schedule(int T, int G, int Hkv, int P, int own_tiles, bool segmented) {
+  const int ns = attn_splits(T, G, Hkv, P, own_tiles);
+  const AttnSchedule equal{ns, 0};
+  if (segmented || P <= 0) return equal;
+  const long base = (long)cdiv((long)G * T, AT_BR) * Hkv;
+  const long nt_u = cdiv(P, AT_BK) + own_tiles;
+  // the block count the equal splits aim at (as attn_splits); they fall short of it or load
+  // the compute units unevenly when the row tiles do not divide it (376 blocks = 120 CUs
+  // with two blocks, 136 with one: the launch takes as long as the two-block CUs)
+  const long target = nt_u >= 64 ? kAttnResidentBlocks : kAttnResidentBlocks / 2;
+  if (base * ns >= target * 7 / 8) return equal;
+  const long chunk = cdiv(base * nt_u, target);
+  // long runs only: a block pays a prologue per row tile it touches, and every row tile
+  // more partials to merge
+  if (chunk < 16 || chunk >= nt_u) return equal;
+  const long slots = attn_balanced_slots(nt_u, chunk);
+  if (slots > kAttnMaxSplits) return equal;
+  return AttnSchedule{(int)slots, (int)chunk};
+}
+
 hipError_t launch_attn_f16(const AttnArgs& a, int q_terms, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.n_split < 1 || a.n_split > kAttnMaxSplits || (q_terms != 1 && q_terms != 2)) return hipErrorInvalidValue;
-  const long nb = (long)cdiv((long)a.G * a.T, AT_BR) * a.Hkv * a.n_split;
+  long nb = (long)cdiv((long)a.G * a.T, AT_BR) * a.Hkv * a.n_split;
+  if (a.sk_chunk > 0) {
+    // one shared prefix only, and the slots a row tile may need within n_split
+    const long nt_u = cdiv(a.P, AT_BK) + a.own_tiles;
+    const long W = (long)cdiv((long)a.G * a.T, AT_BR) * a.Hkv * nt_u;
+    if (a.ptile || a.P <= 0 || attn_balanced_slots(nt_u, a.sk_chunk) > a.n_split || W > INT_MAX / 2)
+      return hipErrorInvalidValue;
+    nb = cdiv(W, a.sk_chunk);
+  }
   const int grid = (int)(cdiv(nb, 8) * 8);
-  if (q_terms == 1) attn_fwd_f16<1><<<grid, 256, 0, s>>>(a);
-  else attn_fwd_f16<2><<<grid, 256, 0, s>>>(a);
+  const bool bal = a.sk_chunk > 0;
+  if (q_terms == 1) {
+    if (bal) attn_fwd_f16<1, true><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_f16<1, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (bal) attn_fwd_f16<2, true><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_f16<2, false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int S, int T, int Hq, int D, uint16_t* oh,
-                             uint16_t* ol, bool f16out, hipStream_t s) {
+                             uint16_t* ol, bool f16out, int G, int P, int own_tiles, int chunk, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (S < 1 || S > kAttnMaxSplits || G < 1 || Hq % G) return hipErrorInvalidValue;
+  const int nt_u = chunk > 0 ? cdiv(P, AT_BK) + own_tiles : 0;
+  if (chunk > 0 && attn_balanced_slots(nt_u, chunk) > S) return hipErrorInvalidValue;
   const int grid = cdiv((long)T * Hq * (D / 4), 256);
   if (S <= 8)
-    attn_merge<8><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out);
+    attn_merge<8><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out, G, nt_u, chunk);
   else
-    attn_merge<kAttnMaxSplits><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out);
+    attn_merge<kAttnMaxSplits><<<grid, 256, 0, s>>>(o_part, lse_part, S, T, Hq, D, 128, oh, ol, f16out, G, nt_u,
+                                                    chunk);
   return hipGetLastError();
 }
 

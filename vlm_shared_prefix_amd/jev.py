@@ -107,6 +107,8 @@ _sig = {
     "jev_tree_plan_rows": (C.c_int32, [_i32p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, C.c_int32,
                                        C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _u64p, _i32p]),
     "jev_segment_plan_tiles": (C.c_int32, [_i32p, C.c_int32, C.c_int32, _i32p, _i32p]),
+    "jev_attn_schedule": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _i32p,
+                                      _i32p, _i32p, _i32p, C.c_int32, _i32p]),
     "jev_profile_start": (C.c_int32, [_vp]),
     "jev_profile_stop": (C.c_int32, [_vp, C.POINTER(jev_kernel_stat), C.c_int32, _i32p]),
     "jev_last_error": (C.c_char_p, []),
@@ -356,6 +358,19 @@ def jev_segment_plan_tiles(pseg, G: int):
     mx = C.c_int32()
     _check(_lib.jev_segment_plan_tiles(_ptr_i32(ps), T, G, _ptr_i32(out), C.byref(mx)), "jev_segment_plan_tiles")
     return out[:nb], mx.value
+
+
+def jev_attn_schedule(T: int, G: int, Hkv: int, P: int, own_tiles: int, segmented: bool = False,
+                      max_spans: int = 0):
+    """(n_split, chunk, blocks, spans [n][7]) of the attention's work split (host only); spans
+    (block, item, slot, first tile, end tile, last, item slot count) under the balanced schedule
+    when max_spans > 0."""
+    ns, ch, nb, n = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int32()
+    sp = np.zeros((max(max_spans, 1), 7), np.int32)
+    _check(_lib.jev_attn_schedule(T, G, Hkv, P, own_tiles, int(bool(segmented)), C.byref(ns), C.byref(ch),
+                                  C.byref(nb), _ptr_i32(sp) if max_spans > 0 else None, max_spans, C.byref(n)),
+           "jev_attn_schedule")
+    return ns.value, ch.value, nb.value, sp[:n.value]
 
 
 def jev_tree_plan_size(stem_ids, stem_lens, cand_tok, cand_lens, n_cands, mode: int):
