@@ -43,6 +43,11 @@ PRECISION_NOTE = {
                    "every projection as one float16 pass (q|k|v only for prefixes of at most 2048 rows, "
                    "else two bfloat16 passes); in the scoring call gate|up, o and q|k|v as two bfloat16 "
                    "passes (hi + lo of the float32 activation); float32 accumulation",
+    "f16_score_gup": "f16_score_gup: down projection as one float16 pass on a float16 weight mirror; gate|up as "
+                     "one float16 pass in prefills and suffix-scoring calls (two bfloat16 passes in tree "
+                     "calls); in prefills q|k|v (prefixes of at most 2048 rows) and o as one float16 pass, in "
+                     "scoring calls as two bfloat16 passes (hi + lo of the float32 activation); float32 "
+                     "accumulation",
     "f16_down_gup_o": "f16_down_gup_o: down projection as one float16 pass on a float16 weight mirror; gate|up "
                       "and o as one float16 pass in the prefill and two bfloat16 passes (hi + lo of the float32 "
                       "activation) in the scoring call; q|k|v as two bfloat16 passes; float32 accumulation",
@@ -60,7 +65,7 @@ def workload_name(cfg):
             f"tokens, {cfg.n_cands} candidates each")
 
 
-def roofline(kind, d):
+def roofline(kind, d, traffic_md=None):
     """Roofline entry of one kernel kind from the library's event timing.
 
     achieved = algorithmic flops per launch (each product counted once) / average
@@ -68,13 +73,14 @@ def roofline(kind, d):
     gemm_swiglu, lm_head_lse) run every product twice (hi and lo planes of the float32
     activations), so the MFMA pipes execute 2x the algorithmic flops: reported as
     executed_tflops / executed_frac.  The float16 GEMMs (kinds ending in _f16) execute
-    each product once.
+    each product once.  traffic_md: the counter summary of this launch shape under profiles/
+    (default {kind}_traffic.md).
     """
     from vlm_shared_prefix_amd import profiling
     n = d["launches"]
     avg_s = d["ms"] / n * 1e-3
     traffic = None
-    stored = profiling.stored_traffic(os.path.join(ROOT, "profiles", f"{kind}_traffic.md"))
+    stored = profiling.stored_traffic(os.path.join(ROOT, "profiles", traffic_md or f"{kind}_traffic.md"))
     if stored and stored[1] == profiling.source_digest():
         traffic = stored[0]
     if d["flops"] > 0:
@@ -747,13 +753,19 @@ def main():
     prof_prefill = J.jev_profile_stop(sess.model)
     roof = None
     if prof_step:
+        # the kind with the most time in the step; when the prefill and the scoring call both
+        # launch it (the float16 SwiGLU), its roofline is taken over the prefill's launches
+        # alone, one launch shape (the scoring call's shape has its own entry below)
         dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
-        roof = roofline(dom, prof_step[dom])
+        roof = roofline(dom, prof_prefill[dom] if dom in prof_prefill else prof_step[dom])
+        if dom in prof_prefill:
+            roof["launches_of"] = f"prefill ({cfg.prefix_len} rows)"
     # the scoring call's own dominant kernel (the prefill's dominates the whole step)
     score_roof = None
     if prof_score:
         dom_s = max(prof_score, key=lambda k: prof_score[k]["ms"])
-        score_roof = roofline(dom_s, prof_score[dom_s])
+        score_roof = roofline(dom_s, prof_score[dom_s], f"{dom_s}_score_traffic.md")
+        score_roof["launches_of"] = f"scoring call ({cfg.n_suffix} suffixes)"
     attn = {"score_call": attention_entry(prof_score, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                           f"shared prefix ({cfg.prefix_len} keys) + own rows of the "
                                           f"{cfg.n_suffix} suffixes"),

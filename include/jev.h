@@ -129,6 +129,11 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
  *   2048 rows; longer prefixes keep q|k|v on two terms (the rounding of K and
  *   V reaches every query's scores, and its error grows with the keys a query
  *   sees, as for the q terms in jev_model_set_attn_q_terms).
+ *   JEV_F16_GATE_UP_SCORE extends the single f16 pass of gate|up from prefills
+ *   to the suffix-scoring calls, whose every candidate log-probability is read
+ *   from one row ("How to Deploy Visual Jev", Step 3: two logits of the last
+ *   position); tree calls keep two terms, since a candidate's tree score sums the
+ *   log-probabilities of up to four rows and their rounding errors with them.
  * jev_model_f16_bytes: size of the mirror buffer for those groups (0 for JEV_F32
  *   models or unknown bits).
  * jev_model_attach_f16: buf dev [bytes >= jev_model_f16_bytes(m, groups)],
@@ -150,6 +155,8 @@ jev_status jev_get_stats(const jev_model *m, jev_stats *out);
 #define JEV_F16_GATE_UP_PREFILL 16  /* w_gate, w_up mirrored, the f16 pass used by prefills only */
 #define JEV_F16_QKV_PREFILL     32  /* wq, wk, wv mirrored, used by prefills of <= 2048 rows  */
 #define JEV_F16_O_PREFILL       64  /* wo mirrored, used by prefills only                    */
+#define JEV_F16_GATE_UP_SCORE  128  /* w_gate, w_up mirrored, used by prefills and by
+                                       jev_score_suffixes / jev_score_segments, not by trees  */
 size_t     jev_model_f16_bytes(const jev_model *m, int32_t groups);
 jev_status jev_model_attach_f16(jev_model *m, int32_t groups, void *buf, size_t bytes, void *stream);
 /* The groups whose float16 pass is in effect (0: none; a prefill-only bit is

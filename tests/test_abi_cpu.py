@@ -139,9 +139,11 @@ def test_mirror_and_skip_arguments(model):
         assert J.jev_model_f16_bytes(m, g) == 2 * b + 256
     # the prefill-only bits mirror the same matrices
     for g, gp in ((J.JEV_F16_GATE_UP, J.JEV_F16_GATE_UP_PREFILL), (J.JEV_F16_QKV, J.JEV_F16_QKV_PREFILL),
-                  (J.JEV_F16_O, J.JEV_F16_O_PREFILL)):
+                  (J.JEV_F16_O, J.JEV_F16_O_PREFILL), (J.JEV_F16_GATE_UP, J.JEV_F16_GATE_UP_SCORE)):
         assert J.jev_model_f16_bytes(m, gp) == J.jev_model_f16_bytes(m, g)
-    assert J.jev_model_f16_bytes(m, 128) == 0
+    assert J.jev_model_f16_bytes(m, J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_GATE_UP_SCORE) == \
+        J.jev_model_f16_bytes(m, J.JEV_F16_GATE_UP)
+    assert J.jev_model_f16_bytes(m, 256) == 0
     with pytest.raises(J.JevError) as e:
         J.jev_model_attach_f16(m, J.JEV_F16_DOWN, _FakeDev(100), stream=0)
     assert e.value.code == J.JEV_E_WORKSPACE

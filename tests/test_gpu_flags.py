@@ -125,3 +125,28 @@ def test_f16_qkv_prefill_length_rule(n_vis, same):
         outs.append(sess.score_suffixes(suf).cpu())
         sess.close()
     assert torch.equal(outs[0], outs[1]) == same
+
+
+def test_f16_gate_up_score_rule():
+    """JEV_F16_GATE_UP_SCORE runs gate|up on one float16 pass in prefills and suffix-scoring
+    calls only: tree calls keep the two bfloat16 terms, so their scores equal those of the
+    prefill-only group bit for bit, while the suffix scores do not."""
+    import torch
+    from vlm_shared_prefix_amd import jev as J
+    from vlm_shared_prefix_amd.session import Session
+    cfg = S.CONFIGS["m64"]
+    src = S.WeightSource(cfg, 0)
+    pre, suf, tree = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0), S.tree_inputs(cfg, 0)
+    outs = {}
+    for precision in ("f16_score_gup", "f16_prefill"):
+        say(f"[gate|up rule] m64 ({precision})")
+        sess = Session(cfg, src.glob, src.layer, precision=precision)
+        groups = J.jev_model_f16_groups(sess.model)
+        assert bool(groups & J.JEV_F16_GATE_UP_SCORE) == (precision == "f16_score_gup")
+        sess.prefill(pre["vis"], pre["text_ids"])
+        score, norm = sess.score_tree(tree, 0)
+        outs[precision] = (sess.score_suffixes(suf).cpu(), score.cpu(), norm.cpu())
+        sess.close()
+    a, b = outs["f16_score_gup"], outs["f16_prefill"]
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert not torch.equal(a[0], b[0])

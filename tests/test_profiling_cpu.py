@@ -48,6 +48,30 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path):
     assert t == pytest.approx(s["traffic_bytes_per_launch"], rel=1e-6) and d == PR.source_digest()
 
 
+def test_traffic_of_one_launch_shape(tmp_path):
+    """With a block count, only the dispatches of that launch shape are averaged (the float16
+    SwiGLU runs 1184 blocks in a 1024-row prefill and 444 in a 378-row scoring call)."""
+    kib = PR.CALIB_BYTES / 1024
+    gemm = "void jevk::gemm_bf16w<true, true>(args)"
+    fetch = [(1, gemm, 1184, "FETCH_SIZE", 1000.0), (2, gemm, 444, "FETCH_SIZE", 300.0),
+             (3, gemm, 1184, "FETCH_SIZE", 3000.0), (4, gemm, 444, "FETCH_SIZE", 500.0),
+             (5, "at::native::vectorized_elementwise_kernel", 8, "FETCH_SIZE", 0.0),
+             (6, "__amd_rocclr_copyBuffer", 8, "FETCH_SIZE", kib / 2)]
+    write = [(1, gemm, 1184, "WRITE_SIZE", 100.0), (2, gemm, 444, "WRITE_SIZE", 30.0),
+             (3, "at::native::vectorized_elementwise_kernel", 8, "WRITE_SIZE", 0.0),
+             (4, "__amd_rocclr_copyBuffer", 8, "WRITE_SIZE", kib)]
+    write_run(tmp_path / "f", fetch)
+    write_run(tmp_path / "w", write)
+    big = PR.summarize(str(tmp_path / "f"), str(tmp_path / "w"), "gemm_bf16w<true, true>", 1184)
+    small = PR.summarize(str(tmp_path / "f"), str(tmp_path / "w"), "gemm_bf16w<true, true>", 444)
+    assert big["dispatches"] == [2, 1] and small["dispatches"] == [2, 1]
+    assert big["traffic_bytes_per_launch"] == pytest.approx(2000.0 * 1024 / 0.5 + 100.0 * 1024)
+    assert small["traffic_bytes_per_launch"] == pytest.approx(400.0 * 1024 / 0.5 + 30.0 * 1024)
+    assert "- launch shape: 444 blocks" in PR.to_markdown(small)
+    with pytest.raises(ValueError):
+        PR.summarize(str(tmp_path / "f"), str(tmp_path / "w"), "gemm_bf16w<true, true>", 999)
+
+
 def test_traffic_needs_a_calibration_copy(tmp_path):
     write_run(tmp_path / "f", [(1, "gemm_bf16w<true, true>", 8, "FETCH_SIZE", 1.0)])
     write_run(tmp_path / "w", [(1, "gemm_bf16w<true, true>", 8, "WRITE_SIZE", 1.0)])

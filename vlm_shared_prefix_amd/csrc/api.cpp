@@ -120,6 +120,7 @@ struct jev_model {
   bool f16_gu = false;     // w_gate, w_up mirrored
   // groups mirrored for prefills only (scoring calls keep their two bfloat16 terms)
   bool f16_gu_prefill = false, f16_qkv_prefill = false, f16_o_prefill = false;
+  bool f16_gu_score = false;   // gate|up on the f16 pass in prefills and suffix-scoring calls
   bool f16_down = false;   // w_down mirrored
   bool f16_qkv = false;    // wq, wk, wv mirrored
   bool f16_o = false;      // wo mirrored
@@ -212,10 +213,11 @@ size_t mirror_align(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 constexpr int32_t kAllGroups = JEV_F16_GATE_UP | JEV_F16_QKV | JEV_F16_DOWN | JEV_F16_O | JEV_F16_GATE_UP_PREFILL |
-                                JEV_F16_QKV_PREFILL | JEV_F16_O_PREFILL;
+                                JEV_F16_QKV_PREFILL | JEV_F16_O_PREFILL | JEV_F16_GATE_UP_SCORE;
 // group of matrix i of a layer (wq, wk, wv, wo, w_gate, w_up, w_down)
 static bool mirrored(int i, int32_t groups) {
-  constexpr int32_t gu = JEV_F16_GATE_UP | JEV_F16_GATE_UP_PREFILL, qkv = JEV_F16_QKV | JEV_F16_QKV_PREFILL,
+  constexpr int32_t gu = JEV_F16_GATE_UP | JEV_F16_GATE_UP_PREFILL | JEV_F16_GATE_UP_SCORE,
+                    qkv = JEV_F16_QKV | JEV_F16_QKV_PREFILL,
                     o = JEV_F16_O | JEV_F16_O_PREFILL;
   static const int32_t group_of[7] = {qkv, qkv, qkv, o, gu, gu, JEV_F16_DOWN};
   return (groups & group_of[i]) != 0;
@@ -234,7 +236,7 @@ extern "C" size_t jev_model_f16_bytes(const jev_model* m, int32_t groups) {
 // Back to the two-term bfloat16 path for every GEMM.
 static void detach_f16(jev_model* m) {
   m->f16_gu = m->f16_down = m->f16_qkv = m->f16_o = false;
-  m->f16_gu_prefill = m->f16_qkv_prefill = m->f16_o_prefill = false;
+  m->f16_gu_prefill = m->f16_qkv_prefill = m->f16_o_prefill = m->f16_gu_score = false;
   m->layers16.clear();
 }
 
@@ -284,7 +286,8 @@ extern "C" jev_status jev_model_attach_f16(jev_model* m, int32_t groups, void* b
   m->f16_qkv = (groups & JEV_F16_QKV) != 0;
   m->f16_o = (groups & JEV_F16_O) != 0;
   m->f16_down = (groups & JEV_F16_DOWN) != 0;
-  m->f16_gu_prefill = !m->f16_gu && (groups & JEV_F16_GATE_UP_PREFILL) != 0;
+  m->f16_gu_score = !m->f16_gu && (groups & JEV_F16_GATE_UP_SCORE) != 0;
+  m->f16_gu_prefill = !m->f16_gu && !m->f16_gu_score && (groups & JEV_F16_GATE_UP_PREFILL) != 0;
   m->f16_qkv_prefill = !m->f16_qkv && (groups & JEV_F16_QKV_PREFILL) != 0;
   m->f16_o_prefill = !m->f16_o && (groups & JEV_F16_O_PREFILL) != 0;
   return JEV_OK;
@@ -294,6 +297,7 @@ extern "C" int32_t jev_model_f16_groups(const jev_model* m) {
   if (!m) return 0;
   return (m->f16_gu ? JEV_F16_GATE_UP : 0) | (m->f16_qkv ? JEV_F16_QKV : 0) | (m->f16_down ? JEV_F16_DOWN : 0) |
          (m->f16_o ? JEV_F16_O : 0) | (m->f16_gu_prefill ? JEV_F16_GATE_UP_PREFILL : 0) |
+         (m->f16_gu_score ? JEV_F16_GATE_UP_SCORE : 0) |
          (m->f16_qkv_prefill ? JEV_F16_QKV_PREFILL : 0) | (m->f16_o_prefill ? JEV_F16_O_PREFILL : 0);
 }
 
@@ -654,7 +658,8 @@ struct Forward {
     // every query's scores, and their rounding error grows with the keys a query sees
     const bool fq = m->f16_qkv || (m->f16_qkv_prefill && pre && seg_max <= kF16QkvPrefillKeys);
     const bool fo = m->f16_o || (m->f16_o_prefill && pre);
-    const bool fd = m->f16_down, fg = m->f16_gu || (m->f16_gu_prefill && pre);
+    const bool fd = m->f16_down,
+               fg = m->f16_gu || (m->f16_gu_prefill && pre) || (m->f16_gu_score && mode != Mode::Tree);
     uint16_t* a_hi = at<uint16_t>(ws, L.act);                 // normalised activations / attention output
     uint16_t* a_lo = a_hi + (size_t)T * wide;
     const AOp A_qkv{nullptr, a_hi, a_lo, fq};

@@ -12,7 +12,9 @@ target kernel's reading:
 averaged over the target kernel's dispatches.  ``source_digest()`` fingerprints
 the kernel sources, so a stored figure can be dropped once they change.
 
-    python -m vlm_shared_prefix_amd.profiling <fetch_dir> <write_dir> <kernel-substring> [out.md]
+    python -m vlm_shared_prefix_amd.profiling <fetch_dir> <write_dir> <kernel-substring> [out.md [blocks]]
+
+(blocks: only the dispatches of that many workgroups, one launch shape of the kernel)
     python -m vlm_shared_prefix_amd.profiling --stats <kernel_trace_dir> [out.md]
     python -m vlm_shared_prefix_amd.profiling --mfma <MfmaUtil/MfmaFlops counter dir> [out.md]
 """
@@ -21,6 +23,7 @@ import glob
 import hashlib
 import os
 import sys
+from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CALIB_BYTES = 512 << 20          # bytes moved by the calibration copy (read once, written once)
@@ -37,8 +40,9 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _counter_rows(run_dir: str, counter: str):
-    """[(dispatch id, kernel name, value)] of one counter, in dispatch order."""
+def _counter_rows(run_dir: str, counter: str, with_blocks: bool = False):
+    """[(dispatch id, kernel name, value)] of one counter, in dispatch order (with_blocks: each
+    row also carries the dispatch's workgroup count)."""
     paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not paths:
         raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
@@ -47,14 +51,21 @@ def _counter_rows(run_dir: str, counter: str):
         with open(p) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+                    row = (int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                    if with_blocks:
+                        row += (int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])),)
+                    out.append(row)
     return sorted(out)
 
 
-def per_dispatch(run_dir: str, counter: str, substring: str):
-    vals = [v for _, name, v in _counter_rows(run_dir, counter) if substring in name]
+def per_dispatch(run_dir: str, counter: str, substring: str, blocks: Optional[int] = None):
+    """Mean counter value over the dispatches of kernels containing `substring` (of `blocks`
+    workgroups only, when given: one launch shape) and their count."""
+    vals = [r[2] for r in _counter_rows(run_dir, counter, with_blocks=True)
+            if substring in r[1] and (blocks is None or r[3] == blocks)]
     if not vals:
-        raise ValueError(f"no dispatch of a kernel containing {substring!r} with {counter}")
+        raise ValueError(f"no dispatch of a kernel containing {substring!r} with {counter}"
+                         + (f" and {blocks} blocks" if blocks is not None else ""))
     return sum(vals) / len(vals), len(vals)
 
 
@@ -71,15 +82,15 @@ def calibration_dispatch(run_dir: str, counter: str):
     return sum(vals) / len(vals), len(vals)
 
 
-def summarize(fetch_dir: str, write_dir: str, kernel: str) -> dict:
+def summarize(fetch_dir: str, write_dir: str, kernel: str, blocks: Optional[int] = None) -> dict:
     f_copy, _ = calibration_dispatch(fetch_dir, "FETCH_SIZE")
     w_copy, _ = calibration_dispatch(write_dir, "WRITE_SIZE")
-    f_k, n_f = per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
-    w_k, n_w = per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    f_k, n_f = per_dispatch(fetch_dir, "FETCH_SIZE", kernel, blocks)
+    w_k, n_w = per_dispatch(write_dir, "WRITE_SIZE", kernel, blocks)
     fetch_scale = f_copy * 1024.0 / CALIB_BYTES
     write_scale = w_copy * 1024.0 / CALIB_BYTES
     traffic = f_k * 1024.0 / fetch_scale + w_k * 1024.0 / write_scale
-    return {"kernel": kernel, "dispatches": [n_f, n_w], "fetch_kib": f_k, "write_kib": w_k,
+    return {"kernel": kernel, "blocks": blocks, "dispatches": [n_f, n_w], "fetch_kib": f_k, "write_kib": w_k,
             "copy_fetch_kib": f_copy, "copy_write_kib": w_copy, "fetch_scale": fetch_scale,
             "write_scale": write_scale, "traffic_bytes_per_launch": traffic, "source_digest": source_digest()}
 
@@ -89,6 +100,7 @@ def to_markdown(s: dict, command: str = "") -> str:
     if command:
         lines += ["Commands (one counter per run):", "", "```", command, "```", ""]
     lines += [
+        f"- launch shape: {s['blocks']} blocks" if s.get("blocks") else "- launch shape: every dispatch of the kernel",
         f"- dispatches averaged: {s['dispatches'][0]} (FETCH_SIZE run), {s['dispatches'][1]} (WRITE_SIZE run)",
         f"- kernel FETCH_SIZE: {s['fetch_kib']:.1f} KiB/dispatch, WRITE_SIZE: {s['write_kib']:.1f} KiB/dispatch",
         f"- calibration copy of {CALIB_BYTES >> 20} MiB: FETCH_SIZE {s['copy_fetch_kib']:.1f} KiB, "
@@ -273,7 +285,8 @@ if __name__ == "__main__":
     if len(sys.argv) < 4:
         print(__doc__)
         sys.exit(2)
-    s = summarize(sys.argv[1], sys.argv[2], sys.argv[3])
+    # FETCH_DIR WRITE_DIR KERNEL [OUT.md [BLOCKS]]
+    s = summarize(sys.argv[1], sys.argv[2], sys.argv[3], int(sys.argv[5]) if len(sys.argv) > 5 else None)
     md = to_markdown(s, os.environ.get("JEV_PMC_COMMAND", ""))
     if len(sys.argv) > 4:
         with open(sys.argv[4], "w") as f:

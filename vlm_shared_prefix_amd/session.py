@@ -36,10 +36,11 @@ PRECISIONS = {"split": 0, "f16_gu": J.JEV_F16_GATE_UP, "f16_down": J.JEV_F16_DOW
               "f16_mlp": J.JEV_F16_GATE_UP | J.JEV_F16_DOWN,
               "f16_down_gup": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL,
               "f16_prefill": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL | J.JEV_F16_O_PREFILL,
+              "f16_score_gup": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_SCORE | J.JEV_F16_QKV_PREFILL | J.JEV_F16_O_PREFILL,
               "f16_down_gup_o": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_O_PREFILL,
               "f16_down_gup_qkv": J.JEV_F16_DOWN | J.JEV_F16_GATE_UP_PREFILL | J.JEV_F16_QKV_PREFILL,
               "f16": J.JEV_F16_GATE_UP | J.JEV_F16_QKV | J.JEV_F16_DOWN | J.JEV_F16_O}
-DEFAULT_PRECISION = "f16_prefill"
+DEFAULT_PRECISION = "f16_score_gup"
 
 
 class Session:
@@ -52,7 +53,9 @@ class Session:
         "f16_down_gup" runs the down projection on one float16 pass everywhere and gate|up on
         one float16 pass in prefills only (scoring calls keep its two terms); "f16_down_gup_o"
         also runs o on one float16 pass in prefills; "f16_prefill" (the default) every prefill
-        GEMM, q|k|v only for prefixes of at most 2048 rows (the library's rule)."""
+        GEMM, q|k|v only for prefixes of at most 2048 rows (the library's rule); "f16_score_gup"
+        as "f16_prefill" with gate|up on one float16 pass in suffix-scoring calls too (tree calls
+        keep its two terms)."""
         if precision not in PRECISIONS:
             raise ValueError(f"precision must be one of {PRECISIONS}, not {precision!r}")
         self.cfg = cfg
