@@ -90,19 +90,21 @@ def test_reattach_and_failed_attach():
     sess.close()
 
 
-@pytest.mark.parametrize("terms", [1, 2])
-def test_attn_q_terms_vs_oracle(terms):
-    """Both q forms of the attention meet the bar on a live configuration."""
+@pytest.mark.parametrize("name,terms", [("m7l", 1), ("m7l", 2), ("mb", 1)])
+def test_attn_q_terms_vs_oracle(name, terms):
+    """Both q forms of the attention meet the bar on live configurations (mb with one term:
+    the balanced schedule's one-term kernel, which its 2560-key prefix would otherwise run
+    with two)."""
     from vlm_shared_prefix_amd import jev as J
-    cfg = S.CONFIGS["m7l"]
-    say(f"[q terms] m7l seed 0, {terms} term(s)")
+    cfg = S.CONFIGS[name]
+    say(f"[q terms] {name} seed 0, {terms} term(s)")
     sess, src = gpu_session(cfg, 0)
     J.jev_model_set_attn_q_terms(sess.model, terms)
     pre, suf = S.prefix_inputs(cfg, 0), S.suffix_inputs(cfg, 0)
     ref = O.score_suffixes(src, cfg, pre, suf)
     sess.prefill(pre["vis"], pre["text_ids"])
     got = sess.score_suffixes(suf).cpu().numpy()
-    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"m7l q terms {terms}")
+    check_suffix_out(got, ref, suf["n_cands"], cfg.dtype, f"{name} q terms {terms}")
     sess.close()
 
 
