@@ -188,12 +188,16 @@ __device__ __forceinline__ const u16* seg_row(const GemmSegs& s, int n, int K) {
   return s.w[2] + (size_t)(n - s.n_end[1]) * K;
 }
 
+// F16: the activation is one float16 plane (Ah; Al unused) against the float16 mirror of
+// the weights, one f16 MFMA pass (the products whose few output columns would make the
+// 128 x 256 kernel split K many ways).
+template <bool F16>
 __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah, const u16* __restrict__ Al,
                                                      int lda, int M, int K, GemmSegs seg, int N, int m_tiles,
                                                      int n_tiles, int splits, int k_chunk, float* __restrict__ C,
                                                      int ldc, size_t split_stride, int accum) {
   __shared__ __attribute__((aligned(16))) u16 sAh[GBM * GLD];
-  __shared__ __attribute__((aligned(16))) u16 sAl[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) u16 sAl[F16 ? 8 : GBM * GLD];
   __shared__ __attribute__((aligned(16))) u16 sW[GBN * GLD];
 
   const int nb = m_tiles * n_tiles * splits;
@@ -229,7 +233,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
       const int gm = (m0 + row < M) ? m0 + row : 0;
       const size_t off = (size_t)gm * lda + k0 + c8 * 8;
       rh[i] = *reinterpret_cast<const uint4*>(Ah + off);
-      rl[i] = *reinterpret_cast<const uint4*>(Al + off);
+      if (!F16) rl[i] = *reinterpret_cast<const uint4*>(Al + off);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -250,8 +254,9 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
       const uint32_t mw = okw ? 0xFFFFFFFFu : 0u;
       *reinterpret_cast<uint4*>(&sAh[row * GLD + c8 * 8]) =
           make_uint4(rh[i].x & ma, rh[i].y & ma, rh[i].z & ma, rh[i].w & ma);
-      *reinterpret_cast<uint4*>(&sAl[row * GLD + c8 * 8]) =
-          make_uint4(rl[i].x & ma, rl[i].y & ma, rl[i].z & ma, rl[i].w & ma);
+      if (!F16)
+        *reinterpret_cast<uint4*>(&sAl[row * GLD + c8 * 8]) =
+            make_uint4(rl[i].x & ma, rl[i].y & ma, rl[i].z & ma, rl[i].w & ma);
       *reinterpret_cast<uint4*>(&sW[row * GLD + c8 * 8]) =
           make_uint4(rw[i].x & mw, rw[i].y & mw, rw[i].z & mw, rw[i].w & mw);
     }
@@ -275,25 +280,44 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16s(const u16* __restrict__ Ah,
       if (wave_active) {
 #pragma unroll
         for (int kk = 0; kk < GBK / 16; ++kk) {
-          bf16x8 ah[2], al[2], bw[2];
+          if constexpr (F16) {
+            f16x8 ah[2], bw[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int r = wm * 64 + i * 32 + ql;
-            ah[i] = *reinterpret_cast<const bf16x8*>(&sAh[r * GLD + kk * 16 + hl * 8]);
-            al[i] = *reinterpret_cast<const bf16x8*>(&sAl[r * GLD + kk * 16 + hl * 8]);
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int c = wn * 64 + j * 32 + ql;
-            bw[j] = *reinterpret_cast<const bf16x8*>(&sW[c * GLD + kk * 16 + hl * 8]);
-          }
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+              const int r = wm * 64 + i * 32 + ql;
+              ah[i] = *reinterpret_cast<const f16x8*>(&sAh[r * GLD + kk * 16 + hl * 8]);
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+              const int c = wn * 64 + j * 32 + ql;
+              bw[j] = *reinterpret_cast<const f16x8*>(&sW[c * GLD + kk * 16 + hl * 8]);
             }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          } else {
+            bf16x8 ah[2], al[2], bw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int r = wm * 64 + i * 32 + ql;
+              ah[i] = *reinterpret_cast<const bf16x8*>(&sAh[r * GLD + kk * 16 + hl * 8]);
+              al[i] = *reinterpret_cast<const bf16x8*>(&sAl[r * GLD + kk * 16 + hl * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int c = wn * 64 + j * 32 + ql;
+              bw[j] = *reinterpret_cast<const bf16x8*>(&sW[c * GLD + kk * 16 + hl * 8]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+              }
+          }
         }
       }
       __syncthreads();
@@ -2148,8 +2172,8 @@ hipError_t launch_gemm_bf16(const uint16_t* Ah, const uint16_t* Al, int lda, int
     gemm_bf16w<false, false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
                                            (size_t)M * N, acc, nullptr, nullptr, nullptr);
   else
-    gemm_bf16s<<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo, (size_t)M * N,
-                                    acc);
+    gemm_bf16s<false><<<grid, 256, 0, s>>>(Ah, Al, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+                                           (size_t)M * N, acc);
   return hipGetLastError();
 }
 
@@ -2172,8 +2196,8 @@ hipError_t launch_gemm_swiglu(const uint16_t* Ah, const uint16_t* Al, int lda, i
 }
 
 // Single-pass float16 GEMMs: the activation as one float16 plane, W the float16 mirror.
-// Always the 128 x 256 kernel; K splits bring the grid to about 448 blocks (1.75 per CU),
-// at most 16, each >= 256 of K (measured on the 7B / 2B projection shapes, split-K
+// The 128 x 256 kernel as a rule; K splits bring the grid to about 448 blocks (1.75 per
+// CU), at most 16, each >= 256 of K (measured on the 7B / 2B projection shapes, split-K
 // consumer included).
 GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap) {
   GemmPlan p{};
@@ -2183,6 +2207,20 @@ GemmPlan gemm_f16_plan(int M, int N, int K, size_t part_cap) {
   // one row tile (few rows: streaming the weights bounds it) may split K up to 32 ways
   sp = std::min<long>(sp, std::min(M <= G2M ? 32 : 16, std::max(1, K / 256)));
   p.splits = (int)std::max<long>(1, sp);
+  // The 128 x 128 kernel instead (gemm_bf16s<true>) when the wide tiles leave the chip
+  // under-filled even with their splits (fewer than 256 blocks: the 2B scoring call's down
+  // projection of 129 rows, 192 -> 456 blocks), or split a short K (<= 4608) four or more
+  // ways, where writing and summing the partials costs more than the wider tile saves (the
+  // 1024-row o projection: 54.4 -> 46.9 us).  Three splits stay wide (the 1024-row q|k|v ran
+  // 13% slower on unsplit narrow tiles), as do long K (the 1024-row down projection).
+  if (M > G2M && K % GBK == 0 && (t * p.splits < 256 || (p.splits >= 4 && K <= 4608))) {
+    const long tn = (long)cdiv(M, GBM) * cdiv(N, GBN);
+    long sn = (448 + tn / 2) / tn;
+    sn = std::min<long>(sn, std::max(1L, 512 / tn));
+    sn = std::min<long>(sn, std::max(1, K / 256));
+    p.wide = false;
+    p.splits = (int)std::max<long>(1, sn);
+  }
   while (p.splits > 1 && (size_t)p.splits * M * N > part_cap) --p.splits;
   return p;
 }
@@ -2194,16 +2232,21 @@ hipError_t launch_gemm_f16(const uint16_t* A, int lda, int M, int K, const GemmS
   if (K % G2K) return hipErrorInvalidValue;
   if (use_skinny(M, K)) return launch_skinny(true, A, nullptr, lda, M, K, seg, N, C, ldc, accum, part_cap, part, s, eff_splits);
   const GemmPlan pl = gemm_f16_plan(M, N, K, part_cap);
-  const int mt = cdiv(M, G2M), nt = cdiv(N, G2N);
-  const int k_chunk = cdiv(cdiv(K, pl.splits), G2K) * G2K;
+  const int bk = pl.wide ? G2K : GBK;
+  const int mt = cdiv(M, pl.wide ? G2M : GBM), nt = cdiv(N, pl.wide ? G2N : GBN);
+  const int k_chunk = cdiv(cdiv(K, pl.splits), bk) * bk;
   const int splits = cdiv(K, k_chunk);
   *eff_splits = splits;
   const int grid = cdiv(mt * nt * splits, 8) * 8;
   float* out = splits == 1 ? C : part;
   const int ldo = splits == 1 ? ldc : N;
   const int acc = splits == 1 ? accum : 0;
-  gemm_bf16w<false, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
-                                               (size_t)M * N, acc, nullptr, nullptr, nullptr);
+  if (pl.wide)
+    gemm_bf16w<false, true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+                                                 (size_t)M * N, acc, nullptr, nullptr, nullptr);
+  else
+    gemm_bf16s<true><<<grid, 256, 0, s>>>(A, nullptr, lda, M, K, seg, N, mt, nt, splits, k_chunk, out, ldo,
+                                          (size_t)M * N, acc);
   return hipGetLastError();
 }
 
