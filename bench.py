@@ -101,6 +101,27 @@ def roofline(kind, d, traffic_md=None):
             "launches": n}
 
 
+def step_rooflines(prof_step, prof_prefill, prof_score, cfg):
+    """(roofline, score_call_roofline) of a step's profiles (kind -> launches, ms, flops, bytes).
+
+    The step's entry is the kind with the most time in the step.  When the prefill and the
+    scoring call both launch it (the float16 SwiGLU), it is taken over the prefill's launches
+    alone, one launch shape, with its traffic from {kind}_traffic.md; the scoring call's own
+    dominant kind gets the second entry, with its traffic from {kind}_score_traffic.md.
+    """
+    roof = score_roof = None
+    if prof_step:
+        dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
+        roof = roofline(dom, prof_prefill[dom] if dom in prof_prefill else prof_step[dom])
+        if dom in prof_prefill:
+            roof["launches_of"] = f"prefill ({cfg.prefix_len} rows)"
+    if prof_score:
+        dom_s = max(prof_score, key=lambda k: prof_score[k]["ms"])
+        score_roof = roofline(dom_s, prof_score[dom_s], f"{dom_s}_score_traffic.md")
+        score_roof["launches_of"] = f"scoring call ({cfg.n_suffix} suffixes)"
+    return roof, score_roof
+
+
 def attention_entry(prof, prefix_kv_bytes, what):
     """MFMA utilisation of the attention launches of one call kind (+ its split merge)."""
     at = prof.get("attn_fwd")
@@ -751,21 +772,7 @@ def main():
     for _ in range(args.profile_steps):
         prefill_only()
     prof_prefill = J.jev_profile_stop(sess.model)
-    roof = None
-    if prof_step:
-        # the kind with the most time in the step; when the prefill and the scoring call both
-        # launch it (the float16 SwiGLU), its roofline is taken over the prefill's launches
-        # alone, one launch shape (the scoring call's shape has its own entry below)
-        dom = max(prof_step, key=lambda k: prof_step[k]["ms"])
-        roof = roofline(dom, prof_prefill[dom] if dom in prof_prefill else prof_step[dom])
-        if dom in prof_prefill:
-            roof["launches_of"] = f"prefill ({cfg.prefix_len} rows)"
-    # the scoring call's own dominant kernel (the prefill's dominates the whole step)
-    score_roof = None
-    if prof_score:
-        dom_s = max(prof_score, key=lambda k: prof_score[k]["ms"])
-        score_roof = roofline(dom_s, prof_score[dom_s], f"{dom_s}_score_traffic.md")
-        score_roof["launches_of"] = f"scoring call ({cfg.n_suffix} suffixes)"
+    roof, score_roof = step_rooflines(prof_step, prof_prefill, prof_score, cfg)
     attn = {"score_call": attention_entry(prof_score, cfg.prefix_len * cfg.n_kv_heads * cfg.head_dim * 4,
                                           f"shared prefix ({cfg.prefix_len} keys) + own rows of the "
                                           f"{cfg.n_suffix} suffixes"),
