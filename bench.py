@@ -595,9 +595,27 @@ def cpu_crosscheck(name, seed):
     t = time.perf_counter()
     for l in range(cfg.n_layers):
         S.WeightSource(cfg, seed, cache_layers=False).layer(l)
+        log(f"crosscheck {name}: drew layer {l + 1} of {cfg.n_layers} alone")
     draw = time.perf_counter() - t
+
+    class _Reporting:
+        """The weight source, reporting each layer the oracle reaches."""
+        def __init__(self, src):
+            self.src = src
+
+        @property
+        def glob(self):
+            return self.src.glob
+
+        def layer(self, l):
+            log(f"crosscheck {name}: oracle at layer {l + 1} of {cfg.n_layers}")
+            return self.src.layer(l)
+
+        def drop_layer(self, l):
+            self.src.drop_layer(l)
+
     t = time.perf_counter()
-    O.score_suffixes(ws, cfg, pre, suf, free_layers=True)
+    O.score_suffixes(_Reporting(ws), cfg, pre, suf, free_layers=True)
     full = time.perf_counter() - t - draw
     n_c = int(np.sum(suf["n_cands"]))
     print(json.dumps({"config": name, "host": host_info(), "full_seconds": round(full, 2),
